@@ -1,0 +1,165 @@
+"""fp64 CPU oracle for causal multi-head self-attention (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg of
+the benchmark may import this package; the product library never does.  It
+shares no code with the HIP path (see ``oracle.c`` for the definition it
+implements and the passages it follows).
+
+All functions take and return float64 NumPy arrays in the [B, H, T, D] layout
+(lse and delta are [B, H, T]).  ``scale`` is widened from the float32 value the
+GPU receives, so both sides compute the same function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_libs: dict = {}
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2 (no fast-math) with OpenMP: the one way the oracle is built."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", src, "-o", tmp, "-lm"],
+                   check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    lib.oracle_attn_fwd.argtypes = [_dp] * 5 + [_i64] * 4 + [ctypes.c_double, _i64]
+    lib.oracle_attn_fwd.restype = None
+    lib.oracle_attn_bwd.argtypes = [_dp] * 8 + [_i64] * 4 + [ctypes.c_double, _i64]
+    lib.oracle_attn_bwd.restype = None
+    lib.oracle_sublayer_fwd.argtypes = [_dp] * 8 + [_i64] * 4 + [ctypes.c_double, _i64]
+    lib.oracle_sublayer_fwd.restype = ctypes.c_int
+    lib.oracle_sublayer_bwd.argtypes = [_dp] * 15 + [_i64] * 4 + [ctypes.c_double, _i64]
+    lib.oracle_sublayer_bwd.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+_override: list = []
+
+
+class use_library:
+    """Context manager: route every call to another build of the oracle source
+    (the planted-mistake tests use it to show that the pins catch slips)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        _override.append(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        _override.pop()
+        return False
+
+
+def _load(path: str | None = None):
+    """The compiled oracle (built on first use).  ``path`` selects another
+    build of the same source, e.g. a copy with a planted mistake in a test."""
+    if path is None and _override:
+        path = _override[-1]
+    if path is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        path = _LIB
+    if path not in _libs:
+        _libs[path] = _bind(path)
+    return _libs[path]
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # a torch tensor
+        a = a.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def widen_scale(scale: float) -> float:
+    """The float32 value the GPU receives, widened exactly to float64."""
+    return float(np.float32(scale))
+
+
+def attn_fwd(q, k, v, scale: float, nthreads: int = 0, lib: str | None = None):
+    """Returns (o [B,H,T,D], lse [B,H,T]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    _load(lib).oracle_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, T, D,
+                            float(scale), int(nthreads))
+    return o, lse
+
+
+def attn_bwd(q, k, v, dO, scale: float, nthreads: int = 0, lib: str | None = None):
+    """Returns (dq, dk, dv, delta) in float64 for the upstream gradient dO."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, H, T, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and dO.shape == q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    delta = np.empty((B, H, T), dtype=np.float64)
+    _load(lib).oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dO), _p(dq), _p(dk), _p(dv),
+                            _p(delta), B, H, T, D, float(scale), int(nthreads))
+    return dq, dk, dv, delta
+
+
+def sublayer_fwd(x, g, bl, Wa, ba, Wp, bp, n_head: int, eps: float = 1e-5,
+                 nthreads: int = 0, lib: str | None = None):
+    """Pre-norm attention sublayer forward.  x: [B,T,C]; Wa: [C,3C]; Wp: [C,C]."""
+    x, g, bl, Wa, ba, Wp, bp = map(_f64, (x, g, bl, Wa, ba, Wp, bp))
+    B, T, C = x.shape
+    y = np.empty_like(x)
+    rc = _load(lib).oracle_sublayer_fwd(_p(x), _p(g), _p(bl), _p(Wa), _p(ba), _p(Wp), _p(bp),
+                                     _p(y), B, T, C, int(n_head), float(eps), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_sublayer_fwd failed ({rc})")
+    return y
+
+
+def sublayer_bwd(x, g, bl, Wa, ba, Wp, bp, dy, n_head: int, eps: float = 1e-5,
+                 nthreads: int = 0, lib: str | None = None):
+    """Gradients of sum(dy * y): returns dict dx, dg, dbl, dWa, dba, dWp, dbp."""
+    x, g, bl, Wa, ba, Wp, bp, dy = map(_f64, (x, g, bl, Wa, ba, Wp, bp, dy))
+    B, T, C = x.shape
+    out = {
+        "dx": np.empty_like(x), "dg": np.empty_like(g), "dbl": np.empty_like(bl),
+        "dWa": np.empty_like(Wa), "dba": np.empty_like(ba), "dWp": np.empty_like(Wp),
+        "dbp": np.empty_like(bp),
+    }
+    rc = _load(lib).oracle_sublayer_bwd(
+        _p(x), _p(g), _p(bl), _p(Wa), _p(ba), _p(Wp), _p(bp), _p(dy),
+        _p(out["dx"]), _p(out["dg"]), _p(out["dbl"]), _p(out["dWa"]), _p(out["dba"]),
+        _p(out["dWp"]), _p(out["dbp"]), B, T, C, int(n_head), float(eps), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_sublayer_bwd failed ({rc})")
+    return out

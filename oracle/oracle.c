@@ -1,0 +1,418 @@
+/*
+ * oracle.c -- fp64 CPU oracle for causal scaled dot-product multi-head
+ * self-attention (forward and backward) and for the pre-norm attention
+ * sublayer around it.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+ * definition that the HIP kernels are checked against.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it.  It
+ * shares no code, header, table or constant with the GPU library, and it
+ * includes nothing from it.
+ *
+ * Everything is double precision, naive loops, in the order the definition
+ * is written.  OpenMP only splits independent (batch, head) pairs or
+ * independent rows across threads; no loop is blocked, fused or reordered.
+ *
+ * Sources (the pages this follows):
+ *  - "LLM from scratch" CS336 tutorial (lmnt.cn), section 5.1 model.py,
+ *    class CausalSelfAttention.forward: scores are q times k-transpose
+ *    multiplied by 1/sqrt(head dim); entries where the lower-triangular
+ *    ones-matrix is zero are filled with -inf; softmax over the last axis;
+ *    the weights multiply v.  Section 3.3 of the same page: -inf on the upper
+ *    triangle so that those weights become 0 after the softmax.
+ *  - "Train Your Own LLM from Scratch" (fishgap), section 1: the causal mask
+ *    is tril(ones(block_size, block_size)), so the diagonal is kept (j <= i).
+ *  - Backward: the pages only run loss.backward() through this op (CS336
+ *    tutorial, section 5.2 train.py).  The gradient is therefore the exact
+ *    derivative of the forward above; the formulas below are the softmax
+ *    chain rule, written out, and are pinned by finite differences in the
+ *    tests, not by any printed formula.
+ *  - Sublayer: CS336 tutorial section 5.1, class LayerNorm (biased variance,
+ *    eps added under the square root), class Block.forward (x + attn(ln_1(x))),
+ *    CausalSelfAttention (c_attn, chunk into q,k,v, view per head, c_proj).
+ *
+ * Layout: q, k, v, o, dO, dq, dk, dv are contiguous [B][H][T][D];
+ * lse and delta are [B][H][T].  lse is the natural-log log-sum-exp of the
+ * scaled scores of each row (a reading: the pages never define it).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static void set_threads(int64_t nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads((int)nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* One row of the causal softmax: p[j] for j = 0..i, from scores s[j].
+ * Returns m (the row max) and writes Z (the normaliser) so that
+ * lse = m + log(Z).  Keys j > i are masked (-inf) and carry weight exactly 0,
+ * so they are simply not part of the sum. */
+static void causal_softmax_row(const double* Qi, const double* K, int64_t i,
+                               int64_t D, double scale, double* s, double* p,
+                               double* m_out, double* Z_out)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= i; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += Qi[d] * K[j * D + d];
+        s[j] = scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    double Z = 0.0;
+    for (int64_t j = 0; j <= i; ++j) Z += exp(s[j] - m);
+    for (int64_t j = 0; j <= i; ++j) p[j] = exp(s[j] - m) / Z;
+    *m_out = m;
+    *Z_out = Z;
+}
+
+/* Forward: o = softmax(mask(scale * q k^T)) v, lse = log sum exp of the row. */
+void oracle_attn_fwd(const double* q, const double* k, const double* v,
+                     double* o, double* lse, int64_t B, int64_t H, int64_t T,
+                     int64_t D, double scale, int64_t nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double* Q = q + bh * T * D;
+        const double* K = k + bh * T * D;
+        const double* V = v + bh * T * D;
+        double* O = o + bh * T * D;
+        double* L = lse + bh * T;
+        double* s = (double*)malloc((size_t)T * sizeof(double));
+        double* p = (double*)malloc((size_t)T * sizeof(double));
+        for (int64_t i = 0; i < T; ++i) {
+            double m, Z;
+            causal_softmax_row(Q + i * D, K, i, D, scale, s, p, &m, &Z);
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int64_t j = 0; j <= i; ++j) acc += p[j] * V[j * D + d];
+                O[i * D + d] = acc;
+            }
+            L[i] = m + log(Z);
+        }
+        free(s);
+        free(p);
+    }
+}
+
+/* Backward of L = sum(dO * O) through the forward above.
+ *   dP_ij = dO_i . v_j               (j <= i)
+ *   Delta_i = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - Delta_i)   (softmax Jacobian)
+ *   dq_i  = scale sum_{j<=i} dS_ij k_j
+ *   dk_j  = scale sum_{i>=j} dS_ij q_i
+ *   dv_j  =       sum_{i>=j} P_ij dO_i
+ * delta receives Delta (row-wise). */
+void oracle_attn_bwd(const double* q, const double* k, const double* v,
+                     const double* dO, double* dq, double* dk, double* dv,
+                     double* delta, int64_t B, int64_t H, int64_t T, int64_t D,
+                     double scale, int64_t nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double* Q = q + bh * T * D;
+        const double* K = k + bh * T * D;
+        const double* V = v + bh * T * D;
+        const double* G = dO + bh * T * D;
+        double* dQ = dq + bh * T * D;
+        double* dK = dk + bh * T * D;
+        double* dV = dv + bh * T * D;
+        double* Dl = delta + bh * T;
+        double* s = (double*)malloc((size_t)T * sizeof(double));
+        double* p = (double*)malloc((size_t)T * sizeof(double));
+        double* dp = (double*)malloc((size_t)T * sizeof(double));
+        memset(dK, 0, (size_t)(T * D) * sizeof(double));
+        memset(dV, 0, (size_t)(T * D) * sizeof(double));
+        for (int64_t i = 0; i < T; ++i) {
+            double m, Z;
+            causal_softmax_row(Q + i * D, K, i, D, scale, s, p, &m, &Z);
+            double Delta = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double acc = 0.0;
+                for (int64_t d = 0; d < D; ++d) acc += G[i * D + d] * V[j * D + d];
+                dp[j] = acc;
+                Delta += p[j] * dp[j];
+            }
+            Dl[i] = Delta;
+            for (int64_t d = 0; d < D; ++d) dQ[i * D + d] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double dS = p[j] * (dp[j] - Delta);
+                for (int64_t d = 0; d < D; ++d) {
+                    dQ[i * D + d] += scale * dS * K[j * D + d];
+                    dK[j * D + d] += scale * dS * Q[i * D + d];
+                    dV[j * D + d] += p[j] * G[i * D + d];
+                }
+            }
+        }
+        free(s);
+        free(p);
+        free(dp);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pre-norm attention sublayer:  y = x + c_proj(attn(split(c_attn(LN(x)))))  */
+/* x, y, dx, dy: [N = B*T][C].  LN weight g[C], bias bl[C].                   */
+/* Wa[C][3C], ba[3C] (qkv = u Wa + ba, columns [q | k | v]), Wp[C][C], bp[C]. */
+/* Head h of q (and of k, v) is columns h*D .. h*D+D-1 of that third.         */
+/* ------------------------------------------------------------------------ */
+
+static void layer_norm_fwd(const double* x, const double* g, const double* bl,
+                           double* u, double* xhat, double* rstd, int64_t N,
+                           int64_t C, double eps)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double mean = 0.0;
+        for (int64_t c = 0; c < C; ++c) mean += x[n * C + c];
+        mean /= (double)C;
+        double var = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            double t = x[n * C + c] - mean;
+            var += t * t;
+        }
+        var /= (double)C; /* biased variance */
+        double r = 1.0 / sqrt(var + eps);
+        rstd[n] = r;
+        for (int64_t c = 0; c < C; ++c) {
+            xhat[n * C + c] = (x[n * C + c] - mean) * r;
+            u[n * C + c] = xhat[n * C + c] * g[c] + bl[c];
+        }
+    }
+}
+
+/* out[N][M] = a[N][Kd] * w[Kd][M] + bias[M] */
+static void linear_fwd(const double* a, const double* w, const double* bias,
+                       double* out, int64_t N, int64_t Kd, int64_t M)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < M; ++j) out[n * M + j] = bias[j];
+        for (int64_t c = 0; c < Kd; ++c) {
+            double av = a[n * Kd + c];
+            for (int64_t j = 0; j < M; ++j) out[n * M + j] += av * w[c * M + j];
+        }
+    }
+}
+
+/* [N][3C] columns of one third -> [B][H][T][D] */
+static void split_heads(const double* qkv, int64_t third, double* dst,
+                        int64_t B, int64_t T, int64_t H, int64_t D)
+{
+    int64_t C = H * D;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t d = 0; d < D; ++d)
+                    dst[((b * H + h) * T + t) * D + d] =
+                        qkv[(b * T + t) * 3 * C + third * C + h * D + d];
+}
+
+/* [B][H][T][D] -> [N][C] (head merge), optionally into one third of [N][3C] */
+static void merge_heads(const double* src, double* dst, int64_t stride,
+                        int64_t offset, int64_t B, int64_t T, int64_t H,
+                        int64_t D)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t d = 0; d < D; ++d)
+                    dst[(b * T + t) * stride + offset + h * D + d] =
+                        src[((b * H + h) * T + t) * D + d];
+}
+
+typedef struct {
+    double *u, *xhat, *rstd, *qkv, *q, *k, *v, *o, *lse, *a;
+} sublayer_cache;
+
+static void sublayer_forward_cached(const double* x, const double* g,
+                                    const double* bl, const double* Wa,
+                                    const double* ba, const double* Wp,
+                                    const double* bp, double* y, int64_t B,
+                                    int64_t T, int64_t C, int64_t H, double eps,
+                                    sublayer_cache* S)
+{
+    int64_t N = B * T, D = C / H;
+    double scale = 1.0 / sqrt((double)D);
+    layer_norm_fwd(x, g, bl, S->u, S->xhat, S->rstd, N, C, eps);
+    linear_fwd(S->u, Wa, ba, S->qkv, N, C, 3 * C);
+    split_heads(S->qkv, 0, S->q, B, T, H, D);
+    split_heads(S->qkv, 1, S->k, B, T, H, D);
+    split_heads(S->qkv, 2, S->v, B, T, H, D);
+    oracle_attn_fwd(S->q, S->k, S->v, S->o, S->lse, B, H, T, D, scale, 0);
+    merge_heads(S->o, S->a, C, 0, B, T, H, D);
+    linear_fwd(S->a, Wp, bp, y, N, C, C);
+    for (int64_t n = 0; n < N * C; ++n) y[n] += x[n];
+}
+
+static int cache_alloc(sublayer_cache* S, int64_t N, int64_t C, int64_t H)
+{
+    S->u = (double*)malloc((size_t)(N * C) * sizeof(double));
+    S->xhat = (double*)malloc((size_t)(N * C) * sizeof(double));
+    S->rstd = (double*)malloc((size_t)N * sizeof(double));
+    S->qkv = (double*)malloc((size_t)(N * 3 * C) * sizeof(double));
+    S->q = (double*)malloc((size_t)(N * C) * sizeof(double));
+    S->k = (double*)malloc((size_t)(N * C) * sizeof(double));
+    S->v = (double*)malloc((size_t)(N * C) * sizeof(double));
+    S->o = (double*)malloc((size_t)(N * C) * sizeof(double));
+    S->lse = (double*)malloc((size_t)(N * H) * sizeof(double));
+    S->a = (double*)malloc((size_t)(N * C) * sizeof(double));
+    return S->u && S->xhat && S->rstd && S->qkv && S->q && S->k && S->v &&
+           S->o && S->lse && S->a;
+}
+
+static void cache_free(sublayer_cache* S)
+{
+    free(S->u); free(S->xhat); free(S->rstd); free(S->qkv); free(S->q);
+    free(S->k); free(S->v); free(S->o); free(S->lse); free(S->a);
+}
+
+int oracle_sublayer_fwd(const double* x, const double* g, const double* bl,
+                        const double* Wa, const double* ba, const double* Wp,
+                        const double* bp, double* y, int64_t B, int64_t T,
+                        int64_t C, int64_t H, double eps, int64_t nthreads)
+{
+    if (H <= 0 || C % H != 0) return 1;
+    set_threads(nthreads);
+    sublayer_cache S;
+    if (!cache_alloc(&S, B * T, C, H)) { cache_free(&S); return 2; }
+    sublayer_forward_cached(x, g, bl, Wa, ba, Wp, bp, y, B, T, C, H, eps, &S);
+    cache_free(&S);
+    return 0;
+}
+
+/* Backward of L = sum(dy * y) with respect to x, g, bl, Wa, ba, Wp, bp. */
+int oracle_sublayer_bwd(const double* x, const double* g, const double* bl,
+                        const double* Wa, const double* ba, const double* Wp,
+                        const double* bp, const double* dy, double* dx,
+                        double* dg, double* dbl, double* dWa, double* dba,
+                        double* dWp, double* dbp, int64_t B, int64_t T,
+                        int64_t C, int64_t H, double eps, int64_t nthreads)
+{
+    if (H <= 0 || C % H != 0) return 1;
+    set_threads(nthreads);
+    int64_t N = B * T, D = C / H, C3 = 3 * C;
+    double scale = 1.0 / sqrt((double)D);
+    sublayer_cache S;
+    double* y = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* da = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* dO = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* dqh = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* dkh = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* dvh = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* dl = (double*)malloc((size_t)(N * H) * sizeof(double));
+    double* dqkv = (double*)malloc((size_t)(N * C3) * sizeof(double));
+    double* du = (double*)malloc((size_t)(N * C) * sizeof(double));
+    int ok = cache_alloc(&S, N, C, H) && y && da && dO && dqh && dkh && dvh && dl &&
+             dqkv && du;
+    if (ok) {
+        sublayer_forward_cached(x, g, bl, Wa, ba, Wp, bp, y, B, T, C, H, eps, &S);
+
+        /* y = x + a Wp + bp */
+        for (int64_t c = 0; c < C; ++c) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) acc += dy[n * C + c];
+            dbp[c] = acc;
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t cp = 0; cp < C; ++cp) {
+            /* dWp[cp][c] = sum_n a[n][cp] dy[n][c] */
+            for (int64_t c = 0; c < C; ++c) dWp[cp * C + c] = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double av = S.a[n * C + cp];
+                for (int64_t c = 0; c < C; ++c) dWp[cp * C + c] += av * dy[n * C + c];
+            }
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t cp = 0; cp < C; ++cp) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < C; ++c) acc += dy[n * C + c] * Wp[cp * C + c];
+                da[n * C + cp] = acc;
+            }
+
+        /* attention, per head */
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t t = 0; t < T; ++t)
+                    for (int64_t d = 0; d < D; ++d)
+                        dO[((b * H + h) * T + t) * D + d] = da[(b * T + t) * C + h * D + d];
+        oracle_attn_bwd(S.q, S.k, S.v, dO, dqh, dkh, dvh, dl, B, H, T, D, scale, 0);
+        merge_heads(dqh, dqkv, C3, 0, B, T, H, D);
+        merge_heads(dkh, dqkv, C3, C, B, T, H, D);
+        merge_heads(dvh, dqkv, C3, 2 * C, B, T, H, D);
+
+        /* qkv = u Wa + ba */
+        for (int64_t j = 0; j < C3; ++j) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) acc += dqkv[n * C3 + j];
+            dba[j] = acc;
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t c = 0; c < C; ++c) {
+            /* dWa[c][j] = sum_n u[n][c] dqkv[n][j] */
+            for (int64_t j = 0; j < C3; ++j) dWa[c * C3 + j] = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double uv = S.u[n * C + c];
+                for (int64_t j = 0; j < C3; ++j) dWa[c * C3 + j] += uv * dqkv[n * C3 + j];
+            }
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t c = 0; c < C; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < C3; ++j) acc += dqkv[n * C3 + j] * Wa[c * C3 + j];
+                du[n * C + c] = acc;
+            }
+
+        /* u = xhat g + bl,  xhat = (x - mean) rstd */
+        for (int64_t c = 0; c < C; ++c) {
+            double ag = 0.0, ab = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                ag += du[n * C + c] * S.xhat[n * C + c];
+                ab += du[n * C + c];
+            }
+            dg[c] = ag;
+            dbl[c] = ab;
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            double m1 = 0.0, m2 = 0.0;
+            for (int64_t c = 0; c < C; ++c) {
+                double dxh = du[n * C + c] * g[c];
+                m1 += dxh;
+                m2 += dxh * S.xhat[n * C + c];
+            }
+            m1 /= (double)C;
+            m2 /= (double)C;
+            for (int64_t c = 0; c < C; ++c) {
+                double dxh = du[n * C + c] * g[c];
+                dx[n * C + c] = S.rstd[n] * (dxh - m1 - S.xhat[n * C + c] * m2) +
+                                dy[n * C + c]; /* residual path */
+            }
+        }
+    }
+    cache_free(&S);
+    free(y); free(da); free(dO); free(dqh); free(dkh); free(dvh); free(dl);
+    free(dqkv); free(du);
+    return ok ? 0 : 2;
+}

@@ -1,0 +1,97 @@
+"""Planted mistakes: each plausible slip in the oracle must fail a pin.
+
+Every case copies oracle/oracle.c to a temporary directory, applies one textual
+mutation (a dropped term, a wrong sign or index, a transposed operand, a
+missing scale), builds it with the same gcc line as the real oracle, routes the
+oracle wrapper to that build and runs the pin battery from
+test_oracle_pins.py.  The case passes only if at least one pin fails.  This
+runs on the CPU only; nothing here touches the GPU library.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import tests.test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "diagonal_dropped_from_normaliser": (
+        "for (int64_t j = 0; j <= i; ++j) Z += exp(s[j] - m);",
+        "for (int64_t j = 0; j < i; ++j) Z += exp(s[j] - m);"),
+    "scale_missing": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "scale_squared": ("s[j] = scale * dot;", "s[j] = scale * scale * dot;"),
+    "lse_without_max": ("L[i] = m + log(Z);", "L[i] = log(Z);"),
+    "lse_log2": ("L[i] = m + log(Z);", "L[i] = m + log2(Z);"),
+    "value_row_index": ("acc += p[j] * V[j * D + d];", "acc += p[j] * V[i * D + d];"),
+    "key_index_transposed": ("dot += Qi[d] * K[j * D + d];", "dot += Qi[d] * K[i * D + d];"),
+    "softmax_jacobian_drops_delta": ("double dS = p[j] * (dp[j] - Delta);",
+                                     "double dS = p[j] * dp[j];"),
+    "softmax_jacobian_sign": ("double dS = p[j] * (dp[j] - Delta);",
+                              "double dS = p[j] * (Delta - dp[j]);"),
+    "dq_missing_scale": ("dQ[i * D + d] += scale * dS * K[j * D + d];",
+                         "dQ[i * D + d] += dS * K[j * D + d];"),
+    "dq_wrong_key_row": ("dQ[i * D + d] += scale * dS * K[j * D + d];",
+                         "dQ[i * D + d] += scale * dS * K[i * D + d];"),
+    "dk_missing_scale": ("dK[j * D + d] += scale * dS * Q[i * D + d];",
+                         "dK[j * D + d] += dS * Q[i * D + d];"),
+    "dk_wrong_query_row": ("dK[j * D + d] += scale * dS * Q[i * D + d];",
+                           "dK[j * D + d] += scale * dS * Q[j * D + d];"),
+    "dv_wrong_grad_row": ("dV[j * D + d] += p[j] * G[i * D + d];",
+                          "dV[j * D + d] += p[j] * G[j * D + d];"),
+    "dp_uses_keys": ("acc += G[i * D + d] * V[j * D + d];", "acc += G[i * D + d] * K[j * D + d];"),
+    "layernorm_unbiased_variance": ("var /= (double)C; /* biased variance */",
+                                    "var /= (double)(C - 1);"),
+    "layernorm_eps_outside_sqrt": ("double r = 1.0 / sqrt(var + eps);",
+                                   "double r = 1.0 / (sqrt(var) + eps);"),
+    "layernorm_bwd_drops_mean_term": ("dx[n * C + c] = S.rstd[n] * (dxh - m1 - S.xhat[n * C + c] * m2) +",
+                                      "dx[n * C + c] = S.rstd[n] * (dxh - S.xhat[n * C + c] * m2) +"),
+    "heads_interleaved": ("qkv[(b * T + t) * 3 * C + third * C + h * D + d];",
+                          "qkv[(b * T + t) * 3 * C + h * 3 * D + third * D + d];"),
+    "residual_dropped_in_bwd": ("                                dy[n * C + c]; /* residual path */",
+                                "                                0.0;"),
+    "weight_grad_transposed": ("for (int64_t c = 0; c < C; ++c) dWp[cp * C + c] += av * dy[n * C + c];",
+                               "for (int64_t c = 0; c < C; ++c) dWp[c * C + cp] += av * dy[n * C + c];"),
+}
+
+BATTERY = [
+    pins.test_golden_forward_worked_example,
+    pins.test_golden_backward_worked_example,
+    pins.test_single_token_is_identity,
+    pins.test_zero_queries_give_running_prefix_mean,
+    pins.test_identity_values_expose_the_weight_matrix,
+    pins.test_backward_identities,
+    lambda: pins.test_against_torch_sdpa_fp64((2, 2, 5, 3)),
+    lambda: pins.test_backward_finite_differences_every_element((1, 2, 8, 4)),
+    pins.test_sublayer_against_torch_library_ops,
+    pins.test_sublayer_finite_differences,
+    pins.test_layernorm_output_is_standardised,
+]
+
+
+def test_unmutated_copy_passes_the_battery(tmp_path):
+    out = oracle.compile_source(SRC, str(tmp_path / "liboracle_copy.so"))
+    with oracle.use_library(out):
+        for pin in BATTERY:
+            pin()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.compile_source(str(mutated), str(tmp_path / "liboracle_mutant.so"))
+    failed = []
+    with oracle.use_library(lib):
+        for pin in BATTERY:
+            try:
+                pin()
+            except AssertionError:
+                failed.append(getattr(pin, "__name__", "lambda"))
+    assert failed, f"planted mistake {name!r} passed every pin"

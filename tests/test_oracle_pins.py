@@ -1,0 +1,389 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with a retyped copy of itself.  They check
+hand-derived worked examples (tests/golden), closed forms, invariants the pages
+state (causal mask: a row cannot see later keys; softmax weights sum to 1), an
+independent library routine (PyTorch's fp64 CPU scaled_dot_product_attention
+with is_causal=True, the SDPA fallback the nanochat page names), and central
+finite differences for the backward pass.  The planted-mistake test in
+test_oracle_mutants.py shows that each plausible slip fails at least one pin.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TINY_SHAPES = [(1, 1, 1, 1), (1, 1, 3, 2), (2, 2, 5, 3), (1, 2, 8, 4)]
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _qkv(shape, seed=0):
+    return _rand(shape, seed), _rand(shape, seed + 1), _rand(shape, seed + 2)
+
+
+def _load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        g = json.load(f)
+    shp = (g["B"], g["H"], g["T"], g["D"])
+    return g, shp
+
+
+# --------------------------------------------------------------------------
+# worked examples (hand-derived, exact)
+# --------------------------------------------------------------------------
+
+def test_golden_forward_worked_example():
+    g, shp = _load_golden("causal_fwd_T3_D1.json")
+    arr = lambda key: np.array(g[key], dtype=np.float64).reshape(shp)
+    o, lse = oracle.attn_fwd(arr("q"), arr("k"), arr("v"), g["scale"])
+    np.testing.assert_allclose(o.ravel(), g["o"], rtol=0, atol=g["tol"] * 20)
+    np.testing.assert_allclose(lse.ravel(), g["lse"], rtol=0, atol=g["tol"] * 20)
+
+
+def test_golden_backward_worked_example():
+    g, shp = _load_golden("causal_bwd_T2_D1.json")
+    arr = lambda key: np.array(g[key], dtype=np.float64).reshape(shp)
+    o, lse = oracle.attn_fwd(arr("q"), arr("k"), arr("v"), g["scale"])
+    np.testing.assert_allclose(o.ravel(), g["o"], atol=g["tol"] * 20, rtol=0)
+    np.testing.assert_allclose(lse.ravel(), g["lse"], atol=g["tol"] * 20, rtol=0)
+    dq, dk, dv, delta = oracle.attn_bwd(arr("q"), arr("k"), arr("v"), arr("dO"), g["scale"])
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("delta", delta)):
+        np.testing.assert_allclose(got.ravel(), g[name], atol=g["tol"] * 20, rtol=0, err_msg=name)
+
+
+# --------------------------------------------------------------------------
+# closed forms and special cases
+# --------------------------------------------------------------------------
+
+def test_single_token_is_identity():
+    """T = 1: the only visible key is the query's own, weight 1: o = v and
+    lse = scale * q.k."""
+    q, k, v = _qkv((3, 2, 1, 5), seed=3)
+    s = 0.37
+    o, lse = oracle.attn_fwd(q, k, v, s)
+    assert np.array_equal(o, v)
+    np.testing.assert_allclose(lse, s * np.sum(q * k, axis=-1), rtol=1e-15, atol=1e-15)
+
+
+def test_row0_equals_v_row0_exactly():
+    """Row 0 sees only key 0 (diagonal kept), so its weight is exactly 1."""
+    q, k, v = _qkv((2, 3, 17, 8), seed=5)
+    o, _ = oracle.attn_fwd(q, k, v, 1 / math.sqrt(8))
+    assert np.array_equal(o[:, :, 0, :], v[:, :, 0, :])
+
+
+def test_zero_queries_give_running_prefix_mean():
+    """q = 0: all visible scores are equal, the weights are uniform over
+    j <= i, so o_i is the mean of v_0..v_i and lse_i = ln(i + 1)."""
+    B, H, T, D = 2, 2, 33, 4
+    _, k, v = _qkv((B, H, T, D), seed=7)
+    q = np.zeros((B, H, T, D))
+    o, lse = oracle.attn_fwd(q, k, v, 0.125)
+    prefix_mean = np.cumsum(v, axis=2) / np.arange(1, T + 1)[None, None, :, None]
+    np.testing.assert_allclose(o, prefix_mean, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(np.arange(1, T + 1)), (B, H, T)),
+                               rtol=0, atol=1e-13)
+
+
+def test_constant_values_pass_through():
+    """Softmax weights of every row sum to 1, so v = c gives o = c."""
+    q, k, _ = _qkv((2, 2, 19, 3), seed=11)
+    v = np.full(q.shape, -2.75)
+    o, _ = oracle.attn_fwd(q, k, v, 0.6)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-14)
+
+
+def test_identity_values_expose_the_weight_matrix():
+    """With D = T and v_j = e_j, o_i is row i of the weight matrix: every row
+    is non-negative, sums to 1, and is exactly 0 above the diagonal (the
+    -inf upper triangle becomes weight 0)."""
+    T = 12
+    q, k, _ = _qkv((1, 1, T, T), seed=13)
+    v = np.eye(T)[None, None]
+    P, _ = oracle.attn_fwd(q, k, v, 0.3)
+    P = P[0, 0]
+    assert np.all(P >= 0)
+    np.testing.assert_allclose(P.sum(axis=1), np.ones(T), rtol=0, atol=1e-15)
+    assert np.all(P[np.triu_indices(T, k=1)] == 0.0)
+    assert np.all(np.diag(P) > 0)
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+
+def test_causality_later_rows_do_not_leak():
+    """Changing q, k, v in rows > i leaves output rows <= i bit-identical."""
+    B, H, T, D = 2, 2, 24, 6
+    q, k, v = _qkv((B, H, T, D), seed=17)
+    o, lse = oracle.attn_fwd(q, k, v, 0.4)
+    for cut in (0, 5, 23):
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        r = _rand((B, H, T - cut - 1, D), 99 + cut)
+        q2[:, :, cut + 1:] += r
+        k2[:, :, cut + 1:] -= 2 * r
+        v2[:, :, cut + 1:] += 3 * r
+        o2, lse2 = oracle.attn_fwd(q2, k2, v2, 0.4)
+        assert np.array_equal(o2[:, :, :cut + 1], o[:, :, :cut + 1])
+        assert np.array_equal(lse2[:, :, :cut + 1], lse[:, :, :cut + 1])
+        if cut + 1 < T:
+            assert not np.array_equal(o2[:, :, cut + 1:], o[:, :, cut + 1:])
+
+
+def test_key_shift_invariance():
+    """k_j -> k_j + c for every j adds scale*q_i.c to every score of row i:
+    o is unchanged and lse_i shifts by scale*q_i.c."""
+    B, H, T, D = 1, 3, 20, 5
+    q, k, v = _qkv((B, H, T, D), seed=19)
+    c = _rand((D,), 23)
+    s = 0.45
+    o, lse = oracle.attn_fwd(q, k, v, s)
+    o2, lse2 = oracle.attn_fwd(q, k + c, v, s)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse + s * (q @ c), rtol=0, atol=1e-12)
+
+
+def test_value_shift_adds_through():
+    q, k, v = _qkv((2, 1, 15, 4), seed=29)
+    c = _rand((4,), 31)
+    o, _ = oracle.attn_fwd(q, k, v, 0.5)
+    o2, _ = oracle.attn_fwd(q, k, v + c, 0.5)
+    np.testing.assert_allclose(o2, o + c, rtol=0, atol=1e-13)
+
+
+def test_batch_head_permutation_equivariance():
+    B, H, T, D = 3, 4, 9, 3
+    q, k, v = _qkv((B, H, T, D), seed=37)
+    dO = _rand((B, H, T, D), 41)
+    o, lse = oracle.attn_fwd(q, k, v, 0.5)
+    dq, dk, dv, de = oracle.attn_bwd(q, k, v, dO, 0.5)
+    perm = np.random.default_rng(43).permutation(B * H)
+    P = lambda a: a.reshape(B * H, *a.shape[2:])[perm].reshape(a.shape)
+    o2, lse2 = oracle.attn_fwd(P(q), P(k), P(v), 0.5)
+    dq2, dk2, dv2, de2 = oracle.attn_bwd(P(q), P(k), P(v), P(dO), 0.5)
+    for a, b in ((o2, o), (lse2, lse), (dq2, dq), (dk2, dk), (dv2, dv), (de2, de)):
+        assert np.array_equal(a, P(b))
+
+
+# --------------------------------------------------------------------------
+# brute force and an independent library routine
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", TINY_SHAPES + [(4, 4, 64, 32)])
+def test_masked_matrix_brute_force(shape):
+    """The explicit matrix form on tiny inputs: S = scale q k^T, -inf strictly
+    above the diagonal, row softmax, O = P V."""
+    q, k, v = _qkv(shape, seed=47)
+    T, D = shape[2], shape[3]
+    s = 1 / math.sqrt(D)
+    S = s * np.einsum("bhid,bhjd->bhij", q, k)
+    S[..., np.triu_indices(T, k=1)[0], np.triu_indices(T, k=1)[1]] = -np.inf
+    P = np.exp(S - S.max(axis=-1, keepdims=True))
+    P /= P.sum(axis=-1, keepdims=True)
+    o, _ = oracle.attn_fwd(q, k, v, s)
+    np.testing.assert_allclose(o, P @ v, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shape", TINY_SHAPES + [(4, 4, 64, 32)])
+def test_against_torch_sdpa_fp64(shape):
+    """PyTorch's fp64 CPU scaled_dot_product_attention with is_causal=True
+    (lower-triangular mask for equal query/key lengths), forward and
+    autograd backward."""
+    q, k, v = _qkv(shape, seed=53)
+    dO = _rand(shape, 59)
+    s = oracle.widen_scale(1 / math.sqrt(shape[3]))
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=s)
+    to.backward(torch.tensor(dO))
+    o, _ = oracle.attn_fwd(q, k, v, s)
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, dO, s)
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# backward: finite differences and identities
+# --------------------------------------------------------------------------
+
+def _loss(q, k, v, dO, s, lib=None):
+    o, _ = oracle.attn_fwd(q, k, v, s, lib=lib)
+    return float(np.sum(o * dO))
+
+
+def _fd_check(q, k, v, dO, s, idx_per_tensor, h=1e-5, tol=2e-7, lib=None):
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, dO, s, lib=lib)
+    tensors = {"q": (q, dq), "k": (k, dk), "v": (v, dv)}
+    worst = 0.0
+    for name, (x, g) in tensors.items():
+        for flat in idx_per_tensor(x):
+            i = np.unravel_index(flat, x.shape)
+            x0 = x[i]
+            x[i] = x0 + h
+            lp = _loss(q, k, v, dO, s, lib)
+            x[i] = x0 - h
+            lm = _loss(q, k, v, dO, s, lib)
+            x[i] = x0
+            fd = (lp - lm) / (2 * h)
+            err = abs(fd - g[i]) / max(1.0, abs(g[i]))
+            worst = max(worst, err)
+            assert err <= tol, f"d{name}{i}: analytic {g[i]!r} vs finite difference {fd!r}"
+    return worst
+
+
+@pytest.mark.parametrize("shape", TINY_SHAPES)
+def test_backward_finite_differences_every_element(shape):
+    q, k, v = _qkv(shape, seed=61)
+    dO = _rand(shape, 67)
+    _fd_check(q, k, v, dO, 1 / math.sqrt(shape[3]), lambda x: range(x.size))
+
+
+def test_backward_finite_differences_tiny_config_sampled():
+    """200 random elements per tensor at the tiny config's shape."""
+    shape = (4, 4, 64, 32)
+    q, k, v = _qkv(shape, seed=71)
+    dO = _rand(shape, 73)
+    rng = np.random.default_rng(79)
+    _fd_check(q, k, v, dO, oracle.widen_scale(1 / math.sqrt(32)),
+              lambda x: rng.choice(x.size, 200, replace=False))
+
+
+def test_backward_identities():
+    """Derived closed forms: dq row 0 = 0 (a one-key softmax has no
+    gradient); rows of dS sum to 0, so sum_j dk_j = 0; sum_j dv_j = sum_i dO_i;
+    Delta_i = dO_i . o_i."""
+    B, H, T, D = 2, 3, 40, 8
+    q, k, v = _qkv((B, H, T, D), seed=83)
+    dO = _rand((B, H, T, D), 89)
+    o, _ = oracle.attn_fwd(q, k, v, 0.35)
+    dq, dk, dv, delta = oracle.attn_bwd(q, k, v, dO, 0.35)
+    assert np.all(dq[:, :, 0, :] == 0.0)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=2), dO.sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(delta, np.sum(dO * o, axis=-1), atol=1e-12)
+
+
+def test_backward_causality():
+    """dq_i depends only on keys j <= i: perturbing k, v rows > i leaves dq
+    rows <= i bit-identical."""
+    B, H, T, D = 1, 2, 16, 4
+    q, k, v = _qkv((B, H, T, D), seed=97)
+    dO = _rand((B, H, T, D), 101)
+    dq, _, _, _ = oracle.attn_bwd(q, k, v, dO, 0.5)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 9:] += 1.0
+    v2[:, :, 9:] -= 1.0
+    dq2, _, _, _ = oracle.attn_bwd(q, k2, v2, dO, 0.5)
+    assert np.array_equal(dq2[:, :, :9], dq[:, :, :9])
+
+
+# --------------------------------------------------------------------------
+# pre-norm attention sublayer
+# --------------------------------------------------------------------------
+
+def _sublayer_params(B, T, C, seed=0):
+    r = np.random.default_rng(seed)
+    return dict(
+        x=r.standard_normal((B, T, C)),
+        g=1.0 + 0.1 * r.standard_normal(C),
+        bl=0.1 * r.standard_normal(C),
+        Wa=0.3 * r.standard_normal((C, 3 * C)),
+        ba=0.1 * r.standard_normal(3 * C),
+        Wp=0.3 * r.standard_normal((C, C)),
+        bp=0.1 * r.standard_normal(C),
+    )
+
+
+def _torch_sublayer(p, H, eps=1e-5):
+    """Independent composition from PyTorch fp64 CPU library ops:
+    F.layer_norm, F.linear, scaled_dot_product_attention(is_causal=True)."""
+    t = {k: torch.tensor(v, requires_grad=True) for k, v in p.items()}
+    x = t["x"]
+    B, T, C = x.shape
+    D = C // H
+    u = torch.nn.functional.layer_norm(x, (C,), t["g"], t["bl"], eps)
+    qkv = torch.nn.functional.linear(u, t["Wa"].t(), t["ba"])
+    q, k, v = qkv.chunk(3, dim=-1)
+    heads = lambda z: z.view(B, T, H, D).transpose(1, 2)
+    a = torch.nn.functional.scaled_dot_product_attention(heads(q), heads(k), heads(v),
+                                                         is_causal=True)
+    a = a.transpose(1, 2).reshape(B, T, C)
+    y = x + torch.nn.functional.linear(a, t["Wp"].t(), t["bp"])
+    return t, y
+
+
+def test_sublayer_against_torch_library_ops():
+    B, T, C, H = 2, 7, 12, 3
+    p = _sublayer_params(B, T, C, seed=103)
+    dy = np.random.default_rng(107).standard_normal((B, T, C))
+    t, y_ref = _torch_sublayer(p, H)
+    y_ref.backward(torch.tensor(dy))
+    y = oracle.sublayer_fwd(**p, n_head=H)
+    grads = oracle.sublayer_bwd(**p, dy=dy, n_head=H)
+    np.testing.assert_allclose(y, y_ref.detach().numpy(), rtol=0, atol=1e-12)
+    for ours, theirs in (("dx", "x"), ("dg", "g"), ("dbl", "bl"), ("dWa", "Wa"),
+                         ("dba", "ba"), ("dWp", "Wp"), ("dbp", "bp")):
+        np.testing.assert_allclose(grads[ours], t[theirs].grad.numpy(), rtol=0, atol=1e-11,
+                                   err_msg=ours)
+
+
+def test_sublayer_residual_path():
+    """Wp = 0 and bp = 0 switch the attention branch off: y = x exactly (the
+    residual path of the pre-norm block)."""
+    B, T, C, H = 1, 5, 8, 2
+    p = _sublayer_params(B, T, C, seed=109)
+    p["Wp"][:] = 0.0
+    p["bp"][:] = 0.0
+    y = oracle.sublayer_fwd(**p, n_head=H)
+    assert np.array_equal(y, p["x"])
+
+
+def test_sublayer_finite_differences():
+    B, T, C, H = 1, 5, 8, 2
+    p = _sublayer_params(B, T, C, seed=113)
+    dy = np.random.default_rng(127).standard_normal((B, T, C))
+    grads = oracle.sublayer_bwd(**p, dy=dy, n_head=H)
+    h = 1e-6
+    rng = np.random.default_rng(131)
+    for name, gname in (("x", "dx"), ("g", "dg"), ("bl", "dbl"), ("Wa", "dWa"),
+                        ("ba", "dba"), ("Wp", "dWp"), ("bp", "dbp")):
+        arr = p[name]
+        for flat in rng.choice(arr.size, min(arr.size, 12), replace=False):
+            i = np.unravel_index(flat, arr.shape)
+            x0 = arr[i]
+            arr[i] = x0 + h
+            lp = float(np.sum(oracle.sublayer_fwd(**p, n_head=H) * dy))
+            arr[i] = x0 - h
+            lm = float(np.sum(oracle.sublayer_fwd(**p, n_head=H) * dy))
+            arr[i] = x0
+            fd = (lp - lm) / (2 * h)
+            g = grads[gname][i]
+            assert abs(fd - g) <= 1e-6 * max(1.0, abs(g)), f"{gname}{i}: {g} vs {fd}"
+
+
+def test_layernorm_output_is_standardised():
+    """LN with g = 1, b = 0: the q third of c_attn with Wa = [I | 0 | 0] and
+    H = 1, q = LN(x); take v = LN(x) too and q = 0 so o_0 = v_0 = LN(x_0):
+    mean 0, biased variance 1/(1 + eps/var)."""
+    B, T, C = 1, 4, 16
+    r = np.random.default_rng(137)
+    x = 3.0 + 2.0 * r.standard_normal((B, T, C))
+    Wa = np.zeros((C, 3 * C))
+    Wa[:, 2 * C:] = np.eye(C)  # v = LN(x); q = k = 0
+    Wp = np.eye(C)
+    y = oracle.sublayer_fwd(x, np.ones(C), np.zeros(C), Wa, np.zeros(3 * C), Wp, np.zeros(C),
+                            n_head=1)
+    ln0 = (y - x)[0, 0]  # o_0 = v_0 = LN(x_0)
+    var = np.var(x[0, 0])
+    assert abs(ln0.mean()) < 1e-14
+    np.testing.assert_allclose(np.mean(ln0 ** 2), var / (var + 1e-5), rtol=1e-13)
