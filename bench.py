@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark: causal multi-head self-attention forward + backward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+attn_fwd (tiled forward, lse out) followed by attn_bwd (Delta, dQ, dK/dV),
+all through the C ABI of libcausal_attn.so, inputs resident in HBM.
+
+Default workload: GPT-2-small attention (B=8, H=12, T=1024, D=64, bf16 storage,
+fp32 accumulation; q, k, v, dO iid N(0, 1), seeds 42+idx).  Metric: causal
+fwd+bwd TFLOP/s with work = 7 * B * H * T^2 * D (forward 2 GEMMs and backward
+5 GEMMs over the causal half), also as a fraction of the bf16 dense MFMA peak.
+
+Prints ONE JSON line.  Extra keys: pct_of_peak, fwd_tflops, per-kernel times,
+the roofline of the dominant kernel and the CPU-oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s at GPT-2-small shape; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/CU/clk
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["causal_head_self_amd/csrc/attn_bf16.hip",
+                  "causal_head_self_amd/csrc/attn_device.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_work(cfg):
+    """Algorithmic work per launch, per kernel (causal-adjusted).  One GEMM
+    over the causal half of one head is T^2 * D flops.  The forward credits 2
+    GEMMs (S, PV); the backward 5: dK/dV is credited with S, dP, dV, dK and dQ
+    with its own dQ product (its recomputed S and dP are not credited again).
+    Delta is HBM work: read o and dO, write delta."""
+    B, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
+    g = float(B * H * T * T * D)
+    es = 2 if cfg.dtype == "bf16" else 4
+    return {
+        "fwd": {"flops": 2 * g},
+        "delta": {"bytes": float(B * H * T * (2 * D * es + 4))},
+        "dq": {"flops": 1 * g},
+        "dkdv": {"flops": 4 * g},
+    }
+
+
+def read_traffic(kernel: str, workload: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_src_sha") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, inputs, threads: int):
+    """The fp64 oracle, as it stands, on the host cores: one fwd+bwd pass
+    over the sample (all heads of the workload), timed with a wall clock."""
+    import oracle
+    q, k, v, dO = inputs
+    s = oracle.widen_scale(cfg.scale)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, s, nthreads=threads)
+    oracle.attn_bwd(q, k, v, dO, s, nthreads=threads)
+    dt = time.perf_counter() - t0
+    work = 7.0 * cfg.B * cfg.H * cfg.T * cfg.T * cfg.D
+    return {
+        "value": round(work / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one fp64 fwd+bwd pass over all {cfg.B * cfg.H} heads of the same workload "
+                   f"(B={cfg.B}, H={cfg.H}, T={cfg.T}, D={cfg.D}); {dt:.2f} s wall; "
+                   f"host {platform.processor() or platform.machine()}"),
+        "seconds": round(dt, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="gpt2s", choices=["tiny", "gpt2s", "gpt400m", "long"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(every (batch, head) pair is independent, so more GPUs would each run their "
+              "own shard of the batch with no exchange).", file=sys.stderr)
+        return 2
+
+    import torch
+    import causal_head_self_amd as cat
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    cat.load_library()  # raises if the HIP library is missing
+    torch.manual_seed(42)
+    cfg = workloads.ATTN_CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    host_inputs = workloads.config_inputs(cfg)
+    q, k, v, dO = (t.to(dev) for t in host_inputs)
+    B, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty_like(lse)
+    scale = cfg.scale
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cat.attn_fwd(q, k, v, o, lse, scale, stream)
+        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # headline: K whole steps between two events, nothing else in the region
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel: the same K steps with an event between consecutive launches
+    names = ["fwd", "delta", "dq", "dkdv"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record(stream)
+        cat.attn_fwd(q, k, v, o, lse, scale, stream)
+        e[1].record(stream)
+        cat.attn_bwd_delta(o, dO, delta, stream)
+        e[2].record(stream)
+        cat.attn_bwd_dq(q, k, v, dO, lse, delta, dq, scale, stream)
+        e[3].record(stream)
+        cat.attn_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, scale, stream)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+               for i, n in enumerate(names)}
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    work = kernel_work(cfg)
+    flops_fb = 7.0 * B * H * T * T * D
+    flops_f = 2.0 * B * H * T * T * D
+    value = flops_fb / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    dominant = max(("fwd", "dq", "dkdv"), key=lambda n: kern_ms[n])
+    achieved = work[dominant]["flops"] / (kern_ms[dominant] * 1e-3) / 1e12
+    sha = kernel_source_sha()
+    workload_name = f"{cfg.name}_B{B}_H{H}_T{T}_D{D}_{cfg.dtype}"
+    roofline = {
+        "bound": "mfma",
+        "kernel": dominant,
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": read_traffic(dominant, workload_name, sha),
+        "algorithmic_flops_per_launch": work[dominant]["flops"],
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            threads = min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(cfg, host_inputs, threads)
+
+    fwd_tflops = flops_f / (kern_ms["fwd"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"causal MHA fwd+bwd, {cfg.name}: B={B} H={H} T={T} D={D} {cfg.dtype} "
+                         "storage / fp32 accumulate, q,k,v,dO iid N(0,1) seeds 42+idx"),
+            "B": B, "H": H, "T": T, "D": D, "global_batch": B, "seq_len": T,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "fwd_tflops": round(fwd_tflops, 3),
+        "fwd_pct_of_peak": round(100.0 * fwd_tflops / peak, 2),
+        "kernel_ms": {n: round(v_, 5) for n, v_ in kern_ms.items()},
+        "kernel_src_sha": sha,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "l2_flushed": False,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

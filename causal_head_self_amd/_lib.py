@@ -1,0 +1,87 @@
+"""ctypes loader for libcausal_attn.so (the C ABI in include/causal_attn.h).
+
+The library is built in-tree by ``python -m causal_head_self_amd.build``.  If
+it is missing, loading raises: there is no fallback path of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcausal_attn.so")
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+STATUS = {
+    0: "ATTN_OK",
+    1: "ATTN_ERR_NULL",
+    2: "ATTN_ERR_SHAPE",
+    3: "ATTN_ERR_UNSUPPORTED_D",
+    4: "ATTN_ERR_DTYPE",
+    5: "ATTN_ERR_ALIGN",
+    6: "ATTN_ERR_OVERFLOW",
+    7: "ATTN_ERR_SCALE",
+    8: "ATTN_ERR_ALIAS",
+    9: "ATTN_ERR_HIP",
+}
+
+# every symbol include/causal_attn.h declares
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_delta", "attn_bwd_dq", "attn_bwd_dkdv",
+           "attn_status_str", "attn_abi_version")
+ABI_VERSION = (1 << 16) | 0
+
+
+class AttnError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(
+            f"{p} is not built: run `python -m causal_head_self_amd.build` "
+            "(the HIP library is required; there is no CPU fallback)")
+    lib = ctypes.CDLL(p)
+    lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, ctypes.c_float,
+                             _int, _vp]
+    lib.attn_fwd.restype = _int
+    lib.attn_bwd.argtypes = [_vp] * 10 + [_int, _int, _int, _int, ctypes.c_float, _int, _vp]
+    lib.attn_bwd.restype = _int
+    lib.attn_bwd_delta.argtypes = [_vp] * 3 + [_int] * 5 + [_vp]
+    lib.attn_bwd_delta.restype = _int
+    lib.attn_bwd_dq.argtypes = [_vp] * 7 + [_int] * 4 + [ctypes.c_float, _int, _vp]
+    lib.attn_bwd_dq.restype = _int
+    lib.attn_bwd_dkdv.argtypes = [_vp] * 8 + [_int] * 4 + [ctypes.c_float, _int, _vp]
+    lib.attn_bwd_dkdv.restype = _int
+    lib.attn_status_str.argtypes = [_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = _int
+    if lib.attn_abi_version() != ABI_VERSION:
+        raise ImportError(f"{p}: ABI version {lib.attn_abi_version():#x}, expected {ABI_VERSION:#x}")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise AttnError(status, status_str(status))

@@ -1,0 +1,201 @@
+// attn_api.hip -- the C ABI declared in include/causal_attn.h: argument
+// validation (all of it before any HIP call) and dispatch to the kernels.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/causal_attn.h"
+#include "attn_kernels.h"
+
+namespace {
+
+struct Buf {
+    const void* p;
+    bool row_tensor;  // [B][H][T] fp32 (lse, delta) instead of [B][H][T][D]
+};
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks shared by every entry point, in the documented order:
+// NULL, shape, dtype, D, scale, overflow, alignment, aliasing.
+template <int NI, int NO>
+int validate(const Buf (&in)[NI], const Buf (&out)[NO], int B, int H, int T, int D, float scale,
+             int dtype)
+{
+    for (const Buf& b : in)
+        if (!b.p) return ATTN_ERR_NULL;
+    for (const Buf& b : out)
+        if (!b.p) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || T < 1) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (D != 32 && D != 64) return ATTN_ERR_UNSUPPORTED_D;
+    if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_ERR_SCALE;
+    const long long BH = (long long)B * H;
+    const long long tiles = (T + 63) / 64;  // the finest row tiling any kernel launches
+    if ((long long)T * D > 0x7fffffffLL || BH * tiles > 0x7fffffffLL ||
+        BH * (long long)T > (1LL << 35))
+        return ATTN_ERR_OVERFLOW;
+    for (const Buf& b : in)
+        if ((uintptr_t)b.p % (b.row_tensor ? 4 : 16)) return ATTN_ERR_ALIGN;
+    for (const Buf& b : out)
+        if ((uintptr_t)b.p % (b.row_tensor ? 4 : 16)) return ATTN_ERR_ALIGN;
+    const size_t rows = (size_t)BH * T;
+    const size_t tensor_bytes = rows * D * (dtype == ATTN_BF16 ? 2 : 4);
+    auto span = [&](const Buf& b) {
+        const uintptr_t lo = (uintptr_t)b.p;
+        return Span{lo, lo + (b.row_tensor ? rows * sizeof(float) : tensor_bytes)};
+    };
+    for (int i = 0; i < NO; ++i) {
+        for (int j = 0; j < NI; ++j)
+            if (overlaps(span(out[i]), span(in[j]))) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlaps(span(out[i]), span(out[j]))) return ATTN_ERR_ALIAS;
+    }
+    return ATTN_OK;
+}
+
+cattn::AttnArgs make_args(int B, int H, int T, int D, float scale)
+{
+    cattn::AttnArgs a{};
+    a.B = B;
+    a.H = H;
+    a.T = T;
+    a.D = D;
+    a.scale = scale;
+    return a;
+}
+
+int status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return CAUSAL_ATTN_ABI_VERSION; }
+
+const char* attn_status_str(int st)
+{
+    switch (st) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H and T must be >= 1";
+    case ATTN_ERR_UNSUPPORTED_D: return "head dim D must be 32 or 64";
+    case ATTN_ERR_DTYPE: return "dtype must be ATTN_F32 or ATTN_BF16";
+    case ATTN_ERR_ALIGN: return "tensors must be 16-byte aligned (lse/delta 4-byte)";
+    case ATTN_ERR_OVERFLOW: return "T*D or the launch grid exceeds 2^31 - 1";
+    case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int T, int D, float scale, int dtype, void* stream)
+{
+    const Buf in[3] = {{q, false}, {k, false}, {v, false}};
+    const Buf out[2] = {{o, false}, {lse, true}};
+    const int st = validate(in, out, B, H, T, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    cattn::AttnArgs a = make_args(B, H, T, D, scale);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.o_out = o;
+    a.lse = lse;
+    hipStream_t s = (hipStream_t)stream;
+    return status(dtype == ATTN_BF16 ? cattn::launch_fwd_bf16(a, s) : cattn::launch_fwd_f32(a, s));
+}
+
+int attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int T, int D,
+                   int dtype, void* stream)
+{
+    const Buf in[2] = {{o, false}, {dO, false}};
+    const Buf out[1] = {{delta, true}};
+    const int st = validate(in, out, B, H, T, D, 1.0f, dtype);
+    if (st != ATTN_OK) return st;
+    cattn::AttnArgs a = make_args(B, H, T, D, 1.0f);
+    a.o = o;
+    a.dO = dO;
+    a.delta = delta;
+    hipStream_t s = (hipStream_t)stream;
+    return status(dtype == ATTN_BF16 ? cattn::launch_delta_bf16(a, s)
+                                     : cattn::launch_delta_f32(a, s));
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                const float* delta, void* dq, int B, int H, int T, int D, float scale, int dtype,
+                void* stream)
+{
+    const Buf in[6] = {{q, false}, {k, false}, {v, false}, {dO, false}, {lse, true},
+                       {delta, true}};
+    const Buf out[1] = {{dq, false}};
+    const int st = validate(in, out, B, H, T, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    cattn::AttnArgs a = make_args(B, H, T, D, scale);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dO = dO;
+    a.lse = const_cast<float*>(lse);
+    a.delta = const_cast<float*>(delta);
+    a.dq = dq;
+    hipStream_t s = (hipStream_t)stream;
+    return status(dtype == ATTN_BF16 ? cattn::launch_dq_bf16(a, s) : cattn::launch_dq_f32(a, s));
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                  const float* delta, void* dk, void* dv, int B, int H, int T, int D,
+                  float scale, int dtype, void* stream)
+{
+    const Buf in[6] = {{q, false}, {k, false}, {v, false}, {dO, false}, {lse, true},
+                       {delta, true}};
+    const Buf out[2] = {{dk, false}, {dv, false}};
+    const int st = validate(in, out, B, H, T, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    cattn::AttnArgs a = make_args(B, H, T, D, scale);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dO = dO;
+    a.lse = const_cast<float*>(lse);
+    a.delta = const_cast<float*>(delta);
+    a.dk = dk;
+    a.dv = dv;
+    hipStream_t s = (hipStream_t)stream;
+    return status(dtype == ATTN_BF16 ? cattn::launch_dkdv_bf16(a, s)
+                                     : cattn::launch_dkdv_f32(a, s));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dO, void* dq, void* dk, void* dv, float* delta, int B, int H, int T,
+             int D, float scale, int dtype, void* stream)
+{
+    const Buf in[6] = {{q, false}, {k, false}, {v, false}, {o, false}, {dO, false}, {lse, true}};
+    const Buf out[4] = {{dq, false}, {dk, false}, {dv, false}, {delta, true}};
+    const int st = validate(in, out, B, H, T, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    cattn::AttnArgs a = make_args(B, H, T, D, scale);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dO = dO;
+    a.lse = const_cast<float*>(lse);
+    a.delta = delta;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf = dtype == ATTN_BF16;
+    hipError_t e = bf ? cattn::launch_delta_bf16(a, s) : cattn::launch_delta_f32(a, s);
+    if (e == hipSuccess) e = bf ? cattn::launch_dq_bf16(a, s) : cattn::launch_dq_f32(a, s);
+    if (e == hipSuccess) e = bf ? cattn::launch_dkdv_bf16(a, s) : cattn::launch_dkdv_f32(a, s);
+    return status(e);
+}
+
+}  // extern "C"

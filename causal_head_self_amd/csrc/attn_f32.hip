@@ -1,0 +1,295 @@
+// attn_f32.hip -- fp32 kernels for causal multi-head self-attention (forward,
+// Delta, dQ, dK/dV), same operation as attn_bf16.hip (CS336 from-scratch
+// tutorial, lmnt.cn, section 5.1 CausalSelfAttention.forward, diagonal kept).
+//
+// fp32 has no full-rate matrix path that keeps fp32 products exact, and the
+// fp32 workloads here are small (the pages' tiny CPU config: T = 64, D = 32),
+// so these kernels use exact fp32 FMA on the vector ALUs: one lane per query
+// (forward, dQ) or per key (dK/dV), with 64-row K/V (or Q/dO) tiles shared
+// through LDS.  Launch latency, not arithmetic, bounds them at that size.
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace cattn {
+
+constexpr int kRows = 64;  // rows per workgroup and per LDS tile (one wave)
+
+template <int HD>
+__device__ __forceinline__ void load_rows_f32(float (*lds)[HD], const float* __restrict__ src,
+                                              int row0, int T, int tid)
+{
+#pragma unroll 4
+    for (int c = tid; c < kRows * HD / 4; c += kRows) {
+        const int r = c / (HD / 4), cc = c % (HD / 4);
+        f32x4 v = f32x4{};
+        if (row0 + r < T) v = *(const f32x4*)(src + (size_t)(row0 + r) * HD + 4 * cc);
+        *(f32x4*)(&lds[r][4 * cc]) = v;
+    }
+}
+
+template <int HD>
+__global__ __launch_bounds__(kRows) void attn_fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int BH, int T, int n_qtiles,
+    float scale_log2)
+{
+    __shared__ __attribute__((aligned(16))) float sK[kRows][HD];
+    __shared__ __attribute__((aligned(16))) float sV[kRows][HD];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x % BH;
+    const int qt = n_qtiles - 1 - blockIdx.x / BH;
+    const size_t head = (size_t)bh * T * HD;
+    const int qrow = qt * kRows + tid;
+    const bool valid = qrow < T;
+
+    float q[HD], o[HD];
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+        q[d] = valid ? Q[head + (size_t)qrow * HD + d] : 0.f;
+        o[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;  // base-2 scaled running max, normaliser
+
+    const int kv_end = min(T, qt * kRows + kRows);
+    const int n_kv = (kv_end + kRows - 1) / kRows;
+    for (int j = 0; j < n_kv; ++j) {
+        const int k0 = j * kRows;
+        __syncthreads();
+        load_rows_f32<HD>(sK, K + head, k0, T, tid);
+        load_rows_f32<HD>(sV, V + head, k0, T, tid);
+        __syncthreads();
+        const int last = min(kRows - 1, qrow - k0);  // last visible key of the tile
+        for (int c0 = 0; c0 <= last; c0 += 16) {
+            float s[16];
+            float mc = -INFINITY;
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                float dot = 0.f;
+#pragma unroll
+                for (int d = 0; d < HD; ++d) dot = fmaf(q[d], sK[c0 + kk][d], dot);
+                s[kk] = (c0 + kk <= last) ? dot * scale_log2 : -INFINITY;
+                mc = fmaxf(mc, s[kk]);
+            }
+            const float m_new = fmaxf(m, mc);
+            const float alpha = fast_exp2(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < HD; ++d) o[d] *= alpha;
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                const float p = fast_exp2(s[kk] - m_new);
+                l += p;
+#pragma unroll
+                for (int d = 0; d < HD; ++d) o[d] = fmaf(p, sV[c0 + kk][d], o[d]);
+            }
+            m = m_new;
+        }
+    }
+    if (valid) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int d = 0; d < HD; ++d) O[head + (size_t)qrow * HD + d] = o[d] * inv;
+        LSE[(size_t)bh * T + qrow] = m * kLn2 + logf(l);
+    }
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_delta_f32_kernel(const float* __restrict__ O,
+                                                             const float* __restrict__ dO,
+                                                             float* __restrict__ Delta,
+                                                             long long rows)
+{
+    constexpr int LPR = HD / 4;
+    const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+    const int sub = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const f32x4 o = *(const f32x4*)(O + row * HD + 4 * sub);
+        const f32x4 g = *(const f32x4*)(dO + row * HD + 4 * sub);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(o[e], g[e], acc);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && sub == 0) Delta[row] = acc;
+}
+
+template <int HD>
+__global__ __launch_bounds__(kRows) void attn_bwd_dq_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    float* __restrict__ dQ, int BH, int T, int n_qtiles, float scale, float scale_log2)
+{
+    __shared__ __attribute__((aligned(16))) float sK[kRows][HD];
+    __shared__ __attribute__((aligned(16))) float sV[kRows][HD];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x % BH;
+    const int qt = n_qtiles - 1 - blockIdx.x / BH;
+    const size_t head = (size_t)bh * T * HD;
+    const int qrow = qt * kRows + tid;
+    const bool valid = qrow < T;
+
+    float q[HD], g[HD], dq[HD];
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+        q[d] = valid ? Q[head + (size_t)qrow * HD + d] : 0.f;
+        g[d] = valid ? dO[head + (size_t)qrow * HD + d] : 0.f;
+        dq[d] = 0.f;
+    }
+    const float lse2 = valid ? LSE[(size_t)bh * T + qrow] * kLog2e : 0.f;
+    const float dlt = valid ? Delta[(size_t)bh * T + qrow] : 0.f;
+
+    const int kv_end = min(T, qt * kRows + kRows);
+    const int n_kv = (kv_end + kRows - 1) / kRows;
+    for (int j = 0; j < n_kv; ++j) {
+        const int k0 = j * kRows;
+        __syncthreads();
+        load_rows_f32<HD>(sK, K + head, k0, T, tid);
+        load_rows_f32<HD>(sV, V + head, k0, T, tid);
+        __syncthreads();
+        const int last = valid ? min(kRows - 1, qrow - k0) : -1;
+        for (int kk = 0; kk <= last; ++kk) {
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int d = 0; d < HD; ++d) {
+                s = fmaf(q[d], sK[kk][d], s);
+                dp = fmaf(g[d], sV[kk][d], dp);
+            }
+            const float p = fast_exp2(fmaf(s, scale_log2, -lse2));
+            const float ds = p * (dp - dlt);
+#pragma unroll
+            for (int d = 0; d < HD; ++d) dq[d] = fmaf(ds, sK[kk][d], dq[d]);
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int d = 0; d < HD; ++d) dQ[head + (size_t)qrow * HD + d] = dq[d] * scale;
+    }
+}
+
+template <int HD>
+__global__ __launch_bounds__(kRows) void attn_bwd_dkdv_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    float* __restrict__ dK, float* __restrict__ dV, int BH, int T, float scale, float scale_log2)
+{
+    __shared__ __attribute__((aligned(16))) float sQ[kRows][HD];
+    __shared__ __attribute__((aligned(16))) float sG[kRows][HD];
+    __shared__ float sL[kRows], sD[kRows];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x % BH;
+    const int kt = blockIdx.x / BH;
+    const size_t head = (size_t)bh * T * HD;
+    const int key = kt * kRows + tid;
+    const bool valid = key < T;
+
+    float k[HD], v[HD], dk[HD], dv[HD];
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+        k[d] = valid ? K[head + (size_t)key * HD + d] : 0.f;
+        v[d] = valid ? V[head + (size_t)key * HD + d] : 0.f;
+        dk[d] = 0.f;
+        dv[d] = 0.f;
+    }
+    const int n_q = (T + kRows - 1) / kRows;
+    for (int i = kt; i < n_q; ++i) {
+        const int q0 = i * kRows;
+        __syncthreads();
+        load_rows_f32<HD>(sQ, Q + head, q0, T, tid);
+        load_rows_f32<HD>(sG, dO + head, q0, T, tid);
+        sL[tid] = (q0 + tid < T) ? LSE[(size_t)bh * T + q0 + tid] * kLog2e : 0.f;
+        sD[tid] = (q0 + tid < T) ? Delta[(size_t)bh * T + q0 + tid] : 0.f;
+        __syncthreads();
+        const int first = valid ? max(0, key - q0) : kRows;  // first query >= key
+        const int end = min(kRows, T - q0);
+        for (int qq = first; qq < end; ++qq) {
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int d = 0; d < HD; ++d) {
+                s = fmaf(sQ[qq][d], k[d], s);
+                dp = fmaf(sG[qq][d], v[d], dp);
+            }
+            const float p = fast_exp2(fmaf(s, scale_log2, -sL[qq]));
+            const float ds = p * (dp - sD[qq]);
+#pragma unroll
+            for (int d = 0; d < HD; ++d) {
+                dk[d] = fmaf(ds, sQ[qq][d], dk[d]);
+                dv[d] = fmaf(p, sG[qq][d], dv[d]);
+            }
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int d = 0; d < HD; ++d) {
+            dK[head + (size_t)key * HD + d] = dk[d] * scale;
+            dV[head + (size_t)key * HD + d] = dv[d];
+        }
+    }
+}
+
+template <int HD>
+static hipError_t fwd(const AttnArgs& a, hipStream_t st)
+{
+    const int BH = a.B * a.H;
+    const int nqt = (a.T + kRows - 1) / kRows;
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<HD>, dim3(nqt * BH), dim3(kRows), 0, st,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.o_out, a.lse, BH, a.T, nqt, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t delta(const AttnArgs& a, hipStream_t st)
+{
+    const long long rows = (long long)a.B * a.H * a.T;
+    constexpr int rpb = 256 / (HD / 4);
+    hipLaunchKernelGGL(attn_delta_f32_kernel<HD>, dim3((unsigned)((rows + rpb - 1) / rpb)),
+                       dim3(256), 0, st, (const float*)a.o, (const float*)a.dO, a.delta, rows);
+    return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t dq(const AttnArgs& a, hipStream_t st)
+{
+    const int BH = a.B * a.H;
+    const int nt = (a.T + kRows - 1) / kRows;
+    hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<HD>, dim3(nt * BH), dim3(kRows), 0, st,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (const float*)a.dO, (const float*)a.lse, (const float*)a.delta,
+                       (float*)a.dq, BH, a.T, nt, a.scale, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t dkdv(const AttnArgs& a, hipStream_t st)
+{
+    const int BH = a.B * a.H;
+    const int nt = (a.T + kRows - 1) / kRows;
+    hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<HD>, dim3(nt * BH), dim3(kRows), 0, st,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (const float*)a.dO, (const float*)a.lse, (const float*)a.delta,
+                       (float*)a.dk, (float*)a.dv, BH, a.T, a.scale, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t st)
+{
+    return a.D == 64 ? fwd<64>(a, st) : fwd<32>(a, st);
+}
+
+hipError_t launch_delta_f32(const AttnArgs& a, hipStream_t st)
+{
+    return a.D == 64 ? delta<64>(a, st) : delta<32>(a, st);
+}
+
+hipError_t launch_dq_f32(const AttnArgs& a, hipStream_t st)
+{
+    return a.D == 64 ? dq<64>(a, st) : dq<32>(a, st);
+}
+
+hipError_t launch_dkdv_f32(const AttnArgs& a, hipStream_t st)
+{
+    return a.D == 64 ? dkdv<64>(a, st) : dkdv<32>(a, st);
+}
+
+}  // namespace cattn

@@ -1,0 +1,34 @@
+// attn_kernels.h -- internal interface between the C ABI (attn_api.hip) and
+// the kernel launchers.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace cattn {
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;   // forward: output; backward: input
+    const void* dO;
+    void* o_out;     // forward output (same buffer as o)
+    void* dq;
+    void* dk;
+    void* dv;
+    float* lse;      // forward: output; backward: input
+    float* delta;    // backward workspace / output
+    int B, H, T, D;
+    float scale;
+};
+
+hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_delta_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_dq_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_dkdv_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t st);
+hipError_t launch_delta_f32(const AttnArgs& a, hipStream_t st);
+hipError_t launch_dq_f32(const AttnArgs& a, hipStream_t st);
+hipError_t launch_dkdv_f32(const AttnArgs& a, hipStream_t st);
+
+}  // namespace cattn

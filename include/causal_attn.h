@@ -1,0 +1,115 @@
+/*
+ * causal_attn.h -- C ABI of the MI355X (gfx950) causal multi-head
+ * self-attention library, libcausal_attn.so.
+ *
+ * The operation (forward) is the causal scaled dot-product attention of one
+ * head, applied independently to every (batch, head) pair:
+ *
+ *     S = scale * Q K^T,  S[i][j] = -inf for j > i  (keys after the query),
+ *     P = softmax over j of S[i][:],  O = P V,
+ *     lse[i] = log(sum_{j<=i} exp(S[i][j]))   (natural log),
+ *
+ * as defined by the CS336 from-scratch tutorial (lmnt.cn), section 5.1
+ * model.py, CausalSelfAttention.forward (scores times 1/sqrt(head dim), the
+ * tril mask filled with -inf, softmax over keys, weights times v), with the
+ * diagonal kept: the mask is tril(ones(T, T)) ("Train Your Own LLM from
+ * Scratch", section 1).  Section 3.3 of the tutorial states the mask's
+ * purpose: -inf above the diagonal, weight 0 after the softmax.  The backward
+ * is the exact gradient of that function; the pages train through it with
+ * loss.backward() (tutorial section 5.2, train.py).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers on the current HIP device.
+ *   - q, k, v, o, dO, dq, dk, dv: contiguous row-major [B][H][T][D] of the
+ *     element type `dtype` (D fastest).  Their addresses must be 16-byte
+ *     aligned.
+ *   - lse and delta: contiguous fp32 [B][H][T], 4-byte aligned.
+ *   - dtype: ATTN_F32 (float) or ATTN_BF16 (bfloat16 storage; every product
+ *     is accumulated in fp32).
+ *   - D must be 32 or 64.  B, H, T >= 1, any T (the last tile is ragged).
+ *   - scale must be finite and > 0 (the pages use 1/sqrt(D)).
+ *   - stream is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns without synchronising: buffers must stay
+ *     alive until the stream has run the work.
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     allocates no memory and keeps no mutable global state; calls on
+ *     different streams with disjoint buffers may run concurrently.
+ *   - Outputs are fully overwritten, never accumulated into.  No output may
+ *     overlap an input or another output.
+ *   - Errors: every argument check runs before any HIP call; on a non-zero
+ *     return no work was enqueued and no output was touched, except
+ *     ATTN_ERR_HIP, which reports a failed kernel launch (outputs undefined).
+ *     Results are deterministic: no atomics, fixed summation order.
+ */
+#ifndef CAUSAL_ATTN_H
+#define CAUSAL_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_F32 = 0,
+    ATTN_BF16 = 1
+} attn_dtype_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,          /* a required pointer is NULL              */
+    ATTN_ERR_SHAPE = 2,         /* B, H or T < 1                            */
+    ATTN_ERR_UNSUPPORTED_D = 3, /* D not in {32, 64}                        */
+    ATTN_ERR_DTYPE = 4,         /* dtype not ATTN_F32 / ATTN_BF16           */
+    ATTN_ERR_ALIGN = 5,         /* tensor not 16-byte (lse/delta 4-byte) aligned */
+    ATTN_ERR_OVERFLOW = 6,      /* T*D or the launch grid exceeds 2^31 - 1  */
+    ATTN_ERR_SCALE = 7,         /* scale not finite or not > 0              */
+    ATTN_ERR_ALIAS = 8,         /* an output overlaps an input or output    */
+    ATTN_ERR_HIP = 9            /* a kernel launch failed                   */
+} attn_status_t;
+
+/* Forward.  Reads q, k, v; writes o ([B][H][T][D], dtype) and lse
+ * ([B][H][T], fp32, natural log of the row's softmax normaliser over the
+ * scaled scores).  lse is what attn_bwd needs to recompute P. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int T, int D, float scale, int dtype, void* stream);
+
+/* Backward of L = sum(dO * O) for the forward above.  Reads q, k, v, o, lse
+ * (as written by attn_fwd with the same arguments) and dO; writes dq, dk, dv
+ * ([B][H][T][D], dtype).  delta is caller-owned fp32 [B][H][T] workspace; on
+ * return it holds Delta[i] = sum_d dO[i][d] * o[i][d], the softmax-backward
+ * row term.  Enqueues three kernels on `stream` (Delta, dQ, dK/dV). */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dO, void* dq, void* dk, void* dv,
+             float* delta, int B, int H, int T, int D, float scale, int dtype,
+             void* stream);
+
+/* The three stages attn_bwd enqueues, callable one by one with the same
+ * argument conventions.  attn_bwd_delta must complete (stream order) before
+ * attn_bwd_dq and attn_bwd_dkdv read delta; those two write disjoint outputs
+ * and may run in either order, or concurrently on two streams.
+ *
+ * attn_bwd_delta: delta[i] = sum_d dO[i][d] * o[i][d] (fp32 accumulation).
+ * attn_bwd_dq:    dq = scale * dS k, with P recomputed from lse and
+ *                 dS = P * (dO v^T - delta).
+ * attn_bwd_dkdv:  dk = scale * dS^T q and dv = P^T dO, same P and dS. */
+int attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int T,
+                   int D, int dtype, void* stream);
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                const float* lse, const float* delta, void* dq, int B, int H, int T,
+                int D, float scale, int dtype, void* stream);
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                  const float* lse, const float* delta, void* dk, void* dv, int B,
+                  int H, int T, int D, float scale, int dtype, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* attn_status_str(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int attn_abi_version(void);
+
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 0)
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAUSAL_ATTN_H */

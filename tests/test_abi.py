@@ -1,0 +1,213 @@
+"""C ABI contract tests that need no GPU.
+
+The library must load, export every symbol include/causal_attn.h declares, and
+reject every bad argument with its status code before any HIP call.  The
+pointers below are never dereferenced: each call returns during validation.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_head_self_amd as cat
+from causal_head_self_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "causal_attn.h")
+
+# Fake, distinct, 16-byte-aligned addresses far apart (never dereferenced).
+P = [0x10000000 * (i + 1) for i in range(12)]
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_python_exports():
+    assert _declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cat.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings():
+    lib = cat.load_library()
+    assert lib.attn_abi_version() == _lib.ABI_VERSION
+    seen = set()
+    for code in range(0, 10):
+        s = cat.attn_status_str(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 10
+    assert cat.attn_status_str(1234) == "unknown status"
+    assert cat.attn_status_str(-1) == "unknown status"
+
+
+def _fwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, T=17, D=64, scale=0.125,
+             dtype=1, stream=None)
+    a.update(kw)
+    return cat.load_library().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                       a["T"], a["D"], a["scale"], a["dtype"], a["stream"])
+
+
+def _bwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], dO=P[5], dq=P[6], dk=P[7], dv=P[8],
+             delta=P[9], B=2, H=3, T=17, D=64, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return cat.load_library().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"],
+                                       a["dq"], a["dk"], a["dv"], a["delta"], a["B"], a["H"],
+                                       a["T"], a["D"], a["scale"], a["dtype"], a["stream"])
+
+
+def _delta(**kw):
+    a = dict(o=P[3], dO=P[5], delta=P[9], B=2, H=3, T=17, D=64, dtype=1, stream=None)
+    a.update(kw)
+    return cat.load_library().attn_bwd_delta(a["o"], a["dO"], a["delta"], a["B"], a["H"],
+                                             a["T"], a["D"], a["dtype"], a["stream"])
+
+
+def _dq(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], dO=P[5], lse=P[4], delta=P[9], dq=P[6], B=2, H=3, T=17,
+             D=64, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return cat.load_library().attn_bwd_dq(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"],
+                                          a["dq"], a["B"], a["H"], a["T"], a["D"], a["scale"],
+                                          a["dtype"], a["stream"])
+
+
+def _dkdv(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], dO=P[5], lse=P[4], delta=P[9], dk=P[7], dv=P[8], B=2, H=3,
+             T=17, D=64, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return cat.load_library().attn_bwd_dkdv(a["q"], a["k"], a["v"], a["dO"], a["lse"],
+                                            a["delta"], a["dk"], a["dv"], a["B"], a["H"],
+                                            a["T"], a["D"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("call,names", [
+    (_delta, ["o", "dO", "delta"]),
+    (_dq, ["q", "k", "v", "dO", "lse", "delta", "dq"]),
+    (_dkdv, ["q", "k", "v", "dO", "lse", "delta", "dk", "dv"]),
+])
+def test_stage_null_pointers(call, names):
+    for name in names:
+        assert call(**{name: None}) == 1, name
+
+
+@pytest.mark.parametrize("call", [_delta, _dq, _dkdv])
+def test_stage_validation(call):
+    assert call(T=0) == 2
+    assert call(dtype=3) == 4
+    assert call(D=128) == 3
+    assert call(T=2 ** 30) == 6
+
+
+def test_stage_alignment_and_aliasing():
+    assert _delta(delta=P[9] + 2) == 5
+    assert _delta(o=P[3] + 8) == 5
+    assert _delta(delta=P[5]) == 8            # delta inside dO
+    assert _dq(dq=P[2]) == 8                  # dq is v
+    assert _dq(dq=P[6] + 4) == 5
+    assert _dq(scale=-2.0) == 7
+    assert _dkdv(dk=P[8]) == 8                # dk is dv
+    assert _dkdv(dv=P[9]) == 8                # dv overlaps delta
+    assert _dkdv(scale=float("nan")) == 7
+    assert _dkdv(lse=P[4] + 1) == 5
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_fwd_null_pointer(name):
+    assert _fwd(**{name: None}) == 1
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse", "dO", "dq", "dk", "dv", "delta"])
+def test_bwd_null_pointer(name):
+    assert _bwd(**{name: None}) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0), dict(B=-1), dict(T=-5)])
+def test_bad_shape(kw):
+    assert _fwd(**kw) == 2
+    assert _bwd(**kw) == 2
+
+
+@pytest.mark.parametrize("D", [0, 1, 16, 48, 96, 128, 256])
+def test_unsupported_head_dim(D):
+    assert _fwd(D=D) == 3
+    assert _bwd(D=D) == 3
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 7])
+def test_bad_dtype(dtype):
+    assert _fwd(dtype=dtype) == 4
+    assert _bwd(dtype=dtype) == 4
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o"])
+def test_fwd_misaligned(name):
+    base = {"q": P[0], "k": P[1], "v": P[2], "o": P[3]}[name]
+    assert _fwd(**{name: base + 8}) == 5
+
+
+def test_lse_alignment():
+    assert _fwd(lse=P[4] + 2) == 5
+    assert _bwd(delta=P[9] + 1) == 5
+
+
+@pytest.mark.parametrize("name", ["dO", "dq", "dk", "dv"])
+def test_bwd_misaligned(name):
+    base = {"dO": P[5], "dq": P[6], "dk": P[7], "dv": P[8]}[name]
+    assert _bwd(**{name: base + 4}) == 5
+
+
+def test_overflow():
+    assert _fwd(T=2 ** 30, D=64) == 6
+    assert _fwd(B=2 ** 20, H=2 ** 10, T=2 ** 10, D=32) == 6
+    assert _bwd(T=2 ** 26, D=64) == 6
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_bad_scale(scale):
+    assert _fwd(scale=scale) == 7
+    assert _bwd(scale=scale) == 7
+
+
+def test_fwd_aliasing():
+    assert _fwd(o=P[0]) == 8          # o is q
+    assert _fwd(lse=P[2] + 64) == 8   # lse inside v
+    assert _fwd(lse=P[3] + 16) == 8   # lse inside o
+
+
+def test_bwd_aliasing():
+    assert _bwd(dq=P[0]) == 8         # dq is q
+    assert _bwd(dk=P[6]) == 8         # dk is dq
+    assert _bwd(delta=P[4]) == 8      # delta is lse
+    assert _bwd(dv=P[5] + 32) == 8    # dv overlaps dO
+
+
+def test_checks_run_in_documented_order():
+    """NULL is reported before shape, shape before dtype, dtype before D."""
+    assert _fwd(q=None, B=0, dtype=9, D=7) == 1
+    assert _fwd(B=0, dtype=9, D=7) == 2
+    assert _fwd(dtype=9, D=7) == 4
+    assert _fwd(D=7, scale=-1.0) == 3
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 32)
+    with pytest.raises(ValueError):
+        cat.attn_fwd(q, q, q, q.clone(), torch.zeros(1, 1, 4))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _lib.load_library(str(tmp_path / "libcausal_attn.so"))

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (max abs error, element by element): 1e-4 for fp32 inputs and 2e-2
+for bf16 inputs with unit-variance values.  The oracle consumes exactly the
+values the GPU receives (bf16 inputs widened to fp64, scale widened from its
+float32 value).  Full-size configurations are checked head by head on sampled
+(batch, head) pairs, in the launch configuration the benchmark times, plus
+properties that hold for every head (exact row 0, determinism).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import ATTN_CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_attention(q, k, v, dO, scale, with_bwd=True):
+    """Run attn_fwd (+ attn_bwd) via the C ABI on device copies of CPU tensors."""
+    import causal_head_self_amd as cat
+    dev = torch.device("cuda")
+    q, k, v, dO = (t.to(dev).contiguous() for t in (q, k, v, dO))
+    B, H, T, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    cat.attn_fwd(q, k, v, o, lse, scale)
+    out = {"o": o, "lse": lse}
+    if with_bwd:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        delta = torch.empty_like(lse)
+        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale)
+        out.update(dq=dq, dk=dk, dv=dv, delta=delta)
+    torch.cuda.synchronize()
+    return {name: t.float().cpu().numpy().astype(np.float64) for name, t in out.items()}
+
+
+def oracle_attention(q, k, v, dO, scale, with_bwd=True):
+    s = oracle.widen_scale(scale)
+    o, lse = oracle.attn_fwd(q, k, v, s)
+    out = {"o": o, "lse": lse}
+    if with_bwd:
+        dq, dk, dv, delta = oracle.attn_bwd(q, k, v, dO, s)
+        out.update(dq=dq, dk=dk, dv=dv, delta=delta)
+    return out
+
+
+def delta_bound(ref, dO):
+    """Delta is defined on the stored output (sum_d dO_id o_id, o in the input
+    dtype), so its error is the bf16 storage rounding of o (relative 2^-9,
+    taken as 2^-8 to cover the kernel's own error in o) plus an absolute
+    4e-3 per element for o near 0, weighted by |dO|."""
+    g = np.abs(dO.double().numpy() if hasattr(dO, "double") else dO)
+    return np.sum(g * (2.0 ** -8 * np.abs(ref["o"]) + 4e-3), axis=-1) + 1e-4
+
+
+def assert_close(got, ref, tol, label, delta_tol=None):
+    for name in ref:
+        if name == "delta" and delta_tol is not None:
+            bad = np.abs(got[name] - ref[name]) > delta_tol
+            assert not np.any(bad), f"{label} delta beyond its derived bound at {np.argwhere(bad)[:5]}"
+            continue
+        err = np.abs(got[name] - ref[name])
+        worst = float(err.max()) if err.size else 0.0
+        idx = np.unravel_index(int(err.argmax()), err.shape) if err.size else ()
+        assert np.all(np.isfinite(got[name])), f"{label} {name}: non-finite output"
+        assert worst <= tol, (f"{label} {name}: max abs err {worst:.3e} at {idx} "
+                              f"(got {got[name][idx]:.6f}, ref {ref[name][idx]:.6f}, "
+                              f"max|ref| {float(np.abs(ref[name]).max()):.3f})")
+
+
+def check_case(B, H, T, D, dtype, seed=workloads.SEED, with_bwd=True):
+    _note(f"[parity] B={B} H={H} T={T} D={D} dtype={dtype} seed={seed}")
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, dtype, seed)
+    scale = 1.0 / math.sqrt(D)
+    got = gpu_attention(q, k, v, dO, scale, with_bwd)
+    ref = oracle_attention(q, k, v, dO, scale, with_bwd)
+    dtol = delta_bound(ref, dO) if dtype == "bf16" and with_bwd else None
+    assert_close(got, ref, TOL[dtype], f"B{B} H{H} T{T} D{D} {dtype}", dtol)
+    return got, ref
+
+
+# ---------------------------------------------------------------------------
+# small and ragged shapes: every element
+# ---------------------------------------------------------------------------
+
+def test_tiny_config_fp32():
+    c = ATTN_CONFIGS["tiny"]
+    check_case(c.B, c.H, c.T, c.D, c.dtype)
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 1, 64), (1, 1, 2, 32), (1, 1, 63, 64), (1, 1, 64, 64), (1, 1, 65, 64),
+    (2, 3, 127, 64), (2, 2, 129, 64), (1, 2, 300, 64), (2, 1, 1000, 32), (1, 1, 257, 32),
+    (3, 1, 513, 64),
+])
+def test_bf16_shapes_and_ragged_tails(shape):
+    check_case(*shape, "bf16", seed=100 + sum(shape))
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 1, 32), (1, 2, 100, 64), (2, 1, 130, 32), (1, 1, 300, 32),
+])
+def test_fp32_shapes_and_ragged_tails(shape):
+    check_case(*shape, "f32", seed=200 + sum(shape))
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations: sampled heads, element by element
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["gpt2s", "gpt400m", "long"])
+def test_full_config_sampled_heads(name):
+    c = ATTN_CONFIGS[name]
+    _note(f"[parity] config {name} B={c.B} H={c.H} T={c.T} D={c.D} {c.dtype} (sampled heads)")
+    q, k, v, dO = workloads.config_inputs(c)
+    got = gpu_attention(q, k, v, dO, c.scale)
+    # every head: row 0 sees only key 0, so o[.., 0, :] == v[.., 0, :] bit for bit
+    v_np = v.float().numpy().astype(np.float64)
+    assert np.array_equal(got["o"][:, :, 0, :], v_np[:, :, 0, :])
+    for name_ in got:
+        assert np.all(np.isfinite(got[name_])), name_
+    heads = [(0, 0), (c.B // 2, c.H // 3), (c.B - 1, c.H - 1)]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle_attention(q[sl], k[sl], v[sl], dO[sl], c.scale)
+        sub = {key: got[key][sl] for key in ref}
+        assert_close(sub, ref, TOL[c.dtype], f"{name} head (b={b}, h={h})",
+                     delta_bound(ref, dO[sl]))
+
+
+# ---------------------------------------------------------------------------
+# exactness pins and invariants on the GPU
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_constant_values_give_constant_output(dtype):
+    B, H, T, D = 2, 2, 300, 64
+    q, k, _, dO = workloads.attention_inputs(B, H, T, D, dtype, seed=7)
+    v = torch.ones_like(q)
+    got = gpu_attention(q, k, v, dO, 1 / math.sqrt(D), with_bwd=False)
+    assert np.max(np.abs(got["o"] - 1.0)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_queries_give_prefix_mean(dtype):
+    B, H, T, D = 1, 2, 200, 32
+    _, k, v, dO = workloads.attention_inputs(B, H, T, D, dtype, seed=9)
+    q = torch.zeros_like(k)
+    got = gpu_attention(q, k, v, dO, 1 / math.sqrt(D), with_bwd=False)
+    vv = v.double().numpy()
+    prefix = np.cumsum(vv, axis=2) / np.arange(1, T + 1)[None, None, :, None]
+    assert np.max(np.abs(got["o"] - prefix)) <= TOL[dtype]
+    assert np.max(np.abs(got["lse"] - np.log(np.arange(1, T + 1)))) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_causality_is_exact(dtype):
+    """Perturbing q, k, v in rows > cut leaves o, lse rows <= cut bit-identical."""
+    B, H, T, D = 1, 2, 333, 64
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, dtype, seed=11)
+    s = 1 / math.sqrt(D)
+    base = gpu_attention(q, k, v, dO, s, with_bwd=False)
+    for cut in (0, 63, 64, 127, 200):
+        q2, k2, v2 = q.clone(), k.clone(), v.clone()
+        q2[:, :, cut + 1:] = -q2[:, :, cut + 1:]
+        k2[:, :, cut + 1:] = 2 * k2[:, :, cut + 1:]
+        v2[:, :, cut + 1:] = 3 * v2[:, :, cut + 1:]
+        got = gpu_attention(q2, k2, v2, dO, s, with_bwd=False)
+        assert np.array_equal(got["o"][:, :, :cut + 1], base["o"][:, :, :cut + 1]), cut
+        assert np.array_equal(got["lse"][:, :, :cut + 1], base["lse"][:, :, :cut + 1]), cut
+
+
+def test_dq_row0_vanishes_and_dk_sums_to_zero():
+    """A one-key softmax has no gradient (dq row 0 = 0); rows of dS sum to 0,
+    so sum_j dk_j = 0; sum_j dv_j = sum_i dO_i.  Within bf16 rounding."""
+    B, H, T, D = 2, 2, 256, 64
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", seed=13)
+    got = gpu_attention(q, k, v, dO, 1 / math.sqrt(D))
+    assert np.max(np.abs(got["dq"][:, :, 0, :])) <= 1e-3
+    # bound: bf16 output rounding (relative 2^-9, taken as 2^-8) summed over keys
+    bound_k = np.abs(got["dk"]).sum(axis=2) * 2.0 ** -8 + 1e-3
+    assert np.all(np.abs(got["dk"].sum(axis=2)) <= bound_k)
+    bound_v = np.abs(got["dv"]).sum(axis=2) * 2.0 ** -8 + 1e-3
+    assert np.all(np.abs(got["dv"].sum(axis=2) - dO.double().numpy().sum(axis=2)) <= bound_v)
+
+
+def test_deterministic_bitwise():
+    c = ATTN_CONFIGS["gpt2s"]
+    q, k, v, dO = workloads.attention_inputs(2, c.H, c.T, c.D, c.dtype, seed=17)
+    a = gpu_attention(q, k, v, dO, c.scale)
+    b = gpu_attention(q, k, v, dO, c.scale)
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name
+
+
+def test_autograd_function_matches_abi():
+    import causal_head_self_amd as cat
+    B, H, T, D = 2, 3, 190, 64
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", seed=19)
+    ref = gpu_attention(q, k, v, dO, 1 / math.sqrt(D))
+    tq, tk, tv = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = cat.causal_attention(tq, tk, tv)
+    o.backward(dO.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(o.detach().float().cpu().numpy(), ref["o"])
+    assert np.array_equal(tq.grad.float().cpu().numpy(), ref["dq"])
+    assert np.array_equal(tk.grad.float().cpu().numpy(), ref["dk"])
+    assert np.array_equal(tv.grad.float().cpu().numpy(), ref["dv"])
+
+
+def test_non_default_stream():
+    import causal_head_self_amd as cat
+    B, H, T, D = 1, 2, 150, 64
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", seed=23)
+    ref = gpu_attention(q, k, v, dO, 0.125, with_bwd=False)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+        cat.attn_fwd(qd, kd, vd, o, lse, 0.125, stream=s)
+    s.synchronize()
+    assert np.array_equal(o.float().cpu().numpy(), ref["o"])
