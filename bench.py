@@ -34,6 +34,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["causal_head_self_amd/csrc/attn_bf16.hip",
+                  "causal_head_self_amd/csrc/attn_bf16_d64.hip",
                   "causal_head_self_amd/csrc/attn_device.h"]
 
 
@@ -50,13 +51,12 @@ def kernel_work(cfg):
     over the causal half of one head is T^2 * D flops.  The forward credits 2
     GEMMs (S, PV); the backward 5: dK/dV is credited with S, dP, dV, dK and dQ
     with its own dQ product (its recomputed S and dP are not credited again).
-    Delta is HBM work: read o and dO, write delta."""
+    The dQ kernel also forms Delta (a row sum of dO * o), which is not
+    credited."""
     B, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
     g = float(B * H * T * T * D)
-    es = 2 if cfg.dtype == "bf16" else 4
     return {
         "fwd": {"flops": 2 * g},
-        "delta": {"bytes": float(B * H * T * (2 * D * es + 4))},
         "dq": {"flops": 1 * g},
         "dkdv": {"flops": 4 * g},
     }
@@ -163,19 +163,17 @@ def main() -> int:
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
     # per-kernel: the same K steps with an event between consecutive launches
-    names = ["fwd", "delta", "dq", "dkdv"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    names = ["fwd", "dq", "dkdv"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e in evs:
         e[0].record(stream)
         cat.attn_fwd(q, k, v, o, lse, scale, stream)
         e[1].record(stream)
-        cat.attn_bwd_delta(o, dO, delta, stream)
+        cat.attn_bwd_dq(q, k, v, o, dO, lse, delta, dq, scale, stream)
         e[2].record(stream)
-        cat.attn_bwd_dq(q, k, v, dO, lse, delta, dq, scale, stream)
-        e[3].record(stream)
         cat.attn_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, scale, stream)
-        e[4].record(stream)
+        e[3].record(stream)
     torch.cuda.synchronize()
     kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                for i, n in enumerate(names)}

@@ -7,7 +7,7 @@ the computation.  PyTorch supplies device memory and streams.
 
     attn_fwd(q, k, v, o, lse, scale)                        -- C ABI attn_fwd
     attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale) -- C ABI attn_bwd
-    attn_bwd_delta / attn_bwd_dq / attn_bwd_dkdv            -- its three stages
+    attn_bwd_dq / attn_bwd_dkdv                             -- its two stages
     causal_attention(q, k, v, scale=None)                   -- autograd op
 
 Tensors are contiguous [B, H, T, D] (D in {32, 64}) of float32 or bfloat16 on
@@ -23,7 +23,8 @@ from ._lib import (ABI_VERSION, ATTN_BF16, ATTN_F32, EXPORTS, LIB_PATH, AttnErro
                    load_library, status_str)
 
 __all__ = [
-    "attn_fwd", "attn_bwd", "attn_bwd_delta", "attn_bwd_dq", "attn_bwd_dkdv", "attn_status_str", "causal_attention", "AttnError",
+    "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_status_str",
+    "causal_attention", "AttnError",
     "ATTN_F32", "ATTN_BF16", "load_library", "LIB_PATH", "EXPORTS", "ABI_VERSION",
 ]
 
@@ -83,22 +84,15 @@ def attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale: float | None = None,
     check(rc)
 
 
-def attn_bwd_delta(o, dO, delta, stream=None) -> None:
-    """C ABI attn_bwd_delta: delta = rowsum(dO * o)."""
-    B, H, T, D = _shape(o)
-    rc = load_library().attn_bwd_delta(_ptr(o, "o"), _ptr(dO, "dO"), _ptr(delta, "delta"),
-                                       B, H, T, D, _dtype_code(o), _stream(stream))
-    check(rc)
-
-
-def attn_bwd_dq(q, k, v, dO, lse, delta, dq, scale: float | None = None, stream=None) -> None:
-    """C ABI attn_bwd_dq."""
+def attn_bwd_dq(q, k, v, o, dO, lse, delta, dq, scale: float | None = None,
+                stream=None) -> None:
+    """C ABI attn_bwd_dq: writes delta and dq."""
     B, H, T, D = _shape(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rc = load_library().attn_bwd_dq(
-        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(dO, "dO"), _ptr(lse, "lse"),
-        _ptr(delta, "delta"), _ptr(dq, "dq"), B, H, T, D, scale, _dtype_code(q),
-        _stream(stream))
+        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(o, "o"), _ptr(dO, "dO"),
+        _ptr(lse, "lse"), _ptr(delta, "delta"), _ptr(dq, "dq"), B, H, T, D, scale,
+        _dtype_code(q), _stream(stream))
     check(rc)
 
 

@@ -28,8 +28,8 @@ STATUS = {
 }
 
 # every symbol include/causal_attn.h declares
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_delta", "attn_bwd_dq", "attn_bwd_dkdv",
-           "attn_status_str", "attn_abi_version")
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_status_str",
+           "attn_abi_version")
 ABI_VERSION = (1 << 16) | 0
 
 
@@ -61,9 +61,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd.restype = _int
     lib.attn_bwd.argtypes = [_vp] * 10 + [_int, _int, _int, _int, ctypes.c_float, _int, _vp]
     lib.attn_bwd.restype = _int
-    lib.attn_bwd_delta.argtypes = [_vp] * 3 + [_int] * 5 + [_vp]
-    lib.attn_bwd_delta.restype = _int
-    lib.attn_bwd_dq.argtypes = [_vp] * 7 + [_int] * 4 + [ctypes.c_float, _int, _vp]
+    lib.attn_bwd_dq.argtypes = [_vp] * 8 + [_int] * 4 + [ctypes.c_float, _int, _vp]
     lib.attn_bwd_dq.restype = _int
     lib.attn_bwd_dkdv.argtypes = [_vp] * 8 + [_int] * 4 + [ctypes.c_float, _int, _vp]
     lib.attn_bwd_dkdv.restype = _int

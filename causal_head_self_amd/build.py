@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcausal_attn.so")
-SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_f32.hip"]
+SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_bf16_d64.hip", "attn_f32.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -27,9 +27,15 @@ FLAGS = [
 ]
 
 
+# Kernel-only sources: NaN inputs are outside the contract (results unspecified),
+# so fmax needs no NaN canonicalisation.  Not used for attn_api.hip, whose
+# argument checks must see NaN.
+KERNEL_ONLY_FLAGS = {"attn_bf16_d64.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *KERNEL_ONLY_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

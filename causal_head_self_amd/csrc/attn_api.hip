@@ -111,38 +111,22 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return status(dtype == ATTN_BF16 ? cattn::launch_fwd_bf16(a, s) : cattn::launch_fwd_f32(a, s));
 }
 
-int attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int T, int D,
-                   int dtype, void* stream)
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, float* delta, void* dq, int B, int H, int T, int D, float scale,
+                int dtype, void* stream)
 {
-    const Buf in[2] = {{o, false}, {dO, false}};
-    const Buf out[1] = {{delta, true}};
-    const int st = validate(in, out, B, H, T, D, 1.0f, dtype);
-    if (st != ATTN_OK) return st;
-    cattn::AttnArgs a = make_args(B, H, T, D, 1.0f);
-    a.o = o;
-    a.dO = dO;
-    a.delta = delta;
-    hipStream_t s = (hipStream_t)stream;
-    return status(dtype == ATTN_BF16 ? cattn::launch_delta_bf16(a, s)
-                                     : cattn::launch_delta_f32(a, s));
-}
-
-int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                const float* delta, void* dq, int B, int H, int T, int D, float scale, int dtype,
-                void* stream)
-{
-    const Buf in[6] = {{q, false}, {k, false}, {v, false}, {dO, false}, {lse, true},
-                       {delta, true}};
-    const Buf out[1] = {{dq, false}};
+    const Buf in[6] = {{q, false}, {k, false}, {v, false}, {o, false}, {dO, false}, {lse, true}};
+    const Buf out[2] = {{delta, true}, {dq, false}};
     const int st = validate(in, out, B, H, T, D, scale, dtype);
     if (st != ATTN_OK) return st;
     cattn::AttnArgs a = make_args(B, H, T, D, scale);
     a.q = q;
     a.k = k;
     a.v = v;
+    a.o = o;
     a.dO = dO;
     a.lse = const_cast<float*>(lse);
-    a.delta = const_cast<float*>(delta);
+    a.delta = delta;
     a.dq = dq;
     hipStream_t s = (hipStream_t)stream;
     return status(dtype == ATTN_BF16 ? cattn::launch_dq_bf16(a, s) : cattn::launch_dq_f32(a, s));
@@ -192,8 +176,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     a.dv = dv;
     hipStream_t s = (hipStream_t)stream;
     const bool bf = dtype == ATTN_BF16;
-    hipError_t e = bf ? cattn::launch_delta_bf16(a, s) : cattn::launch_delta_f32(a, s);
-    if (e == hipSuccess) e = bf ? cattn::launch_dq_bf16(a, s) : cattn::launch_dq_f32(a, s);
+    hipError_t e = bf ? cattn::launch_dq_bf16(a, s) : cattn::launch_dq_f32(a, s);
     if (e == hipSuccess) e = bf ? cattn::launch_dkdv_bf16(a, s) : cattn::launch_dkdv_f32(a, s);
     return status(e);
 }

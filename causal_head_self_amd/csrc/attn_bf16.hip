@@ -459,22 +459,19 @@ static hipError_t launch_dkdv(const AttnArgs& a, hipStream_t st)
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t st)
 {
-    return a.D == 64 ? launch_fwd<64>(a, st) : launch_fwd<32>(a, st);
-}
-
-hipError_t launch_delta_bf16(const AttnArgs& a, hipStream_t st)
-{
-    return a.D == 64 ? launch_delta<64>(a, st) : launch_delta<32>(a, st);
+    return a.D == 64 ? launch_fwd_bf16_d64(a, st) : launch_fwd<32>(a, st);
 }
 
 hipError_t launch_dq_bf16(const AttnArgs& a, hipStream_t st)
 {
-    return a.D == 64 ? launch_dq<64>(a, st) : launch_dq<32>(a, st);
+    if (a.D == 64) return launch_dq_bf16_d64(a, st);  // Delta fused into the dQ kernel
+    const hipError_t e = launch_delta<32>(a, st);
+    return e == hipSuccess ? launch_dq<32>(a, st) : e;
 }
 
 hipError_t launch_dkdv_bf16(const AttnArgs& a, hipStream_t st)
 {
-    return a.D == 64 ? launch_dkdv<64>(a, st) : launch_dkdv<32>(a, st);
+    return a.D == 64 ? launch_dkdv_bf16_d64(a, st) : launch_dkdv<32>(a, st);
 }
 
 }  // namespace cattn

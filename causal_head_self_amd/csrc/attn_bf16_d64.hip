@@ -1,0 +1,612 @@
+// attn_bf16_d64.hip -- gfx950 kernels for causal multi-head self-attention
+// at head dim 64, bf16 storage / fp32 accumulation: forward, dQ and dK/dV.
+//
+// Same operation as attn_bf16.hip (CS336 from-scratch tutorial, lmnt.cn,
+// section 5.1 CausalSelfAttention.forward; the tril mask keeps the diagonal,
+// "Train Your Own LLM from Scratch", section 1; the backward is the exact
+// gradient the pages train through, tutorial section 5.2).  This file is the
+// head-dim-64 specialisation that the GPT-2-small and ~400M shapes run:
+//
+//  * Streamed tiles (64 rows x 128 bytes) travel HBM -> LDS with the
+//    asynchronous global_load_lds (16 bytes per lane; one wave instruction
+//    fills 8 consecutive rows), double-buffered: the copy of tile j+1 is in
+//    flight while tile j is multiplied, with one barrier per tile.
+//  * LDS tiles are row-major with the 16-byte chunks of each row XOR-swizzled
+//    (chunk ^ swz(row)), so that both the row reads of the MFMA A operand
+//    (ds_read_b128, 16 rows per pass) and the transposing reads
+//    (ds_read_b64_tr_b16, 4 rows x 64 bytes per pass) are bank-conflict free.
+//  * Transposed operands (V^T, K^T, Q^T, dO^T) come straight from the
+//    row-major tile through ds_read_b64_tr_b16: inside each 16-lane group,
+//    lane i receives element i%4 of the 8-byte chunks fetched by lanes
+//    4e + i/4 (e = 0..3), i.e. 4 consecutive rows of one column.
+//  * Online softmax (forward): row max in-lane with v_max3 plus one
+//    v_permlane32_swap; the running max is only raised when it grows by more
+//    than 2^8 in the exponent (lazy rescale), so most tiles skip rescaling
+//    the accumulators; the row sum is taken on the bf16 P that feeds the PV
+//    product, two at a time with v_dot2_f32_bf16.
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace cattn {
+namespace d64 {
+
+constexpr int HD = 64;
+constexpr int kThreads = 256;
+constexpr int kRowsPerWG = 128;  // queries (forward, dQ) or keys (dK/dV) per workgroup
+constexpr int kTile = 64;        // rows per streamed tile
+constexpr int kTileBytes = kTile * HD * 2;
+constexpr float kLazyRescale = 8.0f;  // log2 growth of the running max that forces a rescale
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// XOR key of row r: a bijection of (r >> 1) & 7 whose value for the row pairs
+// {4a, 4a+1} and {4a+2, 4a+3} differs in bit 2.
+__device__ __forceinline__ int swz(int r)
+{
+    const int s = (r >> 1) & 7;
+    return ((s & 1) << 2) | (s >> 1);
+}
+
+// Byte offset of 16-byte chunk `c` of row `r` in a swizzled tile.
+__device__ __forceinline__ int chunk_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
+
+// Asynchronous copy of rows [row0, row0 + 64) of a [T][64] bf16 head into a
+// swizzled LDS tile.  Rows >= T read row T-1 instead (always valid memory);
+// the kernels mask those rows.  Each of the 4 waves moves 16 rows.
+__device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restrict__ head,
+                                                int row0, int T, int wave, int lane)
+{
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int rb = wave * 16 + it * 8;     // first row of this 1 KB block
+        const int r = rb + (lane >> 3);        // row written by this lane
+        const int c = (lane & 7) ^ swz(r);     // logical chunk that lands in physical chunk lane&7
+        const int g = min(row0 + r, T - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(head + (size_t)g * HD + c * 8),
+                                         (__attribute__((address_space(3))) void*)(tile + rb * 128),
+                                         16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_async_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ bf16x8 lds_row_read(const char* tile, int off)
+{
+    return *(const bf16x8*)(tile + off);
+}
+
+// Two transposing reads -> the 8-element A operand of one k-step.
+__device__ __forceinline__ bf16x8 lds_tr_read(const char* tile, int off0, int off1)
+{
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off0));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + off1));
+    const v4s cat[2] = {lo, hi};
+    return *(const bf16x8*)cat;
+}
+
+// Combined value over lanes l and l ^ 32 (max or sum).
+__device__ __forceinline__ float halves_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Per-lane LDS offsets of the operand reads (constant over the kernel).
+struct Offsets {
+    int nat[4];     // row read: row li, chunk 2*ks + hi   (add 4096 for rows 32..63)
+    int tr[2][2];   // transposed read [half][dt]          (add 2048 per k-step)
+    __device__ __forceinline__ Offsets(int lane)
+    {
+        const int li = lane & 31, hi = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) nat[ks] = chunk_off(li, 2 * ks + hi);
+        const int j = lane & 15, g16 = lane >> 4;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const int row = 8 * half + 4 * hi + (j >> 2);
+                const int chunk = 2 * (2 * dt + (g16 & 1)) + ((j & 3) >> 1);
+                tr[half][dt] = chunk_off(row, chunk) + 8 * (j & 1);
+            }
+    }
+};
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& acc, int first)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)acc[first + e];
+    return r;
+}
+
+// sum of 8 bf16 values in fp32, two per v_dot2_f32_bf16
+__device__ __forceinline__ float sum8(bf16x8 v, float acc)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        bf16x2 p = {v[e], v[e + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+    }
+    return acc;
+}
+
+// S = A B over the 64 rows of an LDS tile: rows 0..31 -> s0, rows 32..63 -> s1.
+// A is read from the tile (row reads), B comes from registers.
+__device__ __forceinline__ void tile_product(const char* tile, const Offsets& off,
+                                             const bf16x8 (&breg)[4], f32x16& s0, f32x16& s1)
+{
+    bf16x8 a[8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        a[ks] = lds_row_read(tile, off.nat[ks]);
+        a[4 + ks] = lds_row_read(tile, 4096 + off.nat[ks]);
+    }
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        s0 = mfma32x32x16(a[ks], breg[ks], s0);
+        s1 = mfma32x32x16(a[4 + ks], breg[ks], s1);
+    }
+}
+
+// Causal mask of a (key-subtile, query-lane) score tile: element r of s0
+// holds row 8(r/4) + 4hi + r%4 of the tile (+32 in s1); it stays iff that
+// row offset is <= lim, otherwise it becomes -inf.
+__device__ __forceinline__ void mask_upto(f32x16& s0, f32x16& s1, int lim)
+{
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + (r & 3);
+        s0[r] = kk <= lim ? s0[r] : -INFINITY;
+        s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// forward: 128 queries per workgroup (32 per wave), 64-key tiles.
+// Software-pipelined: step j issues the S^T MFMAs of tile j+1 before the
+// softmax of tile j, so the matrix cores run while the VALU takes the exps;
+// K tiles run one tile ahead of V tiles through LDS.  Every wave needs tiles
+// 0..last_w; only the last one crosses its diagonal, so only that step masks
+// (its compares depend on the wave alone and are hoisted out of the loop).
+// The loop is unrolled by two so the score registers alternate without copies.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_d64_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int n_qtiles, float scale,
+    float scale_log2)
+{
+    __shared__ __attribute__((aligned(1024))) char sKb[2][kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sVb[2][kTileBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, hi = lane >> 5;
+    const int bh = blockIdx.x % BH;
+    const int qt = n_qtiles - 1 - blockIdx.x / BH;  // heaviest tiles first
+    const size_t head = (size_t)bh * T * HD;
+    const bf16* Kh = K + head;
+    const bf16* Vh = V + head;
+    const int q0w = qt * kRowsPerWG + wave * 32;  // wave-uniform
+    const int qrow = q0w + li;
+    const Offsets off(lane);
+
+    const int kv_end = min(T, qt * kRowsPerWG + kRowsPerWG);
+    const int n_kv = (kv_end + kTile - 1) / kTile;
+    const int last_w = min(n_kv - 1, (q0w + 31) / kTile);  // tiles 0..last_w-1 are fully visible
+
+    tile_load_async(sKb[0], Kh, 0, T, wave, lane);
+    tile_load_async(sVb[0], Vh, 0, T, wave, lane);
+    if (n_kv > 1) tile_load_async(sKb[1], Kh, kTile, T, wave, lane);
+
+    bf16x8 qreg[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        qreg[ks] = (qrow < T) ? *(const bf16x8*)(Q + head + (size_t)qrow * HD + 16 * ks + 8 * hi)
+                              : zero_bf16x8();
+    f32x16 oacc[2] = {f32x16{}, f32x16{}};
+    float m = -INFINITY;  // running max (raw dot-product units), shared by lanes l, l^32
+    float l = 0.f;        // this lane's part of the normaliser
+
+    // softmax of tile j (scores in s0, s1) and O^T += V^T P^T
+    auto softmax_pv = [&](bool kMask, int j, f32x16& s0, f32x16& s1) {
+        const int k0 = j * kTile;
+        bool two = true;  // keys 32..63 of the tile are visible to some row of the wave
+        if (kMask) {
+            two = k0 + 32 <= q0w + 31;
+            mask_upto(s0, s1, qrow - k0 - 4 * hi);
+        }
+        float mt = fmaxf(s0[0], fmaxf(s0[1], s0[2]));
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) mt = fmaxf(mt, fmaxf(s0[r], s0[r + 1]));
+        mt = fmaxf(mt, fmaxf(s0[15], s1[0]));
+#pragma unroll
+        for (int r = 1; r < 15; r += 2) mt = fmaxf(mt, fmaxf(s1[r], s1[r + 1]));
+        mt = fmaxf(mt, s1[15]);
+        mt = halves_max(mt);
+        const float m_new = fmaxf(m, mt);
+        if (__builtin_expect(__any((m_new - m) * scale_log2 > kLazyRescale), 0)) {
+            const float alpha = fast_exp2((m - m_new) * scale_log2);
+            m = m_new;
+            l *= alpha;
+            oacc[0] *= alpha;
+            oacc[1] *= alpha;
+        }
+        const float mc = m * scale_log2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s0[r] = fast_exp2(fmaf(s0[r], scale_log2, -mc));
+            s1[r] = fast_exp2(fmaf(s1[r], scale_log2, -mc));
+        }
+        const char* sV = sVb[j & 1];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (kMask && c >= 2 && !two) break;
+            const bf16x8 pb = pack8(c < 2 ? s0 : s1, 8 * (c & 1));
+            l = sum8(pb, l);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const bf16x8 a = lds_tr_read(sV, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
+                oacc[dt] = mfma32x32x16(a, pb, oacc[dt]);
+            }
+        }
+    };
+
+    // one step: after the barrier K(j+1) sits in sKb[(j+1)&1] and V(j) in sVb[j&1], and every
+    // wave is done with K(j) and V(j-1), whose buffers are refilled with K(j+2) and V(j+1).
+    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1) {
+        wait_async_copies();
+        __syncthreads();
+        if (j + 2 < n_kv) tile_load_async(sKb[j & 1], Kh, (j + 2) * kTile, T, wave, lane);
+        if (j + 1 < n_kv) tile_load_async(sVb[(j + 1) & 1], Vh, (j + 1) * kTile, T, wave, lane);
+        if (j <= last_w) {
+            if (j < last_w) tile_product(sKb[(j + 1) & 1], off, qreg, n0, n1);  // S^T of tile j+1 first
+            softmax_pv(j == last_w, j, c0, c1);
+        }
+    };
+
+    wait_async_copies();
+    __syncthreads();
+    f32x16 sa0, sa1, sb0, sb1;
+    tile_product(sKb[0], off, qreg, sa0, sa1);
+    for (int j = 0; j < n_kv; j += 2) {
+        step(j, sa0, sa1, sb0, sb1);
+        if (j + 1 < n_kv) step(j + 1, sb0, sb1, sa0, sa1);
+    }
+
+    l = halves_sum(l);
+    if (qrow < T) {
+        const float inv = 1.0f / l;
+        bf16* orow = O + head + (size_t)qrow * HD;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store_bf16x4(orow + 32 * dt + 8 * g + 4 * hi, oacc[dt][4 * g] * inv,
+                             oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
+                             oacc[dt][4 * g + 3] * inv);
+        if (hi == 0) LSE[(size_t)bh * T + qrow] = m * scale + logf(l);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and Delta): 128 queries per workgroup, 64-key K/V tiles, pipelined like
+// the forward: step j issues S^T and dP^T of tile j+1, then forms dS^T of
+// tile j and accumulates dQ^T += K^T dS^T.  K(j) (transposed reads) and K(j+1)
+// (row reads) are both live, so K cycles through three LDS buffers; V tiles
+// (row reads only) run one ahead through two.
+// Delta_i = sum_d dO_id O_id is formed from the rows the wave holds as MFMA
+// operands and written out for the dK/dV kernel.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ Delta, bf16* __restrict__ dQ, int BH, int T, int n_qtiles, float scale,
+    float scale_log2)
+{
+    __shared__ __attribute__((aligned(1024))) char sKb[3][kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sVb[2][kTileBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, hi = lane >> 5;
+    const int bh = blockIdx.x % BH;
+    const int qt = n_qtiles - 1 - blockIdx.x / BH;
+    const size_t head = (size_t)bh * T * HD;
+    const bf16* Kh = K + head;
+    const bf16* Vh = V + head;
+    const int q0w = qt * kRowsPerWG + wave * 32;
+    const int qrow = q0w + li;
+    const bool valid = qrow < T;
+    const Offsets off(lane);
+
+    const int kv_end = min(T, qt * kRowsPerWG + kRowsPerWG);
+    const int n_kv = (kv_end + kTile - 1) / kTile;
+    const int last_w = min(n_kv - 1, (q0w + 31) / kTile);
+
+    tile_load_async(sKb[0], Kh, 0, T, wave, lane);
+    tile_load_async(sVb[0], Vh, 0, T, wave, lane);
+    if (n_kv > 1) {
+        tile_load_async(sKb[1], Kh, kTile, T, wave, lane);
+        tile_load_async(sVb[1], Vh, kTile, T, wave, lane);
+    }
+
+    bf16x8 qreg[4], greg[4];
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const size_t o = head + (size_t)qrow * HD + 16 * ks + 8 * hi;
+        qreg[ks] = valid ? *(const bf16x8*)(Q + o) : zero_bf16x8();
+        greg[ks] = valid ? *(const bf16x8*)(dO + o) : zero_bf16x8();
+        const bf16x8 orow = valid ? *(const bf16x8*)(O + o) : zero_bf16x8();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsum = fmaf((float)greg[ks][e], (float)orow[e], dsum);
+    }
+    const float dlt = halves_sum(dsum);  // this lane's 32 columns + the other half's 32
+    if (valid && hi == 0) Delta[(size_t)bh * T + qrow] = dlt;
+    // rows >= T: -lse = -inf makes P (and dS) exactly 0
+    const float nlse2 = valid ? -LSE[(size_t)bh * T + qrow] * kLog2e : -INFINITY;
+    f32x16 dqacc[2] = {f32x16{}, f32x16{}};
+
+    // dS^T of tile j (scores s, dP^T p) and dQ^T += K^T dS^T
+    auto ds_dq = [&](bool kMask, int j, f32x16& s0, f32x16& s1, f32x16& p0, f32x16& p1) {
+        const int k0 = j * kTile;
+        bool two = true;
+        if (kMask) {
+            two = k0 + 32 <= q0w + 31;
+            mask_upto(s0, s1, qrow - k0 - 4 * hi);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s0[r] = fast_exp2(fmaf(s0[r], scale_log2, nlse2)) * (p0[r] - dlt);
+            s1[r] = fast_exp2(fmaf(s1[r], scale_log2, nlse2)) * (p1[r] - dlt);
+        }
+        const char* sK = sKb[j % 3];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (kMask && c >= 2 && !two) break;
+            const bf16x8 db = pack8(c < 2 ? s0 : s1, 8 * (c & 1));
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const bf16x8 a = lds_tr_read(sK, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
+                dqacc[dt] = mfma32x32x16(a, db, dqacc[dt]);
+            }
+        }
+    };
+
+    // after the barrier: K(j), K(j+1) in sKb[j%3], sKb[(j+1)%3]; V(j+1) in sVb[(j+1)&1];
+    // every wave is done with K(j-1) and V(j), refilled with K(j+2) and V(j+2).
+    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& d0, f32x16& d1, f32x16& n0,
+                    f32x16& n1, f32x16& e0, f32x16& e1) {
+        wait_async_copies();
+        __syncthreads();
+        if (j + 2 < n_kv) {
+            tile_load_async(sKb[(j + 2) % 3], Kh, (j + 2) * kTile, T, wave, lane);
+            tile_load_async(sVb[j & 1], Vh, (j + 2) * kTile, T, wave, lane);
+        }
+        if (j <= last_w) {
+            if (j < last_w) {  // S^T and dP^T of tile j+1 first
+                tile_product(sKb[(j + 1) % 3], off, qreg, n0, n1);
+                tile_product(sVb[(j + 1) & 1], off, greg, e0, e1);
+            }
+            ds_dq(j == last_w, j, c0, c1, d0, d1);
+        }
+    };
+
+    wait_async_copies();
+    __syncthreads();
+    f32x16 sa0, sa1, pa0, pa1, sb0, sb1, pb0, pb1;
+    tile_product(sKb[0], off, qreg, sa0, sa1);
+    tile_product(sVb[0], off, greg, pa0, pa1);
+    for (int j = 0; j < n_kv; j += 2) {
+        step(j, sa0, sa1, pa0, pa1, sb0, sb1, pb0, pb1);
+        if (j + 1 < n_kv) step(j + 1, sb0, sb1, pb0, pb1, sa0, sa1, pa0, pa1);
+    }
+
+    if (valid) {
+        bf16* row = dQ + head + (size_t)qrow * HD;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store_bf16x4(row + 32 * dt + 8 * g + 4 * hi, dqacc[dt][4 * g] * scale,
+                             dqacc[dt][4 * g + 1] * scale, dqacc[dt][4 * g + 2] * scale,
+                             dqacc[dt][4 * g + 3] * scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 128 keys per workgroup (32 per wave), 64-query Q/dO tiles
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int T, float scale, float scale_log2)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[2][2][kTileBytes];  // [stage][Q, dO]
+    __shared__ __attribute__((aligned(16))) float srow[2][2][kTile];        // [stage][-lse2, Delta]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, hi = lane >> 5;
+    const int bh = blockIdx.x % BH;
+    const int kb = blockIdx.x / BH;  // ascending: the first keys see the most queries
+    const size_t head = (size_t)bh * T * HD;
+    const bf16* Qh = Q + head;
+    const bf16* Gh = dO + head;
+    const float* Lh = LSE + (size_t)bh * T;
+    const float* Dh = Delta + (size_t)bh * T;
+    const int kv0 = kb * kRowsPerWG;
+    const int k0w = kv0 + wave * 32;
+    const int key = k0w + li;
+    const bool valid = key < T;
+    const Offsets off(lane);
+
+    const int n_q = (T + kTile - 1) / kTile;
+    const int i0 = kv0 / kTile;
+    tile_load_async(smem[0][0], Qh, i0 * kTile, T, wave, lane);
+    tile_load_async(smem[0][1], Gh, i0 * kTile, T, wave, lane);
+    if (tid < kTile) {
+        // rows >= T: -lse = -inf makes P (and dS) exactly 0
+        const int q = i0 * kTile + tid;
+        srow[0][0][tid] = q < T ? -Lh[q] * kLog2e : -INFINITY;
+        srow[0][1][tid] = q < T ? Dh[q] : 0.f;
+    }
+
+    bf16x8 kreg[4], vreg[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const size_t o = head + (size_t)key * HD + 16 * ks + 8 * hi;
+        kreg[ks] = valid ? *(const bf16x8*)(K + o) : zero_bf16x8();
+        vreg[ks] = valid ? *(const bf16x8*)(V + o) : zero_bf16x8();
+    }
+    f32x16 dkacc[2] = {f32x16{}, f32x16{}}, dvacc[2] = {f32x16{}, f32x16{}};
+
+    for (int i = i0; i < n_q; ++i) {
+        const int buf = (i - i0) & 1;
+        wait_async_copies();
+        __syncthreads();
+        float nl_next = 0.f, dl_next = 0.f;
+        const bool more = i + 1 < n_q;
+        if (more) {
+            tile_load_async(smem[buf ^ 1][0], Qh, (i + 1) * kTile, T, wave, lane);
+            tile_load_async(smem[buf ^ 1][1], Gh, (i + 1) * kTile, T, wave, lane);
+            if (tid < kTile) {
+                const int q = (i + 1) * kTile + tid;
+                nl_next = q < T ? -Lh[q] * kLog2e : -INFINITY;
+                dl_next = q < T ? Dh[q] : 0.f;
+            }
+        }
+        const int q0 = i * kTile;
+        if (q0 + kTile - 1 >= k0w) {  // some query of the tile sees some key of the wave
+            const bool first = q0 + 31 >= k0w;  // queries 0..31 of the tile matter
+            const char* sQ = smem[buf][0];
+            const char* sG = smem[buf][1];
+            bf16x8 qa[8], ga[8];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                qa[ks] = lds_row_read(sQ, off.nat[ks]);
+                qa[4 + ks] = lds_row_read(sQ, 4096 + off.nat[ks]);
+                ga[ks] = lds_row_read(sG, off.nat[ks]);
+                ga[4 + ks] = lds_row_read(sG, 4096 + off.nat[ks]);
+            }
+            f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                s0 = mfma32x32x16(qa[ks], kreg[ks], s0);
+                s1 = mfma32x32x16(qa[4 + ks], kreg[ks], s1);
+                p0 = mfma32x32x16(ga[ks], vreg[ks], p0);
+                p1 = mfma32x32x16(ga[4 + ks], vreg[ks], p1);
+            }
+            // element r of s0 holds query q0 + 8(r/4) + 4hi + r%4 (+32 in s1) of key `key`
+            if (q0 < k0w + 31) {  // the tile crosses this wave's diagonal: query < key -> masked
+                const int lim = key - q0 - 4 * hi;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qq = 8 * (r >> 2) + (r & 3);
+                    s0[r] = qq >= lim ? s0[r] : -INFINITY;
+                    s1[r] = qq + 32 >= lim ? s1[r] : -INFINITY;
+                }
+            }
+            const float* nl = srow[buf][0];
+            const float* dl = srow[buf][1];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int qa_ = 8 * g + 4 * hi;  // queries qa_..qa_+3 (subtile 0), +32 (subtile 1)
+                const f32x4 nl0 = *(const f32x4*)(nl + qa_), nl1 = *(const f32x4*)(nl + 32 + qa_);
+                const f32x4 dl0 = *(const f32x4*)(dl + qa_), dl1 = *(const f32x4*)(dl + 32 + qa_);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    const float pa = fast_exp2(fmaf(s0[r], scale_log2, nl0[e]));
+                    const float pb = fast_exp2(fmaf(s1[r], scale_log2, nl1[e]));
+                    s0[r] = pa;
+                    s1[r] = pb;
+                    p0[r] = pa * (p0[r] - dl0[e]);  // dS
+                    p1[r] = pb * (p1[r] - dl1[e]);
+                }
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS over the 64 queries
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (c < 2 && !first) continue;
+                const bf16x8 pb = pack8(c < 2 ? s0 : s1, 8 * (c & 1));
+                const bf16x8 db = pack8(c < 2 ? p0 : p1, 8 * (c & 1));
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    const int o0 = c * 2048 + off.tr[0][dt], o1 = c * 2048 + off.tr[1][dt];
+                    dvacc[dt] = mfma32x32x16(lds_tr_read(sG, o0, o1), pb, dvacc[dt]);
+                    dkacc[dt] = mfma32x32x16(lds_tr_read(sQ, o0, o1), db, dkacc[dt]);
+                }
+            }
+        }
+        if (more && tid < kTile) {
+            srow[buf ^ 1][0][tid] = nl_next;
+            srow[buf ^ 1][1][tid] = dl_next;
+        }
+    }
+
+    if (valid) {
+        bf16* krow = dK + head + (size_t)key * HD;
+        bf16* vrow = dV + head + (size_t)key * HD;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hi;
+                store_bf16x4(krow + d, dkacc[dt][4 * g] * scale, dkacc[dt][4 * g + 1] * scale,
+                             dkacc[dt][4 * g + 2] * scale, dkacc[dt][4 * g + 3] * scale);
+                store_bf16x4(vrow + d, dvacc[dt][4 * g], dvacc[dt][4 * g + 1],
+                             dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]);
+            }
+    }
+}
+
+}  // namespace d64
+
+hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
+{
+    const int BH = a.B * a.H;
+    const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
+    hipLaunchKernelGGL(d64::attn_fwd_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o_out, a.lse,
+                       BH, a.T, nqt, a.scale, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st)
+{
+    const int BH = a.B * a.H;
+    const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
+    hipLaunchKernelGGL(d64::attn_bwd_dq_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o,
+                       (const bf16*)a.dO, (const float*)a.lse, a.delta, (bf16*)a.dq, BH, a.T, nqt,
+                       a.scale, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st)
+{
+    const int BH = a.B * a.H;
+    const int nkt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
+    hipLaunchKernelGGL(d64::attn_bwd_dkdv_d64_kernel, dim3(nkt * BH), dim3(d64::kThreads), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dO,
+                       (const float*)a.lse, (const float*)a.delta, (bf16*)a.dk, (bf16*)a.dv, BH,
+                       a.T, a.scale, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+}  // namespace cattn

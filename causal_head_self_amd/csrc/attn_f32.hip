@@ -277,13 +277,10 @@ hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t st)
     return a.D == 64 ? fwd<64>(a, st) : fwd<32>(a, st);
 }
 
-hipError_t launch_delta_f32(const AttnArgs& a, hipStream_t st)
-{
-    return a.D == 64 ? delta<64>(a, st) : delta<32>(a, st);
-}
-
 hipError_t launch_dq_f32(const AttnArgs& a, hipStream_t st)
 {
+    const hipError_t e = a.D == 64 ? delta<64>(a, st) : delta<32>(a, st);
+    if (e != hipSuccess) return e;
     return a.D == 64 ? dq<64>(a, st) : dq<32>(a, st);
 }
 

@@ -22,12 +22,14 @@ struct AttnArgs {
     float scale;
 };
 
+// launch_dq_* computes delta (from o and dO) as well as dq.
 hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t st);
-hipError_t launch_delta_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dq_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dkdv_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st);
+hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st);
+hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st);
 hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t st);
-hipError_t launch_delta_f32(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dq_f32(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dkdv_f32(const AttnArgs& a, hipStream_t st);
 

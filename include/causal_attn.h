@@ -76,26 +76,24 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * (as written by attn_fwd with the same arguments) and dO; writes dq, dk, dv
  * ([B][H][T][D], dtype).  delta is caller-owned fp32 [B][H][T] workspace; on
  * return it holds Delta[i] = sum_d dO[i][d] * o[i][d], the softmax-backward
- * row term.  Enqueues three kernels on `stream` (Delta, dQ, dK/dV). */
+ * row term.  Enqueues its two stages on `stream` (dQ with Delta, then
+ * dK/dV). */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv,
              float* delta, int B, int H, int T, int D, float scale, int dtype,
              void* stream);
 
-/* The three stages attn_bwd enqueues, callable one by one with the same
- * argument conventions.  attn_bwd_delta must complete (stream order) before
- * attn_bwd_dq and attn_bwd_dkdv read delta; those two write disjoint outputs
- * and may run in either order, or concurrently on two streams.
+/* The two stages attn_bwd enqueues, callable one by one with the same
+ * argument conventions, in this order on one stream (or with an event
+ * between them): attn_bwd_dkdv reads the delta that attn_bwd_dq writes.
  *
- * attn_bwd_delta: delta[i] = sum_d dO[i][d] * o[i][d] (fp32 accumulation).
- * attn_bwd_dq:    dq = scale * dS k, with P recomputed from lse and
- *                 dS = P * (dO v^T - delta).
- * attn_bwd_dkdv:  dk = scale * dS^T q and dv = P^T dO, same P and dS. */
-int attn_bwd_delta(const void* o, const void* dO, float* delta, int B, int H, int T,
-                   int D, int dtype, void* stream);
-int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
-                const float* lse, const float* delta, void* dq, int B, int H, int T,
-                int D, float scale, int dtype, void* stream);
+ * attn_bwd_dq:   delta[i] = sum_d dO[i][d] * o[i][d] (fp32 accumulation) and
+ *                dq = scale * dS k, with P recomputed from lse and
+ *                dS = P * (dO v^T - delta).
+ * attn_bwd_dkdv: dk = scale * dS^T q and dv = P^T dO, same P and dS. */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                const void* dO, const float* lse, float* delta, void* dq, int B,
+                int H, int T, int D, float scale, int dtype, void* stream);
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
                   const float* lse, const float* delta, void* dk, void* dv, int B,
                   int H, int T, int D, float scale, int dtype, void* stream);

@@ -67,20 +67,13 @@ def _bwd(**kw):
                                        a["T"], a["D"], a["scale"], a["dtype"], a["stream"])
 
 
-def _delta(**kw):
-    a = dict(o=P[3], dO=P[5], delta=P[9], B=2, H=3, T=17, D=64, dtype=1, stream=None)
-    a.update(kw)
-    return cat.load_library().attn_bwd_delta(a["o"], a["dO"], a["delta"], a["B"], a["H"],
-                                             a["T"], a["D"], a["dtype"], a["stream"])
-
-
 def _dq(**kw):
-    a = dict(q=P[0], k=P[1], v=P[2], dO=P[5], lse=P[4], delta=P[9], dq=P[6], B=2, H=3, T=17,
-             D=64, scale=0.125, dtype=1, stream=None)
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], dO=P[5], lse=P[4], delta=P[9], dq=P[6], B=2, H=3,
+             T=17, D=64, scale=0.125, dtype=1, stream=None)
     a.update(kw)
-    return cat.load_library().attn_bwd_dq(a["q"], a["k"], a["v"], a["dO"], a["lse"], a["delta"],
-                                          a["dq"], a["B"], a["H"], a["T"], a["D"], a["scale"],
-                                          a["dtype"], a["stream"])
+    return cat.load_library().attn_bwd_dq(a["q"], a["k"], a["v"], a["o"], a["dO"], a["lse"],
+                                          a["delta"], a["dq"], a["B"], a["H"], a["T"], a["D"],
+                                          a["scale"], a["dtype"], a["stream"])
 
 
 def _dkdv(**kw):
@@ -93,8 +86,7 @@ def _dkdv(**kw):
 
 
 @pytest.mark.parametrize("call,names", [
-    (_delta, ["o", "dO", "delta"]),
-    (_dq, ["q", "k", "v", "dO", "lse", "delta", "dq"]),
+    (_dq, ["q", "k", "v", "o", "dO", "lse", "delta", "dq"]),
     (_dkdv, ["q", "k", "v", "dO", "lse", "delta", "dk", "dv"]),
 ])
 def test_stage_null_pointers(call, names):
@@ -102,7 +94,7 @@ def test_stage_null_pointers(call, names):
         assert call(**{name: None}) == 1, name
 
 
-@pytest.mark.parametrize("call", [_delta, _dq, _dkdv])
+@pytest.mark.parametrize("call", [_dq, _dkdv])
 def test_stage_validation(call):
     assert call(T=0) == 2
     assert call(dtype=3) == 4
@@ -111,9 +103,10 @@ def test_stage_validation(call):
 
 
 def test_stage_alignment_and_aliasing():
-    assert _delta(delta=P[9] + 2) == 5
-    assert _delta(o=P[3] + 8) == 5
-    assert _delta(delta=P[5]) == 8            # delta inside dO
+    assert _dq(delta=P[9] + 2) == 5
+    assert _dq(o=P[3] + 8) == 5
+    assert _dq(delta=P[5]) == 8               # delta inside dO
+    assert _dq(delta=P[6]) == 8               # delta inside dq
     assert _dq(dq=P[2]) == 8                  # dq is v
     assert _dq(dq=P[6] + 4) == 5
     assert _dq(scale=-2.0) == 7

@@ -3,7 +3,13 @@ MHA (HIP kernels) -> c_proj + residual) against the fp64 oracle sublayer.
 
 x, y and dx keep the plain bf16 tolerance 2e-2.  Tensors that are not unit
 variance (weight and bias gradients, summed over B*T rows, and the LN-weight
-gradient) are compared as |gpu - ref| <= 2e-2 * max(1, rms(ref)).
+gradient) are compared element by element as
+
+    |gpu - ref| <= 2e-2 * max(1, rms(ref)) + 2^-8 * |ref|,
+
+i.e. the stated tolerance after normalising the tensor to unit rms, plus the
+bf16 storage rounding of the element itself (relative 2^-9, taken as 2^-8 to
+cover the bf16 inputs of the product that produced it).
 """
 import sys
 
@@ -44,11 +50,17 @@ def _compare(got, ref):
     for name, r in ref.items():
         g = got[name]
         assert np.all(np.isfinite(g)), name
-        err = float(np.max(np.abs(g - r)))
-        tol = TOL if name in plain else TOL * max(1.0, float(np.sqrt(np.mean(r ** 2))))
-        print(f"  {name}: max abs err {err:.3e} (tol {tol:.3e}, rms(ref) "
-              f"{float(np.sqrt(np.mean(r ** 2))):.3e})", flush=True)
-        assert err <= tol, f"{name}: max abs err {err:.3e} > {tol:.3e}"
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        err = np.abs(g - r)
+        if name in plain:
+            tol = np.full_like(r, TOL)
+        else:
+            tol = TOL * max(1.0, rms) + 2.0 ** -8 * np.abs(r)
+        worst = int(np.argmax(err - tol))
+        print(f"  {name}: max abs err {float(err.max()):.3e}, worst margin at |ref| "
+              f"{abs(float(r.flat[worst])):.3e} (err {float(err.flat[worst]):.3e}, tol "
+              f"{float(tol.flat[worst]):.3e}), rms(ref) {rms:.3e}", flush=True)
+        assert np.all(err <= tol), f"{name}: error beyond its bound at flat index {worst}"
 
 
 def test_sublayer_small():
