@@ -52,20 +52,45 @@ __device__ __forceinline__ int swz(int r)
 __device__ __forceinline__ int chunk_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 
 // Asynchronous copy of rows [row0, row0 + 64) of a [T][64] bf16 head into a
-// swizzled LDS tile.  Rows >= T read row T-1 instead (always valid memory);
-// the kernels mask those rows.  Each of the 4 waves moves 16 rows.
-__device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restrict__ head,
-                                                int row0, int T, int wave, int lane)
-{
+// swizzled LDS tile.  Each of the 4 waves moves 16 rows, 8 per instruction:
+// lane l writes physical chunk l & 7 of row l >> 3 of its 1 KB block and so
+// fetches that row's logical chunk (l & 7) ^ swz(row).  The per-lane byte
+// offsets are constant; a full tile then needs only a scalar base per copy.
+// Rows >= T (last tile only) read row T-1 instead (always valid memory); the
+// kernels mask those rows.
+struct TileCopy {
+    uint32_t off[2];  // byte offset of this lane's 16 bytes inside a full tile, per instruction
+    int row[2];       // tile row this lane fetches
+    int chunk[2];     // logical chunk this lane fetches
+    __device__ __forceinline__ TileCopy(int wave, int lane)
+    {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int rb = wave * 16 + it * 8;     // first row of this 1 KB block
-        const int r = rb + (lane >> 3);        // row written by this lane
-        const int c = (lane & 7) ^ swz(r);     // logical chunk that lands in physical chunk lane&7
-        const int g = min(row0 + r, T - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(head + (size_t)g * HD + c * 8),
-                                         (__attribute__((address_space(3))) void*)(tile + rb * 128),
-                                         16, 0, 0);
+        for (int it = 0; it < 2; ++it) {
+            row[it] = wave * 16 + it * 8 + (lane >> 3);
+            chunk[it] = (lane & 7) ^ swz(row[it]);
+            off[it] = (uint32_t)(row[it] * HD + chunk[it] * 8) * 2u;
+        }
+    }
+};
+
+__device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restrict__ head,
+                                                int row0, int T, int wave, const TileCopy& tc)
+{
+    if (row0 + kTile <= T) {  // wave-uniform: every row exists
+        const char* base = (const char*)(head + (size_t)row0 * HD);
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+            __builtin_amdgcn_global_load_lds((const void*)(base + tc.off[it]),
+                                             (__attribute__((address_space(3))) void*)(tile + (wave * 16 + it * 8) * 128),
+                                             16, 0, 0);
+    } else {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int g = min(row0 + tc.row[it], T - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(head + (size_t)g * HD + tc.chunk[it] * 8),
+                                             (__attribute__((address_space(3))) void*)(tile + (wave * 16 + it * 8) * 128),
+                                             16, 0, 0);
+        }
     }
 }
 
@@ -184,13 +209,18 @@ __device__ __forceinline__ void mask_upto(f32x16& s0, f32x16& s1, int lim)
 // (its compares depend on the wave alone and are hoisted out of the loop).
 // The loop is unrolled by two so the score registers alternate without copies.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_d64_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_d64_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int n_qtiles, float scale,
     float scale_log2)
 {
-    __shared__ __attribute__((aligned(1024))) char sKb[2][kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sVb[2][kTileBytes];
+    // Separate arrays per buffer (not one indexed array): with the buffer of every
+    // access known at compile time, the compiler can tell that an LDS read does not
+    // touch the buffer an asynchronous copy is filling, and does not wait for it.
+    __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -203,14 +233,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_d64_kernel(
     const int q0w = qt * kRowsPerWG + wave * 32;  // wave-uniform
     const int qrow = q0w + li;
     const Offsets off(lane);
+    const TileCopy tc(wave, lane);
 
     const int kv_end = min(T, qt * kRowsPerWG + kRowsPerWG);
     const int n_kv = (kv_end + kTile - 1) / kTile;
     const int last_w = min(n_kv - 1, (q0w + 31) / kTile);  // tiles 0..last_w-1 are fully visible
 
-    tile_load_async(sKb[0], Kh, 0, T, wave, lane);
-    tile_load_async(sVb[0], Vh, 0, T, wave, lane);
-    if (n_kv > 1) tile_load_async(sKb[1], Kh, kTile, T, wave, lane);
+    tile_load_async(sK0, Kh, 0, T, wave, tc);
+    tile_load_async(sV0, Vh, 0, T, wave, tc);
+    if (n_kv > 1) tile_load_async(sK1, Kh, kTile, T, wave, tc);
 
     bf16x8 qreg[4];
 #pragma unroll
@@ -222,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_d64_kernel(
     float l = 0.f;        // this lane's part of the normaliser
 
     // softmax of tile j (scores in s0, s1) and O^T += V^T P^T
-    auto softmax_pv = [&](bool kMask, int j, f32x16& s0, f32x16& s1) {
+    auto softmax_pv = [&](bool kMask, int j, const char* sV, f32x16& s0, f32x16& s1) {
         const int k0 = j * kTile;
         bool two = true;  // keys 32..63 of the tile are visible to some row of the wave
         if (kMask) {
@@ -251,7 +282,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_d64_kernel(
             s0[r] = fast_exp2(fmaf(s0[r], scale_log2, -mc));
             s1[r] = fast_exp2(fmaf(s1[r], scale_log2, -mc));
         }
-        const char* sV = sVb[j & 1];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (kMask && c >= 2 && !two) break;
@@ -265,26 +295,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_d64_kernel(
         }
     };
 
-    // one step: after the barrier K(j+1) sits in sKb[(j+1)&1] and V(j) in sVb[j&1], and every
-    // wave is done with K(j) and V(j-1), whose buffers are refilled with K(j+2) and V(j+1).
-    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1) {
+    // one step: after the barrier K(j+1) sits in kn and V(j) in vc, and every wave is
+    // done with K(j) (in kl) and V(j-1) (in vl), which are refilled with K(j+2), V(j+1).
+    auto step = [&](int j, char* kl, const char* kn, const char* vc, char* vl, f32x16& c0,
+                    f32x16& c1, f32x16& n0, f32x16& n1) {
         wait_async_copies();
         __syncthreads();
-        if (j + 2 < n_kv) tile_load_async(sKb[j & 1], Kh, (j + 2) * kTile, T, wave, lane);
-        if (j + 1 < n_kv) tile_load_async(sVb[(j + 1) & 1], Vh, (j + 1) * kTile, T, wave, lane);
+        if (j + 2 < n_kv) tile_load_async(kl, Kh, (j + 2) * kTile, T, wave, tc);
+        if (j + 1 < n_kv) tile_load_async(vl, Vh, (j + 1) * kTile, T, wave, tc);
         if (j <= last_w) {
-            if (j < last_w) tile_product(sKb[(j + 1) & 1], off, qreg, n0, n1);  // S^T of tile j+1 first
-            softmax_pv(j == last_w, j, c0, c1);
+            if (j < last_w) tile_product(kn, off, qreg, n0, n1);  // S^T of tile j+1 first
+            softmax_pv(j == last_w, j, vc, c0, c1);
         }
     };
 
     wait_async_copies();
     __syncthreads();
     f32x16 sa0, sa1, sb0, sb1;
-    tile_product(sKb[0], off, qreg, sa0, sa1);
+    tile_product(sK0, off, qreg, sa0, sa1);
     for (int j = 0; j < n_kv; j += 2) {
-        step(j, sa0, sa1, sb0, sb1);
-        if (j + 1 < n_kv) step(j + 1, sb0, sb1, sa0, sa1);
+        step(j, sK0, sK1, sV0, sV1, sa0, sa1, sb0, sb1);
+        if (j + 1 < n_kv) step(j + 1, sK1, sK0, sV1, sV0, sb0, sb1, sa0, sa1);
     }
 
     l = halves_sum(l);
@@ -303,11 +334,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_d64_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ (and Delta): 128 queries per workgroup, 64-key K/V tiles, pipelined like
-// the forward: step j issues S^T and dP^T of tile j+1, then forms dS^T of
-// tile j and accumulates dQ^T += K^T dS^T.  K(j) (transposed reads) and K(j+1)
-// (row reads) are both live, so K cycles through three LDS buffers; V tiles
-// (row reads only) run one ahead through two.
+// dQ (and Delta): 128 queries per workgroup, 64-key K/V tiles, double-buffered
+// (the copy of tile j+1 is in flight while tile j is used).  Per tile: S^T and
+// dP^T from row reads of K and V, dS^T = P^T (dP^T - Delta), then
+// dQ^T += K^T dS^T with K^T from transposing reads.  Only the wave's last tile
+// crosses its diagonal and is masked.
 // Delta_i = sum_d dO_id O_id is formed from the rows the wave holds as MFMA
 // operands and written out for the dK/dV kernel.
 // ---------------------------------------------------------------------------
@@ -317,8 +348,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
     float* __restrict__ Delta, bf16* __restrict__ dQ, int BH, int T, int n_qtiles, float scale,
     float scale_log2)
 {
-    __shared__ __attribute__((aligned(1024))) char sKb[3][kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sVb[2][kTileBytes];
+    // one array per buffer, so that reads are provably apart from in-flight copies
+    __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -332,17 +366,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
     const int qrow = q0w + li;
     const bool valid = qrow < T;
     const Offsets off(lane);
+    const TileCopy tc(wave, lane);
 
     const int kv_end = min(T, qt * kRowsPerWG + kRowsPerWG);
     const int n_kv = (kv_end + kTile - 1) / kTile;
     const int last_w = min(n_kv - 1, (q0w + 31) / kTile);
 
-    tile_load_async(sKb[0], Kh, 0, T, wave, lane);
-    tile_load_async(sVb[0], Vh, 0, T, wave, lane);
-    if (n_kv > 1) {
-        tile_load_async(sKb[1], Kh, kTile, T, wave, lane);
-        tile_load_async(sVb[1], Vh, kTile, T, wave, lane);
-    }
+    tile_load_async(sK0, Kh, 0, T, wave, tc);
+    tile_load_async(sV0, Vh, 0, T, wave, tc);
 
     bf16x8 qreg[4], greg[4];
     float dsum = 0.f;
@@ -361,59 +392,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
     const float nlse2 = valid ? -LSE[(size_t)bh * T + qrow] * kLog2e : -INFINITY;
     f32x16 dqacc[2] = {f32x16{}, f32x16{}};
 
-    // dS^T of tile j (scores s, dP^T p) and dQ^T += K^T dS^T
-    auto ds_dq = [&](bool kMask, int j, f32x16& s0, f32x16& s1, f32x16& p0, f32x16& p1) {
+    // after the barrier K(j), V(j) sit in kc, vc; every wave is done with tile j-1
+    // (in kl, vl), whose buffers are refilled with tile j+1.
+    auto step = [&](int j, const char* kc, const char* vc, char* kl, char* vl) {
+        wait_async_copies();
+        __syncthreads();
+        if (j + 1 < n_kv) {
+            tile_load_async(kl, Kh, (j + 1) * kTile, T, wave, tc);
+            tile_load_async(vl, Vh, (j + 1) * kTile, T, wave, tc);
+        }
+        if (j > last_w) return;
+        f32x16 s0, s1, p0, p1;
+        tile_product(kc, off, qreg, s0, s1);  // S^T
+        tile_product(vc, off, greg, p0, p1);  // dP^T
         const int k0 = j * kTile;
         bool two = true;
-        if (kMask) {
+        if (j == last_w) {
             two = k0 + 32 <= q0w + 31;
             mask_upto(s0, s1, qrow - k0 - 4 * hi);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            s0[r] = fast_exp2(fmaf(s0[r], scale_log2, nlse2)) * (p0[r] - dlt);
+            s0[r] = fast_exp2(fmaf(s0[r], scale_log2, nlse2)) * (p0[r] - dlt);  // dS^T
             s1[r] = fast_exp2(fmaf(s1[r], scale_log2, nlse2)) * (p1[r] - dlt);
         }
-        const char* sK = sKb[j % 3];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            if (kMask && c >= 2 && !two) break;
+            if (c >= 2 && !two) break;
             const bf16x8 db = pack8(c < 2 ? s0 : s1, 8 * (c & 1));
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) {
-                const bf16x8 a = lds_tr_read(sK, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
+                const bf16x8 a = lds_tr_read(kc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
                 dqacc[dt] = mfma32x32x16(a, db, dqacc[dt]);
             }
         }
     };
 
-    // after the barrier: K(j), K(j+1) in sKb[j%3], sKb[(j+1)%3]; V(j+1) in sVb[(j+1)&1];
-    // every wave is done with K(j-1) and V(j), refilled with K(j+2) and V(j+2).
-    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& d0, f32x16& d1, f32x16& n0,
-                    f32x16& n1, f32x16& e0, f32x16& e1) {
-        wait_async_copies();
-        __syncthreads();
-        if (j + 2 < n_kv) {
-            tile_load_async(sKb[(j + 2) % 3], Kh, (j + 2) * kTile, T, wave, lane);
-            tile_load_async(sVb[j & 1], Vh, (j + 2) * kTile, T, wave, lane);
-        }
-        if (j <= last_w) {
-            if (j < last_w) {  // S^T and dP^T of tile j+1 first
-                tile_product(sKb[(j + 1) % 3], off, qreg, n0, n1);
-                tile_product(sVb[(j + 1) & 1], off, greg, e0, e1);
-            }
-            ds_dq(j == last_w, j, c0, c1, d0, d1);
-        }
-    };
-
-    wait_async_copies();
-    __syncthreads();
-    f32x16 sa0, sa1, pa0, pa1, sb0, sb1, pb0, pb1;
-    tile_product(sKb[0], off, qreg, sa0, sa1);
-    tile_product(sVb[0], off, greg, pa0, pa1);
     for (int j = 0; j < n_kv; j += 2) {
-        step(j, sa0, sa1, pa0, pa1, sb0, sb1, pb0, pb1);
-        if (j + 1 < n_kv) step(j + 1, sb0, sb1, pb0, pb1, sa0, sa1, pa0, pa1);
+        step(j, sK0, sV0, sK1, sV1);
+        if (j + 1 < n_kv) step(j + 1, sK1, sV1, sK0, sV0);
     }
 
     if (valid) {
@@ -429,15 +446,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 128 keys per workgroup (32 per wave), 64-query Q/dO tiles
+// dK, dV: 128 keys per workgroup (32 per wave), 64-query Q/dO tiles from the
+// diagonal to T, double-buffered.  Per tile: S and dP from row reads of Q and
+// dO (one key column per lane), P from lse, dS = P (dP - Delta), then
+// dV^T += dO^T P and dK^T += Q^T dS with transposing reads.  Only the wave's
+// first tile crosses its diagonal and is masked; rows >= T carry lse = +inf.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int T, float scale, float scale_log2)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[2][2][kTileBytes];  // [stage][Q, dO]
-    __shared__ __attribute__((aligned(16))) float srow[2][2][kTile];        // [stage][-lse2, Delta]
+    // one array per buffer, so that reads are provably apart from in-flight copies
+    __shared__ __attribute__((aligned(1024))) char sQ0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sQ1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sG0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sG1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, Delta] per row
+    __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -454,16 +480,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
     const int key = k0w + li;
     const bool valid = key < T;
     const Offsets off(lane);
+    const TileCopy tc(wave, lane);
 
     const int n_q = (T + kTile - 1) / kTile;
     const int i0 = kv0 / kTile;
-    tile_load_async(smem[0][0], Qh, i0 * kTile, T, wave, lane);
-    tile_load_async(smem[0][1], Gh, i0 * kTile, T, wave, lane);
+    const int first_w = k0w / kTile;  // first tile with a query >= a key of this wave
+    tile_load_async(sQ0, Qh, i0 * kTile, T, wave, tc);
+    tile_load_async(sG0, Gh, i0 * kTile, T, wave, tc);
     if (tid < kTile) {
-        // rows >= T: -lse = -inf makes P (and dS) exactly 0
         const int q = i0 * kTile + tid;
-        srow[0][0][tid] = q < T ? -Lh[q] * kLog2e : -INFINITY;
-        srow[0][1][tid] = q < T ? Dh[q] : 0.f;
+        sR0[0][tid] = q < T ? -Lh[q] * kLog2e : -INFINITY;
+        sR0[1][tid] = q < T ? Dh[q] : 0.f;
     }
 
     bf16x8 kreg[4], vreg[4];
@@ -475,44 +502,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
     }
     f32x16 dkacc[2] = {f32x16{}, f32x16{}}, dvacc[2] = {f32x16{}, f32x16{}};
 
-    for (int i = i0; i < n_q; ++i) {
-        const int buf = (i - i0) & 1;
+    // lse and Delta of tile i+1 travel through registers two steps: loaded (clamped
+    // row, always valid memory) during step i-1, written to LDS at the end of step i.
+    // So no wait for them ever covers the tile copies issued at the top of a step
+    // (vmcnt counts in issue order).
+    auto load_rows = [&](int i, float& lr, float& dr) {
+        const int q = min(i * kTile + tid, T - 1);
+        if (tid < kTile && i < n_q) {
+            lr = Lh[q];
+            dr = Dh[q];
+        }
+    };
+    float la = 0.f, da = 0.f, lb = 0.f, db = 0.f;
+    load_rows(i0 + 1, la, da);
+
+    // after the barrier tile i sits in qc, gc, rc; every wave is done with tile i-1
+    // (in ql, gl, rl), whose buffers are refilled with tile i+1.
+    auto step = [&](int i, const char* qc, const char* gc, const float (*rc)[kTile], char* ql,
+                    char* gl, float (*rl)[kTile], float& l_ready, float& d_ready, float& l_load,
+                    float& d_load) {
         wait_async_copies();
         __syncthreads();
-        float nl_next = 0.f, dl_next = 0.f;
         const bool more = i + 1 < n_q;
         if (more) {
-            tile_load_async(smem[buf ^ 1][0], Qh, (i + 1) * kTile, T, wave, lane);
-            tile_load_async(smem[buf ^ 1][1], Gh, (i + 1) * kTile, T, wave, lane);
-            if (tid < kTile) {
-                const int q = (i + 1) * kTile + tid;
-                nl_next = q < T ? -Lh[q] * kLog2e : -INFINITY;
-                dl_next = q < T ? Dh[q] : 0.f;
-            }
+            tile_load_async(ql, Qh, (i + 1) * kTile, T, wave, tc);
+            tile_load_async(gl, Gh, (i + 1) * kTile, T, wave, tc);
         }
-        const int q0 = i * kTile;
-        if (q0 + kTile - 1 >= k0w) {  // some query of the tile sees some key of the wave
-            const bool first = q0 + 31 >= k0w;  // queries 0..31 of the tile matter
-            const char* sQ = smem[buf][0];
-            const char* sG = smem[buf][1];
-            bf16x8 qa[8], ga[8];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                qa[ks] = lds_row_read(sQ, off.nat[ks]);
-                qa[4 + ks] = lds_row_read(sQ, 4096 + off.nat[ks]);
-                ga[ks] = lds_row_read(sG, off.nat[ks]);
-                ga[4 + ks] = lds_row_read(sG, 4096 + off.nat[ks]);
-            }
-            f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                s0 = mfma32x32x16(qa[ks], kreg[ks], s0);
-                s1 = mfma32x32x16(qa[4 + ks], kreg[ks], s1);
-                p0 = mfma32x32x16(ga[ks], vreg[ks], p0);
-                p1 = mfma32x32x16(ga[4 + ks], vreg[ks], p1);
-            }
-            // element r of s0 holds query q0 + 8(r/4) + 4hi + r%4 (+32 in s1) of key `key`
-            if (q0 < k0w + 31) {  // the tile crosses this wave's diagonal: query < key -> masked
+        load_rows(i + 2, l_load, d_load);
+        if (i >= first_w) {
+            const int q0 = i * kTile;
+            f32x16 s0, s1, p0, p1;
+            tile_product(qc, off, kreg, s0, s1);  // S (lane = key column)
+            tile_product(gc, off, vreg, p0, p1);  // dP
+            bool first = true;  // queries 0..31 of the tile matter
+            if (i == first_w) {
+                first = q0 + 31 >= k0w;
+                // element r of s0 holds query q0 + 8(r/4) + 4hi + r%4 (+32 in s1):
+                // masked (query < key) unless 8(r/4)+r%4 >= key - q0 - 4hi
                 const int lim = key - q0 - 4 * hi;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -521,13 +547,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
                     s1[r] = qq + 32 >= lim ? s1[r] : -INFINITY;
                 }
             }
-            const float* nl = srow[buf][0];
-            const float* dl = srow[buf][1];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int qa_ = 8 * g + 4 * hi;  // queries qa_..qa_+3 (subtile 0), +32 (subtile 1)
-                const f32x4 nl0 = *(const f32x4*)(nl + qa_), nl1 = *(const f32x4*)(nl + 32 + qa_);
-                const f32x4 dl0 = *(const f32x4*)(dl + qa_), dl1 = *(const f32x4*)(dl + 32 + qa_);
+                const int qa = 8 * g + 4 * hi;  // queries qa..qa+3 (subtile 0), +32 (subtile 1)
+                const f32x4 nl0 = *(const f32x4*)(rc[0] + qa), nl1 = *(const f32x4*)(rc[0] + 32 + qa);
+                const f32x4 dl0 = *(const f32x4*)(rc[1] + qa), dl1 = *(const f32x4*)(rc[1] + 32 + qa);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
@@ -539,7 +563,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
                     p1[r] = pb * (p1[r] - dl1[e]);
                 }
             }
-            // dV^T += dO^T P, dK^T += Q^T dS over the 64 queries
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if (c < 2 && !first) continue;
@@ -548,15 +571,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
 #pragma unroll
                 for (int dt = 0; dt < 2; ++dt) {
                     const int o0 = c * 2048 + off.tr[0][dt], o1 = c * 2048 + off.tr[1][dt];
-                    dvacc[dt] = mfma32x32x16(lds_tr_read(sG, o0, o1), pb, dvacc[dt]);
-                    dkacc[dt] = mfma32x32x16(lds_tr_read(sQ, o0, o1), db, dkacc[dt]);
+                    dvacc[dt] = mfma32x32x16(lds_tr_read(gc, o0, o1), pb, dvacc[dt]);
+                    dkacc[dt] = mfma32x32x16(lds_tr_read(qc, o0, o1), db, dkacc[dt]);
                 }
             }
         }
         if (more && tid < kTile) {
-            srow[buf ^ 1][0][tid] = nl_next;
-            srow[buf ^ 1][1][tid] = dl_next;
+            const int q = (i + 1) * kTile + tid;  // rows >= T: -lse = -inf makes P exactly 0
+            rl[0][tid] = q < T ? -l_ready * kLog2e : -INFINITY;
+            rl[1][tid] = q < T ? d_ready : 0.f;
         }
+    };
+
+    for (int i = i0; i < n_q; i += 2) {
+        step(i, sQ0, sG0, sR0, sQ1, sG1, sR1, la, da, lb, db);
+        if (i + 1 < n_q) step(i + 1, sQ1, sG1, sR1, sQ0, sG0, sR0, lb, db, la, da);
     }
 
     if (valid) {
