@@ -57,9 +57,24 @@ int validate(const Buf (&in)[NI], const Buf (&out)[NO], int B, int H, int T, int
     return ATTN_OK;
 }
 
+// Compute units of the current device, queried once per device.
+int cu_count()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+        cached[dev] = n > 0 ? n : -1;
+    }
+    return cached[dev] > 0 ? cached[dev] : 0;
+}
+
 cattn::AttnArgs make_args(int B, int H, int T, int D, float scale)
 {
     cattn::AttnArgs a{};
+    a.n_cu = cu_count();
     a.B = B;
     a.H = H;
     a.T = T;

@@ -200,6 +200,22 @@ __device__ __forceinline__ void mask_upto(f32x16& s0, f32x16& s1, int lim)
     }
 }
 
+// Work placement.  Items are numbered heaviest first.  When a launch fits the
+// machine in one pass, MI355X places workgroups x, x + n_cu, x + 2 n_cu, ... on
+// one compute unit and workgroup x on XCD x % 8 (observed with per-workgroup
+// hardware ids).  Every odd layer of n_cu workgroups takes its items in reverse,
+// in blocks of 8 so that x % 8 and with it the XCD of each head's items does not
+// change; each compute unit then holds a heavy, a middle and a light item
+// instead of three of about the same weight.  A partial last layer keeps the
+// plain order.  The map is a permutation of [0, n_items) for any n_cu.
+__device__ __forceinline__ int item_of(int x, int n_items, int n_cu)
+{
+    if (n_cu <= 0 || (n_cu & 7)) return x;
+    const int r = x / n_cu, p = x - r * n_cu;
+    if (!(r & 1) || (r + 1) * n_cu > n_items) return x;
+    return r * n_cu + 8 * ((n_cu >> 3) - 1 - (p >> 3)) + (p & 7);
+}
+
 // ---------------------------------------------------------------------------
 // forward: 128 queries per workgroup (32 per wave), 64-key tiles.
 // Software-pipelined: step j issues the S^T MFMAs of tile j+1 before the
@@ -212,7 +228,7 @@ __device__ __forceinline__ void mask_upto(f32x16& s0, f32x16& s1, int lim)
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_d64_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int n_qtiles, float scale,
-    float scale_log2)
+    float scale_log2, int n_cu)
 {
     // Separate arrays per buffer (not one indexed array): with the buffer of every
     // access known at compile time, the compiler can tell that an LDS read does not
@@ -225,8 +241,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, hi = lane >> 5;
-    const int bh = blockIdx.x % BH;
-    const int qt = n_qtiles - 1 - blockIdx.x / BH;  // heaviest tiles first
+    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
+    const int bh = item % BH;
+    const int qt = n_qtiles - 1 - item / BH;  // heaviest tiles first
     const size_t head = (size_t)bh * T * HD;
     const bf16* Kh = K + head;
     const bf16* Vh = V + head;
@@ -346,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE,
     float* __restrict__ Delta, bf16* __restrict__ dQ, int BH, int T, int n_qtiles, float scale,
-    float scale_log2)
+    float scale_log2, int n_cu)
 {
     // one array per buffer, so that reads are provably apart from in-flight copies
     __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
@@ -357,8 +374,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, hi = lane >> 5;
-    const int bh = blockIdx.x % BH;
-    const int qt = n_qtiles - 1 - blockIdx.x / BH;
+    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
+    const int bh = item % BH;
+    const int qt = n_qtiles - 1 - item / BH;  // heaviest tiles first
     const size_t head = (size_t)bh * T * HD;
     const bf16* Kh = K + head;
     const bf16* Vh = V + head;
@@ -455,7 +473,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int T, float scale, float scale_log2)
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int T, float scale, float scale_log2,
+    int n_cu)
 {
     // one array per buffer, so that reads are provably apart from in-flight copies
     __shared__ __attribute__((aligned(1024))) char sQ0[kTileBytes];
@@ -468,8 +487,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, hi = lane >> 5;
-    const int bh = blockIdx.x % BH;
-    const int kb = blockIdx.x / BH;  // ascending: the first keys see the most queries
+    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
+    const int bh = item % BH;
+    const int kb = item / BH;  // ascending: the first keys see the most queries
     const size_t head = (size_t)bh * T * HD;
     const bf16* Qh = Q + head;
     const bf16* Gh = dO + head;
@@ -612,7 +632,7 @@ hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     hipLaunchKernelGGL(d64::attn_fwd_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o_out, a.lse,
-                       BH, a.T, nqt, a.scale, a.scale * kLog2e);
+                       BH, a.T, nqt, a.scale, a.scale * kLog2e, a.n_cu);
     return hipGetLastError();
 }
 
@@ -623,7 +643,7 @@ hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st)
     hipLaunchKernelGGL(d64::attn_bwd_dq_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o,
                        (const bf16*)a.dO, (const float*)a.lse, a.delta, (bf16*)a.dq, BH, a.T, nqt,
-                       a.scale, a.scale * kLog2e);
+                       a.scale, a.scale * kLog2e, a.n_cu);
     return hipGetLastError();
 }
 
@@ -634,7 +654,7 @@ hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st)
     hipLaunchKernelGGL(d64::attn_bwd_dkdv_d64_kernel, dim3(nkt * BH), dim3(d64::kThreads), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dO,
                        (const float*)a.lse, (const float*)a.delta, (bf16*)a.dk, (bf16*)a.dv, BH,
-                       a.T, a.scale, a.scale * kLog2e);
+                       a.T, a.scale, a.scale * kLog2e, a.n_cu);
     return hipGetLastError();
 }
 

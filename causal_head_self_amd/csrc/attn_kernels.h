@@ -20,6 +20,7 @@ struct AttnArgs {
     float* delta;    // backward workspace / output
     int B, H, T, D;
     float scale;
+    int n_cu;        // compute units of the current device (work placement)
 };
 
 // launch_dq_* computes delta (from o and dO) as well as dq.
