@@ -465,12 +465,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
 
 // ---------------------------------------------------------------------------
 // dK, dV: 128 keys per workgroup (32 per wave), 64-query Q/dO tiles from the
-// diagonal to T, double-buffered.  Per tile: S and dP from row reads of Q and
-// dO (one key column per lane), P from lse, dS = P (dP - Delta), then
-// dV^T += dO^T P and dK^T += Q^T dS with transposing reads.  Only the wave's
-// first tile crosses its diagonal and is masked; rows >= T carry lse = +inf.
+// diagonal to T, double-buffered.  Each tile is taken in two halves of 32
+// queries so that only one S block and one dP block are live at a time (the
+// kernel fits 3 waves per SIMD).  Per half: S and dP from row reads of Q and
+// dO (one key column per lane), with the dP accumulator starting from -Delta
+// of its row, so that it comes out as dP - Delta; P from lse; dS = P (dP -
+// Delta); then dV^T += dO^T P and dK^T += Q^T dS with transposing reads.
+// Only the wave's first tile crosses its diagonal and is masked; rows >= T
+// carry -lse = -inf (P = 0) and Delta = 0.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_dkdv_d64_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int T, float scale, float scale_log2,
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
     __shared__ __attribute__((aligned(1024))) char sQ1[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sG0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sG1[kTileBytes];
-    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, Delta] per row
+    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
     __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -510,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
     if (tid < kTile) {
         const int q = i0 * kTile + tid;
         sR0[0][tid] = q < T ? -Lh[q] * kLog2e : -INFINITY;
-        sR0[1][tid] = q < T ? Dh[q] : 0.f;
+        sR0[1][tid] = q < T ? -Dh[q] : 0.f;
     }
 
     bf16x8 kreg[4], vreg[4];
@@ -536,6 +540,56 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
     float la = 0.f, da = 0.f, lb = 0.f, db = 0.f;
     load_rows(i0 + 1, la, da);
 
+    // queries 32h .. 32h+31 of the tile in qc / gc / rc
+    auto half = [&](int h, bool diag, int q0, const char* qc, const char* gc,
+                    const float (*rc)[kTile]) {
+        f32x16 sv = f32x16{}, dp;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {  // dP starts from -Delta of its row
+            const f32x4 nd = *(const f32x4*)(rc[1] + 32 * h + 8 * g + 4 * hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            sv = mfma32x32x16(lds_row_read(qc, 4096 * h + off.nat[ks]), kreg[ks], sv);   // S
+            dp = mfma32x32x16(lds_row_read(gc, 4096 * h + off.nat[ks]), vreg[ks], dp);   // dP - Delta
+        }
+        if (diag) {
+            // element r holds query q0 + 32h + 8(r/4) + 4hi + r%4: masked (query < key)
+            // unless 8(r/4) + r%4 >= key - q0 - 32h - 4hi
+            const int lim = key - q0 - 32 * h - 4 * hi;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qq = 8 * (r >> 2) + (r & 3);
+                sv[r] = qq >= lim ? sv[r] : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 nl = *(const f32x4*)(rc[0] + 32 * h + 8 * g + 4 * hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                const float pr = fast_exp2(fmaf(sv[r], scale_log2, nl[e]));
+                sv[r] = pr;
+                dp[r] *= pr;  // dS
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const int c = 2 * h + cc;  // 16-query chunk of the tile
+            const bf16x8 pb = pack8(sv, 8 * cc);
+            const bf16x8 sb = pack8(dp, 8 * cc);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const int o0 = c * 2048 + off.tr[0][dt], o1 = c * 2048 + off.tr[1][dt];
+                dvacc[dt] = mfma32x32x16(lds_tr_read(gc, o0, o1), pb, dvacc[dt]);
+                dkacc[dt] = mfma32x32x16(lds_tr_read(qc, o0, o1), sb, dkacc[dt]);
+            }
+        }
+    };
+
     // after the barrier tile i sits in qc, gc, rc; every wave is done with tile i-1
     // (in ql, gl, rl), whose buffers are refilled with tile i+1.
     auto step = [&](int i, const char* qc, const char* gc, const float (*rc)[kTile], char* ql,
@@ -551,55 +605,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_d64_kernel(
         load_rows(i + 2, l_load, d_load);
         if (i >= first_w) {
             const int q0 = i * kTile;
-            f32x16 s0, s1, p0, p1;
-            tile_product(qc, off, kreg, s0, s1);  // S (lane = key column)
-            tile_product(gc, off, vreg, p0, p1);  // dP
-            bool first = true;  // queries 0..31 of the tile matter
-            if (i == first_w) {
-                first = q0 + 31 >= k0w;
-                // element r of s0 holds query q0 + 8(r/4) + 4hi + r%4 (+32 in s1):
-                // masked (query < key) unless 8(r/4)+r%4 >= key - q0 - 4hi
-                const int lim = key - q0 - 4 * hi;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qq = 8 * (r >> 2) + (r & 3);
-                    s0[r] = qq >= lim ? s0[r] : -INFINITY;
-                    s1[r] = qq + 32 >= lim ? s1[r] : -INFINITY;
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int qa = 8 * g + 4 * hi;  // queries qa..qa+3 (subtile 0), +32 (subtile 1)
-                const f32x4 nl0 = *(const f32x4*)(rc[0] + qa), nl1 = *(const f32x4*)(rc[0] + 32 + qa);
-                const f32x4 dl0 = *(const f32x4*)(rc[1] + qa), dl1 = *(const f32x4*)(rc[1] + 32 + qa);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e;
-                    const float pa = fast_exp2(fmaf(s0[r], scale_log2, nl0[e]));
-                    const float pb = fast_exp2(fmaf(s1[r], scale_log2, nl1[e]));
-                    s0[r] = pa;
-                    s1[r] = pb;
-                    p0[r] = pa * (p0[r] - dl0[e]);  // dS
-                    p1[r] = pb * (p1[r] - dl1[e]);
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (c < 2 && !first) continue;
-                const bf16x8 pb = pack8(c < 2 ? s0 : s1, 8 * (c & 1));
-                const bf16x8 db = pack8(c < 2 ? p0 : p1, 8 * (c & 1));
-#pragma unroll
-                for (int dt = 0; dt < 2; ++dt) {
-                    const int o0 = c * 2048 + off.tr[0][dt], o1 = c * 2048 + off.tr[1][dt];
-                    dvacc[dt] = mfma32x32x16(lds_tr_read(gc, o0, o1), pb, dvacc[dt]);
-                    dkacc[dt] = mfma32x32x16(lds_tr_read(qc, o0, o1), db, dkacc[dt]);
-                }
-            }
+            const bool diag = i == first_w;
+            // on the diagonal tile, queries 0..31 matter only if one of them is >= a key
+            if (!diag || q0 + 31 >= k0w) half(0, diag, q0, qc, gc, rc);
+            half(1, diag, q0, qc, gc, rc);
         }
         if (more && tid < kTile) {
             const int q = (i + 1) * kTile + tid;  // rows >= T: -lse = -inf makes P exactly 0
             rl[0][tid] = q < T ? -l_ready * kLog2e : -INFINITY;
-            rl[1][tid] = q < T ? d_ready : 0.f;
+            rl[1][tid] = q < T ? -d_ready : 0.f;
         }
     };
 
