@@ -60,34 +60,38 @@ __device__ __forceinline__ int chunk_off(int r, int c) { return r * 128 + ((c ^ 
 // kernels mask those rows.
 struct TileCopy {
     uint32_t off[2];  // byte offset of this lane's 16 bytes inside a full tile, per instruction
-    int row[2];       // tile row this lane fetches
-    int chunk[2];     // logical chunk this lane fetches
     __device__ __forceinline__ TileCopy(int wave, int lane)
     {
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            row[it] = wave * 16 + it * 8 + (lane >> 3);
-            chunk[it] = (lane & 7) ^ swz(row[it]);
-            off[it] = (uint32_t)(row[it] * HD + chunk[it] * 8) * 2u;
+            const int row = wave * 16 + it * 8 + (lane >> 3);
+            off[it] = (uint32_t)(row * HD + (((lane & 7) ^ swz(row)) * 8)) * 2u;
         }
     }
 };
 
+// All addresses are a wave-uniform base plus a 32-bit per-lane offset (the
+// scalar-base form of global_load_lds), which keeps 64-bit address arithmetic
+// out of the vector registers.
 __device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restrict__ head,
                                                 int row0, int T, int wave, const TileCopy& tc)
 {
+    const char* base = (const char*)head;
     if (row0 + kTile <= T) {  // wave-uniform: every row exists
-        const char* base = (const char*)(head + (size_t)row0 * HD);
+        const char* b = base + (size_t)row0 * (HD * 2);
 #pragma unroll
         for (int it = 0; it < 2; ++it)
-            __builtin_amdgcn_global_load_lds((const void*)(base + tc.off[it]),
+            __builtin_amdgcn_global_load_lds((const void*)(b + tc.off[it]),
                                              (__attribute__((address_space(3))) void*)(tile + (wave * 16 + it * 8) * 128),
                                              16, 0, 0);
     } else {
+        const int lane = __lane_id();
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int g = min(row0 + tc.row[it], T - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(head + (size_t)g * HD + tc.chunk[it] * 8),
+            const int row = wave * 16 + it * 8 + (lane >> 3);
+            const uint32_t o = (uint32_t)min(row0 + row, T - 1) * (HD * 2u) +
+                               (uint32_t)((lane & 7) ^ swz(row)) * 16u;
+            __builtin_amdgcn_global_load_lds((const void*)(base + o),
                                              (__attribute__((address_space(3))) void*)(tile + (wave * 16 + it * 8) * 128),
                                              16, 0, 0);
         }
@@ -218,9 +222,10 @@ __device__ __forceinline__ int item_of(int x, int n_items, int n_cu)
 
 // ---------------------------------------------------------------------------
 // forward: 128 queries per workgroup (32 per wave), 64-key tiles.
-// Software-pipelined: step j issues the S^T MFMAs of tile j+1 before the
-// softmax of tile j, so the matrix cores run while the VALU takes the exps;
-// K tiles run one tile ahead of V tiles through LDS.  Every wave needs tiles
+// Software-pipelined: while step j takes the softmax of tile j and its PV
+// product, it also issues the S^T MFMAs of tile j+1, interleaved chunk by
+// chunk with the exponentials, so the matrix core and the VALU of a wave run
+// at once; K tiles run one tile ahead of V tiles through LDS.  Every wave needs tiles
 // 0..last_w; only the last one crosses its diagonal, so only that step masks
 // (its compares depend on the wave alone and are hoisted out of the loop).
 // The loop is unrolled by two so the score registers alternate without copies.
@@ -269,14 +274,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     float m = -INFINITY;  // running max (raw dot-product units), shared by lanes l, l^32
     float l = 0.f;        // this lane's part of the normaliser
 
-    // softmax of tile j (scores in s0, s1) and O^T += V^T P^T
-    auto softmax_pv = [&](bool kMask, int j, const char* sV, f32x16& s0, f32x16& s1) {
-        const int k0 = j * kTile;
-        bool two = true;  // keys 32..63 of the tile are visible to some row of the wave
-        if (kMask) {
-            two = k0 + 32 <= q0w + 31;
-            mask_upto(s0, s1, qrow - k0 - 4 * hi);
-        }
+    // running max over the scores of a tile; lazy rescale of the accumulators
+    auto update_max = [&](const f32x16& s0, const f32x16& s1) {
         float mt = fmaxf(s0[0], fmaxf(s0[1], s0[2]));
 #pragma unroll
         for (int r = 3; r < 15; r += 2) mt = fmaxf(mt, fmaxf(s0[r], s0[r + 1]));
@@ -293,21 +292,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             oacc[0] *= alpha;
             oacc[1] *= alpha;
         }
+    };
+
+    // Softmax of tile j and O^T += V^T P^T, chunk by chunk (16 keys each), with
+    // the S^T MFMAs of tile j+1 interleaved, so that the matrix core runs while
+    // this wave's VALU takes the exponentials.  The LDS operands of each MFMA are
+    // read one chunk ahead.  On the wave's last tile (diag) the scores are masked
+    // first and there is no next tile.  One code path for both cases: two
+    // separately inlined variants of this body made the register allocator spill.
+    auto tile = [&](bool diag, int j, const char* kn, const char* vc, f32x16& s0, f32x16& s1,
+                    f32x16& n0, f32x16& n1) {
+        if (diag) mask_upto(s0, s1, qrow - j * kTile - 4 * hi);
+        update_max(s0, s1);
         const float mc = m * scale_log2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s0[r] = fast_exp2(fmaf(s0[r], scale_log2, -mc));
-            s1[r] = fast_exp2(fmaf(s1[r], scale_log2, -mc));
-        }
+        n0 = f32x16{};
+        n1 = f32x16{};
+        bf16x8 ra = lds_row_read(kn, off.nat[0]);
+        bf16x8 rb = lds_row_read(kn, 4096 + off.nat[0]);
+        bf16x8 ta = lds_tr_read(vc, off.tr[0][0], off.tr[1][0]);
+        bf16x8 tb = lds_tr_read(vc, off.tr[0][1], off.tr[1][1]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            if (kMask && c >= 2 && !two) break;
-            const bf16x8 pb = pack8(c < 2 ? s0 : s1, 8 * (c & 1));
-            l = sum8(pb, l);
+            const f32x16& sc = c < 2 ? s0 : s1;
+            const int b = 8 * (c & 1);
+            float p[8];
+            n0 = mfma32x32x16(ra, qreg[c], n0);
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-                const bf16x8 a = lds_tr_read(sV, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
-                oacc[dt] = mfma32x32x16(a, pb, oacc[dt]);
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(sc[b + e], scale_log2, -mc));
+            n1 = mfma32x32x16(rb, qreg[c], n1);
+            if (c < 3) {
+                ra = lds_row_read(kn, off.nat[c + 1]);
+                rb = lds_row_read(kn, 4096 + off.nat[c + 1]);
+            }
+#pragma unroll
+            for (int e = 4; e < 8; ++e) p[e] = fast_exp2(fmaf(sc[b + e], scale_log2, -mc));
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[e] = (bf16)p[e];
+            oacc[0] = mfma32x32x16(ta, pb, oacc[0]);
+            l = sum8(pb, l);
+            oacc[1] = mfma32x32x16(tb, pb, oacc[1]);
+            if (c < 3) {
+                ta = lds_tr_read(vc, (c + 1) * 2048 + off.tr[0][0], (c + 1) * 2048 + off.tr[1][0]);
+                tb = lds_tr_read(vc, (c + 1) * 2048 + off.tr[0][1], (c + 1) * 2048 + off.tr[1][1]);
             }
         }
     };
@@ -320,10 +347,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         __syncthreads();
         if (j + 2 < n_kv) tile_load_async(kl, Kh, (j + 2) * kTile, T, wave, tc);
         if (j + 1 < n_kv) tile_load_async(vl, Vh, (j + 1) * kTile, T, wave, tc);
-        if (j <= last_w) {
-            if (j < last_w) tile_product(kn, off, qreg, n0, n1);  // S^T of tile j+1 first
-            softmax_pv(j == last_w, j, vc, c0, c1);
-        }
+        if (j <= last_w) tile(j == last_w, j, kn, vc, c0, c1, n0, n1);
     };
 
     wait_async_copies();
