@@ -2,8 +2,9 @@
 """Benchmark: causal multi-head self-attention forward + backward on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-attn_fwd (tiled forward, lse out) followed by attn_bwd (Delta, dQ, dK/dV),
-all through the C ABI of libcausal_attn.so, inputs resident in HBM.
+attn_fwd (tiled forward, lse out) followed by attn_bwd (Delta, dQ, dK/dV in
+one launch), all through the C ABI of libcausal_attn.so, inputs resident in
+HBM.
 
 Default workload: GPT-2-small attention (B=8, H=12, T=1024, D=64, bf16 storage,
 fp32 accumulation; q, k, v, dO iid N(0, 1), seeds 42+idx).  Metric: causal
@@ -49,16 +50,15 @@ def kernel_source_sha() -> str:
 def kernel_work(cfg):
     """Algorithmic work per launch, per kernel (causal-adjusted).  One GEMM
     over the causal half of one head is T^2 * D flops.  The forward credits 2
-    GEMMs (S, PV); the backward 5: dK/dV is credited with S, dP, dV, dK and dQ
-    with its own dQ product (its recomputed S and dP are not credited again).
-    The dQ kernel also forms Delta (a row sum of dO * o), which is not
+    GEMMs (S, PV); the backward launch 5: its dK/dV items are credited with
+    S, dP, dV and dK, its dQ items with the dQ product (their recomputed S
+    and dP are not credited again).  Delta (a row sum of dO * o) is not
     credited."""
     B, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
     g = float(B * H * T * T * D)
     return {
         "fwd": {"flops": 2 * g},
-        "dq": {"flops": 1 * g},
-        "dkdv": {"flops": 4 * g},
+        "bwd": {"flops": 5 * g},
     }
 
 
@@ -163,17 +163,16 @@ def main() -> int:
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
     # per-kernel: the same K steps with an event between consecutive launches
-    names = ["fwd", "dq", "dkdv"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # (attn_fwd and attn_bwd are one kernel launch each at head dim 64)
+    names = ["fwd", "bwd"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e in evs:
         e[0].record(stream)
         cat.attn_fwd(q, k, v, o, lse, scale, stream)
         e[1].record(stream)
-        cat.attn_bwd_dq(q, k, v, o, dO, lse, delta, dq, scale, stream)
+        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream)
         e[2].record(stream)
-        cat.attn_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, scale, stream)
-        e[3].record(stream)
     torch.cuda.synchronize()
     kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                for i, n in enumerate(names)}
@@ -192,7 +191,7 @@ def main() -> int:
     value = flops_fb / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
 
-    dominant = max(("fwd", "dq", "dkdv"), key=lambda n: kern_ms[n])
+    dominant = max(names, key=lambda n: kern_ms[n])
     achieved = work[dominant]["flops"] / (kern_ms[dominant] * 1e-3) / 1e12
     sha = kernel_source_sha()
     workload_name = f"{cfg.name}_B{B}_H{H}_T{T}_D{D}_{cfg.dtype}"

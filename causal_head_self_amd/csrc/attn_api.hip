@@ -190,9 +190,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     a.dk = dk;
     a.dv = dv;
     hipStream_t s = (hipStream_t)stream;
-    const bool bf = dtype == ATTN_BF16;
-    hipError_t e = bf ? cattn::launch_dq_bf16(a, s) : cattn::launch_dq_f32(a, s);
-    if (e == hipSuccess) e = bf ? cattn::launch_dkdv_bf16(a, s) : cattn::launch_dkdv_f32(a, s);
+    if (dtype == ATTN_BF16) return status(cattn::launch_bwd_bf16(a, s));
+    hipError_t e = cattn::launch_dq_f32(a, s);
+    if (e == hipSuccess) e = cattn::launch_dkdv_f32(a, s);
     return status(e);
 }
 

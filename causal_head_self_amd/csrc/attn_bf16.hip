@@ -474,4 +474,11 @@ hipError_t launch_dkdv_bf16(const AttnArgs& a, hipStream_t st)
     return a.D == 64 ? launch_dkdv_bf16_d64(a, st) : launch_dkdv<32>(a, st);
 }
 
+hipError_t launch_bwd_bf16(const AttnArgs& a, hipStream_t st)
+{
+    if (a.D == 64) return launch_bwd_bf16_d64(a, st);  // dQ and dK/dV items in one grid
+    const hipError_t e = launch_dq_bf16(a, st);
+    return e == hipSuccess ? launch_dkdv_bf16(a, st) : e;
+}
+
 }  // namespace cattn

@@ -221,14 +221,12 @@ __device__ __forceinline__ int item_of(int x, int n_items, int n_cu)
 }
 
 // ---------------------------------------------------------------------------
-// forward: 128 queries per workgroup (32 per wave), 64-key tiles.
-// Software-pipelined: while step j takes the softmax of tile j and its PV
-// product, it also issues the S^T MFMAs of tile j+1, interleaved chunk by
-// chunk with the exponentials, so the matrix core and the VALU of a wave run
-// at once; K tiles run one tile ahead of V tiles through LDS.  Every wave needs tiles
-// 0..last_w; only the last one crosses its diagonal, so only that step masks
-// (its compares depend on the wave alone and are hoisted out of the loop).
-// The loop is unrolled by two so the score registers alternate without copies.
+// forward: 128 queries per workgroup (32 per wave), 64-key K and V tiles,
+// double-buffered through LDS (the copy of tile j+1 is in flight while tile j
+// is used).  On gfx950 a wave's MFMAs and VALU instructions largely serialise
+// on its SIMD, so the kernel keeps the VALU count per tile low and lets the
+// three waves that share a SIMD overlap each other's LDS latency.  Every wave
+// needs tiles 0..last_w; only the last one crosses its diagonal and is masked.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_d64_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -263,7 +261,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
     tile_load_async(sK0, Kh, 0, T, wave, tc);
     tile_load_async(sV0, Vh, 0, T, wave, tc);
-    if (n_kv > 1) tile_load_async(sK1, Kh, kTile, T, wave, tc);
 
     bf16x8 qreg[4];
 #pragma unroll
@@ -274,16 +271,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     float m = -INFINITY;  // running max (raw dot-product units), shared by lanes l, l^32
     float l = 0.f;        // this lane's part of the normaliser
 
-    // running max over the scores of a tile; lazy rescale of the accumulators
+    // running max over the scores of a tile (two chains of v_max3); lazy rescale
+    // of the accumulators
     auto update_max = [&](const f32x16& s0, const f32x16& s1) {
-        float mt = fmaxf(s0[0], fmaxf(s0[1], s0[2]));
+        float xa = fmaxf(s0[0], fmaxf(s0[1], s0[2]));
+        float xb = fmaxf(s1[0], fmaxf(s1[1], s1[2]));
 #pragma unroll
-        for (int r = 3; r < 15; r += 2) mt = fmaxf(mt, fmaxf(s0[r], s0[r + 1]));
-        mt = fmaxf(mt, fmaxf(s0[15], s1[0]));
-#pragma unroll
-        for (int r = 1; r < 15; r += 2) mt = fmaxf(mt, fmaxf(s1[r], s1[r + 1]));
-        mt = fmaxf(mt, s1[15]);
-        mt = halves_max(mt);
+        for (int r = 3; r < 15; r += 2) {
+            xa = fmaxf(xa, fmaxf(s0[r], s0[r + 1]));
+            xb = fmaxf(xb, fmaxf(s1[r], s1[r + 1]));
+        }
+        const float mt = halves_max(fmaxf(fmaxf(xa, s0[15]), fmaxf(xb, s1[15])));
         const float m_new = fmaxf(m, mt);
         if (__builtin_expect(__any((m_new - m) * scale_log2 > kLazyRescale), 0)) {
             const float alpha = fast_exp2((m - m_new) * scale_log2);
@@ -294,69 +292,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         }
     };
 
-    // Softmax of tile j and O^T += V^T P^T, chunk by chunk (16 keys each), with
-    // the S^T MFMAs of tile j+1 interleaved, so that the matrix core runs while
-    // this wave's VALU takes the exponentials.  The LDS operands of each MFMA are
-    // read one chunk ahead.  On the wave's last tile (diag) the scores are masked
-    // first and there is no next tile.  One code path for both cases: two
-    // separately inlined variants of this body made the register allocator spill.
-    auto tile = [&](bool diag, int j, const char* kn, const char* vc, f32x16& s0, f32x16& s1,
-                    f32x16& n0, f32x16& n1) {
+    // Tile j: S^T = K Q^T (all eight A operands read first), then all V^T
+    // operands of the PV product are read while the softmax runs, so that none
+    // of this wave's MFMAs waits on LDS; the other waves of the SIMD fill the
+    // matrix core meanwhile.  On the wave's last tile (diag) the scores are masked.
+    // One code path for both cases: two separately inlined variants of this body
+    // made the register allocator spill.
+    auto tile = [&](bool diag, int j, const char* kc, const char* vc) {
+        f32x16 s0, s1;
+        tile_product(kc, off, qreg, s0, s1);
+        bf16x8 tv[4][2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+                tv[c][dt] = lds_tr_read(vc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
         if (diag) mask_upto(s0, s1, qrow - j * kTile - 4 * hi);
         update_max(s0, s1);
         const float mc = m * scale_log2;
-        n0 = f32x16{};
-        n1 = f32x16{};
-        bf16x8 ra = lds_row_read(kn, off.nat[0]);
-        bf16x8 rb = lds_row_read(kn, 4096 + off.nat[0]);
-        bf16x8 ta = lds_tr_read(vc, off.tr[0][0], off.tr[1][0]);
-        bf16x8 tb = lds_tr_read(vc, off.tr[0][1], off.tr[1][1]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const f32x16& sc = c < 2 ? s0 : s1;
             const int b = 8 * (c & 1);
-            float p[8];
-            n0 = mfma32x32x16(ra, qreg[c], n0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(sc[b + e], scale_log2, -mc));
-            n1 = mfma32x32x16(rb, qreg[c], n1);
-            if (c < 3) {
-                ra = lds_row_read(kn, off.nat[c + 1]);
-                rb = lds_row_read(kn, 4096 + off.nat[c + 1]);
-            }
-#pragma unroll
-            for (int e = 4; e < 8; ++e) p[e] = fast_exp2(fmaf(sc[b + e], scale_log2, -mc));
             bf16x8 pb;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = (bf16)p[e];
-            oacc[0] = mfma32x32x16(ta, pb, oacc[0]);
+            for (int e = 0; e < 8; ++e) pb[e] = (bf16)fast_exp2(fmaf(sc[b + e], scale_log2, -mc));
             l = sum8(pb, l);
-            oacc[1] = mfma32x32x16(tb, pb, oacc[1]);
-            if (c < 3) {
-                ta = lds_tr_read(vc, (c + 1) * 2048 + off.tr[0][0], (c + 1) * 2048 + off.tr[1][0]);
-                tb = lds_tr_read(vc, (c + 1) * 2048 + off.tr[0][1], (c + 1) * 2048 + off.tr[1][1]);
-            }
+            oacc[0] = mfma32x32x16(tv[c][0], pb, oacc[0]);
+            oacc[1] = mfma32x32x16(tv[c][1], pb, oacc[1]);
         }
     };
 
-    // one step: after the barrier K(j+1) sits in kn and V(j) in vc, and every wave is
-    // done with K(j) (in kl) and V(j-1) (in vl), which are refilled with K(j+2), V(j+1).
-    auto step = [&](int j, char* kl, const char* kn, const char* vc, char* vl, f32x16& c0,
-                    f32x16& c1, f32x16& n0, f32x16& n1) {
+    // one step: after the barrier K(j), V(j) sit in kc, vc and every wave is done
+    // with tile j-1 (in kl, vl), whose buffers are refilled with tile j+1.
+    auto step = [&](int j, const char* kc, const char* vc, char* kl, char* vl) {
         wait_async_copies();
         __syncthreads();
-        if (j + 2 < n_kv) tile_load_async(kl, Kh, (j + 2) * kTile, T, wave, tc);
-        if (j + 1 < n_kv) tile_load_async(vl, Vh, (j + 1) * kTile, T, wave, tc);
-        if (j <= last_w) tile(j == last_w, j, kn, vc, c0, c1, n0, n1);
+        if (j + 1 < n_kv) {
+            tile_load_async(kl, Kh, (j + 1) * kTile, T, wave, tc);
+            tile_load_async(vl, Vh, (j + 1) * kTile, T, wave, tc);
+        }
+        if (j <= last_w) tile(j == last_w, j, kc, vc);
     };
 
-    wait_async_copies();
-    __syncthreads();
-    f32x16 sa0, sa1, sb0, sb1;
-    tile_product(sK0, off, qreg, sa0, sa1);
     for (int j = 0; j < n_kv; j += 2) {
-        step(j, sK0, sK1, sV0, sV1, sa0, sa1, sb0, sb1);
-        if (j + 1 < n_kv) step(j + 1, sK1, sK0, sV1, sV0, sb0, sb1, sa0, sa1);
+        step(j, sK0, sV0, sK1, sV1);
+        if (j + 1 < n_kv) step(j + 1, sK1, sV1, sK0, sV0);
     }
 
     l = halves_sum(l);
@@ -374,36 +355,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     }
 }
 
+// Arguments of the backward work items.
+struct BwdParams {
+    const bf16* Q;
+    const bf16* K;
+    const bf16* V;
+    const bf16* O;
+    const bf16* dO;
+    const float* LSE;
+    float* Delta;  // dQ items write it; dK/dV items read it unless they form it from O
+    bf16* dQ;
+    bf16* dK;
+    bf16* dV;
+    int BH, T;
+    float scale, scale_log2;
+};
+
 // ---------------------------------------------------------------------------
-// dQ (and Delta): 128 queries per workgroup, 64-key K/V tiles, double-buffered
+// dQ (and Delta) of one 128-query block: 64-key K/V tiles, double-buffered
 // (the copy of tile j+1 is in flight while tile j is used).  Per tile: S^T and
 // dP^T from row reads of K and V, dS^T = P^T (dP^T - Delta), then
 // dQ^T += K^T dS^T with K^T from transposing reads.  Only the wave's last tile
 // crosses its diagonal and is masked.
 // Delta_i = sum_d dO_id O_id is formed from the rows the wave holds as MFMA
-// operands and written out for the dK/dV kernel.
+// operands and written out.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE,
-    float* __restrict__ Delta, bf16* __restrict__ dQ, int BH, int T, int n_qtiles, float scale,
-    float scale_log2, int n_cu)
+__device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char* sK0, char* sK1,
+                                        char* sV0, char* sV1)
 {
-    // one array per buffer, so that reads are provably apart from in-flight copies
-    __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
-
+    const int BH = a.BH, T = a.T;
+    const float scale = a.scale, scale_log2 = a.scale_log2;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, hi = lane >> 5;
-    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    const int bh = item % BH;
-    const int qt = n_qtiles - 1 - item / BH;  // heaviest tiles first
+    (void)BH;
     const size_t head = (size_t)bh * T * HD;
-    const bf16* Kh = K + head;
-    const bf16* Vh = V + head;
+    const bf16* Kh = a.K + head;
+    const bf16* Vh = a.V + head;
     const int q0w = qt * kRowsPerWG + wave * 32;
     const int qrow = q0w + li;
     const bool valid = qrow < T;
@@ -422,16 +410,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const size_t o = head + (size_t)qrow * HD + 16 * ks + 8 * hi;
-        qreg[ks] = valid ? *(const bf16x8*)(Q + o) : zero_bf16x8();
-        greg[ks] = valid ? *(const bf16x8*)(dO + o) : zero_bf16x8();
-        const bf16x8 orow = valid ? *(const bf16x8*)(O + o) : zero_bf16x8();
+        qreg[ks] = valid ? *(const bf16x8*)(a.Q + o) : zero_bf16x8();
+        greg[ks] = valid ? *(const bf16x8*)(a.dO + o) : zero_bf16x8();
+        const bf16x8 orow = valid ? *(const bf16x8*)(a.O + o) : zero_bf16x8();
 #pragma unroll
         for (int e = 0; e < 8; ++e) dsum = fmaf((float)greg[ks][e], (float)orow[e], dsum);
     }
     const float dlt = halves_sum(dsum);  // this lane's 32 columns + the other half's 32
-    if (valid && hi == 0) Delta[(size_t)bh * T + qrow] = dlt;
+    if (valid && hi == 0) a.Delta[(size_t)bh * T + qrow] = dlt;
     // rows >= T: -lse = -inf makes P (and dS) exactly 0
-    const float nlse2 = valid ? -LSE[(size_t)bh * T + qrow] * kLog2e : -INFINITY;
+    const float nlse2 = valid ? -a.LSE[(size_t)bh * T + qrow] * kLog2e : -INFINITY;
     f32x16 dqacc[2] = {f32x16{}, f32x16{}};
 
     // after the barrier K(j), V(j) sit in kc, vc; every wave is done with tile j-1
@@ -464,8 +452,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
             const bf16x8 db = pack8(c < 2 ? s0 : s1, 8 * (c & 1));
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) {
-                const bf16x8 a = lds_tr_read(kc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
-                dqacc[dt] = mfma32x32x16(a, db, dqacc[dt]);
+                const bf16x8 av = lds_tr_read(kc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
+                dqacc[dt] = mfma32x32x16(av, db, dqacc[dt]);
             }
         }
     };
@@ -476,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
     }
 
     if (valid) {
-        bf16* row = dQ + head + (size_t)qrow * HD;
+        bf16* row = a.dQ + head + (size_t)qrow * HD;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -488,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 128 keys per workgroup (32 per wave), 64-query Q/dO tiles from the
+// dK, dV of one 128-key block (32 keys per wave): 64-query Q/dO tiles from the
 // diagonal to T, double-buffered.  Each tile is taken in two halves of 32
 // queries so that only one S block and one dP block are live at a time (the
 // kernel fits 3 waves per SIMD).  Per half: S and dP from row reads of Q and
@@ -497,32 +485,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_d64_kernel(
 // Delta); then dV^T += dO^T P and dK^T += Q^T dS with transposing reads.
 // Only the wave's first tile crosses its diagonal and is masked; rows >= T
 // carry -lse = -inf (P = 0) and Delta = 0.
+// kDeltaFromO: Delta of each tile is formed here from the O tile, which is
+// copied along with Q and dO: each wave, once its own copies of the next tile
+// have landed, sums dO * O over the 16 rows it copied (4 lanes per row) and
+// leaves -Delta in the row buffer, which the next step's barrier publishes.
+// Otherwise Delta is read from memory (written by a dQ pass).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_dkdv_d64_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int T, float scale, float scale_log2,
-    int n_cu)
+template <bool kDeltaFromO>
+__device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, char* sQ0, char* sQ1,
+                                          char* sG0, char* sG1, char* sO0, char* sO1,
+                                          float (*sR0)[kTile], float (*sR1)[kTile])
 {
-    // one array per buffer, so that reads are provably apart from in-flight copies
-    __shared__ __attribute__((aligned(1024))) char sQ0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sQ1[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sG0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sG1[kTileBytes];
-    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
-    __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
-
+    const int T = a.T;
+    const float scale = a.scale, scale_log2 = a.scale_log2;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, hi = lane >> 5;
-    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    const int bh = item % BH;
-    const int kb = item / BH;  // ascending: the first keys see the most queries
     const size_t head = (size_t)bh * T * HD;
-    const bf16* Qh = Q + head;
-    const bf16* Gh = dO + head;
-    const float* Lh = LSE + (size_t)bh * T;
-    const float* Dh = Delta + (size_t)bh * T;
+    const bf16* Qh = a.Q + head;
+    const bf16* Gh = a.dO + head;
+    const bf16* Oh = a.O + head;
+    const float* Lh = a.LSE + (size_t)bh * T;
+    const float* Dh = kDeltaFromO ? nullptr : a.Delta + (size_t)bh * T;
     const int kv0 = kb * kRowsPerWG;
     const int k0w = kv0 + wave * 32;
     const int key = k0w + li;
@@ -533,36 +517,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int n_q = (T + kTile - 1) / kTile;
     const int i0 = kv0 / kTile;
     const int first_w = k0w / kTile;  // first tile with a query >= a key of this wave
+
+    // Per-row values of tile i (lse, and Delta when it is read from memory) travel
+    // to LDS by the same asynchronous copy as the tiles, 4 bytes per lane of one
+    // wave (rows >= T read row T-1).  Once a wave's own copies of a tile have
+    // landed it turns them into the forms used below, in place: -lse*log2e (-inf
+    // past T) and -Delta (0 past T); with kDeltaFromO every wave forms -Delta of
+    // the 16 rows it copied from dO and O (4 lanes per row).  The next barrier
+    // publishes them.
+    auto rows_load_async = [&](int i, float (*rt)[kTile]) {
+        const uint32_t o = (uint32_t)min(i * kTile + lane, T - 1) * 4u;
+        if (wave == 0)
+            __builtin_amdgcn_global_load_lds((const void*)((const char*)Lh + o),
+                                             (__attribute__((address_space(3))) void*)rt[0], 4, 0, 0);
+        if (!kDeltaFromO && wave == 1)
+            __builtin_amdgcn_global_load_lds((const void*)((const char*)Dh + o),
+                                             (__attribute__((address_space(3))) void*)rt[1], 4, 0, 0);
+    };
+    auto rows_finish = [&](int i, const char* gt, const char* ot, float (*rt)[kTile]) {
+        // The lane-dependent addresses are recomputed here from an opaque copy of the
+        // lane index rather than kept live across the loop (registers are the limit).
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const bool in = i * kTile + ln < T;
+        if (wave == 0) rt[0][ln] = in ? -rt[0][ln] * kLog2e : -INFINITY;
+        if (!kDeltaFromO && wave == 1) rt[1][ln] = in ? -rt[1][ln] : 0.f;
+        if (kDeltaFromO) {
+            const int row = wave * 16 + (ln >> 2), c0 = 2 * (ln & 3);
+            float d = 0.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int o = chunk_off(row, c0 + c);
+                const bf16x8 gv = lds_row_read(gt, o), ov = lds_row_read(ot, o);
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                for (int e = 0; e < 8; e += 2)
+                    d = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{gv[e], gv[e + 1]},
+                                                        bf16x2{ov[e], ov[e + 1]}, d, false);
+            }
+            // sum over the 4 lanes of the row (DPP quad permutations 1,0,3,2 and 2,3,0,1)
+            d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0xB1, 0xF, 0xF, false));
+            d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0x4E, 0xF, 0xF, false));
+            if ((ln & 3) == 0) rt[1][row] = i * kTile + row < T ? -d : 0.f;
+        }
+    };
+
     tile_load_async(sQ0, Qh, i0 * kTile, T, wave, tc);
     tile_load_async(sG0, Gh, i0 * kTile, T, wave, tc);
-    if (tid < kTile) {
-        const int q = i0 * kTile + tid;
-        sR0[0][tid] = q < T ? -Lh[q] * kLog2e : -INFINITY;
-        sR0[1][tid] = q < T ? -Dh[q] : 0.f;
-    }
+    if (kDeltaFromO) tile_load_async(sO0, Oh, i0 * kTile, T, wave, tc);
+    rows_load_async(i0, sR0);
 
     bf16x8 kreg[4], vreg[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const size_t o = head + (size_t)key * HD + 16 * ks + 8 * hi;
-        kreg[ks] = valid ? *(const bf16x8*)(K + o) : zero_bf16x8();
-        vreg[ks] = valid ? *(const bf16x8*)(V + o) : zero_bf16x8();
+        kreg[ks] = valid ? *(const bf16x8*)(a.K + o) : zero_bf16x8();
+        vreg[ks] = valid ? *(const bf16x8*)(a.V + o) : zero_bf16x8();
     }
+    wait_async_copies();
+    rows_finish(i0, sG0, sO0, sR0);
     f32x16 dkacc[2] = {f32x16{}, f32x16{}}, dvacc[2] = {f32x16{}, f32x16{}};
-
-    // lse and Delta of tile i+1 travel through registers two steps: loaded (clamped
-    // row, always valid memory) during step i-1, written to LDS at the end of step i.
-    // So no wait for them ever covers the tile copies issued at the top of a step
-    // (vmcnt counts in issue order).
-    auto load_rows = [&](int i, float& lr, float& dr) {
-        const int q = min(i * kTile + tid, T - 1);
-        if (tid < kTile && i < n_q) {
-            lr = Lh[q];
-            dr = Dh[q];
-        }
-    };
-    float la = 0.f, da = 0.f, lb = 0.f, db = 0.f;
-    load_rows(i0 + 1, la, da);
 
     // queries 32h .. 32h+31 of the tile in qc / gc / rc
     auto half = [&](int h, bool diag, int q0, const char* qc, const char* gc,
@@ -614,19 +628,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         }
     };
 
-    // after the barrier tile i sits in qc, gc, rc; every wave is done with tile i-1
-    // (in ql, gl, rl), whose buffers are refilled with tile i+1.
+    // after the barrier tile i sits in qc, gc, (oc,) rc; every wave is done with tile
+    // i-1 (in ql, gl, ol, rl), whose buffers are refilled with tile i+1.
     auto step = [&](int i, const char* qc, const char* gc, const float (*rc)[kTile], char* ql,
-                    char* gl, float (*rl)[kTile], float& l_ready, float& d_ready, float& l_load,
-                    float& d_load) {
+                    char* gl, char* ol, float (*rl)[kTile]) {
         wait_async_copies();
         __syncthreads();
         const bool more = i + 1 < n_q;
         if (more) {
             tile_load_async(ql, Qh, (i + 1) * kTile, T, wave, tc);
             tile_load_async(gl, Gh, (i + 1) * kTile, T, wave, tc);
+            if (kDeltaFromO) tile_load_async(ol, Oh, (i + 1) * kTile, T, wave, tc);
+            rows_load_async(i + 1, rl);
         }
-        load_rows(i + 2, l_load, d_load);
         if (i >= first_w) {
             const int q0 = i * kTile;
             const bool diag = i == first_w;
@@ -634,21 +648,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             if (!diag || q0 + 31 >= k0w) half(0, diag, q0, qc, gc, rc);
             half(1, diag, q0, qc, gc, rc);
         }
-        if (more && tid < kTile) {
-            const int q = (i + 1) * kTile + tid;  // rows >= T: -lse = -inf makes P exactly 0
-            rl[0][tid] = q < T ? -l_ready * kLog2e : -INFINITY;
-            rl[1][tid] = q < T ? -d_ready : 0.f;
+        if (more) {
+            wait_async_copies();
+            rows_finish(i + 1, gl, ol, rl);
         }
     };
 
     for (int i = i0; i < n_q; i += 2) {
-        step(i, sQ0, sG0, sR0, sQ1, sG1, sR1, la, da, lb, db);
-        if (i + 1 < n_q) step(i + 1, sQ1, sG1, sR1, sQ0, sG0, sR0, lb, db, la, da);
+        step(i, sQ0, sG0, sR0, sQ1, sG1, sO1, sR1);
+        if (i + 1 < n_q) step(i + 1, sQ1, sG1, sR1, sQ0, sG0, sO0, sR0);
     }
 
     if (valid) {
-        bf16* krow = dK + head + (size_t)key * HD;
-        bf16* vrow = dV + head + (size_t)key * HD;
+        bf16* krow = a.dK + head + (size_t)key * HD;
+        bf16* vrow = a.dV + head + (size_t)key * HD;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -660,6 +673,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                              dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]);
             }
     }
+}
+
+// dQ alone (also writes Delta).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_dq_d64_kernel(
+    BwdParams a, int n_qtiles, int n_cu)
+{
+    // one array per buffer, so that reads are provably apart from in-flight copies
+    __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
+    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
+    dq_item(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1);
+}
+
+// dK, dV alone, from a Delta in memory.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_dkdv_d64_kernel(
+    BwdParams a, int n_cu)
+{
+    __shared__ __attribute__((aligned(1024))) char sQ0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sQ1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sG0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sG1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
+    __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
+    dkdv_item<false>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1, nullptr, nullptr, sR0, sR1);
+}
+
+// ---------------------------------------------------------------------------
+// The whole backward in one launch: dK/dV items (forming Delta from O) and dQ
+// items (writing Delta) are independent, so one grid holds both and each
+// item's start (loading its resident rows from HBM) overlaps the others'
+// compute instead of every item of a kernel loading at once.  Items run in
+// order of decreasing tile count, a dK/dV item before a dQ item of the same
+// count (a dK/dV tile costs more): level v holds the dK/dV items of key block v
+// and the dQ items of query block n - 1 - v, BH of each.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_d64_kernel(
+    BwdParams a, int n_blocks, int n_cu)
+{
+    __shared__ __attribute__((aligned(1024))) char s0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s2[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s3[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s4[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s5[kTileBytes];
+    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];
+    __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
+    const int BH = a.BH;
+    const int level = item / (2 * BH), r = item - level * 2 * BH;
+    if (r < BH)
+        dkdv_item<true>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1);
+    else
+        dq_item(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
 }
 
 }  // namespace d64
@@ -674,14 +743,32 @@ hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
     return hipGetLastError();
 }
 
+static d64::BwdParams bwd_params(const AttnArgs& a)
+{
+    d64::BwdParams p;
+    p.Q = (const bf16*)a.q;
+    p.K = (const bf16*)a.k;
+    p.V = (const bf16*)a.v;
+    p.O = (const bf16*)a.o;
+    p.dO = (const bf16*)a.dO;
+    p.LSE = a.lse;
+    p.Delta = a.delta;
+    p.dQ = (bf16*)a.dq;
+    p.dK = (bf16*)a.dk;
+    p.dV = (bf16*)a.dv;
+    p.BH = a.B * a.H;
+    p.T = a.T;
+    p.scale = a.scale;
+    p.scale_log2 = a.scale * kLog2e;
+    return p;
+}
+
 hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     hipLaunchKernelGGL(d64::attn_bwd_dq_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o,
-                       (const bf16*)a.dO, (const float*)a.lse, a.delta, (bf16*)a.dq, BH, a.T, nqt,
-                       a.scale, a.scale * kLog2e, a.n_cu);
+                       bwd_params(a), nqt, a.n_cu);
     return hipGetLastError();
 }
 
@@ -690,9 +777,16 @@ hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st)
     const int BH = a.B * a.H;
     const int nkt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     hipLaunchKernelGGL(d64::attn_bwd_dkdv_d64_kernel, dim3(nkt * BH), dim3(d64::kThreads), 0, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dO,
-                       (const float*)a.lse, (const float*)a.delta, (bf16*)a.dk, (bf16*)a.dv, BH,
-                       a.T, a.scale, a.scale * kLog2e, a.n_cu);
+                       bwd_params(a), a.n_cu);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16_d64(const AttnArgs& a, hipStream_t st)
+{
+    const int BH = a.B * a.H;
+    const int nb = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
+    hipLaunchKernelGGL(d64::attn_bwd_d64_kernel, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st,
+                       bwd_params(a), nb, a.n_cu);
     return hipGetLastError();
 }
 

@@ -30,6 +30,9 @@ hipError_t launch_dkdv_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st);
+// the whole bf16 backward (Delta, dq, dk, dv)
+hipError_t launch_bwd_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_bwd_bf16_d64(const AttnArgs& a, hipStream_t st);
 hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dq_f32(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dkdv_f32(const AttnArgs& a, hipStream_t st);

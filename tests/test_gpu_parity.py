@@ -117,6 +117,46 @@ def test_fp32_shapes_and_ragged_tails(shape):
     check_case(*shape, "f32", seed=200 + sum(shape))
 
 
+@pytest.mark.parametrize("shape,dtype", [
+    ((1, 1, 65, 64), "bf16"), ((2, 3, 300, 64), "bf16"), ((1, 2, 257, 32), "bf16"),
+    ((1, 2, 100, 64), "f32"),
+])
+def test_split_backward_entry_points(shape, dtype):
+    """attn_bwd_dq (which also writes Delta) followed by attn_bwd_dkdv (which
+    reads it) is a separate code path from attn_bwd; both must match the
+    oracle, and the split path must agree with attn_bwd."""
+    import causal_head_self_amd as cat
+    B, H, T, D = shape
+    _note(f"[parity] split backward B={B} H={H} T={T} D={D} dtype={dtype}")
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, dtype, 300 + sum(shape))
+    scale = 1.0 / math.sqrt(D)
+    dev = torch.device("cuda")
+    qd, kd, vd, gd = (t.to(dev).contiguous() for t in (q, k, v, dO))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    cat.attn_fwd(qd, kd, vd, o, lse, scale)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    delta = torch.empty_like(lse)
+    cat.attn_bwd_dq(qd, kd, vd, o, gd, lse, delta, dq, scale)
+    cat.attn_bwd_dkdv(qd, kd, vd, gd, lse, delta, dk, dv, scale)
+    fq, fk, fv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    fdelta = torch.empty_like(lse)
+    cat.attn_bwd(qd, kd, vd, o, lse, gd, fq, fk, fv, fdelta, scale)
+    torch.cuda.synchronize()
+    as_np = lambda t: t.float().cpu().numpy().astype(np.float64)
+    got = {"dq": as_np(dq), "dk": as_np(dk), "dv": as_np(dv), "delta": as_np(delta)}
+    fused = {"dq": as_np(fq), "dk": as_np(fk), "dv": as_np(fv), "delta": as_np(fdelta)}
+    full = oracle_attention(q, k, v, dO, scale)
+    dtol = delta_bound(full, dO) if dtype == "bf16" else None
+    ref = {n: full[n] for n in got}
+    assert_close(got, ref, TOL[dtype], f"split B{B} H{H} T{T} D{D} {dtype}", dtol)
+    assert_close(fused, ref, TOL[dtype], f"fused B{B} H{H} T{T} D{D} {dtype}", dtol)
+    # the two paths compute Delta and dS in different orders; they agree to the
+    # bf16 storage rounding of the gradients
+    for n in ("dq", "dk", "dv"):
+        assert np.max(np.abs(got[n] - fused[n])) <= TOL[dtype], n
+
+
 # ---------------------------------------------------------------------------
 # full-size configurations: sampled heads, element by element
 # ---------------------------------------------------------------------------
