@@ -476,14 +476,14 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV of one 128-key block (32 keys per wave): 64-query Q/dO tiles from the
-// diagonal to T, double-buffered.  Each tile is taken in two halves of 32
+// dK, dV of one 128-key block (32 keys per wave): 64-query Q/dO tiles from T
+// down to the diagonal, double-buffered.  Each tile is taken in two halves of 32
 // queries so that only one S block and one dP block are live at a time (the
 // kernel fits 3 waves per SIMD).  Per half: S and dP from row reads of Q and
 // dO (one key column per lane), with the dP accumulator starting from -Delta
 // of its row, so that it comes out as dP - Delta; P from lse; dS = P (dP -
 // Delta); then dV^T += dO^T P and dK^T += Q^T dS with transposing reads.
-// Only the wave's first tile crosses its diagonal and is masked; rows >= T
+// Only the last tile a wave visits crosses its diagonal and is masked; rows >= T
 // carry -lse = -inf (P = 0) and Delta = 0.
 // kDeltaFromO: Delta of each tile is formed here from the O tile, which is
 // copied along with Q and dO: each wave, once its own copies of the next tile
@@ -562,10 +562,12 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         }
     };
 
-    tile_load_async(sQ0, Qh, i0 * kTile, T, wave, tc);
-    tile_load_async(sG0, Gh, i0 * kTile, T, wave, tc);
-    if (kDeltaFromO) tile_load_async(sO0, Oh, i0 * kTile, T, wave, tc);
-    rows_load_async(i0, sR0);
+    // Tiles are visited from the last one down to the diagonal, so that every item
+    // of a head streams the same tile at about the same time (they share it in L2).
+    tile_load_async(sQ0, Qh, (n_q - 1) * kTile, T, wave, tc);
+    tile_load_async(sG0, Gh, (n_q - 1) * kTile, T, wave, tc);
+    if (kDeltaFromO) tile_load_async(sO0, Oh, (n_q - 1) * kTile, T, wave, tc);
+    rows_load_async(n_q - 1, sR0);
 
     bf16x8 kreg[4], vreg[4];
 #pragma unroll
@@ -575,7 +577,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         vreg[ks] = valid ? *(const bf16x8*)(a.V + o) : zero_bf16x8();
     }
     wait_async_copies();
-    rows_finish(i0, sG0, sO0, sR0);
+    rows_finish(n_q - 1, sG0, sO0, sR0);
     f32x16 dkacc[2] = {f32x16{}, f32x16{}}, dvacc[2] = {f32x16{}, f32x16{}};
 
     // queries 32h .. 32h+31 of the tile in qc / gc / rc
@@ -629,17 +631,17 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     };
 
     // after the barrier tile i sits in qc, gc, (oc,) rc; every wave is done with tile
-    // i-1 (in ql, gl, ol, rl), whose buffers are refilled with tile i+1.
+    // i+1 (in ql, gl, ol, rl), whose buffers are refilled with tile i-1.
     auto step = [&](int i, const char* qc, const char* gc, const float (*rc)[kTile], char* ql,
                     char* gl, char* ol, float (*rl)[kTile]) {
         wait_async_copies();
         __syncthreads();
-        const bool more = i + 1 < n_q;
+        const bool more = i > i0;
         if (more) {
-            tile_load_async(ql, Qh, (i + 1) * kTile, T, wave, tc);
-            tile_load_async(gl, Gh, (i + 1) * kTile, T, wave, tc);
-            if (kDeltaFromO) tile_load_async(ol, Oh, (i + 1) * kTile, T, wave, tc);
-            rows_load_async(i + 1, rl);
+            tile_load_async(ql, Qh, (i - 1) * kTile, T, wave, tc);
+            tile_load_async(gl, Gh, (i - 1) * kTile, T, wave, tc);
+            if (kDeltaFromO) tile_load_async(ol, Oh, (i - 1) * kTile, T, wave, tc);
+            rows_load_async(i - 1, rl);
         }
         if (i >= first_w) {
             const int q0 = i * kTile;
@@ -650,13 +652,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         }
         if (more) {
             wait_async_copies();
-            rows_finish(i + 1, gl, ol, rl);
+            rows_finish(i - 1, gl, ol, rl);
         }
     };
 
-    for (int i = i0; i < n_q; i += 2) {
+    for (int i = n_q - 1; i >= i0; i -= 2) {
         step(i, sQ0, sG0, sR0, sQ1, sG1, sO1, sR1);
-        if (i + 1 < n_q) step(i + 1, sQ1, sG1, sR1, sQ0, sG0, sO0, sR0);
+        if (i - 1 >= i0) step(i - 1, sQ1, sG1, sR1, sQ0, sG0, sO0, sR0);
     }
 
     if (valid) {
