@@ -105,12 +105,96 @@ def cpu_baseline(cfg, inputs, threads: int):
     }
 
 
+def sublayer_bench(args) -> int:
+    """The pre-norm attention sublayer around the GPT-2-small shape: LayerNorm,
+    c_attn, split to heads, causal attention (the HIP kernels), merge, c_proj,
+    residual; forward and backward through torch autograd.  Work per step:
+    the c_attn and c_proj GEMMs (2*N*C*3C + 2*N*C*C forward, 3x that forward
+    plus backward) plus the attention's 7*B*H*T^2*D.  The attention share is
+    the time of attn_fwd + attn_bwd alone at the same shape over the step time."""
+    import torch
+    import causal_head_self_amd as cat
+    from causal_head_self_amd.sublayer import attention_sublayer
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    cat.load_library()
+    cfg = workloads.SUBLAYER_CONFIG
+    inp = workloads.sublayer_inputs(cfg)
+    names = ["x", "g", "bl", "Wa", "ba", "Wp", "bp"]
+    dev = {n: inp[n].cuda().requires_grad_(True) for n in names}
+    dy = inp["dy"].cuda()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for n in names:
+            dev[n].grad = None
+        y = attention_sublayer(dev["x"], dev["g"], dev["bl"], dev["Wa"], dev["ba"], dev["Wp"],
+                               dev["bp"], cfg.H)
+        y.backward(dy)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # attention alone at the same shape
+    B, T, C, H = cfg.B, cfg.T, cfg.C, cfg.H
+    D = C // H
+    q = torch.randn(B, H, T, D, device="cuda", dtype=torch.bfloat16)
+    k, v, dO = torch.randn_like(q), torch.randn_like(q), torch.randn_like(q)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty(B, H, T, device="cuda")
+    delta = torch.empty_like(lse)
+    sc = 1.0 / math.sqrt(D)
+    for _ in range(args.warmup):
+        cat.attn_fwd(q, k, v, o, lse, sc, stream)
+        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, sc, stream)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        cat.attn_fwd(q, k, v, o, lse, sc, stream)
+        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, sc, stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = t0.elapsed_time(t1) / args.steps
+
+    N = B * T
+    gemm_fwd = 2.0 * N * C * 3 * C + 2.0 * N * C * C
+    attn = 7.0 * B * H * T * T * D
+    work = 3.0 * gemm_fwd + attn
+    value = work / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "causal attention sublayer fwd+bwd TFLOP/s (LN, c_attn, attention, c_proj, residual)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": (f"pre-norm attention sublayer, B={B} T={T} C={C} H={H} {cfg.dtype}; "
+                                "x, dy N(0,1), GPT-2 init weights, seeds 42+idx"),
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "attention_ms": round(attn_ms, 5),
+        "attention_share": round(attn_ms / ms, 4),
+        "attention_tflops": round(attn / (attn_ms * 1e-3) / 1e12, 3),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="gpt2s", choices=["tiny", "gpt2s", "gpt400m", "long"])
+    ap.add_argument("--config", default="gpt2s",
+                    choices=["tiny", "gpt2s", "gpt400m", "long", "sublayer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
@@ -121,6 +205,9 @@ def main() -> int:
               "(every (batch, head) pair is independent, so more GPUs would each run their "
               "own shard of the batch with no exchange).", file=sys.stderr)
         return 2
+
+    if args.config == "sublayer":
+        return sublayer_bench(args)
 
     import torch
     import causal_head_self_amd as cat

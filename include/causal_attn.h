@@ -76,16 +76,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * (as written by attn_fwd with the same arguments) and dO; writes dq, dk, dv
  * ([B][H][T][D], dtype).  delta is caller-owned fp32 [B][H][T] workspace; on
  * return it holds Delta[i] = sum_d dO[i][d] * o[i][d], the softmax-backward
- * row term.  Enqueues its two stages on `stream` (dQ with Delta, then
- * dK/dV). */
+ * row term.  For bf16 at D = 64 this is one kernel launch on `stream` whose
+ * dK/dV work forms Delta itself from o and dO; otherwise it enqueues the two
+ * stages below (dQ with Delta, then dK/dV).  Either way the results equal
+ * those of the two stages up to the fp32 summation order. */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv,
              float* delta, int B, int H, int T, int D, float scale, int dtype,
              void* stream);
 
-/* The two stages attn_bwd enqueues, callable one by one with the same
- * argument conventions, in this order on one stream (or with an event
- * between them): attn_bwd_dkdv reads the delta that attn_bwd_dq writes.
+/* The backward as two stages, callable one by one with the same argument
+ * conventions, in this order on one stream (or with an event between them):
+ * attn_bwd_dkdv reads the delta that attn_bwd_dq writes.
  *
  * attn_bwd_dq:   delta[i] = sum_d dO[i][d] * o[i][d] (fp32 accumulation) and
  *                dq = scale * dS k, with P recomputed from lse and
