@@ -420,7 +420,39 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     if (valid && hi == 0) a.Delta[(size_t)bh * T + qrow] = dlt;
     // rows >= T: -lse = -inf makes P (and dS) exactly 0
     const float nlse2 = valid ? -a.LSE[(size_t)bh * T + qrow] * kLog2e : -INFINITY;
+    // dP^T accumulators start from this block (-Delta of the lane's query in every
+    // register), so that the MFMAs yield dP - Delta without a subtraction per element
+    f32x16 ndl;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndl[r] = -dlt;
     f32x16 dqacc[2] = {f32x16{}, f32x16{}};
+
+    // keys 32h .. 32h+31 of tile j: S^T, dP^T - Delta, dS^T, dQ^T += K^T dS^T
+    auto half = [&](int h, bool diag, int k0, const char* kc, const char* vc) {
+        f32x16 sv = f32x16{}, pv = ndl;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            sv = mfma32x32x16(lds_row_read(kc, 4096 * h + off.nat[ks]), qreg[ks], sv);  // S^T
+            pv = mfma32x32x16(lds_row_read(vc, 4096 * h + off.nat[ks]), greg[ks], pv);  // dP^T - Delta
+        }
+        if (diag) {  // key row 32h + 8(r/4) + 4hi + r%4 is visible to query qrow iff <= qrow - k0
+            const int lim = qrow - k0 - 4 * hi - 32 * h;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = 8 * (r >> 2) + (r & 3) <= lim ? sv[r] : -INFINITY;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(fmaf(sv[r], scale_log2, nlse2)) * pv[r];  // dS^T
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const int c = 2 * h + cc;
+            const bf16x8 db = pack8(sv, 8 * cc);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const bf16x8 av = lds_tr_read(kc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
+                dqacc[dt] = mfma32x32x16(av, db, dqacc[dt]);
+            }
+        }
+    };
 
     // after the barrier K(j), V(j) sit in kc, vc; every wave is done with tile j-1
     // (in kl, vl), whose buffers are refilled with tile j+1.
@@ -432,30 +464,11 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
             tile_load_async(vl, Vh, (j + 1) * kTile, T, wave, tc);
         }
         if (j > last_w) return;
-        f32x16 s0, s1, p0, p1;
-        tile_product(kc, off, qreg, s0, s1);  // S^T
-        tile_product(vc, off, greg, p0, p1);  // dP^T
         const int k0 = j * kTile;
-        bool two = true;
-        if (j == last_w) {
-            two = k0 + 32 <= q0w + 31;
-            mask_upto(s0, s1, qrow - k0 - 4 * hi);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s0[r] = fast_exp2(fmaf(s0[r], scale_log2, nlse2)) * (p0[r] - dlt);  // dS^T
-            s1[r] = fast_exp2(fmaf(s1[r], scale_log2, nlse2)) * (p1[r] - dlt);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (c >= 2 && !two) break;
-            const bf16x8 db = pack8(c < 2 ? s0 : s1, 8 * (c & 1));
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-                const bf16x8 av = lds_tr_read(kc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
-                dqacc[dt] = mfma32x32x16(av, db, dqacc[dt]);
-            }
-        }
+        const bool diag = j == last_w;
+        half(0, diag, k0, kc, vc);
+        // keys 32..63 of the diagonal tile matter only if a query of the wave reaches them
+        if (!diag || k0 + 32 <= q0w + 31) half(1, diag, k0, kc, vc);
     };
 
     for (int j = 0; j < n_kv; j += 2) {
