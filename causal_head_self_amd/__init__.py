@@ -8,7 +8,10 @@ the computation.  PyTorch supplies device memory and streams.
     attn_fwd(q, k, v, o, lse, scale)                        -- C ABI attn_fwd
     attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale) -- C ABI attn_bwd
     attn_bwd_dq / attn_bwd_dkdv                             -- its two stages
+    attn_fwd_strided / attn_bwd_strided                     -- on strided views
     causal_attention(q, k, v, scale=None)                   -- autograd op
+    causal_attention_qkv(qkv, n_head)                       -- autograd op on the
+        fused [B, T, 3C] c_attn output, returning [B, T, C] with no layout copies
 
 Tensors are contiguous [B, H, T, D] (D in {32, 64}) of float32 or bfloat16 on
 the current GPU; lse and delta are float32 [B, H, T].
@@ -19,12 +22,13 @@ import math
 
 import torch
 
-from ._lib import (ABI_VERSION, ATTN_BF16, ATTN_F32, EXPORTS, LIB_PATH, AttnError, check,
-                   load_library, status_str)
+from ._lib import (ABI_VERSION, ATTN_BF16, ATTN_F32, EXPORTS, LIB_PATH, AttnError, AttnView,
+                   check, load_library, status_str)
 
 __all__ = [
-    "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_status_str",
-    "causal_attention", "AttnError",
+    "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
+    "attn_bwd_strided", "attn_status_str", "causal_attention", "causal_attention_qkv",
+    "qkv_heads", "AttnError",
     "ATTN_F32", "ATTN_BF16", "load_library", "LIB_PATH", "EXPORTS", "ABI_VERSION",
 ]
 
@@ -106,6 +110,90 @@ def attn_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, scale: float | None = None,
         _ptr(delta, "delta"), _ptr(dk, "dk"), _ptr(dv, "dv"), B, H, T, D, scale,
         _dtype_code(q), _stream(stream))
     check(rc)
+
+
+def _view(t: torch.Tensor, name: str) -> AttnView:
+    """A [B, H, T, D] tensor (any strides, D contiguous) as an attn_view_t."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name} must be a [B, H, T, D] view with contiguous D")
+    sb, sh, st, _ = t.stride()
+    return AttnView(t.data_ptr(), sb, sh, st)
+
+
+def attn_fwd_strided(q, k, v, o, lse, scale: float | None = None, stream=None) -> None:
+    """C ABI attn_fwd_strided: q, k, v, o are [B, H, T, D] views (D contiguous)."""
+    B, H, T, D = _shape(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().attn_fwd_strided(
+        _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
+        B, H, T, D, scale, _dtype_code(q), _stream(stream))
+    check(rc)
+
+
+def attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale: float | None = None,
+                     stream=None) -> None:
+    """C ABI attn_bwd_strided: every [B, H, T, D] argument is a view."""
+    B, H, T, D = _shape(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().attn_bwd_strided(
+        _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
+        _view(dO, "dO"), _view(dq, "dq"), _view(dk, "dk"), _view(dv, "dv"),
+        _ptr(delta, "delta"), B, H, T, D, scale, _dtype_code(q), _stream(stream))
+    check(rc)
+
+
+def qkv_heads(qkv: torch.Tensor, n_head: int):
+    """q, k, v as [B, H, T, D] views of a [B, T, 3C] tensor (no copies)."""
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    D = C // n_head
+    x = qkv.view(B, T, 3, n_head, D)
+    return tuple(x[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+
+
+class _CausalAttentionQKV(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, qkv, n_head):
+        if qkv.dim() != 3 or qkv.shape[-1] % (3 * n_head) != 0 or qkv.stride(-1) != 1:
+            raise ValueError("qkv must be [B, T, 3C] with contiguous last dim and C % n_head == 0")
+        qkv = qkv if qkv.is_contiguous() else qkv.contiguous()
+        B, T, C3 = qkv.shape
+        C = C3 // 3
+        q, k, v = qkv_heads(qkv, n_head)
+        y = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
+        o = y.view(B, T, n_head, C // n_head).permute(0, 2, 1, 3)  # [B, H, T, D] view of y
+        lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
+        attn_fwd_strided(q, k, v, o, lse)
+        ctx.save_for_backward(qkv, y, lse)
+        ctx.n_head = n_head
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        qkv, y, lse = ctx.saved_tensors
+        n_head = ctx.n_head
+        B, T, C3 = qkv.shape
+        C = C3 // 3
+        D = C // n_head
+        dy = dy if dy.stride(-1) == 1 else dy.contiguous()
+        q, k, v = qkv_heads(qkv, n_head)
+        o = y.view(B, T, n_head, D).permute(0, 2, 1, 3)
+        dO = dy.view(B, T, n_head, D).permute(0, 2, 1, 3) if dy.is_contiguous() else \
+            dy.contiguous().view(B, T, n_head, D).permute(0, 2, 1, 3)
+        dqkv = torch.empty_like(qkv)
+        dq, dk, dv = qkv_heads(dqkv, n_head)
+        delta = torch.empty_like(lse)
+        attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta)
+        return dqkv, None
+
+
+def causal_attention_qkv(qkv: torch.Tensor, n_head: int) -> torch.Tensor:
+    """Causal attention on the fused c_attn output: qkv [B, T, 3C] (q, k, v
+    chunks of C, each [B, T, H, D]) -> y [B, T, C] (heads merged), read and
+    written in place through strided views (bf16, head dim 64)."""
+    return _CausalAttentionQKV.apply(qkv, n_head)
 
 
 def _same_layout(name, t, ref):

@@ -25,12 +25,19 @@ STATUS = {
     7: "ATTN_ERR_SCALE",
     8: "ATTN_ERR_ALIAS",
     9: "ATTN_ERR_HIP",
+    10: "ATTN_ERR_LAYOUT",
 }
 
 # every symbol include/causal_attn.h declares
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_status_str",
-           "attn_abi_version")
-ABI_VERSION = (1 << 16) | 0
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
+           "attn_bwd_strided", "attn_status_str", "attn_abi_version")
+ABI_VERSION = (1 << 16) | 1
+
+
+class AttnView(ctypes.Structure):
+    """attn_view_t: a [B][H][T][D] tensor with element strides."""
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_longlong),
+                ("stride_h", ctypes.c_longlong), ("stride_t", ctypes.c_longlong)]
 
 
 class AttnError(RuntimeError):
@@ -65,6 +72,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_dq.restype = _int
     lib.attn_bwd_dkdv.argtypes = [_vp] * 8 + [_int] * 4 + [ctypes.c_float, _int, _vp]
     lib.attn_bwd_dkdv.restype = _int
+    lib.attn_fwd_strided.argtypes = [AttnView] * 4 + [_vp, _int, _int, _int, _int,
+                                                      ctypes.c_float, _int, _vp]
+    lib.attn_fwd_strided.restype = _int
+    lib.attn_bwd_strided.argtypes = ([AttnView] * 4 + [_vp] + [AttnView] * 4 +
+                                     [_vp, _int, _int, _int, _int, ctypes.c_float, _int, _vp])
+    lib.attn_bwd_strided.restype = _int
     lib.attn_status_str.argtypes = [_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []

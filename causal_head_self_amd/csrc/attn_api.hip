@@ -75,6 +75,8 @@ cattn::AttnArgs make_args(int B, int H, int T, int D, float scale)
 {
     cattn::AttnArgs a{};
     a.n_cu = cu_count();
+    const cattn::Strides c{(long long)H * T * D, (long long)T * D, D};
+    a.sq = a.sk = a.sv = a.so = a.sdo = a.sdq = a.sdk = a.sdv = c;
     a.B = B;
     a.H = H;
     a.T = T;
@@ -84,6 +86,88 @@ cattn::AttnArgs make_args(int B, int H, int T, int D, float scale)
 }
 
 int status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// ---- strided views ----------------------------------------------------------
+
+struct VSpan {
+    const attn_view_t* v;
+    bool output;
+};
+
+// Elements a view can touch: [lo, hi) relative to its data pointer.
+long long view_extent(const attn_view_t& v, int B, int H, int T, int D)
+{
+    return (long long)(B - 1) * v.stride_b + (long long)(H - 1) * v.stride_h +
+           (long long)(T - 1) * v.stride_t + D;
+}
+
+// Conservative disjointness test of two views of one element size (bytes es).
+bool views_disjoint(const attn_view_t& a, const attn_view_t& b, int B, int H, int T, int D, int es)
+{
+    const uintptr_t alo = (uintptr_t)a.data, ahi = alo + (uintptr_t)view_extent(a, B, H, T, D) * es;
+    const uintptr_t blo = (uintptr_t)b.data, bhi = blo + (uintptr_t)view_extent(b, B, H, T, D) * es;
+    if (ahi <= blo || bhi <= alo) return true;
+    // intersecting ranges: accept translates of one lattice whose token footprints
+    // do not meet modulo stride_t
+    if (a.stride_b != b.stride_b || a.stride_h != b.stride_h || a.stride_t != b.stride_t)
+        return false;
+    const long long st = a.stride_t;
+    if (st <= 0 || a.stride_b % st != 0) return false;
+    const long long w = (long long)(H - 1) * a.stride_h + D;  // footprint of one token
+    const long long diff = (long long)((intptr_t)blo - (intptr_t)alo);
+    if (diff % es != 0) return false;
+    const long long r = (((diff / es) % st) + st) % st;
+    return r >= w && st - r >= w;
+}
+
+int validate_views(const VSpan* vs, int n, const float* const* rows, int nrows, int B, int H,
+                   int T, int D, float scale, int dtype)
+{
+    for (int i = 0; i < n; ++i)
+        if (!vs[i].v->data) return ATTN_ERR_NULL;
+    for (int i = 0; i < nrows; ++i)
+        if (!rows[i]) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || T < 1) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (D != 32 && D != 64) return ATTN_ERR_UNSUPPORTED_D;
+    if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_ERR_SCALE;
+    if (dtype != ATTN_BF16 || D != 64) return ATTN_ERR_LAYOUT;
+    const long long BH = (long long)B * H;
+    if ((long long)T * D > 0x7fffffffLL || BH * ((T + 63) / 64) > 0x7fffffffLL ||
+        BH * (long long)T > (1LL << 35))
+        return ATTN_ERR_OVERFLOW;
+    for (int i = 0; i < n; ++i) {
+        const attn_view_t& v = *vs[i].v;
+        if (v.stride_b < 0 || v.stride_h < 0 || v.stride_t < D || v.stride_b % 8 ||
+            v.stride_h % 8 || v.stride_t % 8 || (long long)T * v.stride_t * 2 >= (1LL << 32))
+            return ATTN_ERR_LAYOUT;
+    }
+    for (int i = 0; i < n; ++i)
+        if ((uintptr_t)vs[i].v->data % 16) return ATTN_ERR_ALIGN;
+    for (int i = 0; i < nrows; ++i)
+        if ((uintptr_t)rows[i] % 4) return ATTN_ERR_ALIGN;
+    // aliasing: outputs against everything (views and row tensors)
+    const size_t row_bytes = (size_t)BH * T * sizeof(float);
+    for (int i = 0; i < n; ++i) {
+        if (!vs[i].output) continue;
+        for (int j = 0; j < n; ++j)
+            if (j != i && !(vs[j].output && j < i) &&
+                !views_disjoint(*vs[i].v, *vs[j].v, B, H, T, D, 2))
+                return ATTN_ERR_ALIAS;
+        const uintptr_t lo = (uintptr_t)vs[i].v->data;
+        const uintptr_t hi = lo + (uintptr_t)view_extent(*vs[i].v, B, H, T, D) * 2;
+        for (int j = 0; j < nrows; ++j) {
+            const uintptr_t rlo = (uintptr_t)rows[j], rhi = rlo + row_bytes;
+            if (lo < rhi && rlo < hi) return ATTN_ERR_ALIAS;
+        }
+    }
+    return ATTN_OK;
+}
+
+cattn::Strides strides_of(const attn_view_t& v)
+{
+    return cattn::Strides{v.stride_b, v.stride_h, (int)v.stride_t};
+}
 
 }  // namespace
 
@@ -104,6 +188,9 @@ const char* attn_status_str(int st)
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    case ATTN_ERR_LAYOUT:
+        return "strided views need bf16, D = 64, strides that are non-negative multiples of 8 "
+               "with stride_t >= D, and T * stride_t * 2 < 2^32";
     default: return "unknown status";
     }
 }
@@ -194,6 +281,75 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     hipError_t e = cattn::launch_dq_f32(a, s);
     if (e == hipSuccess) e = cattn::launch_dkdv_f32(a, s);
     return status(e);
+}
+
+int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                     int B, int H, int T, int D, float scale, int dtype, void* stream)
+{
+    const VSpan vs[4] = {{&q, false}, {&k, false}, {&v, false}, {&o, true}};
+    const float* rows[1] = {lse};
+    int st = validate_views(vs, 4, rows, 1, B, H, T, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    // lse (an output) must not overlap an input view either
+    const uintptr_t rlo = (uintptr_t)lse, rhi = rlo + (size_t)B * H * T * sizeof(float);
+    for (int i = 0; i < 3; ++i) {
+        const uintptr_t lo = (uintptr_t)vs[i].v->data;
+        const uintptr_t hi = lo + (uintptr_t)view_extent(*vs[i].v, B, H, T, D) * 2;
+        if (lo < rhi && rlo < hi) return ATTN_ERR_ALIAS;
+    }
+    cattn::AttnArgs a = make_args(B, H, T, D, scale);
+    a.q = q.data;
+    a.k = k.data;
+    a.v = v.data;
+    a.o = o.data;
+    a.o_out = o.data;
+    a.lse = lse;
+    a.sq = strides_of(q);
+    a.sk = strides_of(k);
+    a.sv = strides_of(v);
+    a.so = strides_of(o);
+    return status(cattn::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
+                     const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
+                     attn_view_t dv, float* delta, int B, int H, int T, int D, float scale,
+                     int dtype, void* stream)
+{
+    const VSpan vs[8] = {{&q, false}, {&k, false}, {&v, false}, {&o, false},
+                         {&dO, false}, {&dq, true}, {&dk, true}, {&dv, true}};
+    const float* rows[2] = {lse, delta};
+    int st = validate_views(vs, 8, rows, 2, B, H, T, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    // delta (an output) must not overlap lse or an input view
+    const size_t rb = (size_t)B * H * T * sizeof(float);
+    const uintptr_t dlo = (uintptr_t)delta, dhi = dlo + rb;
+    if (dlo < (uintptr_t)lse + rb && (uintptr_t)lse < dhi) return ATTN_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i) {
+        const uintptr_t lo = (uintptr_t)vs[i].v->data;
+        const uintptr_t hi = lo + (uintptr_t)view_extent(*vs[i].v, B, H, T, D) * 2;
+        if (lo < dhi && dlo < hi) return ATTN_ERR_ALIAS;
+    }
+    cattn::AttnArgs a = make_args(B, H, T, D, scale);
+    a.q = q.data;
+    a.k = k.data;
+    a.v = v.data;
+    a.o = o.data;
+    a.dO = dO.data;
+    a.lse = const_cast<float*>(lse);
+    a.delta = delta;
+    a.dq = dq.data;
+    a.dk = dk.data;
+    a.dv = dv.data;
+    a.sq = strides_of(q);
+    a.sk = strides_of(k);
+    a.sv = strides_of(v);
+    a.so = strides_of(o);
+    a.sdo = strides_of(dO);
+    a.sdq = strides_of(dq);
+    a.sdk = strides_of(dk);
+    a.sdv = strides_of(dv);
+    return status(cattn::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -57,15 +57,16 @@ __device__ __forceinline__ int chunk_off(int r, int c) { return r * 128 + ((c ^ 
 // fetches that row's logical chunk (l & 7) ^ swz(row).  The per-lane byte
 // offsets are constant; a full tile then needs only a scalar base per copy.
 // Rows >= T (last tile only) read row T-1 instead (always valid memory); the
-// kernels mask those rows.
+// kernels mask those rows.  Rows are `st` elements apart in memory (64 for a
+// contiguous [B][H][T][64] tensor).
 struct TileCopy {
-    uint32_t off[2];  // byte offset of this lane's 16 bytes inside a full tile, per instruction
+    uint32_t cb[2];  // byte offset of this lane's 16 bytes inside its row, per instruction
     __device__ __forceinline__ TileCopy(int wave, int lane)
     {
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int row = wave * 16 + it * 8 + (lane >> 3);
-            off[it] = (uint32_t)(row * HD + (((lane & 7) ^ swz(row)) * 8)) * 2u;
+            cb[it] = (uint32_t)((lane & 7) ^ swz(row)) * 16u;
         }
     }
 };
@@ -73,24 +74,26 @@ struct TileCopy {
 // All addresses are a wave-uniform base plus a 32-bit per-lane offset (the
 // scalar-base form of global_load_lds), which keeps 64-bit address arithmetic
 // out of the vector registers.
-__device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restrict__ head,
+__device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restrict__ head, int st,
                                                 int row0, int T, int wave, const TileCopy& tc)
 {
     const char* base = (const char*)head;
+    const uint32_t sb = (uint32_t)st * 2u;
+    const int lane = __lane_id();
     if (row0 + kTile <= T) {  // wave-uniform: every row exists
-        const char* b = base + (size_t)row0 * (HD * 2);
+        const char* b = base + (size_t)row0 * sb;
 #pragma unroll
-        for (int it = 0; it < 2; ++it)
-            __builtin_amdgcn_global_load_lds((const void*)(b + tc.off[it]),
+        for (int it = 0; it < 2; ++it) {
+            const uint32_t o = (uint32_t)(wave * 16 + it * 8 + (lane >> 3)) * sb + tc.cb[it];
+            __builtin_amdgcn_global_load_lds((const void*)(b + o),
                                              (__attribute__((address_space(3))) void*)(tile + (wave * 16 + it * 8) * 128),
                                              16, 0, 0);
+        }
     } else {
-        const int lane = __lane_id();
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int row = wave * 16 + it * 8 + (lane >> 3);
-            const uint32_t o = (uint32_t)min(row0 + row, T - 1) * (HD * 2u) +
-                               (uint32_t)((lane & 7) ^ swz(row)) * 16u;
+            const uint32_t o = (uint32_t)min(row0 + row, T - 1) * sb + tc.cb[it];
             __builtin_amdgcn_global_load_lds((const void*)(base + o),
                                              (__attribute__((address_space(3))) void*)(tile + (wave * 16 + it * 8) * 128),
                                              16, 0, 0);
@@ -220,6 +223,21 @@ __device__ __forceinline__ int item_of(int x, int n_items, int n_cu)
     return r * n_cu + 8 * ((n_cu >> 3) - 1 - (p >> 3)) + (p & 7);
 }
 
+// A [B][H][T][64] bf16 tensor with element strides: (b, h, t, d) sits at
+// p + b*sb + h*sh + t*st + d.  Contiguous tensors have sb = H*T*64,
+// sh = T*64, st = 64.
+struct View {
+    bf16* p;
+    long long sb, sh;
+    int st;
+};
+
+__device__ __forceinline__ bf16* head_of(const View& v, int bh, int H)
+{
+    const int b = bh / H, h = bh - b * H;
+    return v.p + (long long)b * v.sb + (long long)h * v.sh;
+}
+
 // ---------------------------------------------------------------------------
 // forward: 128 queries per workgroup (32 per wave), 64-key K and V tiles,
 // double-buffered through LDS (the copy of tile j+1 is in flight while tile j
@@ -229,9 +247,8 @@ __device__ __forceinline__ int item_of(int x, int n_items, int n_cu)
 // needs tiles 0..last_w; only the last one crosses its diagonal and is masked.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_d64_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int T, int n_qtiles, float scale,
-    float scale_log2, int n_cu)
+    View Q, View K, View V, View O, float* __restrict__ LSE, int BH, int H, int T, int n_qtiles,
+    float scale, float scale_log2, int n_cu)
 {
     // Separate arrays per buffer (not one indexed array): with the buffer of every
     // access known at compile time, the compiler can tell that an LDS read does not
@@ -247,9 +264,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     const int bh = item % BH;
     const int qt = n_qtiles - 1 - item / BH;  // heaviest tiles first
-    const size_t head = (size_t)bh * T * HD;
-    const bf16* Kh = K + head;
-    const bf16* Vh = V + head;
+    const bf16* Kh = head_of(K, bh, H);
+    const bf16* Vh = head_of(V, bh, H);
     const int q0w = qt * kRowsPerWG + wave * 32;  // wave-uniform
     const int qrow = q0w + li;
     const Offsets off(lane);
@@ -259,13 +275,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int n_kv = (kv_end + kTile - 1) / kTile;
     const int last_w = min(n_kv - 1, (q0w + 31) / kTile);  // tiles 0..last_w-1 are fully visible
 
-    tile_load_async(sK0, Kh, 0, T, wave, tc);
-    tile_load_async(sV0, Vh, 0, T, wave, tc);
+    tile_load_async(sK0, Kh, K.st, 0, T, wave, tc);
+    tile_load_async(sV0, Vh, V.st, 0, T, wave, tc);
 
     bf16x8 qreg[4];
+    const bf16* qh = head_of(Q, bh, H);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-        qreg[ks] = (qrow < T) ? *(const bf16x8*)(Q + head + (size_t)qrow * HD + 16 * ks + 8 * hi)
+        qreg[ks] = (qrow < T) ? *(const bf16x8*)(qh + (size_t)qrow * Q.st + 16 * ks + 8 * hi)
                               : zero_bf16x8();
     f32x16 oacc[2] = {f32x16{}, f32x16{}};
     float m = -INFINITY;  // running max (raw dot-product units), shared by lanes l, l^32
@@ -329,8 +346,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         wait_async_copies();
         __syncthreads();
         if (j + 1 < n_kv) {
-            tile_load_async(kl, Kh, (j + 1) * kTile, T, wave, tc);
-            tile_load_async(vl, Vh, (j + 1) * kTile, T, wave, tc);
+            tile_load_async(kl, Kh, K.st, (j + 1) * kTile, T, wave, tc);
+            tile_load_async(vl, Vh, V.st, (j + 1) * kTile, T, wave, tc);
         }
         if (j <= last_w) tile(j == last_w, j, kc, vc);
     };
@@ -343,7 +360,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     l = halves_sum(l);
     if (qrow < T) {
         const float inv = 1.0f / l;
-        bf16* orow = O + head + (size_t)qrow * HD;
+        bf16* orow = head_of(O, bh, H) + (size_t)qrow * O.st;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -357,17 +374,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
 // Arguments of the backward work items.
 struct BwdParams {
-    const bf16* Q;
-    const bf16* K;
-    const bf16* V;
-    const bf16* O;
-    const bf16* dO;
+    View Q, K, V, O, dO;
     const float* LSE;
     float* Delta;  // dQ items write it; dK/dV items read it unless they form it from O
-    bf16* dQ;
-    bf16* dK;
-    bf16* dV;
-    int BH, T;
+    View dQ, dK, dV;
+    int BH, H, T;
     float scale, scale_log2;
 };
 
@@ -389,9 +400,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, hi = lane >> 5;
     (void)BH;
-    const size_t head = (size_t)bh * T * HD;
-    const bf16* Kh = a.K + head;
-    const bf16* Vh = a.V + head;
+    const bf16* Kh = head_of(a.K, bh, a.H);
+    const bf16* Vh = head_of(a.V, bh, a.H);
     const int q0w = qt * kRowsPerWG + wave * 32;
     const int qrow = q0w + li;
     const bool valid = qrow < T;
@@ -402,17 +412,19 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     const int n_kv = (kv_end + kTile - 1) / kTile;
     const int last_w = min(n_kv - 1, (q0w + 31) / kTile);
 
-    tile_load_async(sK0, Kh, 0, T, wave, tc);
-    tile_load_async(sV0, Vh, 0, T, wave, tc);
+    tile_load_async(sK0, Kh, a.K.st, 0, T, wave, tc);
+    tile_load_async(sV0, Vh, a.V.st, 0, T, wave, tc);
 
     bf16x8 qreg[4], greg[4];
     float dsum = 0.f;
+    const bf16* qr = head_of(a.Q, bh, a.H) + (size_t)qrow * a.Q.st + 8 * hi;
+    const bf16* gr = head_of(a.dO, bh, a.H) + (size_t)qrow * a.dO.st + 8 * hi;
+    const bf16* orr = head_of(a.O, bh, a.H) + (size_t)qrow * a.O.st + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const size_t o = head + (size_t)qrow * HD + 16 * ks + 8 * hi;
-        qreg[ks] = valid ? *(const bf16x8*)(a.Q + o) : zero_bf16x8();
-        greg[ks] = valid ? *(const bf16x8*)(a.dO + o) : zero_bf16x8();
-        const bf16x8 orow = valid ? *(const bf16x8*)(a.O + o) : zero_bf16x8();
+        qreg[ks] = valid ? *(const bf16x8*)(qr + 16 * ks) : zero_bf16x8();
+        greg[ks] = valid ? *(const bf16x8*)(gr + 16 * ks) : zero_bf16x8();
+        const bf16x8 orow = valid ? *(const bf16x8*)(orr + 16 * ks) : zero_bf16x8();
 #pragma unroll
         for (int e = 0; e < 8; ++e) dsum = fmaf((float)greg[ks][e], (float)orow[e], dsum);
     }
@@ -460,8 +472,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
         wait_async_copies();
         __syncthreads();
         if (j + 1 < n_kv) {
-            tile_load_async(kl, Kh, (j + 1) * kTile, T, wave, tc);
-            tile_load_async(vl, Vh, (j + 1) * kTile, T, wave, tc);
+            tile_load_async(kl, Kh, a.K.st, (j + 1) * kTile, T, wave, tc);
+            tile_load_async(vl, Vh, a.V.st, (j + 1) * kTile, T, wave, tc);
         }
         if (j > last_w) return;
         const int k0 = j * kTile;
@@ -477,7 +489,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     }
 
     if (valid) {
-        bf16* row = a.dQ + head + (size_t)qrow * HD;
+        bf16* row = head_of(a.dQ, bh, a.H) + (size_t)qrow * a.dQ.st;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -514,10 +526,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, hi = lane >> 5;
-    const size_t head = (size_t)bh * T * HD;
-    const bf16* Qh = a.Q + head;
-    const bf16* Gh = a.dO + head;
-    const bf16* Oh = a.O + head;
+    const bf16* Qh = head_of(a.Q, bh, a.H);
+    const bf16* Gh = head_of(a.dO, bh, a.H);
+    const bf16* Oh = head_of(a.O, bh, a.H);
     const float* Lh = a.LSE + (size_t)bh * T;
     const float* Dh = kDeltaFromO ? nullptr : a.Delta + (size_t)bh * T;
     const int kv0 = kb * kRowsPerWG;
@@ -577,17 +588,18 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
 
     // Tiles are visited from the last one down to the diagonal, so that every item
     // of a head streams the same tile at about the same time (they share it in L2).
-    tile_load_async(sQ0, Qh, (n_q - 1) * kTile, T, wave, tc);
-    tile_load_async(sG0, Gh, (n_q - 1) * kTile, T, wave, tc);
-    if (kDeltaFromO) tile_load_async(sO0, Oh, (n_q - 1) * kTile, T, wave, tc);
+    tile_load_async(sQ0, Qh, a.Q.st, (n_q - 1) * kTile, T, wave, tc);
+    tile_load_async(sG0, Gh, a.dO.st, (n_q - 1) * kTile, T, wave, tc);
+    if (kDeltaFromO) tile_load_async(sO0, Oh, a.O.st, (n_q - 1) * kTile, T, wave, tc);
     rows_load_async(n_q - 1, sR0);
 
     bf16x8 kreg[4], vreg[4];
+    const bf16* kr = head_of(a.K, bh, a.H) + (size_t)key * a.K.st + 8 * hi;
+    const bf16* vr = head_of(a.V, bh, a.H) + (size_t)key * a.V.st + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const size_t o = head + (size_t)key * HD + 16 * ks + 8 * hi;
-        kreg[ks] = valid ? *(const bf16x8*)(a.K + o) : zero_bf16x8();
-        vreg[ks] = valid ? *(const bf16x8*)(a.V + o) : zero_bf16x8();
+        kreg[ks] = valid ? *(const bf16x8*)(kr + 16 * ks) : zero_bf16x8();
+        vreg[ks] = valid ? *(const bf16x8*)(vr + 16 * ks) : zero_bf16x8();
     }
     wait_async_copies();
     rows_finish(n_q - 1, sG0, sO0, sR0);
@@ -651,9 +663,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         __syncthreads();
         const bool more = i > i0;
         if (more) {
-            tile_load_async(ql, Qh, (i - 1) * kTile, T, wave, tc);
-            tile_load_async(gl, Gh, (i - 1) * kTile, T, wave, tc);
-            if (kDeltaFromO) tile_load_async(ol, Oh, (i - 1) * kTile, T, wave, tc);
+            tile_load_async(ql, Qh, a.Q.st, (i - 1) * kTile, T, wave, tc);
+            tile_load_async(gl, Gh, a.dO.st, (i - 1) * kTile, T, wave, tc);
+            if (kDeltaFromO) tile_load_async(ol, Oh, a.O.st, (i - 1) * kTile, T, wave, tc);
             rows_load_async(i - 1, rl);
         }
         if (i >= first_w) {
@@ -675,8 +687,8 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     }
 
     if (valid) {
-        bf16* krow = a.dK + head + (size_t)key * HD;
-        bf16* vrow = a.dV + head + (size_t)key * HD;
+        bf16* krow = head_of(a.dK, bh, a.H) + (size_t)key * a.dK.st;
+        bf16* vrow = head_of(a.dV, bh, a.H) + (size_t)key * a.dV.st;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -748,30 +760,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
 }  // namespace d64
 
+static d64::View view(const void* p, const Strides& s)
+{
+    return d64::View{(bf16*)p, s.sb, s.sh, s.st};
+}
+
 hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     hipLaunchKernelGGL(d64::attn_fwd_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o_out, a.lse,
-                       BH, a.T, nqt, a.scale, a.scale * kLog2e, a.n_cu);
+                       view(a.q, a.sq), view(a.k, a.sk), view(a.v, a.sv), view(a.o_out, a.so),
+                       a.lse, BH, a.H, a.T, nqt, a.scale, a.scale * kLog2e, a.n_cu);
     return hipGetLastError();
 }
 
 static d64::BwdParams bwd_params(const AttnArgs& a)
 {
     d64::BwdParams p;
-    p.Q = (const bf16*)a.q;
-    p.K = (const bf16*)a.k;
-    p.V = (const bf16*)a.v;
-    p.O = (const bf16*)a.o;
-    p.dO = (const bf16*)a.dO;
+    p.Q = view(a.q, a.sq);
+    p.K = view(a.k, a.sk);
+    p.V = view(a.v, a.sv);
+    p.O = view(a.o, a.so);
+    p.dO = view(a.dO, a.sdo);
     p.LSE = a.lse;
     p.Delta = a.delta;
-    p.dQ = (bf16*)a.dq;
-    p.dK = (bf16*)a.dk;
-    p.dV = (bf16*)a.dv;
+    p.dQ = view(a.dq, a.sdq);
+    p.dK = view(a.dk, a.sdk);
+    p.dV = view(a.dv, a.sdv);
     p.BH = a.B * a.H;
+    p.H = a.H;
     p.T = a.T;
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;

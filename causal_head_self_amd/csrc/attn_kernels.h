@@ -6,6 +6,12 @@
 
 namespace cattn {
 
+// Element strides of a [B][H][T][D] tensor whose D elements are contiguous.
+struct Strides {
+    long long sb, sh;  // between batches, between heads
+    int st;            // between tokens
+};
+
 struct AttnArgs {
     const void* q;
     const void* k;
@@ -21,6 +27,8 @@ struct AttnArgs {
     int B, H, T, D;
     float scale;
     int n_cu;        // compute units of the current device (work placement)
+    // strides of q, k, v, o, dO, dq, dk, dv (contiguous unless a strided entry point set them)
+    Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
 };
 
 // launch_dq_* computes delta (from o and dO) as well as dq.

@@ -63,7 +63,8 @@ typedef enum {
     ATTN_ERR_OVERFLOW = 6,      /* T*D or the launch grid exceeds 2^31 - 1  */
     ATTN_ERR_SCALE = 7,         /* scale not finite or not > 0              */
     ATTN_ERR_ALIAS = 8,         /* an output overlaps an input or output    */
-    ATTN_ERR_HIP = 9            /* a kernel launch failed                   */
+    ATTN_ERR_HIP = 9,           /* a kernel launch failed                   */
+    ATTN_ERR_LAYOUT = 10        /* strided views: unsupported dtype/D or strides */
 } attn_status_t;
 
 /* Forward.  Reads q, k, v; writes o ([B][H][T][D], dtype) and lse
@@ -100,13 +101,58 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
                   const float* lse, const float* delta, void* dk, void* dv, int B,
                   int H, int T, int D, float scale, int dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Strided views.  The pages' tensors are per-head views of the c_attn output,
+ * q, k, v = split(x W_attn + b) viewed as [B][T][H][D] and transposed to
+ * [B][H][T][D] (CS336 tutorial, section 5.1, CausalSelfAttention.forward), and
+ * the attention output goes back through the inverse transpose into [B][T][C].
+ * These entry points take such views directly, so no layout copy is needed.
+ *
+ * attn_view_t describes a [B][H][T][D] tensor whose D elements are contiguous:
+ * element (b, h, t, d) is at data + b*stride_b + h*stride_h + t*stride_t + d,
+ * strides counted in elements of the call's dtype.  Examples (C = H*D):
+ *   contiguous [B][H][T][D]:        stride_b = H*T*D, stride_h = T*D, stride_t = D
+ *   [B][T][H][D] (= [B][T][C]):      stride_b = T*C,   stride_h = D,   stride_t = C
+ *   q of a [B][T][3][H][D] qkv:      stride_b = 3*T*C, stride_h = D,   stride_t = 3*C
+ *                                    (k at data + C, v at data + 2*C)
+ *
+ * Supported for dtype ATTN_BF16 with D = 64 (else ATTN_ERR_LAYOUT).  Each view
+ * needs a 16-byte-aligned data pointer, non-negative strides that are
+ * multiples of 8, stride_t >= D, and T * stride_t * 2 bytes below 2^32
+ * (ATTN_ERR_LAYOUT otherwise).  lse and delta stay contiguous fp32 [B][H][T].
+ * Aliasing: inputs may share memory with each other.  An output must not share
+ * an element with an input or another output.  The check (ATTN_ERR_ALIAS) is
+ * conservative: two views whose address ranges intersect are accepted only if
+ * they have equal strides, stride_b is a multiple of stride_t, and their
+ * per-token footprints of (H-1)*stride_h + D elements do not meet modulo
+ * stride_t (as for q, k, v or dq, dk, dv in one [B][T][3][H][D] buffer).
+ * Results equal those of attn_fwd / attn_bwd on contiguous copies of the same
+ * values, bit for bit. */
+typedef struct {
+    void* data;
+    long long stride_b;
+    long long stride_h;
+    long long stride_t;
+} attn_view_t;
+
+/* attn_fwd on strided views (q, k, v read; o written). */
+int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                     int B, int H, int T, int D, float scale, int dtype, void* stream);
+
+/* attn_bwd on strided views (q, k, v, o, dO read; dq, dk, dv written), in one
+ * kernel launch; delta as in attn_bwd. */
+int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
+                     const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
+                     attn_view_t dv, float* delta, int B, int H, int T, int D, float scale,
+                     int dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_str(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 0)
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

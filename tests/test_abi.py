@@ -41,11 +41,11 @@ def test_abi_version_and_status_strings():
     lib = cat.load_library()
     assert lib.attn_abi_version() == _lib.ABI_VERSION
     seen = set()
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = cat.attn_status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 10
+    assert len(seen) == 11
     assert cat.attn_status_str(1234) == "unknown status"
     assert cat.attn_status_str(-1) == "unknown status"
 
@@ -204,3 +204,83 @@ def test_python_wrapper_rejects_cpu_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         _lib.load_library(str(tmp_path / "libcausal_attn.so"))
+
+
+# ---------------------------------------------------------------------------
+# strided views (attn_fwd_strided / attn_bwd_strided): every call below holds
+# an invalid argument, so it returns during validation
+# ---------------------------------------------------------------------------
+
+B_, H_, T_, D_ = 2, 3, 17, 64
+C_ = H_ * D_
+
+
+def _v(ptr, sb=H_ * T_ * D_, sh=T_ * D_, st=D_):
+    return _lib.AttnView(ptr, sb, sh, st)
+
+
+def _qkv_views(base, elem=2):
+    """q, k, v views of one [B][T][3][H][D] buffer at `base`."""
+    sb, sh, st = T_ * 3 * C_, D_, 3 * C_
+    return [_v(base + i * C_ * elem, sb, sh, st) for i in range(3)]
+
+
+def _fwd_s(views=None, lse=P[4], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1):
+    v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3])]
+    return cat.load_library().attn_fwd_strided(v[0], v[1], v[2], v[3], lse, B, H, T, D, scale,
+                                               dtype, None)
+
+
+def _bwd_s(views=None, lse=P[4], delta=P[9], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1):
+    v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3]), _v(P[5]), _v(P[6]), _v(P[7]),
+                  _v(P[8])]
+    return cat.load_library().attn_bwd_strided(v[0], v[1], v[2], v[3], lse, v[4], v[5], v[6],
+                                               v[7], delta, B, H, T, D, scale, dtype, None)
+
+
+def test_strided_null_shape_scale():
+    assert _fwd_s(views=[_v(0), _v(P[1]), _v(P[2]), _v(P[3])]) == 1
+    assert _fwd_s(lse=0) == 1
+    assert _bwd_s(delta=0) == 1
+    assert _fwd_s(T=0) == 2
+    assert _bwd_s(H=0) == 2
+    assert _fwd_s(scale=0.0) == 7
+    assert _bwd_s(scale=float("nan")) == 7
+
+
+def test_strided_supports_only_bf16_d64():
+    assert _fwd_s(dtype=0) == 10
+    assert _bwd_s(dtype=0) == 10
+    assert _fwd_s(D=32) == 10
+    assert _fwd_s(D=48) == 3
+    assert _fwd_s(dtype=7) == 4
+
+
+def test_strided_stride_rules():
+    base = [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3])]
+    bad = [_v(P[0], st=60), _v(P[0], st=68), _v(P[0], sh=4), _v(P[0], sb=-64),
+           _v(P[0], st=1 << 27)]  # stride_t < D, not /8, not /8, negative, T*st*2 >= 2^32
+    for b in bad:
+        assert _fwd_s(views=[b] + base[1:]) == 10, (b.stride_b, b.stride_h, b.stride_t)
+    assert _fwd_s(views=base[:3] + [_v(P[3] + 8)]) == 5  # o not 16-byte aligned
+    assert _fwd_s(lse=P[4] + 2) == 5
+
+
+def test_strided_alias_rules():
+    q, k, v = _qkv_views(P[0])
+    # inputs may share memory (q, k, v of one qkv buffer); o may not overlap them
+    assert _fwd_s(views=[q, k, v, _v(P[0] + 64)]) == 8
+    # o equal to an input lattice translate that meets it
+    assert _fwd_s(views=[q, k, v, _qkv_views(P[0] + 2 * 64)[0]]) == 8
+    # lse inside an input
+    assert _fwd_s(views=[q, k, v, _v(P[3])], lse=P[0] + 256) == 8
+    # dq, dk, dv interleaved in one [B][T][3][H][D] buffer pass the view check; the
+    # call then fails on delta overlapping lse, which is checked after it
+    dq, dk, dv = _qkv_views(P[6])
+    assert _bwd_s(views=[q, k, v, _v(P[3]), _v(P[5]), dq, dk, dv], delta=P[4]) == 8
+    # two outputs at the same address
+    assert _bwd_s(views=[q, k, v, _v(P[3]), _v(P[5]), dq, dq, dv]) == 8
+    # outputs of one lattice whose token footprints meet (offset 32 elements, footprint 192)
+    sb, sh, st = T_ * 3 * C_, D_, 3 * C_
+    near = _lib.AttnView(P[6] + 64, sb, sh, st)
+    assert _bwd_s(views=[q, k, v, _v(P[3]), _v(P[5]), dq, near, dv]) == 8

@@ -274,3 +274,64 @@ def test_non_default_stream():
         cat.attn_fwd(qd, kd, vd, o, lse, 0.125, stream=s)
     s.synchronize()
     assert np.array_equal(o.float().cpu().numpy(), ref["o"])
+
+
+# ---------------------------------------------------------------------------
+# strided views: q, k, v read straight out of a [B, T, 3C] c_attn output, o and
+# the gradients written in the merged [B, T, C] / [B, T, 3C] layouts
+# ---------------------------------------------------------------------------
+
+def _to_qkv(q, k, v):
+    """[B, H, T, D] x3 -> [B, T, 3C] with C = H*D (the c_attn output layout)."""
+    B, H, T, D = q.shape
+    return torch.cat([t.permute(0, 2, 1, 3).reshape(B, T, H * D) for t in (q, k, v)], dim=-1)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 65, 64), (2, 3, 300, 64), (3, 1, 129, 64)])
+def test_strided_views_match_oracle_and_contiguous_path(shape):
+    import causal_head_self_amd as cat
+    B, H, T, D = shape
+    _note(f"[parity] strided views B={B} H={H} T={T} D={D} bf16")
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", 400 + sum(shape))
+    scale = 1.0 / math.sqrt(D)
+    dev = torch.device("cuda")
+    qkv = _to_qkv(q, k, v).to(dev)
+    qv, kv, vv = cat.qkv_heads(qkv, H)
+    y = torch.empty((B, T, H * D), dtype=torch.bfloat16, device=dev)
+    ov = y.view(B, T, H, D).permute(0, 2, 1, 3)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    cat.attn_fwd_strided(qv, kv, vv, ov, lse, scale)
+    gy = dO.permute(0, 2, 1, 3).reshape(B, T, H * D).to(dev)
+    gv = gy.view(B, T, H, D).permute(0, 2, 1, 3)
+    dqkv = torch.empty_like(qkv)
+    dqv, dkv, dvv = cat.qkv_heads(dqkv, H)
+    delta = torch.empty_like(lse)
+    cat.attn_bwd_strided(qv, kv, vv, ov, lse, gv, dqv, dkv, dvv, delta, scale)
+    # the contiguous path on copies of the same values
+    ref_gpu = gpu_attention(q, k, v, dO, scale)
+    torch.cuda.synchronize()
+    as_np = lambda t: t.float().cpu().numpy().astype(np.float64)
+    got = {"o": as_np(ov), "lse": as_np(lse), "dq": as_np(dqv), "dk": as_np(dkv),
+           "dv": as_np(dvv), "delta": as_np(delta)}
+    for name, val in got.items():
+        assert np.array_equal(val, ref_gpu[name]), f"{name}: strided differs from contiguous"
+    ref = oracle_attention(q, k, v, dO, scale)
+    assert_close(got, ref, TOL["bf16"], f"strided B{B} H{H} T{T}", delta_bound(ref, dO))
+
+
+def test_qkv_autograd_matches_split_heads():
+    import causal_head_self_amd as cat
+    B, H, T, D = 2, 4, 200, 64
+    _note(f"[parity] causal_attention_qkv B={B} H={H} T={T} D={D}")
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", 77)
+    dev = torch.device("cuda")
+    qkv = _to_qkv(q, k, v).to(dev).requires_grad_(True)
+    y = cat.causal_attention_qkv(qkv, H)
+    gy = dO.permute(0, 2, 1, 3).reshape(B, T, H * D).to(dev)
+    y.backward(gy)
+    qs, ks, vs = (t.to(dev).requires_grad_(True) for t in (q, k, v))
+    o = cat.causal_attention(qs, ks, vs)
+    o.backward(dO.to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(B, T, H, D).permute(0, 2, 1, 3), o)
+    assert torch.equal(qkv.grad, _to_qkv(qs.grad, ks.grad, vs.grad))
