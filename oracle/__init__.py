@@ -44,9 +44,9 @@ def build(force: bool = True) -> str:
 
 def _bind(path: str):
     lib = ctypes.CDLL(path)
-    lib.oracle_attn_fwd.argtypes = [_dp] * 5 + [_i64] * 4 + [ctypes.c_double, _i64]
+    lib.oracle_attn_fwd.argtypes = [_dp] * 5 + [_i64] * 4 + [ctypes.c_double, _i64, _i64]
     lib.oracle_attn_fwd.restype = None
-    lib.oracle_attn_bwd.argtypes = [_dp] * 8 + [_i64] * 4 + [ctypes.c_double, _i64]
+    lib.oracle_attn_bwd.argtypes = [_dp] * 8 + [_i64] * 4 + [ctypes.c_double, _i64, _i64]
     lib.oracle_attn_bwd.restype = None
     lib.oracle_sublayer_fwd.argtypes = [_dp] * 8 + [_i64] * 4 + [ctypes.c_double, _i64]
     lib.oracle_sublayer_fwd.restype = ctypes.c_int
@@ -109,27 +109,31 @@ def widen_scale(scale: float) -> float:
     return float(np.float32(scale))
 
 
-def attn_fwd(q, k, v, scale: float, nthreads: int = 0, lib: str | None = None):
-    """Returns (o [B,H,T,D], lse [B,H,T]) in float64."""
+def attn_fwd(q, k, v, scale: float, nthreads: int = 0, lib: str | None = None,
+             window: int = 0):
+    """Returns (o [B,H,T,D], lse [B,H,T]) in float64.  window = W > 0 restricts
+    query i to keys i-W < j <= i (sliding window); 0 is the full causal mask."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, T, D = q.shape
     assert k.shape == q.shape and v.shape == q.shape
     o = np.empty_like(q)
     lse = np.empty((B, H, T), dtype=np.float64)
     _load(lib).oracle_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, T, D,
-                            float(scale), int(nthreads))
+                            float(scale), int(window), int(nthreads))
     return o, lse
 
 
-def attn_bwd(q, k, v, dO, scale: float, nthreads: int = 0, lib: str | None = None):
-    """Returns (dq, dk, dv, delta) in float64 for the upstream gradient dO."""
+def attn_bwd(q, k, v, dO, scale: float, nthreads: int = 0, lib: str | None = None,
+             window: int = 0):
+    """Returns (dq, dk, dv, delta) in float64 for the upstream gradient dO
+    (window as in attn_fwd)."""
     q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
     B, H, T, D = q.shape
     assert k.shape == q.shape and v.shape == q.shape and dO.shape == q.shape
     dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
     delta = np.empty((B, H, T), dtype=np.float64)
     _load(lib).oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dO), _p(dq), _p(dk), _p(dv),
-                            _p(delta), B, H, T, D, float(scale), int(nthreads))
+                            _p(delta), B, H, T, D, float(scale), int(window), int(nthreads))
     return dq, dk, dv, delta
 
 

@@ -61,24 +61,33 @@ int oracle_max_threads(void)
 #endif
 }
 
-/* One row of the causal softmax: p[j] for j = 0..i, from scores s[j].
+/* First key row i sees.  window = 0: every earlier key (the causal mask of
+ * CS336 section 5.1).  window = W > 0: the W most recent keys, i - W < j <= i
+ * (the sliding-window attention that nanochat section 9 lists; the band of the
+ * causal mask, read with the diagonal kept as above). */
+static int64_t first_key(int64_t i, int64_t window)
+{
+    return (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
+}
+
+/* One row of the causal softmax: p[j] for j = j0..i, from scores s[j].
  * Returns m (the row max) and writes Z (the normaliser) so that
- * lse = m + log(Z).  Keys j > i are masked (-inf) and carry weight exactly 0,
- * so they are simply not part of the sum. */
+ * lse = m + log(Z).  Keys j > i (and j < j0 in a window) are masked (-inf)
+ * and carry weight exactly 0, so they are simply not part of the sum. */
 static void causal_softmax_row(const double* Qi, const double* K, int64_t i,
-                               int64_t D, double scale, double* s, double* p,
+                               int64_t j0, int64_t D, double scale, double* s, double* p,
                                double* m_out, double* Z_out)
 {
     double m = -INFINITY;
-    for (int64_t j = 0; j <= i; ++j) {
+    for (int64_t j = j0; j <= i; ++j) {
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += Qi[d] * K[j * D + d];
         s[j] = scale * dot;
         if (s[j] > m) m = s[j];
     }
     double Z = 0.0;
-    for (int64_t j = 0; j <= i; ++j) Z += exp(s[j] - m);
-    for (int64_t j = 0; j <= i; ++j) p[j] = exp(s[j] - m) / Z;
+    for (int64_t j = j0; j <= i; ++j) Z += exp(s[j] - m);
+    for (int64_t j = j0; j <= i; ++j) p[j] = exp(s[j] - m) / Z;
     *m_out = m;
     *Z_out = Z;
 }
@@ -86,7 +95,7 @@ static void causal_softmax_row(const double* Qi, const double* K, int64_t i,
 /* Forward: o = softmax(mask(scale * q k^T)) v, lse = log sum exp of the row. */
 void oracle_attn_fwd(const double* q, const double* k, const double* v,
                      double* o, double* lse, int64_t B, int64_t H, int64_t T,
-                     int64_t D, double scale, int64_t nthreads)
+                     int64_t D, double scale, int64_t window, int64_t nthreads)
 {
     set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -100,10 +109,11 @@ void oracle_attn_fwd(const double* q, const double* k, const double* v,
         double* p = (double*)malloc((size_t)T * sizeof(double));
         for (int64_t i = 0; i < T; ++i) {
             double m, Z;
-            causal_softmax_row(Q + i * D, K, i, D, scale, s, p, &m, &Z);
+            const int64_t j0 = first_key(i, window);
+            causal_softmax_row(Q + i * D, K, i, j0, D, scale, s, p, &m, &Z);
             for (int64_t d = 0; d < D; ++d) {
                 double acc = 0.0;
-                for (int64_t j = 0; j <= i; ++j) acc += p[j] * V[j * D + d];
+                for (int64_t j = j0; j <= i; ++j) acc += p[j] * V[j * D + d];
                 O[i * D + d] = acc;
             }
             L[i] = m + log(Z);
@@ -124,7 +134,7 @@ void oracle_attn_fwd(const double* q, const double* k, const double* v,
 void oracle_attn_bwd(const double* q, const double* k, const double* v,
                      const double* dO, double* dq, double* dk, double* dv,
                      double* delta, int64_t B, int64_t H, int64_t T, int64_t D,
-                     double scale, int64_t nthreads)
+                     double scale, int64_t window, int64_t nthreads)
 {
     set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -144,9 +154,10 @@ void oracle_attn_bwd(const double* q, const double* k, const double* v,
         memset(dV, 0, (size_t)(T * D) * sizeof(double));
         for (int64_t i = 0; i < T; ++i) {
             double m, Z;
-            causal_softmax_row(Q + i * D, K, i, D, scale, s, p, &m, &Z);
+            const int64_t j0 = first_key(i, window);
+            causal_softmax_row(Q + i * D, K, i, j0, D, scale, s, p, &m, &Z);
             double Delta = 0.0;
-            for (int64_t j = 0; j <= i; ++j) {
+            for (int64_t j = j0; j <= i; ++j) {
                 double acc = 0.0;
                 for (int64_t d = 0; d < D; ++d) acc += G[i * D + d] * V[j * D + d];
                 dp[j] = acc;
@@ -154,7 +165,7 @@ void oracle_attn_bwd(const double* q, const double* k, const double* v,
             }
             Dl[i] = Delta;
             for (int64_t d = 0; d < D; ++d) dQ[i * D + d] = 0.0;
-            for (int64_t j = 0; j <= i; ++j) {
+            for (int64_t j = j0; j <= i; ++j) {
                 double dS = p[j] * (dp[j] - Delta);
                 for (int64_t d = 0; d < D; ++d) {
                     dQ[i * D + d] += scale * dS * K[j * D + d];
@@ -258,7 +269,7 @@ static void sublayer_forward_cached(const double* x, const double* g,
     split_heads(S->qkv, 0, S->q, B, T, H, D);
     split_heads(S->qkv, 1, S->k, B, T, H, D);
     split_heads(S->qkv, 2, S->v, B, T, H, D);
-    oracle_attn_fwd(S->q, S->k, S->v, S->o, S->lse, B, H, T, D, scale, 0);
+    oracle_attn_fwd(S->q, S->k, S->v, S->o, S->lse, B, H, T, D, scale, 0, 0);
     merge_heads(S->o, S->a, C, 0, B, T, H, D);
     linear_fwd(S->a, Wp, bp, y, N, C, C);
     for (int64_t n = 0; n < N * C; ++n) y[n] += x[n];
@@ -356,7 +367,7 @@ int oracle_sublayer_bwd(const double* x, const double* g, const double* bl,
                 for (int64_t t = 0; t < T; ++t)
                     for (int64_t d = 0; d < D; ++d)
                         dO[((b * H + h) * T + t) * D + d] = da[(b * T + t) * C + h * D + d];
-        oracle_attn_bwd(S.q, S.k, S.v, dO, dqh, dkh, dvh, dl, B, H, T, D, scale, 0);
+        oracle_attn_bwd(S.q, S.k, S.v, dO, dqh, dkh, dvh, dl, B, H, T, D, scale, 0, 0);
         merge_heads(dqh, dqkv, C3, 0, B, T, H, D);
         merge_heads(dkh, dqkv, C3, C, B, T, H, D);
         merge_heads(dvh, dqkv, C3, 2 * C, B, T, H, D);

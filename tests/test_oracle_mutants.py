@@ -19,8 +19,11 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 MUTANTS = {
     "diagonal_dropped_from_normaliser": (
-        "for (int64_t j = 0; j <= i; ++j) Z += exp(s[j] - m);",
-        "for (int64_t j = 0; j < i; ++j) Z += exp(s[j] - m);"),
+        "for (int64_t j = j0; j <= i; ++j) Z += exp(s[j] - m);",
+        "for (int64_t j = j0; j < i; ++j) Z += exp(s[j] - m);"),
+    "window_one_key_too_many": (
+        "return (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;",
+        "return (window > 0 && i - window > 0) ? i - window : 0;"),
     "scale_missing": ("s[j] = scale * dot;", "s[j] = dot;"),
     "scale_squared": ("s[j] = scale * dot;", "s[j] = scale * scale * dot;"),
     "lse_without_max": ("L[i] = m + log(Z);", "L[i] = log(Z);"),
@@ -68,6 +71,7 @@ BATTERY = [
     pins.test_sublayer_against_torch_library_ops,
     pins.test_sublayer_finite_differences,
     pins.test_layernorm_output_is_standardised,
+    lambda: pins.test_window_against_torch_sdpa_band_mask(3),
 ]
 
 

@@ -387,3 +387,78 @@ def test_layernorm_output_is_standardised():
     var = np.var(x[0, 0])
     assert abs(ln0.mean()) < 1e-14
     np.testing.assert_allclose(np.mean(ln0 ** 2), var / (var + 1e-5), rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# sliding window (query i sees keys i-W < j <= i): nanochat section 9 lists
+# sliding-window attention; the band is the causal mask with the W most
+# recent keys kept
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window", [0, 9, 50])
+def test_window_at_least_T_is_the_causal_result(window):
+    shape = (2, 2, 9, 4)
+    q, k, v = _qkv(shape, seed=301)
+    dO = _rand(shape, 303)
+    o, lse = oracle.attn_fwd(q, k, v, 0.4)
+    dq, dk, dv, delta = oracle.attn_bwd(q, k, v, dO, 0.4)
+    ow, lsew = oracle.attn_fwd(q, k, v, 0.4, window=window)
+    dqw, dkw, dvw, deltaw = oracle.attn_bwd(q, k, v, dO, 0.4, window=window)
+    for a, b in ((o, ow), (lse, lsew), (dq, dqw), (dk, dkw), (dv, dvw), (delta, deltaw)):
+        assert np.array_equal(a, b)
+
+
+def test_window_one_is_the_identity():
+    """W = 1: each query sees only itself, so o = v, lse = s q_i.k_i, P = 1
+    and dS = 0 (dq = dk = 0), dv = dO."""
+    shape = (2, 3, 7, 5)
+    q, k, v = _qkv(shape, seed=307)
+    dO = _rand(shape, 311)
+    o, lse = oracle.attn_fwd(q, k, v, 0.3, window=1)
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, dO, 0.3, window=1)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.3 * np.sum(q * k, axis=-1), rtol=0, atol=1e-14)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    np.testing.assert_allclose(dv, dO, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("window", [2, 3, 5])
+def test_window_against_torch_sdpa_band_mask(window):
+    """PyTorch fp64 scaled_dot_product_attention with an explicit band mask
+    (True where i-W < j <= i), forward and autograd backward."""
+    shape = (2, 2, 9, 3)
+    q, k, v = _qkv(shape, seed=313)
+    dO = _rand(shape, 317)
+    s = 0.45
+    T = shape[2]
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    band = torch.tensor((j <= i) & (j > i - window))
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=band, scale=s)
+    to.backward(torch.tensor(dO))
+    o, _ = oracle.attn_fwd(q, k, v, s, window=window)
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, dO, s, window=window)
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_window_backward_finite_differences():
+    shape = (1, 2, 8, 4)
+    q, k, v = _qkv(shape, seed=331)
+    dO = _rand(shape, 337)
+    W = 3
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, dO, 0.5, window=W)
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for flat in range(x.size):
+            idx = np.unravel_index(flat, x.shape)
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = float(np.sum(oracle.attn_fwd(q, k, v, 0.5, window=W)[0] * dO))
+            x[idx] = x0 - h
+            lm = float(np.sum(oracle.attn_fwd(q, k, v, 0.5, window=W)[0] * dO))
+            x[idx] = x0
+            assert abs((lp - lm) / (2 * h) - g[idx]) < 2e-7, (name, idx)
