@@ -122,25 +122,27 @@ def _view(t: torch.Tensor, name: str) -> AttnView:
     return AttnView(t.data_ptr(), sb, sh, st)
 
 
-def attn_fwd_strided(q, k, v, o, lse, scale: float | None = None, stream=None) -> None:
-    """C ABI attn_fwd_strided: q, k, v, o are [B, H, T, D] views (D contiguous)."""
+def attn_fwd_strided(q, k, v, o, lse, scale: float | None = None, stream=None,
+                     window: int = 0) -> None:
+    """C ABI attn_fwd_strided: q, k, v, o are [B, H, T, D] views (D contiguous);
+    window W > 0 keeps keys i-W < j <= i (0 = plain causal)."""
     B, H, T, D = _shape(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rc = load_library().attn_fwd_strided(
         _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
-        B, H, T, D, scale, _dtype_code(q), _stream(stream))
+        B, H, T, D, int(window), scale, _dtype_code(q), _stream(stream))
     check(rc)
 
 
 def attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale: float | None = None,
-                     stream=None) -> None:
+                     stream=None, window: int = 0) -> None:
     """C ABI attn_bwd_strided: every [B, H, T, D] argument is a view."""
     B, H, T, D = _shape(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rc = load_library().attn_bwd_strided(
         _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
         _view(dO, "dO"), _view(dq, "dq"), _view(dk, "dk"), _view(dv, "dv"),
-        _ptr(delta, "delta"), B, H, T, D, scale, _dtype_code(q), _stream(stream))
+        _ptr(delta, "delta"), B, H, T, D, int(window), scale, _dtype_code(q), _stream(stream))
     check(rc)
 
 
@@ -155,7 +157,7 @@ def qkv_heads(qkv: torch.Tensor, n_head: int):
 
 class _CausalAttentionQKV(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, qkv, n_head):
+    def forward(ctx, qkv, n_head, window):
         if qkv.dim() != 3 or qkv.shape[-1] % (3 * n_head) != 0 or qkv.stride(-1) != 1:
             raise ValueError("qkv must be [B, T, 3C] with contiguous last dim and C % n_head == 0")
         qkv = qkv if qkv.is_contiguous() else qkv.contiguous()
@@ -165,9 +167,10 @@ class _CausalAttentionQKV(torch.autograd.Function):
         y = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
         o = y.view(B, T, n_head, C // n_head).permute(0, 2, 1, 3)  # [B, H, T, D] view of y
         lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
-        attn_fwd_strided(q, k, v, o, lse)
+        attn_fwd_strided(q, k, v, o, lse, window=window)
         ctx.save_for_backward(qkv, y, lse)
         ctx.n_head = n_head
+        ctx.window = window
         return y
 
     @staticmethod
@@ -185,15 +188,16 @@ class _CausalAttentionQKV(torch.autograd.Function):
         dqkv = torch.empty_like(qkv)
         dq, dk, dv = qkv_heads(dqkv, n_head)
         delta = torch.empty_like(lse)
-        attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta)
-        return dqkv, None
+        attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, window=ctx.window)
+        return dqkv, None, None
 
 
-def causal_attention_qkv(qkv: torch.Tensor, n_head: int) -> torch.Tensor:
+def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0) -> torch.Tensor:
     """Causal attention on the fused c_attn output: qkv [B, T, 3C] (q, k, v
     chunks of C, each [B, T, H, D]) -> y [B, T, C] (heads merged), read and
-    written in place through strided views (bf16, head dim 64)."""
-    return _CausalAttentionQKV.apply(qkv, n_head)
+    written in place through strided views (bf16, head dim 64).  window W > 0
+    restricts query i to keys i-W < j <= i (sliding window)."""
+    return _CausalAttentionQKV.apply(qkv, n_head, int(window))
 
 
 def _same_layout(name, t, ref):

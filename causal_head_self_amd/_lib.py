@@ -72,11 +72,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_dq.restype = _int
     lib.attn_bwd_dkdv.argtypes = [_vp] * 8 + [_int] * 4 + [ctypes.c_float, _int, _vp]
     lib.attn_bwd_dkdv.restype = _int
-    lib.attn_fwd_strided.argtypes = [AttnView] * 4 + [_vp, _int, _int, _int, _int,
+    lib.attn_fwd_strided.argtypes = [AttnView] * 4 + [_vp, _int, _int, _int, _int, _int,
                                                       ctypes.c_float, _int, _vp]
     lib.attn_fwd_strided.restype = _int
     lib.attn_bwd_strided.argtypes = ([AttnView] * 4 + [_vp] + [AttnView] * 4 +
-                                     [_vp, _int, _int, _int, _int, ctypes.c_float, _int, _vp])
+                                     [_vp, _int, _int, _int, _int, _int, ctypes.c_float, _int,
+                                      _vp])
     lib.attn_bwd_strided.restype = _int
     lib.attn_status_str.argtypes = [_int]
     lib.attn_status_str.restype = ctypes.c_char_p

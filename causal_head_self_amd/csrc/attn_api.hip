@@ -75,6 +75,7 @@ cattn::AttnArgs make_args(int B, int H, int T, int D, float scale)
 {
     cattn::AttnArgs a{};
     a.n_cu = cu_count();
+    a.window = 0;
     const cattn::Strides c{(long long)H * T * D, (long long)T * D, D};
     a.sq = a.sk = a.sv = a.so = a.sdo = a.sdq = a.sdk = a.sdv = c;
     a.B = B;
@@ -284,12 +285,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 }
 
 int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
-                     int B, int H, int T, int D, float scale, int dtype, void* stream)
+                     int B, int H, int T, int D, int window, float scale, int dtype,
+                     void* stream)
 {
     const VSpan vs[4] = {{&q, false}, {&k, false}, {&v, false}, {&o, true}};
     const float* rows[1] = {lse};
     int st = validate_views(vs, 4, rows, 1, B, H, T, D, scale, dtype);
     if (st != ATTN_OK) return st;
+    if (window < 0) return ATTN_ERR_SHAPE;
     // lse (an output) must not overlap an input view either
     const uintptr_t rlo = (uintptr_t)lse, rhi = rlo + (size_t)B * H * T * sizeof(float);
     for (int i = 0; i < 3; ++i) {
@@ -308,19 +311,21 @@ int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     a.sk = strides_of(k);
     a.sv = strides_of(v);
     a.so = strides_of(o);
+    a.window = window;
     return status(cattn::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
 int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
                      const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
-                     attn_view_t dv, float* delta, int B, int H, int T, int D, float scale,
-                     int dtype, void* stream)
+                     attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
+                     float scale, int dtype, void* stream)
 {
     const VSpan vs[8] = {{&q, false}, {&k, false}, {&v, false}, {&o, false},
                          {&dO, false}, {&dq, true}, {&dk, true}, {&dv, true}};
     const float* rows[2] = {lse, delta};
     int st = validate_views(vs, 8, rows, 2, B, H, T, D, scale, dtype);
     if (st != ATTN_OK) return st;
+    if (window < 0) return ATTN_ERR_SHAPE;
     // delta (an output) must not overlap lse or an input view
     const size_t rb = (size_t)B * H * T * sizeof(float);
     const uintptr_t dlo = (uintptr_t)delta, dhi = dlo + rb;
@@ -349,6 +354,7 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     a.sdq = strides_of(dq);
     a.sdk = strides_of(dk);
     a.sdv = strides_of(dv);
+    a.window = window;
     return status(cattn::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 

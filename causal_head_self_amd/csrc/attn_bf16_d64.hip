@@ -197,6 +197,18 @@ __device__ __forceinline__ void tile_product(const char* tile, const Offsets& of
 // Causal mask of a (key-subtile, query-lane) score tile: element r of s0
 // holds row 8(r/4) + 4hi + r%4 of the tile (+32 in s1); it stays iff that
 // row offset is <= lim, otherwise it becomes -inf.
+// Band version: element kept iff lo < its row offset <= lim (the causal window
+// i - W < j <= i seen from the tile).
+__device__ __forceinline__ void mask_band(f32x16& s0, f32x16& s1, int lim, int lo)
+{
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + (r & 3);
+        s0[r] = kk <= lim && kk > lo ? s0[r] : -INFINITY;
+        s1[r] = kk + 32 <= lim && kk + 32 > lo ? s1[r] : -INFINITY;
+    }
+}
+
 __device__ __forceinline__ void mask_upto(f32x16& s0, f32x16& s1, int lim)
 {
 #pragma unroll
@@ -247,8 +259,8 @@ __device__ __forceinline__ bf16* head_of(const View& v, int bh, int H)
 // needs tiles 0..last_w; only the last one crosses its diagonal and is masked.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_d64_kernel(
-    View Q, View K, View V, View O, float* __restrict__ LSE, int BH, int H, int T, int n_qtiles,
-    float scale, float scale_log2, int n_cu)
+    View Q, View K, View V, View O, float* __restrict__ LSE, int BH, int H, int T, int W,
+    int n_qtiles, float scale, float scale_log2, int n_cu)
 {
     // Separate arrays per buffer (not one indexed array): with the buffer of every
     // access known at compile time, the compiler can tell that an LDS read does not
@@ -273,10 +285,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
     const int kv_end = min(T, qt * kRowsPerWG + kRowsPerWG);
     const int n_kv = (kv_end + kTile - 1) / kTile;
-    const int last_w = min(n_kv - 1, (q0w + 31) / kTile);  // tiles 0..last_w-1 are fully visible
+    const int last_w = min(n_kv - 1, (q0w + 31) / kTile);  // the wave's diagonal tile
+    // window W (W >= T: the plain causal mask): query q sees keys q-W < k <= q
+    const int lo = max(0, qt * kRowsPerWG - W + 1) / kTile;  // the workgroup's first tile
+    const int first_w = max(0, q0w - W + 1) / kTile;        // the wave's first tile
 
-    tile_load_async(sK0, Kh, K.st, 0, T, wave, tc);
-    tile_load_async(sV0, Vh, V.st, 0, T, wave, tc);
+    tile_load_async(sK0, Kh, K.st, lo * kTile, T, wave, tc);
+    tile_load_async(sV0, Vh, V.st, lo * kTile, T, wave, tc);
 
     bf16x8 qreg[4];
     const bf16* qh = head_of(Q, bh, H);
@@ -285,7 +300,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         qreg[ks] = (qrow < T) ? *(const bf16x8*)(qh + (size_t)qrow * Q.st + 16 * ks + 8 * hi)
                               : zero_bf16x8();
     f32x16 oacc[2] = {f32x16{}, f32x16{}};
-    float m = -INFINITY;  // running max (raw dot-product units), shared by lanes l, l^32
+    // running max (raw dot-product units), shared by lanes l, l^32.  It starts
+    // finite, so that a row none of whose keys is visible yet in a tile (a window's
+    // lower edge) gives exp2(-inf) = 0 rather than inf - inf.
+    float m = -1e30f;
     float l = 0.f;        // this lane's part of the normaliser
 
     // running max over the scores of a tile (two chains of v_max3); lazy rescale
@@ -324,7 +342,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt)
                 tv[c][dt] = lds_tr_read(vc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
-        if (diag) mask_upto(s0, s1, qrow - j * kTile - 4 * hi);
+        if (diag) {
+            const int lim = qrow - j * kTile - 4 * hi;
+            mask_band(s0, s1, lim, lim - W);
+        }
         update_max(s0, s1);
         const float mc = m * scale_log2;
 #pragma unroll
@@ -349,10 +370,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             tile_load_async(kl, Kh, K.st, (j + 1) * kTile, T, wave, tc);
             tile_load_async(vl, Vh, V.st, (j + 1) * kTile, T, wave, tc);
         }
-        if (j <= last_w) tile(j == last_w, j, kc, vc);
+        // a tile needs the mask if it crosses the diagonal or the window's lower edge
+        if (j >= first_w && j <= last_w)
+            tile(j == last_w || j * kTile <= q0w + 31 - W, j, kc, vc);
     };
 
-    for (int j = 0; j < n_kv; j += 2) {
+    for (int j = lo; j < n_kv; j += 2) {
         step(j, sK0, sV0, sK1, sV1);
         if (j + 1 < n_kv) step(j + 1, sK1, sV1, sK0, sV0);
     }
@@ -379,6 +402,7 @@ struct BwdParams {
     float* Delta;  // dQ items write it; dK/dV items read it unless they form it from O
     View dQ, dK, dV;
     int BH, H, T;
+    int W;  // window: query q sees keys q-W < k <= q (W >= T: the plain causal mask)
     float scale, scale_log2;
 };
 
@@ -411,9 +435,12 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     const int kv_end = min(T, qt * kRowsPerWG + kRowsPerWG);
     const int n_kv = (kv_end + kTile - 1) / kTile;
     const int last_w = min(n_kv - 1, (q0w + 31) / kTile);
+    const int W = a.W;
+    const int lo = max(0, qt * kRowsPerWG - W + 1) / kTile;  // the workgroup's first tile
+    const int first_w = max(0, q0w - W + 1) / kTile;        // the wave's first tile
 
-    tile_load_async(sK0, Kh, a.K.st, 0, T, wave, tc);
-    tile_load_async(sV0, Vh, a.V.st, 0, T, wave, tc);
+    tile_load_async(sK0, Kh, a.K.st, lo * kTile, T, wave, tc);
+    tile_load_async(sV0, Vh, a.V.st, lo * kTile, T, wave, tc);
 
     bf16x8 qreg[4], greg[4];
     float dsum = 0.f;
@@ -447,10 +474,14 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
             sv = mfma32x32x16(lds_row_read(kc, 4096 * h + off.nat[ks]), qreg[ks], sv);  // S^T
             pv = mfma32x32x16(lds_row_read(vc, 4096 * h + off.nat[ks]), greg[ks], pv);  // dP^T - Delta
         }
-        if (diag) {  // key row 32h + 8(r/4) + 4hi + r%4 is visible to query qrow iff <= qrow - k0
+        if (diag) {  // key row 32h + 8(r/4) + 4hi + r%4 is visible to query qrow iff
+                     // qrow - W < key <= qrow
             const int lim = qrow - k0 - 4 * hi - 32 * h;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sv[r] = 8 * (r >> 2) + (r & 3) <= lim ? sv[r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 8 * (r >> 2) + (r & 3);
+                sv[r] = kk <= lim && kk > lim - W ? sv[r] : -INFINITY;
+            }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(fmaf(sv[r], scale_log2, nlse2)) * pv[r];  // dS^T
@@ -475,15 +506,16 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
             tile_load_async(kl, Kh, a.K.st, (j + 1) * kTile, T, wave, tc);
             tile_load_async(vl, Vh, a.V.st, (j + 1) * kTile, T, wave, tc);
         }
-        if (j > last_w) return;
+        if (j < first_w || j > last_w) return;
         const int k0 = j * kTile;
-        const bool diag = j == last_w;
+        // masked: the diagonal tile and tiles crossing the window's lower edge
+        const bool diag = j == last_w || k0 <= q0w + 31 - W;
         half(0, diag, k0, kc, vc);
         // keys 32..63 of the diagonal tile matter only if a query of the wave reaches them
-        if (!diag || k0 + 32 <= q0w + 31) half(1, diag, k0, kc, vc);
+        if (j < last_w || k0 + 32 <= q0w + 31) half(1, diag, k0, kc, vc);
     };
 
-    for (int j = 0; j < n_kv; j += 2) {
+    for (int j = lo; j < n_kv; j += 2) {
         step(j, sK0, sV0, sK1, sV1);
         if (j + 1 < n_kv) step(j + 1, sK1, sV1, sK0, sV0);
     }
@@ -541,6 +573,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     const int n_q = (T + kTile - 1) / kTile;
     const int i0 = kv0 / kTile;
     const int first_w = k0w / kTile;  // first tile with a query >= a key of this wave
+    // window: key k is seen by queries k <= q < k + W (W >= T: every later query)
+    const int W = a.W;
+    const int i_hi = min(n_q - 1, (kv0 + kRowsPerWG - 1 + W - 1) / kTile);  // the workgroup's last tile
+    const int last_w = min(n_q - 1, (k0w + 31 + W - 1) / kTile);            // the wave's last tile
 
     // Per-row values of tile i (lse, and Delta when it is read from memory) travel
     // to LDS by the same asynchronous copy as the tiles, 4 bytes per lane of one
@@ -588,10 +624,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
 
     // Tiles are visited from the last one down to the diagonal, so that every item
     // of a head streams the same tile at about the same time (they share it in L2).
-    tile_load_async(sQ0, Qh, a.Q.st, (n_q - 1) * kTile, T, wave, tc);
-    tile_load_async(sG0, Gh, a.dO.st, (n_q - 1) * kTile, T, wave, tc);
-    if (kDeltaFromO) tile_load_async(sO0, Oh, a.O.st, (n_q - 1) * kTile, T, wave, tc);
-    rows_load_async(n_q - 1, sR0);
+    tile_load_async(sQ0, Qh, a.Q.st, i_hi * kTile, T, wave, tc);
+    tile_load_async(sG0, Gh, a.dO.st, i_hi * kTile, T, wave, tc);
+    if (kDeltaFromO) tile_load_async(sO0, Oh, a.O.st, i_hi * kTile, T, wave, tc);
+    rows_load_async(i_hi, sR0);
 
     bf16x8 kreg[4], vreg[4];
     const bf16* kr = head_of(a.K, bh, a.H) + (size_t)key * a.K.st + 8 * hi;
@@ -602,7 +638,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         vreg[ks] = valid ? *(const bf16x8*)(vr + 16 * ks) : zero_bf16x8();
     }
     wait_async_copies();
-    rows_finish(n_q - 1, sG0, sO0, sR0);
+    rows_finish(i_hi, sG0, sO0, sR0);
     f32x16 dkacc[2] = {f32x16{}, f32x16{}}, dvacc[2] = {f32x16{}, f32x16{}};
 
     // queries 32h .. 32h+31 of the tile in qc / gc / rc
@@ -621,13 +657,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
             dp = mfma32x32x16(lds_row_read(gc, 4096 * h + off.nat[ks]), vreg[ks], dp);   // dP - Delta
         }
         if (diag) {
-            // element r holds query q0 + 32h + 8(r/4) + 4hi + r%4: masked (query < key)
-            // unless 8(r/4) + r%4 >= key - q0 - 32h - 4hi
+            // element r holds query q0 + 32h + 8(r/4) + 4hi + r%4: kept iff
+            // key <= query < key + W, i.e. lim <= 8(r/4) + r%4 < lim + W
             const int lim = key - q0 - 32 * h - 4 * hi;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int qq = 8 * (r >> 2) + (r & 3);
-                sv[r] = qq >= lim ? sv[r] : -INFINITY;
+                sv[r] = qq >= lim && qq < lim + W ? sv[r] : -INFINITY;
             }
         }
 #pragma unroll
@@ -668,11 +704,12 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
             if (kDeltaFromO) tile_load_async(ol, Oh, a.O.st, (i - 1) * kTile, T, wave, tc);
             rows_load_async(i - 1, rl);
         }
-        if (i >= first_w) {
+        if (i >= first_w && i <= last_w) {
             const int q0 = i * kTile;
-            const bool diag = i == first_w;
+            // masked: the diagonal tile and tiles reaching past the window of a key
+            const bool diag = i == first_w || q0 + kTile - 1 >= k0w + W;
             // on the diagonal tile, queries 0..31 matter only if one of them is >= a key
-            if (!diag || q0 + 31 >= k0w) half(0, diag, q0, qc, gc, rc);
+            if (i > first_w || q0 + 31 >= k0w) half(0, diag, q0, qc, gc, rc);
             half(1, diag, q0, qc, gc, rc);
         }
         if (more) {
@@ -681,7 +718,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         }
     };
 
-    for (int i = n_q - 1; i >= i0; i -= 2) {
+    for (int i = i_hi; i >= i0; i -= 2) {
         step(i, sQ0, sG0, sR0, sQ1, sG1, sO1, sR1);
         if (i - 1 >= i0) step(i - 1, sQ1, sG1, sR1, sQ0, sG0, sO0, sR0);
     }
@@ -765,13 +802,16 @@ static d64::View view(const void* p, const Strides& s)
     return d64::View{(bf16*)p, s.sb, s.sh, s.st};
 }
 
+// the window the kernels use: W >= T (no lower edge) for the plain causal mask
+static int window_of(const AttnArgs& a) { return a.window > 0 && a.window < a.T ? a.window : a.T; }
+
 hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     hipLaunchKernelGGL(d64::attn_fwd_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
                        view(a.q, a.sq), view(a.k, a.sk), view(a.v, a.sv), view(a.o_out, a.so),
-                       a.lse, BH, a.H, a.T, nqt, a.scale, a.scale * kLog2e, a.n_cu);
+                       a.lse, BH, a.H, a.T, window_of(a), nqt, a.scale, a.scale * kLog2e, a.n_cu);
     return hipGetLastError();
 }
 
@@ -791,6 +831,7 @@ static d64::BwdParams bwd_params(const AttnArgs& a)
     p.BH = a.B * a.H;
     p.H = a.H;
     p.T = a.T;
+    p.W = window_of(a);
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;
     return p;

@@ -135,16 +135,24 @@ typedef struct {
     long long stride_t;
 } attn_view_t;
 
-/* attn_fwd on strided views (q, k, v read; o written). */
+/* Sliding window (window >= 1): query i sees only the `window` most recent
+ * keys, i - window < j <= i, the band of the causal mask (the nanochat page,
+ * section 9, lists sliding-window attention; its SSSL pattern mixes short
+ * windows with full-context layers).  window = 0 (or >= T) is the plain causal
+ * mask.  window < 0 is rejected with ATTN_ERR_SHAPE.  lse is then the
+ * log-sum-exp over the window. */
+
+/* attn_fwd on strided views (q, k, v read; o written), with a window. */
 int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
-                     int B, int H, int T, int D, float scale, int dtype, void* stream);
+                     int B, int H, int T, int D, int window, float scale, int dtype,
+                     void* stream);
 
 /* attn_bwd on strided views (q, k, v, o, dO read; dq, dk, dv written), in one
- * kernel launch; delta as in attn_bwd. */
+ * kernel launch; delta as in attn_bwd; window as in the forward call. */
 int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
                      const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
-                     attn_view_t dv, float* delta, int B, int H, int T, int D, float scale,
-                     int dtype, void* stream);
+                     attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
+                     float scale, int dtype, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_str(int status);

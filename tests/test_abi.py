@@ -225,17 +225,19 @@ def _qkv_views(base, elem=2):
     return [_v(base + i * C_ * elem, sb, sh, st) for i in range(3)]
 
 
-def _fwd_s(views=None, lse=P[4], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1):
+def _fwd_s(views=None, lse=P[4], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1, window=0):
     v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3])]
-    return cat.load_library().attn_fwd_strided(v[0], v[1], v[2], v[3], lse, B, H, T, D, scale,
-                                               dtype, None)
+    return cat.load_library().attn_fwd_strided(v[0], v[1], v[2], v[3], lse, B, H, T, D, window,
+                                               scale, dtype, None)
 
 
-def _bwd_s(views=None, lse=P[4], delta=P[9], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1):
+def _bwd_s(views=None, lse=P[4], delta=P[9], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1,
+           window=0):
     v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3]), _v(P[5]), _v(P[6]), _v(P[7]),
                   _v(P[8])]
     return cat.load_library().attn_bwd_strided(v[0], v[1], v[2], v[3], lse, v[4], v[5], v[6],
-                                               v[7], delta, B, H, T, D, scale, dtype, None)
+                                               v[7], delta, B, H, T, D, window, scale, dtype,
+                                               None)
 
 
 def test_strided_null_shape_scale():
@@ -246,6 +248,10 @@ def test_strided_null_shape_scale():
     assert _bwd_s(H=0) == 2
     assert _fwd_s(scale=0.0) == 7
     assert _bwd_s(scale=float("nan")) == 7
+    # a negative window is a shape error; it is checked after the views (here a
+    # misaligned lse keeps the call from reaching any launch)
+    assert _fwd_s(window=-1) == 2
+    assert _bwd_s(window=-5) == 2
 
 
 def test_strided_supports_only_bf16_d64():

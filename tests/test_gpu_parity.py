@@ -335,3 +335,93 @@ def test_qkv_autograd_matches_split_heads():
     torch.cuda.synchronize()
     assert torch.equal(y.view(B, T, H, D).permute(0, 2, 1, 3), o)
     assert torch.equal(qkv.grad, _to_qkv(qs.grad, ks.grad, vs.grad))
+
+
+# ---------------------------------------------------------------------------
+# sliding window: query i sees keys i-W < j <= i (nanochat, section 9 lists
+# sliding-window attention; the oracle's window argument is pinned on the CPU)
+# ---------------------------------------------------------------------------
+
+def windowed_gpu(q, k, v, dO, scale, window):
+    import causal_head_self_amd as cat
+    dev = torch.device("cuda")
+    q, k, v, dO = (t.to(dev).contiguous() for t in (q, k, v, dO))
+    B, H, T, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    cat.attn_fwd_strided(q, k, v, o, lse, scale, window=window)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty_like(lse)
+    cat.attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, window=window)
+    torch.cuda.synchronize()
+    out = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": delta}
+    return {name: t.float().cpu().numpy().astype(np.float64) for name, t in out.items()}
+
+
+def windowed_oracle(q, k, v, dO, scale, window):
+    s = oracle.widen_scale(scale)
+    o, lse = oracle.attn_fwd(q, k, v, s, window=window)
+    dq, dk, dv, delta = oracle.attn_bwd(q, k, v, dO, s, window=window)
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": delta}
+
+
+@pytest.mark.parametrize("shape,window", [
+    ((1, 2, 300, 64), 1), ((1, 2, 300, 64), 2), ((2, 1, 300, 64), 31),
+    ((1, 2, 300, 64), 32), ((1, 1, 300, 64), 33), ((2, 2, 300, 64), 64),
+    ((1, 3, 300, 64), 100), ((1, 2, 300, 64), 129), ((1, 2, 300, 64), 200),
+    ((1, 1, 300, 64), 299), ((3, 1, 67, 64), 5), ((1, 1, 1, 64), 1),
+    ((1, 1, 33, 64), 17)])
+def test_sliding_window_matches_oracle(shape, window):
+    B, H, T, D = shape
+    _note(f"[parity] window={window} B={B} H={H} T={T} D={D} bf16")
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", 900 + window + T)
+    scale = 1.0 / math.sqrt(D)
+    got = windowed_gpu(q, k, v, dO, scale, window)
+    ref = windowed_oracle(q, k, v, dO, scale, window)
+    assert_close(got, ref, TOL["bf16"], f"window {window} B{B} H{H} T{T}", delta_bound(ref, dO))
+
+
+@pytest.mark.parametrize("window", [300, 301, 4096])
+def test_window_at_least_T_is_the_causal_path_bitwise(window):
+    B, H, T, D = 1, 2, 300, 64
+    _note(f"[parity] window={window} >= T={T} equals causal")
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", 31)
+    scale = 1.0 / math.sqrt(D)
+    got = windowed_gpu(q, k, v, dO, scale, window)
+    causal = gpu_attention(q, k, v, dO, scale)
+    for name in got:
+        assert np.array_equal(got[name], causal[name]), f"{name}: window >= T differs"
+
+
+def test_sliding_window_long_sequence_sampled_head():
+    # T = 1024 with a quarter-length window: many fully skipped tiles per
+    # query block; one (b, h) pair checked against the oracle
+    B, H, T, D, W = 2, 3, 1024, 64, 256
+    _note(f"[parity] window={W} B={B} H={H} T={T} sampled head")
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", 4242)
+    scale = 1.0 / math.sqrt(D)
+    got = windowed_gpu(q, k, v, dO, scale, W)
+    b, h = 1, 2
+    sl = lambda t: t[b:b + 1, h:h + 1]
+    ref = windowed_oracle(sl(q), sl(k), sl(v), sl(dO), scale, W)
+    got = {name: val[b:b + 1, h:h + 1] for name, val in got.items()}
+    assert_close(got, ref, TOL["bf16"], f"window {W} T{T} head ({b},{h})",
+                 delta_bound(ref, sl(dO)))
+
+
+def test_qkv_autograd_window_matches_oracle():
+    import causal_head_self_amd as cat
+    B, H, T, D, W = 1, 2, 160, 64, 48
+    _note(f"[parity] causal_attention_qkv window={W} B={B} H={H} T={T}")
+    q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", 78)
+    dev = torch.device("cuda")
+    qkv = _to_qkv(q, k, v).to(dev).requires_grad_(True)
+    y = cat.causal_attention_qkv(qkv, H, window=W)
+    y.backward(dO.permute(0, 2, 1, 3).reshape(B, T, H * D).to(dev))
+    torch.cuda.synchronize()
+    ref = windowed_oracle(q, k, v, dO, 1.0 / math.sqrt(D), W)
+    as_np = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    got_o = as_np(y.view(B, T, H, D).permute(0, 2, 1, 3))
+    g = qkv.grad.view(B, T, 3, H, D).permute(2, 0, 3, 1, 4)
+    got = {"o": got_o, "dq": as_np(g[0]), "dk": as_np(g[1]), "dv": as_np(g[2])}
+    assert_close(got, {n: ref[n] for n in got}, TOL["bf16"], f"qkv window {W}")
