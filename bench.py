@@ -47,15 +47,24 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_work(cfg):
+def visible_pairs(T: int, window: int = 0) -> float:
+    """(query, key) pairs that take part, by the causal convention: T^2 / 2
+    for the causal mask (the diagonal not counted separately), T*W - W^2/2
+    for a sliding window of W < T keys (the same formula at W = T)."""
+    if window <= 0 or window >= T:
+        return T * T / 2.0
+    return T * window - window * window / 2.0
+
+
+def kernel_work(cfg, window: int = 0):
     """Algorithmic work per launch, per kernel (causal-adjusted).  One GEMM
-    over the causal half of one head is T^2 * D flops.  The forward credits 2
-    GEMMs (S, PV); the backward launch 5: its dK/dV items are credited with
-    S, dP, dV and dK, its dQ items with the dQ product (their recomputed S
-    and dP are not credited again).  Delta (a row sum of dO * o) is not
-    credited."""
+    over the causal half of one head is T^2 * D flops (2 D flops per visible
+    pair).  The forward credits 2 GEMMs (S, PV); the backward 5: its dK/dV
+    work is credited with S, dP, dV and dK, its dQ work with the dQ product
+    (their recomputed S and dP are not credited again).  Delta (a row sum of
+    dO * o) is not credited."""
     B, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
-    g = float(B * H * T * T * D)
+    g = float(B * H * D) * 2.0 * visible_pairs(T, window)
     return {
         "fwd": {"flops": 2 * g},
         "bwd": {"flops": 5 * g},
@@ -82,17 +91,17 @@ def read_traffic(kernel: str, workload: str, sha: str):
         return None
 
 
-def cpu_baseline(cfg, inputs, threads: int):
+def cpu_baseline(cfg, inputs, threads: int, window: int = 0):
     """The fp64 oracle, as it stands, on the host cores: one fwd+bwd pass
     over the sample (all heads of the workload), timed with a wall clock."""
     import oracle
     q, k, v, dO = inputs
     s = oracle.widen_scale(cfg.scale)
     t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, s, nthreads=threads)
-    oracle.attn_bwd(q, k, v, dO, s, nthreads=threads)
+    oracle.attn_fwd(q, k, v, s, window=window, nthreads=threads)
+    oracle.attn_bwd(q, k, v, dO, s, window=window, nthreads=threads)
     dt = time.perf_counter() - t0
-    work = 7.0 * cfg.B * cfg.H * cfg.T * cfg.T * cfg.D
+    work = 7.0 * cfg.B * cfg.H * cfg.D * 2.0 * visible_pairs(cfg.T, window)
     return {
         "value": round(work / dt / 1e12, 6),
         "unit": "TFLOP/s",
@@ -194,7 +203,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="gpt2s",
-                    choices=["tiny", "gpt2s", "gpt400m", "long", "sublayer"])
+                    choices=["tiny", "gpt2s", "gpt400m", "long", "gpt2s_d128", "sublayer"])
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window W (bf16, D 64/128): query i sees keys i-W < j <= i")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
@@ -230,9 +241,27 @@ def main() -> int:
     scale = cfg.scale
     stream = torch.cuda.current_stream()
 
+    W = args.window
+    if W < 0 or (W and (cfg.dtype != "bf16" or D not in (64, 128))):
+        print("bench.py: --window needs W >= 0 and a bf16 workload with D 64 or 128",
+              file=sys.stderr)
+        return 2
+
+    def fwd():
+        if W:
+            cat.attn_fwd_strided(q, k, v, o, lse, scale, stream, window=W)
+        else:
+            cat.attn_fwd(q, k, v, o, lse, scale, stream)
+
+    def bwd():
+        if W:
+            cat.attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream, window=W)
+        else:
+            cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream)
+
     def step():
-        cat.attn_fwd(q, k, v, o, lse, scale, stream)
-        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream)
+        fwd()
+        bwd()
 
     for _ in range(args.warmup):
         step()
@@ -249,16 +278,17 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # per-kernel: the same K steps with an event between consecutive launches
-    # (attn_fwd and attn_bwd are one kernel launch each at head dim 64)
+    # per-kernel: the same K steps with an event between consecutive calls
+    # (attn_fwd and attn_bwd are one kernel launch each at head dim 64; at 128
+    # attn_bwd is two, dQ then dK/dV, timed together as "bwd")
     names = ["fwd", "bwd"]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e in evs:
         e[0].record(stream)
-        cat.attn_fwd(q, k, v, o, lse, scale, stream)
+        fwd()
         e[1].record(stream)
-        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream)
+        bwd()
         e[2].record(stream)
     torch.cuda.synchronize()
     kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
@@ -272,16 +302,16 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    work = kernel_work(cfg)
-    flops_fb = 7.0 * B * H * T * T * D
-    flops_f = 2.0 * B * H * T * T * D
+    work = kernel_work(cfg, W)
+    flops_f = work["fwd"]["flops"]
+    flops_fb = flops_f + work["bwd"]["flops"]
     value = flops_fb / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
 
     dominant = max(names, key=lambda n: kern_ms[n])
     achieved = work[dominant]["flops"] / (kern_ms[dominant] * 1e-3) / 1e12
     sha = kernel_source_sha()
-    workload_name = f"{cfg.name}_B{B}_H{H}_T{T}_D{D}_{cfg.dtype}"
+    workload_name = f"{cfg.name}_B{B}_H{H}_T{T}_D{D}_{cfg.dtype}" + (f"_W{W}" if W else "")
     roofline = {
         "bound": "mfma",
         "kernel": dominant,
@@ -299,7 +329,7 @@ def main() -> int:
             threads = min(16, len(os.sched_getaffinity(0)))
         except AttributeError:
             threads = min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(cfg, host_inputs, threads)
+        cpu = cpu_baseline(cfg, host_inputs, threads, W)
 
     fwd_tflops = flops_f / (kern_ms["fwd"] * 1e-3) / 1e12
     out = {
@@ -317,8 +347,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": (f"causal MHA fwd+bwd, {cfg.name}: B={B} H={H} T={T} D={D} {cfg.dtype} "
-                         "storage / fp32 accumulate, q,k,v,dO iid N(0,1) seeds 42+idx"),
-            "B": B, "H": H, "T": T, "D": D, "global_batch": B, "seq_len": T,
+                         "storage / fp32 accumulate, q,k,v,dO iid N(0,1) seeds 42+idx"
+                         + (f", sliding window W={W}" if W else "")),
+            "B": B, "H": H, "T": T, "D": D, "window": W, "global_batch": B, "seq_len": T,
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100.0 * value / peak, 2),

@@ -13,7 +13,7 @@ the computation.  PyTorch supplies device memory and streams.
     causal_attention_qkv(qkv, n_head)                       -- autograd op on the
         fused [B, T, 3C] c_attn output, returning [B, T, C] with no layout copies
 
-Tensors are contiguous [B, H, T, D] (D in {32, 64}) of float32 or bfloat16 on
+Tensors are contiguous [B, H, T, D] (D in {32, 64}; 128 in bf16) of float32 or bfloat16 on
 the current GPU; lse and delta are float32 [B, H, T].
 """
 from __future__ import annotations
@@ -195,7 +195,7 @@ class _CausalAttentionQKV(torch.autograd.Function):
 def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0) -> torch.Tensor:
     """Causal attention on the fused c_attn output: qkv [B, T, 3C] (q, k, v
     chunks of C, each [B, T, H, D]) -> y [B, T, C] (heads merged), read and
-    written in place through strided views (bf16, head dim 64).  window W > 0
+    written in place through strided views (bf16, head dim 64 or 128).  window W > 0
     restricts query i to keys i-W < j <= i (sliding window)."""
     return _CausalAttentionQKV.apply(qkv, n_head, int(window))
 

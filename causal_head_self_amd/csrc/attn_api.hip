@@ -19,6 +19,9 @@ struct Span {
 
 bool overlaps(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Head dims with kernels: 32 and 64 in both dtypes, 128 in bf16.
+bool head_dim_ok(int D, int dtype) { return D == 32 || D == 64 || (D == 128 && dtype == ATTN_BF16); }
+
 // Checks shared by every entry point, in the documented order:
 // NULL, shape, dtype, D, scale, overflow, alignment, aliasing.
 template <int NI, int NO>
@@ -31,7 +34,7 @@ int validate(const Buf (&in)[NI], const Buf (&out)[NO], int B, int H, int T, int
         if (!b.p) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || T < 1) return ATTN_ERR_SHAPE;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
-    if (D != 32 && D != 64) return ATTN_ERR_UNSUPPORTED_D;
+    if (!head_dim_ok(D, dtype)) return ATTN_ERR_UNSUPPORTED_D;
     if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_ERR_SCALE;
     const long long BH = (long long)B * H;
     const long long tiles = (T + 63) / 64;  // the finest row tiling any kernel launches
@@ -130,9 +133,9 @@ int validate_views(const VSpan* vs, int n, const float* const* rows, int nrows, 
         if (!rows[i]) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || T < 1) return ATTN_ERR_SHAPE;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
-    if (D != 32 && D != 64) return ATTN_ERR_UNSUPPORTED_D;
+    if (!head_dim_ok(D, dtype)) return ATTN_ERR_UNSUPPORTED_D;
     if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_ERR_SCALE;
-    if (dtype != ATTN_BF16 || D != 64) return ATTN_ERR_LAYOUT;
+    if (dtype != ATTN_BF16 || (D != 64 && D != 128)) return ATTN_ERR_LAYOUT;
     const long long BH = (long long)B * H;
     if ((long long)T * D > 0x7fffffffLL || BH * ((T + 63) / 64) > 0x7fffffffLL ||
         BH * (long long)T > (1LL << 35))
@@ -182,7 +185,7 @@ const char* attn_status_str(int st)
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, H and T must be >= 1";
-    case ATTN_ERR_UNSUPPORTED_D: return "head dim D must be 32 or 64";
+    case ATTN_ERR_UNSUPPORTED_D: return "head dim D must be 32 or 64 (or 128 with bf16)";
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_F32 or ATTN_BF16";
     case ATTN_ERR_ALIGN: return "tensors must be 16-byte aligned (lse/delta 4-byte)";
     case ATTN_ERR_OVERFLOW: return "T*D or the launch grid exceeds 2^31 - 1";
@@ -190,7 +193,7 @@ const char* attn_status_str(int st)
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
     case ATTN_ERR_LAYOUT:
-        return "strided views need bf16, D = 64, strides that are non-negative multiples of 8 "
+        return "strided views need bf16, D = 64 or 128, strides that are non-negative multiples of 8 "
                "with stride_t >= D, and T * stride_t * 2 < 2^32";
     default: return "unknown status";
     }

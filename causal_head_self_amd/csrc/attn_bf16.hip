@@ -459,24 +459,24 @@ static hipError_t launch_dkdv(const AttnArgs& a, hipStream_t st)
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t st)
 {
-    return a.D == 64 ? launch_fwd_bf16_d64(a, st) : launch_fwd<32>(a, st);
+    return a.D == 32 ? launch_fwd<32>(a, st) : launch_fwd_bf16_d64(a, st);  // D = 64 or 128
 }
 
 hipError_t launch_dq_bf16(const AttnArgs& a, hipStream_t st)
 {
-    if (a.D == 64) return launch_dq_bf16_d64(a, st);  // Delta fused into the dQ kernel
+    if (a.D != 32) return launch_dq_bf16_d64(a, st);  // Delta fused into the dQ kernel
     const hipError_t e = launch_delta<32>(a, st);
     return e == hipSuccess ? launch_dq<32>(a, st) : e;
 }
 
 hipError_t launch_dkdv_bf16(const AttnArgs& a, hipStream_t st)
 {
-    return a.D == 64 ? launch_dkdv_bf16_d64(a, st) : launch_dkdv<32>(a, st);
+    return a.D == 32 ? launch_dkdv<32>(a, st) : launch_dkdv_bf16_d64(a, st);
 }
 
 hipError_t launch_bwd_bf16(const AttnArgs& a, hipStream_t st)
 {
-    if (a.D == 64) return launch_bwd_bf16_d64(a, st);  // dQ and dK/dV items in one grid
+    if (a.D != 32) return launch_bwd_bf16_d64(a, st);  // D = 64: dQ and dK/dV items in one grid
     const hipError_t e = launch_dq_bf16(a, st);
     return e == hipSuccess ? launch_dkdv_bf16(a, st) : e;
 }

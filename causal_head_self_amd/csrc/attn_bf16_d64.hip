@@ -30,11 +30,19 @@
 namespace cattn {
 namespace d64 {
 
-constexpr int HD = 64;
+constexpr int HD = 64;           // columns per panel
 constexpr int kThreads = 256;
 constexpr int kRowsPerWG = 128;  // queries (forward, dQ) or keys (dK/dV) per workgroup
 constexpr int kTile = 64;        // rows per streamed tile
-constexpr int kTileBytes = kTile * HD * 2;
+constexpr int kTileBytes = kTile * HD * 2;  // one panel of a tile
+
+// Head dim 64 * NP (NP = 1 or 2).  A streamed tile is NP panels of kTileBytes,
+// panel p holding columns 64p .. 64p+63 of its 64 rows in the swizzled layout
+// below, so that every copy and operand read works on one panel as it does at
+// head dim 64.  Register-resident rows and accumulators grow with NP; at NP = 2
+// the kernels run 2 waves per SIMD instead of 3.
+template <int NP>
+constexpr int kWavesPerEU = NP == 1 ? 3 : 2;
 constexpr float kLazyRescale = 8.0f;  // log2 growth of the running max that forces a rescale
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -99,6 +107,15 @@ __device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restri
                                              16, 0, 0);
         }
     }
+}
+
+// The NP panels of a tile: columns 64p.. of the head go to panel p.
+template <int NP>
+__device__ __forceinline__ void tiles_load_async(char* tile, const bf16* __restrict__ head, int st,
+                                                 int row0, int T, int wave, const TileCopy& tc)
+{
+    tile_load_async(tile, head, st, row0, T, wave, tc);
+    if constexpr (NP == 2) tile_load_async(tile + kTileBytes, head + HD, st, row0, T, wave, tc);
 }
 
 __device__ __forceinline__ void wait_async_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -175,22 +192,28 @@ __device__ __forceinline__ float sum8(bf16x8 v, float acc)
 }
 
 // S = A B over the 64 rows of an LDS tile: rows 0..31 -> s0, rows 32..63 -> s1.
-// A is read from the tile (row reads), B comes from registers.
+// A is read from the tile (row reads, panel by panel), B comes from registers
+// (k-steps 4p .. 4p+3 for panel p).
+template <int NP>
 __device__ __forceinline__ void tile_product(const char* tile, const Offsets& off,
-                                             const bf16x8 (&breg)[4], f32x16& s0, f32x16& s1)
+                                             const bf16x8 (&breg)[4 * NP], f32x16& s0, f32x16& s1)
 {
-    bf16x8 a[8];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        a[ks] = lds_row_read(tile, off.nat[ks]);
-        a[4 + ks] = lds_row_read(tile, 4096 + off.nat[ks]);
-    }
     s0 = f32x16{};
     s1 = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        s0 = mfma32x32x16(a[ks], breg[ks], s0);
-        s1 = mfma32x32x16(a[4 + ks], breg[ks], s1);
+    for (int p = 0; p < NP; ++p) {
+        const char* t = tile + p * kTileBytes;
+        bf16x8 a[8];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            a[ks] = lds_row_read(t, off.nat[ks]);
+            a[4 + ks] = lds_row_read(t, 4096 + off.nat[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            s0 = mfma32x32x16(a[ks], breg[4 * p + ks], s0);
+            s1 = mfma32x32x16(a[4 + ks], breg[4 * p + ks], s1);
+        }
     }
 }
 
@@ -258,17 +281,18 @@ __device__ __forceinline__ bf16* head_of(const View& v, int bh, int H)
 // three waves that share a SIMD overlap each other's LDS latency.  Every wave
 // needs tiles 0..last_w; only the last one crosses its diagonal and is masked.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_d64_kernel(
+template <int NP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_fwd_d64_kernel(
     View Q, View K, View V, View O, float* __restrict__ LSE, int BH, int H, int T, int W,
     int n_qtiles, float scale, float scale_log2, int n_cu)
 {
     // Separate arrays per buffer (not one indexed array): with the buffer of every
     // access known at compile time, the compiler can tell that an LDS read does not
     // touch the buffer an asynchronous copy is filling, and does not wait for it.
-    __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK0[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[NP * kTileBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -290,16 +314,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int lo = max(0, qt * kRowsPerWG - W + 1) / kTile;  // the workgroup's first tile
     const int first_w = max(0, q0w - W + 1) / kTile;        // the wave's first tile
 
-    tile_load_async(sK0, Kh, K.st, lo * kTile, T, wave, tc);
-    tile_load_async(sV0, Vh, V.st, lo * kTile, T, wave, tc);
+    tiles_load_async<NP>(sK0, Kh, K.st, lo * kTile, T, wave, tc);
+    tiles_load_async<NP>(sV0, Vh, V.st, lo * kTile, T, wave, tc);
 
-    bf16x8 qreg[4];
+    bf16x8 qreg[4 * NP];
     const bf16* qh = head_of(Q, bh, H);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4 * NP; ++ks)
         qreg[ks] = (qrow < T) ? *(const bf16x8*)(qh + (size_t)qrow * Q.st + 16 * ks + 8 * hi)
                               : zero_bf16x8();
-    f32x16 oacc[2] = {f32x16{}, f32x16{}};
+    f32x16 oacc[2 * NP];
+#pragma unroll
+    for (int dt = 0; dt < 2 * NP; ++dt) oacc[dt] = f32x16{};
     // running max (raw dot-product units), shared by lanes l, l^32.  It starts
     // finite, so that a row none of whose keys is visible yet in a tile (a window's
     // lower edge) gives exp2(-inf) = 0 rather than inf - inf.
@@ -322,8 +348,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             const float alpha = fast_exp2((m - m_new) * scale_log2);
             m = m_new;
             l *= alpha;
-            oacc[0] *= alpha;
-            oacc[1] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 2 * NP; ++dt) oacc[dt] *= alpha;
         }
     };
 
@@ -335,13 +361,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     // made the register allocator spill.
     auto tile = [&](bool diag, int j, const char* kc, const char* vc) {
         f32x16 s0, s1;
-        tile_product(kc, off, qreg, s0, s1);
-        bf16x8 tv[4][2];
+        tile_product<NP>(kc, off, qreg, s0, s1);
+        bf16x8 tv[4][2 * NP];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
-                tv[c][dt] = lds_tr_read(vc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt)
+                    tv[c][2 * p + dt] = lds_tr_read(vc + p * kTileBytes, c * 2048 + off.tr[0][dt],
+                                                    c * 2048 + off.tr[1][dt]);
         if (diag) {
             const int lim = qrow - j * kTile - 4 * hi;
             mask_band(s0, s1, lim, lim - W);
@@ -356,8 +385,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
             for (int e = 0; e < 8; ++e) pb[e] = (bf16)fast_exp2(fmaf(sc[b + e], scale_log2, -mc));
             l = sum8(pb, l);
-            oacc[0] = mfma32x32x16(tv[c][0], pb, oacc[0]);
-            oacc[1] = mfma32x32x16(tv[c][1], pb, oacc[1]);
+#pragma unroll
+            for (int dt = 0; dt < 2 * NP; ++dt) oacc[dt] = mfma32x32x16(tv[c][dt], pb, oacc[dt]);
         }
     };
 
@@ -367,8 +396,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         wait_async_copies();
         __syncthreads();
         if (j + 1 < n_kv) {
-            tile_load_async(kl, Kh, K.st, (j + 1) * kTile, T, wave, tc);
-            tile_load_async(vl, Vh, V.st, (j + 1) * kTile, T, wave, tc);
+            tiles_load_async<NP>(kl, Kh, K.st, (j + 1) * kTile, T, wave, tc);
+            tiles_load_async<NP>(vl, Vh, V.st, (j + 1) * kTile, T, wave, tc);
         }
         // a tile needs the mask if it crosses the diagonal or the window's lower edge
         if (j >= first_w && j <= last_w)
@@ -385,7 +414,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         const float inv = 1.0f / l;
         bf16* orow = head_of(O, bh, H) + (size_t)qrow * O.st;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < 2 * NP; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
                 store_bf16x4(orow + 32 * dt + 8 * g + 4 * hi, oacc[dt][4 * g] * inv,
@@ -415,6 +444,7 @@ struct BwdParams {
 // Delta_i = sum_d dO_id O_id is formed from the rows the wave holds as MFMA
 // operands and written out.
 // ---------------------------------------------------------------------------
+template <int NP>
 __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char* sK0, char* sK1,
                                         char* sV0, char* sV1)
 {
@@ -439,16 +469,16 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     const int lo = max(0, qt * kRowsPerWG - W + 1) / kTile;  // the workgroup's first tile
     const int first_w = max(0, q0w - W + 1) / kTile;        // the wave's first tile
 
-    tile_load_async(sK0, Kh, a.K.st, lo * kTile, T, wave, tc);
-    tile_load_async(sV0, Vh, a.V.st, lo * kTile, T, wave, tc);
+    tiles_load_async<NP>(sK0, Kh, a.K.st, lo * kTile, T, wave, tc);
+    tiles_load_async<NP>(sV0, Vh, a.V.st, lo * kTile, T, wave, tc);
 
-    bf16x8 qreg[4], greg[4];
+    bf16x8 qreg[4 * NP], greg[4 * NP];
     float dsum = 0.f;
     const bf16* qr = head_of(a.Q, bh, a.H) + (size_t)qrow * a.Q.st + 8 * hi;
     const bf16* gr = head_of(a.dO, bh, a.H) + (size_t)qrow * a.dO.st + 8 * hi;
     const bf16* orr = head_of(a.O, bh, a.H) + (size_t)qrow * a.O.st + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4 * NP; ++ks) {
         qreg[ks] = valid ? *(const bf16x8*)(qr + 16 * ks) : zero_bf16x8();
         greg[ks] = valid ? *(const bf16x8*)(gr + 16 * ks) : zero_bf16x8();
         const bf16x8 orow = valid ? *(const bf16x8*)(orr + 16 * ks) : zero_bf16x8();
@@ -464,16 +494,21 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     f32x16 ndl;
 #pragma unroll
     for (int r = 0; r < 16; ++r) ndl[r] = -dlt;
-    f32x16 dqacc[2] = {f32x16{}, f32x16{}};
+    f32x16 dqacc[2 * NP];
+#pragma unroll
+    for (int dt = 0; dt < 2 * NP; ++dt) dqacc[dt] = f32x16{};
 
     // keys 32h .. 32h+31 of tile j: S^T, dP^T - Delta, dS^T, dQ^T += K^T dS^T
     auto half = [&](int h, bool diag, int k0, const char* kc, const char* vc) {
         f32x16 sv = f32x16{}, pv = ndl;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            sv = mfma32x32x16(lds_row_read(kc, 4096 * h + off.nat[ks]), qreg[ks], sv);  // S^T
-            pv = mfma32x32x16(lds_row_read(vc, 4096 * h + off.nat[ks]), greg[ks], pv);  // dP^T - Delta
-        }
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int o = p * kTileBytes + 4096 * h + off.nat[ks];
+                sv = mfma32x32x16(lds_row_read(kc, o), qreg[4 * p + ks], sv);  // S^T
+                pv = mfma32x32x16(lds_row_read(vc, o), greg[4 * p + ks], pv);  // dP^T - Delta
+            }
         if (diag) {  // key row 32h + 8(r/4) + 4hi + r%4 is visible to query qrow iff
                      // qrow - W < key <= qrow
             const int lim = qrow - k0 - 4 * hi - 32 * h;
@@ -490,10 +525,13 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
             const int c = 2 * h + cc;
             const bf16x8 db = pack8(sv, 8 * cc);
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-                const bf16x8 av = lds_tr_read(kc, c * 2048 + off.tr[0][dt], c * 2048 + off.tr[1][dt]);
-                dqacc[dt] = mfma32x32x16(av, db, dqacc[dt]);
-            }
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    const int o = p * kTileBytes + c * 2048;
+                    const bf16x8 av = lds_tr_read(kc, o + off.tr[0][dt], o + off.tr[1][dt]);
+                    dqacc[2 * p + dt] = mfma32x32x16(av, db, dqacc[2 * p + dt]);
+                }
         }
     };
 
@@ -503,8 +541,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
         wait_async_copies();
         __syncthreads();
         if (j + 1 < n_kv) {
-            tile_load_async(kl, Kh, a.K.st, (j + 1) * kTile, T, wave, tc);
-            tile_load_async(vl, Vh, a.V.st, (j + 1) * kTile, T, wave, tc);
+            tiles_load_async<NP>(kl, Kh, a.K.st, (j + 1) * kTile, T, wave, tc);
+            tiles_load_async<NP>(vl, Vh, a.V.st, (j + 1) * kTile, T, wave, tc);
         }
         if (j < first_w || j > last_w) return;
         const int k0 = j * kTile;
@@ -523,7 +561,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     if (valid) {
         bf16* row = head_of(a.dQ, bh, a.H) + (size_t)qrow * a.dQ.st;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < 2 * NP; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
                 store_bf16x4(row + 32 * dt + 8 * g + 4 * hi, dqacc[dt][4 * g] * scale,
@@ -548,7 +586,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
 // leaves -Delta in the row buffer, which the next step's barrier publishes.
 // Otherwise Delta is read from memory (written by a dQ pass).
 // ---------------------------------------------------------------------------
-template <bool kDeltaFromO>
+template <int NP, bool kDeltaFromO>
 __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, char* sQ0, char* sQ1,
                                           char* sG0, char* sG1, char* sO0, char* sO1,
                                           float (*sR0)[kTile], float (*sR1)[kTile])
@@ -606,8 +644,8 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
             const int row = wave * 16 + (ln >> 2), c0 = 2 * (ln & 3);
             float d = 0.f;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int o = chunk_off(row, c0 + c);
+            for (int c = 0; c < 2 * NP; ++c) {
+                const int o = (c >> 1) * kTileBytes + chunk_off(row, c0 + (c & 1));
                 const bf16x8 gv = lds_row_read(gt, o), ov = lds_row_read(ot, o);
                 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -624,22 +662,22 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
 
     // Tiles are visited from the last one down to the diagonal, so that every item
     // of a head streams the same tile at about the same time (they share it in L2).
-    tile_load_async(sQ0, Qh, a.Q.st, i_hi * kTile, T, wave, tc);
-    tile_load_async(sG0, Gh, a.dO.st, i_hi * kTile, T, wave, tc);
-    if (kDeltaFromO) tile_load_async(sO0, Oh, a.O.st, i_hi * kTile, T, wave, tc);
+    tiles_load_async<NP>(sQ0, Qh, a.Q.st, i_hi * kTile, T, wave, tc);
+    tiles_load_async<NP>(sG0, Gh, a.dO.st, i_hi * kTile, T, wave, tc);
+    if (kDeltaFromO) tiles_load_async<NP>(sO0, Oh, a.O.st, i_hi * kTile, T, wave, tc);
     rows_load_async(i_hi, sR0);
 
-    bf16x8 kreg[4], vreg[4];
+    bf16x8 kreg[4 * NP], vreg[4 * NP];
     const bf16* kr = head_of(a.K, bh, a.H) + (size_t)key * a.K.st + 8 * hi;
     const bf16* vr = head_of(a.V, bh, a.H) + (size_t)key * a.V.st + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4 * NP; ++ks) {
         kreg[ks] = valid ? *(const bf16x8*)(kr + 16 * ks) : zero_bf16x8();
         vreg[ks] = valid ? *(const bf16x8*)(vr + 16 * ks) : zero_bf16x8();
     }
     wait_async_copies();
     rows_finish(i_hi, sG0, sO0, sR0);
-    f32x16 dkacc[2] = {f32x16{}, f32x16{}}, dvacc[2] = {f32x16{}, f32x16{}};
+    f32x16 dkacc[2 * NP] = {}, dvacc[2 * NP] = {};
 
     // queries 32h .. 32h+31 of the tile in qc / gc / rc
     auto half = [&](int h, bool diag, int q0, const char* qc, const char* gc,
@@ -652,10 +690,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
             for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
         }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            sv = mfma32x32x16(lds_row_read(qc, 4096 * h + off.nat[ks]), kreg[ks], sv);   // S
-            dp = mfma32x32x16(lds_row_read(gc, 4096 * h + off.nat[ks]), vreg[ks], dp);   // dP - Delta
-        }
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int o = p * kTileBytes + 4096 * h + off.nat[ks];
+                sv = mfma32x32x16(lds_row_read(qc, o), kreg[4 * p + ks], sv);   // S
+                dp = mfma32x32x16(lds_row_read(gc, o), vreg[4 * p + ks], dp);   // dP - Delta
+            }
         if (diag) {
             // element r holds query q0 + 32h + 8(r/4) + 4hi + r%4: kept iff
             // key <= query < key + W, i.e. lim <= 8(r/4) + r%4 < lim + W
@@ -683,11 +724,14 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
             const bf16x8 pb = pack8(sv, 8 * cc);
             const bf16x8 sb = pack8(dp, 8 * cc);
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-                const int o0 = c * 2048 + off.tr[0][dt], o1 = c * 2048 + off.tr[1][dt];
-                dvacc[dt] = mfma32x32x16(lds_tr_read(gc, o0, o1), pb, dvacc[dt]);
-                dkacc[dt] = mfma32x32x16(lds_tr_read(qc, o0, o1), sb, dkacc[dt]);
-            }
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    const int o0 = p * kTileBytes + c * 2048 + off.tr[0][dt];
+                    const int o1 = p * kTileBytes + c * 2048 + off.tr[1][dt];
+                    dvacc[2 * p + dt] = mfma32x32x16(lds_tr_read(gc, o0, o1), pb, dvacc[2 * p + dt]);
+                    dkacc[2 * p + dt] = mfma32x32x16(lds_tr_read(qc, o0, o1), sb, dkacc[2 * p + dt]);
+                }
         }
     };
 
@@ -699,9 +743,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         __syncthreads();
         const bool more = i > i0;
         if (more) {
-            tile_load_async(ql, Qh, a.Q.st, (i - 1) * kTile, T, wave, tc);
-            tile_load_async(gl, Gh, a.dO.st, (i - 1) * kTile, T, wave, tc);
-            if (kDeltaFromO) tile_load_async(ol, Oh, a.O.st, (i - 1) * kTile, T, wave, tc);
+            tiles_load_async<NP>(ql, Qh, a.Q.st, (i - 1) * kTile, T, wave, tc);
+            tiles_load_async<NP>(gl, Gh, a.dO.st, (i - 1) * kTile, T, wave, tc);
+            if (kDeltaFromO) tiles_load_async<NP>(ol, Oh, a.O.st, (i - 1) * kTile, T, wave, tc);
             rows_load_async(i - 1, rl);
         }
         if (i >= first_w && i <= last_w) {
@@ -727,7 +771,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         bf16* krow = head_of(a.dK, bh, a.H) + (size_t)key * a.dK.st;
         bf16* vrow = head_of(a.dV, bh, a.H) + (size_t)key * a.dV.st;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < 2 * NP; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * dt + 8 * g + 4 * hi;
@@ -740,30 +784,32 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
 }
 
 // dQ alone (also writes Delta).
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_dq_d64_kernel(
+template <int NP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dq_d64_kernel(
     BwdParams a, int n_qtiles, int n_cu)
 {
     // one array per buffer, so that reads are provably apart from in-flight copies
-    __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK0[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sK1[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV0[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sV1[NP * kTileBytes];
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    dq_item(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1);
+    dq_item<NP>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1);
 }
 
 // dK, dV alone, from a Delta in memory.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_dkdv_d64_kernel(
+template <int NP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dkdv_d64_kernel(
     BwdParams a, int n_cu)
 {
-    __shared__ __attribute__((aligned(1024))) char sQ0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sQ1[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sG0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char sG1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sQ0[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sQ1[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sG0[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sG1[NP * kTileBytes];
     __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
     __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    dkdv_item<false>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1, nullptr, nullptr, sR0, sR1);
+    dkdv_item<NP, false>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1, nullptr, nullptr, sR0, sR1);
 }
 
 // ---------------------------------------------------------------------------
@@ -790,9 +836,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int BH = a.BH;
     const int level = item / (2 * BH), r = item - level * 2 * BH;
     if (r < BH)
-        dkdv_item<true>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1);
+        dkdv_item<1, true>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1);
     else
-        dq_item(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
+        dq_item<1>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
 }
 
 }  // namespace d64
@@ -809,7 +855,8 @@ hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
-    hipLaunchKernelGGL(d64::attn_fwd_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
+    auto k = a.D == 128 ? d64::attn_fwd_d64_kernel<2> : d64::attn_fwd_d64_kernel<1>;
+    hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
                        view(a.q, a.sq), view(a.k, a.sk), view(a.v, a.sv), view(a.o_out, a.so),
                        a.lse, BH, a.H, a.T, window_of(a), nqt, a.scale, a.scale * kLog2e, a.n_cu);
     return hipGetLastError();
@@ -841,8 +888,8 @@ hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
-    hipLaunchKernelGGL(d64::attn_bwd_dq_d64_kernel, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
-                       bwd_params(a), nqt, a.n_cu);
+    auto k = a.D == 128 ? d64::attn_bwd_dq_d64_kernel<2> : d64::attn_bwd_dq_d64_kernel<1>;
+    hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nqt, a.n_cu);
     return hipGetLastError();
 }
 
@@ -850,13 +897,17 @@ hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nkt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
-    hipLaunchKernelGGL(d64::attn_bwd_dkdv_d64_kernel, dim3(nkt * BH), dim3(d64::kThreads), 0, st,
-                       bwd_params(a), a.n_cu);
+    auto k = a.D == 128 ? d64::attn_bwd_dkdv_d64_kernel<2> : d64::attn_bwd_dkdv_d64_kernel<1>;
+    hipLaunchKernelGGL(k, dim3(nkt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), a.n_cu);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
+    if (a.D == 128) {  // two launches: the LDS of a fused item would leave one per CU
+        const hipError_t e = launch_dq_bf16_d64(a, st);
+        return e == hipSuccess ? launch_dkdv_bf16_d64(a, st) : e;
+    }
     const int BH = a.B * a.H;
     const int nb = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     hipLaunchKernelGGL(d64::attn_bwd_d64_kernel, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st,

@@ -28,7 +28,7 @@ struct AttnArgs {
     float scale;
     int n_cu;        // compute units of the current device (work placement)
     int window;      // sliding window W (query q sees keys q-W < k <= q); 0 = plain causal.
-                     // Only the bf16 D=64 kernels take it; the entry points with a
+                     // Only the bf16 D=64/128 kernels take it; the entry points with a
                      // window argument accept no other case.
     // strides of q, k, v, o, dO, dq, dk, dv (contiguous unless a strided entry point set them)
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;

@@ -33,7 +33,7 @@ def attention_sublayer(x, ln_w, ln_b, w_attn, b_attn, w_proj, b_proj, n_head: in
     D = C // n_head
     u = F.layer_norm(x, (C,), ln_w, ln_b, eps).reshape(B * T, C)
     qkv = torch.addmm(b_attn, u, w_attn)  # [B*T, 3C]
-    if D == 64 and qkv.dtype == torch.bfloat16:
+    if D in (64, 128) and qkv.dtype == torch.bfloat16:
         a = causal_attention_qkv(qkv.view(B, T, 3 * C), n_head).view(B * T, C)
         return x + torch.addmm(b_proj, a, w_proj).reshape(B, T, C)
     q, k, v = qkv.split(C, dim=-1)

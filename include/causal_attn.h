@@ -26,7 +26,8 @@
  *   - lse and delta: contiguous fp32 [B][H][T], 4-byte aligned.
  *   - dtype: ATTN_F32 (float) or ATTN_BF16 (bfloat16 storage; every product
  *     is accumulated in fp32).
- *   - D must be 32 or 64.  B, H, T >= 1, any T (the last tile is ragged).
+ *   - D must be 32 or 64, or 128 with ATTN_BF16.  B, H, T >= 1, any T (the
+ *     last tile is ragged).
  *   - scale must be finite and > 0 (the pages use 1/sqrt(D)).
  *   - stream is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     on it and the call returns without synchronising: buffers must stay
@@ -57,7 +58,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,          /* a required pointer is NULL              */
     ATTN_ERR_SHAPE = 2,         /* B, H or T < 1                            */
-    ATTN_ERR_UNSUPPORTED_D = 3, /* D not in {32, 64}                        */
+    ATTN_ERR_UNSUPPORTED_D = 3, /* D not in {32, 64} (bf16: {32, 64, 128})  */
     ATTN_ERR_DTYPE = 4,         /* dtype not ATTN_F32 / ATTN_BF16           */
     ATTN_ERR_ALIGN = 5,         /* tensor not 16-byte (lse/delta 4-byte) aligned */
     ATTN_ERR_OVERFLOW = 6,      /* T*D or the launch grid exceeds 2^31 - 1  */
@@ -116,7 +117,7 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
  *   q of a [B][T][3][H][D] qkv:      stride_b = 3*T*C, stride_h = D,   stride_t = 3*C
  *                                    (k at data + C, v at data + 2*C)
  *
- * Supported for dtype ATTN_BF16 with D = 64 (else ATTN_ERR_LAYOUT).  Each view
+ * Supported for dtype ATTN_BF16 with D = 64 or 128 (else ATTN_ERR_LAYOUT).  Each view
  * needs a 16-byte-aligned data pointer, non-negative strides that are
  * multiples of 8, stride_t >= D, and T * stride_t * 2 bytes below 2^32
  * (ATTN_ERR_LAYOUT otherwise).  lse and delta stay contiguous fp32 [B][H][T].

@@ -98,7 +98,8 @@ def test_stage_null_pointers(call, names):
 def test_stage_validation(call):
     assert call(T=0) == 2
     assert call(dtype=3) == 4
-    assert call(D=128) == 3
+    assert call(D=96) == 3
+    assert call(D=128, dtype=0) == 3
     assert call(T=2 ** 30) == 6
 
 
@@ -132,10 +133,21 @@ def test_bad_shape(kw):
     assert _bwd(**kw) == 2
 
 
-@pytest.mark.parametrize("D", [0, 1, 16, 48, 96, 128, 256])
+@pytest.mark.parametrize("D", [0, 1, 16, 48, 96, 256])
 def test_unsupported_head_dim(D):
     assert _fwd(D=D) == 3
     assert _bwd(D=D) == 3
+
+
+def test_head_dim_128_is_bf16_only():
+    # fp32 has no D = 128 kernels; in bf16 the D check passes and the next
+    # check in order (alignment of a misaligned lse) is the one that fires
+    assert _fwd(D=128, dtype=0) == 3
+    assert _bwd(D=128, dtype=0) == 3
+    assert _fwd(D=128, dtype=1, lse=P[4] + 1) == 5
+    assert _bwd(D=128, dtype=1, lse=P[4] + 1) == 5
+    assert _dq(D=128, dtype=1, lse=P[4] + 1) == 5
+    assert _dkdv(D=128, dtype=1, lse=P[4] + 1) == 5
 
 
 @pytest.mark.parametrize("dtype", [-1, 2, 7])
@@ -254,11 +266,15 @@ def test_strided_null_shape_scale():
     assert _bwd_s(window=-5) == 2
 
 
-def test_strided_supports_only_bf16_d64():
+def test_strided_supports_only_bf16_d64_d128():
     assert _fwd_s(dtype=0) == 10
     assert _bwd_s(dtype=0) == 10
     assert _fwd_s(D=32) == 10
     assert _fwd_s(D=48) == 3
+    assert _fwd_s(D=128, dtype=0) == 3
+    v128 = [_v(P[i], H_ * T_ * 128, T_ * 128, 128) for i in range(4)]
+    assert _fwd_s(views=v128, D=128, lse=P[4] + 1) == 5  # D=128 passes the layout check
+    assert _fwd_s(D=128, lse=P[4] + 1) == 10              # stride_t 64 < D
     assert _fwd_s(dtype=7) == 4
 
 

@@ -11,6 +11,8 @@ Shapes follow the pages' model configurations:
   * gpt400m   -- the ~400M config of the train-llm-from-scratch hub page
                  (n_embed 1024, n_head 16, context 1024), bf16;
   * long      -- the same head shape at a 4096-token context, bf16;
+  * gpt2s_d128 -- the gpt2s width (768) and context in 6 heads of 128, bf16
+                 (head dim 128 is not one of the pages' shapes);
   * sublayer  -- the GPT-2-small pre-norm attention sublayer (LayerNorm ->
                  c_attn -> causal MHA -> c_proj + residual), bf16.
 
@@ -67,6 +69,7 @@ ATTN_CONFIGS = {
     "gpt2s": AttnConfig("gpt2s", B=8, H=12, T=1024, D=64, dtype="bf16"),
     "gpt400m": AttnConfig("gpt400m", B=8, H=16, T=1024, D=64, dtype="bf16"),
     "long": AttnConfig("long", B=2, H=16, T=4096, D=64, dtype="bf16"),
+    "gpt2s_d128": AttnConfig("gpt2s_d128", B=8, H=6, T=1024, D=128, dtype="bf16"),
 }
 
 SUBLAYER_CONFIG = SublayerConfig("sublayer", B=8, T=1024, C=768, H=12, n_layer=12, dtype="bf16")
