@@ -52,6 +52,9 @@ def _bind(path: str):
     lib.oracle_sublayer_fwd.restype = ctypes.c_int
     lib.oracle_sublayer_bwd.argtypes = [_dp] * 15 + [_i64] * 4 + [ctypes.c_double, _i64]
     lib.oracle_sublayer_bwd.restype = ctypes.c_int
+    lib.oracle_attn_decode.argtypes = ([_dp] * 3 + [ctypes.POINTER(ctypes.c_int64)] + [_dp] * 2 +
+                                       [_i64] * 4 + [ctypes.c_double, _i64, _i64])
+    lib.oracle_attn_decode.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -135,6 +138,25 @@ def attn_bwd(q, k, v, dO, scale: float, nthreads: int = 0, lib: str | None = Non
     _load(lib).oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dO), _p(dq), _p(dk), _p(dv),
                             _p(delta), B, H, T, D, float(scale), int(window), int(nthreads))
     return dq, dk, dv, delta
+
+
+def attn_decode(q, k_cache, v_cache, lens, scale: float, window: int = 0, nthreads: int = 0,
+                lib: str | None = None):
+    """One new token per sequence against its KV cache.  q: [B, H, D];
+    k_cache, v_cache: [B, Tmax, H, D]; lens: [B] cached positions per sequence
+    (the token itself is the last).  Returns (o [B, H, D], lse [B, H]) in
+    float64; a sequence with len 0 gets o = 0, lse = -inf."""
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, Tmax, H, D = kc.shape
+    assert q.shape == (B, H, D) and vc.shape == kc.shape
+    ln = np.ascontiguousarray(np.asarray(lens, dtype=np.int64))
+    assert ln.shape == (B,) and np.all(ln >= 0) and np.all(ln <= Tmax)
+    o = np.empty((B, H, D), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    _load(lib).oracle_attn_decode(_p(q), _p(kc), _p(vc), ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                               _p(o), _p(lse), B, H, Tmax, D, float(scale), int(window),
+                               int(nthreads))
+    return o, lse
 
 
 def sublayer_fwd(x, g, bl, Wa, ba, Wp, bp, n_head: int, eps: float = 1e-5,

@@ -181,6 +181,60 @@ void oracle_attn_bwd(const double* q, const double* k, const double* v,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Decode: one new token per sequence against its key/value cache.            */
+/* nanochat, section 8 (inference engine): the KV cache is kept in FA3's      */
+/* native (B, T, H, D) layout; a prompt is prefilled into it, then tokens are */
+/* produced one at a time, each attending to every cached position up to and  */
+/* including its own (CS336 tutorial, section 7.4, names the KV cache among   */
+/* the inference-side optimisations).  The token of sequence b is at position */
+/* len_b - 1 and its key and value are already in the cache, so its output is */
+/* row len_b - 1 of the causal forward above over that sequence; with a       */
+/* window W > 0, the W most recent positions.                                 */
+/* q, o: [B][H][D]; kc, vc: [B][Tmax][H][D]; lens: [B] (0 <= len_b <= Tmax);  */
+/* lse: [B][H].  len_b = 0 (nothing cached): o = 0 and lse = -inf.            */
+/* ------------------------------------------------------------------------ */
+void oracle_attn_decode(const double* q, const double* kc, const double* vc,
+                        const int64_t* lens, double* o, double* lse, int64_t B,
+                        int64_t H, int64_t Tmax, int64_t D, double scale,
+                        int64_t window, int64_t nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const int64_t b = bh / H, h = bh % H;
+        const int64_t len = lens[b];
+        const double* Q = q + bh * D;
+        double* O = o + bh * D;
+        if (len <= 0) {
+            for (int64_t d = 0; d < D; ++d) O[d] = 0.0;
+            lse[bh] = -INFINITY;
+            continue;
+        }
+        const int64_t last = len - 1;  /* the new token's position */
+        const int64_t j0 = first_key(last, window);
+        double* s = (double*)malloc((size_t)len * sizeof(double));
+        double m = -INFINITY;
+        for (int64_t j = j0; j <= last; ++j) {
+            const double* Kj = kc + ((b * Tmax + j) * H + h) * D;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += Q[d] * Kj[d];
+            s[j] = dot * scale;
+            if (s[j] > m) m = s[j];
+        }
+        double Z = 0.0;
+        for (int64_t j = j0; j <= last; ++j) Z += exp(s[j] - m);
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int64_t j = j0; j <= last; ++j)
+                acc += exp(s[j] - m) / Z * vc[((b * Tmax + j) * H + h) * D + d];
+            O[d] = acc;
+        }
+        lse[bh] = m + log(Z);
+        free(s);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Pre-norm attention sublayer:  y = x + c_proj(attn(split(c_attn(LN(x)))))  */
 /* x, y, dx, dy: [N = B*T][C].  LN weight g[C], bias bl[C].                   */
 /* Wa[C][3C], ba[3C] (qkv = u Wa + ba, columns [q | k | v]), Wp[C][C], bp[C]. */

@@ -55,6 +55,14 @@ MUTANTS = {
                           "qkv[(b * T + t) * 3 * C + h * 3 * D + third * D + d];"),
     "residual_dropped_in_bwd": ("                                dy[n * C + c]; /* residual path */",
                                 "                                0.0;"),
+    "decode_cache_in_bhtd_order": ("const double* Kj = kc + ((b * Tmax + j) * H + h) * D;",
+                                   "const double* Kj = kc + ((b * H + h) * Tmax + j) * D;"),
+    "decode_token_one_position_early": ("const int64_t last = len - 1;  /* the new token's position */",
+                                        "const int64_t last = len - 2;"),
+    "decode_values_from_keys": ("acc += exp(s[j] - m) / Z * vc[((b * Tmax + j) * H + h) * D + d];",
+                                "acc += exp(s[j] - m) / Z * kc[((b * Tmax + j) * H + h) * D + d];"),
+    "decode_scale_missing": ("s[j] = dot * scale;", "s[j] = dot;"),
+    "decode_lse_without_max": ("lse[bh] = m + log(Z);", "lse[bh] = log(Z);"),
     "weight_grad_transposed": ("for (int64_t c = 0; c < C; ++c) dWp[cp * C + c] += av * dy[n * C + c];",
                                "for (int64_t c = 0; c < C; ++c) dWp[c * C + cp] += av * dy[n * C + c];"),
 }
@@ -72,6 +80,8 @@ BATTERY = [
     pins.test_sublayer_finite_differences,
     pins.test_layernorm_output_is_standardised,
     lambda: pins.test_window_against_torch_sdpa_band_mask(3),
+    lambda: pins.test_decode_against_torch_sdpa_single_query(3),
+    pins.test_decode_closed_forms,
 ]
 
 

@@ -462,3 +462,87 @@ def test_window_backward_finite_differences():
             lm = float(np.sum(oracle.attn_fwd(q, k, v, 0.5, window=W)[0] * dO))
             x[idx] = x0
             assert abs((lp - lm) / (2 * h) - g[idx]) < 2e-7, (name, idx)
+
+
+# --------------------------------------------------------------------------
+# decode against a KV cache (nanochat, section 8: FA3 (B, T, H, D) cache,
+# prefill then one token at a time)
+# --------------------------------------------------------------------------
+
+def _cache(B, Tmax, H, D, seed):
+    return _rand((B, H, D), seed), _rand((B, Tmax, H, D), seed + 1), _rand((B, Tmax, H, D), seed + 2)
+
+
+@pytest.mark.parametrize("window", [0, 1, 3, 50])
+def test_decode_against_torch_sdpa_single_query(window):
+    """Each (b, h): PyTorch fp64 SDPA of the one query over the visible cache
+    rows, and torch.logsumexp of the scaled scores for lse."""
+    B, Tmax, H, D = 4, 12, 3, 5
+    q, kc, vc = _cache(B, Tmax, H, D, 401)
+    lens = [7, 1, 12, 9]
+    s = 0.37
+    o, lse = oracle.attn_decode(q, kc, vc, lens, s, window=window)
+    for b in range(B):
+        n = lens[b]
+        j0 = max(0, n - window) if window else 0
+        for h in range(H):
+            tq = torch.tensor(q[b, h][None, None, None, :])           # [1, 1, 1, D]
+            tk = torch.tensor(kc[b, j0:n, h][None, None])             # [1, 1, n-j0, D]
+            tv = torch.tensor(vc[b, j0:n, h][None, None])
+            to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=s)
+            np.testing.assert_allclose(o[b, h], to[0, 0, 0].numpy(), rtol=0, atol=1e-13)
+            tl = torch.logsumexp(s * (tk[0, 0] @ tq[0, 0, 0]), dim=0)
+            assert abs(lse[b, h] - float(tl)) < 1e-13
+
+
+@pytest.mark.parametrize("window", [0, 4])
+def test_decode_is_the_last_row_of_the_causal_forward(window):
+    """Prefill and decode agree: the token at position len-1 decoded against
+    the cache gets row len-1 of the causal forward over the same sequence."""
+    B, H, T, D = 2, 3, 10, 4
+    q, k, v = _qkv((B, H, T, D), seed=411)
+    o_full, lse_full = oracle.attn_fwd(q, k, v, 0.5, window=window)
+    kc = np.ascontiguousarray(k.transpose(0, 2, 1, 3))  # [B, T, H, D]
+    vc = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    for n in (1, 2, 5, T):
+        o, lse = oracle.attn_decode(q[:, :, n - 1], kc, vc, [n] * B, 0.5, window=window)
+        np.testing.assert_allclose(o, o_full[:, :, n - 1], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse, lse_full[:, :, n - 1], rtol=0, atol=1e-14)
+
+
+def test_decode_closed_forms():
+    B, Tmax, H, D = 2, 6, 2, 3
+    q, kc, vc = _cache(B, Tmax, H, D, 421)
+    # one cached position: the output is that value row, lse its scaled score
+    o, lse = oracle.attn_decode(q, kc, vc, [1, 1], 0.7)
+    assert np.array_equal(o, vc[:, 0])
+    np.testing.assert_allclose(lse, 0.7 * np.einsum("bhd,bhd->bh", q, kc[:, 0]), atol=1e-15)
+    # a zero query weighs the visible rows equally
+    o, lse = oracle.attn_decode(np.zeros_like(q), kc, vc, [6, 4], 0.7, window=3)
+    np.testing.assert_allclose(o[0], vc[0, 3:6].mean(axis=0), atol=1e-15)
+    np.testing.assert_allclose(o[1], vc[1, 1:4].mean(axis=0), atol=1e-15)
+    np.testing.assert_allclose(lse, math.log(3.0), atol=1e-15)
+    # nothing cached
+    o, lse = oracle.attn_decode(q, kc, vc, [0, 3], 0.7)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0]))
+
+
+def test_decode_reads_only_the_visible_cache_rows():
+    """Rows at or past len, and before the window, do not matter; the visible
+    rows enter as a set (any order of the positions gives the same result)."""
+    B, Tmax, H, D = 2, 9, 2, 4
+    q, kc, vc = _cache(B, Tmax, H, D, 431)
+    lens, W = [7, 5], 4
+    o, lse = oracle.attn_decode(q, kc, vc, lens, 0.5, window=W)
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b, n in enumerate(lens):
+        kc2[b, n:] = 1e3
+        vc2[b, n:] = -1e3
+        kc2[b, :n - W] = 5e2
+        vc2[b, :n - W] = 7e2
+    o2, lse2 = oracle.attn_decode(q, kc2, vc2, lens, 0.5, window=W)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    perm = np.array([0, 1, 2, 6, 4, 3, 5, 7, 8])  # positions 3..6 reordered (b = 0)
+    o3, lse3 = oracle.attn_decode(q, kc[:, perm], vc[:, perm], lens, 0.5, window=W)
+    np.testing.assert_allclose(o3[0], o[0], atol=1e-14)
+    np.testing.assert_allclose(lse3[0], lse[0], atol=1e-14)
