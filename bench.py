@@ -36,6 +36,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["causal_head_self_amd/csrc/attn_bf16.hip",
                   "causal_head_self_amd/csrc/attn_bf16_d64.hip",
+                  "causal_head_self_amd/csrc/attn_decode.hip",
                   "causal_head_self_amd/csrc/attn_device.h"]
 
 
@@ -197,13 +198,99 @@ def sublayer_bench(args) -> int:
     return 0
 
 
+def decode_bench(args) -> int:
+    """One decode step against a full KV cache (nanochat, section 8: (B, T, H, D)
+    cache, one new token per sequence): attn_decode, its per-slice partial and
+    merge launches together.  The op streams the visible cache once, so the
+    metric is bytes per second against the HBM peak.  Algorithmic bytes per
+    call: the visible K and V rows (2 * sum_b len_b * H * D * 2), q and o
+    (B * H * D * 2 each), lse (B * H * 4) and the lengths (B * 4); the
+    workspace round trip (B * H * slices * (D + 4) * 4 twice) is not counted."""
+    import torch
+    import causal_head_self_amd as cat
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    cat.load_library()
+    cfg = workloads.DECODE_CONFIGS[args.config]
+    B, H, T_max, D = cfg.B, cfg.H, cfg.T_max, cfg.D
+    dev = torch.device("cuda:0")
+    host = workloads.decode_inputs(B, H, T_max, D)
+    q, kc, vc = (t.to(dev) for t in host)
+    lens = cfg.lens()
+    ln = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(cat.decode_workspace_bytes(B, H, T_max, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cat.attn_decode(q, kc, vc, ln, o, lse, ws, cfg.scale, 0, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+
+    kv_bytes = 2.0 * sum(lens) * H * D * 2
+    alg_bytes = kv_bytes + 2.0 * B * H * D * 2 + B * H * 4 + B * 4
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            threads = min(16, os.cpu_count() or 1)
+        c0 = time.perf_counter()
+        oracle.attn_decode(host[0], host[1], host[2], lens, oracle.widen_scale(cfg.scale),
+                           nthreads=threads)
+        dt = time.perf_counter() - c0
+        cpu = {"value": round(alg_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": (f"one fp64 decode step over the whole workload ({B * H} heads, "
+                          f"{sum(lens)} cached positions); {dt:.3f} s wall; host "
+                          f"{platform.processor() or platform.machine()}"),
+               "seconds": round(dt, 4)}
+    out = {
+        "metric": "decode attention against a KV cache: algorithmic bytes per second",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"{cfg.name}: one token per sequence against a full "
+                                f"[B={B}][T={T_max}][H={H}][D={D}] bf16 cache, fp32 arithmetic; "
+                                "q, k, v iid N(0,1) seeds 42+idx"),
+                   "B": B, "H": H, "T_max": T_max, "D": D, "cached_positions": lens,
+                   "global_batch": B, "seq_len": T_max, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "attn_decode (partial + combine launches)",
+                     "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic("decode", f"{cfg.name}_B{B}_H{H}_T{T_max}_D{D}",
+                                             kernel_source_sha()),
+                     "algorithmic_bytes_per_call": alg_bytes},
+        "cpu_baseline": cpu,
+        "l2_flushed": False,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="gpt2s",
-                    choices=["tiny", "gpt2s", "gpt400m", "long", "gpt2s_d128", "sublayer"])
+                    choices=["tiny", "gpt2s", "gpt400m", "long", "gpt2s_d128", "sublayer",
+                             "decode_gpt2s", "decode_gpt2s_b64", "decode_long"])
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window W (bf16, D 64/128): query i sees keys i-W < j <= i")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,6 +306,8 @@ def main() -> int:
 
     if args.config == "sublayer":
         return sublayer_bench(args)
+    if args.config.startswith("decode_"):
+        return decode_bench(args)
 
     import torch
     import causal_head_self_amd as cat

@@ -12,6 +12,8 @@ the computation.  PyTorch supplies device memory and streams.
     causal_attention(q, k, v, scale=None)                   -- autograd op
     causal_attention_qkv(qkv, n_head)                       -- autograd op on the
         fused [B, T, 3C] c_attn output, returning [B, T, C] with no layout copies
+    attn_decode / decode_attention                          -- one new token per
+        sequence against a [B, T_max, H, D] KV cache
 
 Tensors are contiguous [B, H, T, D] (D in {32, 64}; 128 in bf16) of float32 or bfloat16 on
 the current GPU; lse and delta are float32 [B, H, T].
@@ -27,8 +29,8 @@ from ._lib import (ABI_VERSION, ATTN_BF16, ATTN_F32, EXPORTS, LIB_PATH, AttnErro
 
 __all__ = [
     "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
-    "attn_bwd_strided", "attn_status_str", "causal_attention", "causal_attention_qkv",
-    "qkv_heads", "AttnError",
+    "attn_bwd_strided", "attn_decode", "decode_workspace_bytes", "decode_attention",
+    "attn_status_str", "causal_attention", "causal_attention_qkv", "qkv_heads", "AttnError",
     "ATTN_F32", "ATTN_BF16", "load_library", "LIB_PATH", "EXPORTS", "ABI_VERSION",
 ]
 
@@ -198,6 +200,45 @@ def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0) -> tor
     written in place through strided views (bf16, head dim 64 or 128).  window W > 0
     restricts query i to keys i-W < j <= i (sliding window)."""
     return _CausalAttentionQKV.apply(qkv, n_head, int(window))
+
+
+def decode_workspace_bytes(B: int, H: int, T_max: int, D: int) -> int:
+    """C ABI attn_decode_workspace_bytes."""
+    return int(load_library().attn_decode_workspace_bytes(int(B), int(H), int(T_max), int(D)))
+
+
+def attn_decode(q, k_cache, v_cache, cache_lens, o, lse, workspace, scale: float | None = None,
+                window: int = 0, stream=None) -> None:
+    """C ABI attn_decode: q, o [B, H, D]; k_cache, v_cache [B, T_max, H, D] (bf16);
+    cache_lens int32 [B]; lse fp32 [B, H]; workspace a byte (uint8) tensor of at
+    least decode_workspace_bytes(B, H, T_max, D)."""
+    if k_cache.dim() != 4:
+        raise ValueError(f"k_cache must be [B, T_max, H, D], got {tuple(k_cache.shape)}")
+    B, T_max, H, D = (int(s) for s in k_cache.shape)
+    if tuple(q.shape) != (B, H, D) or tuple(o.shape) != (B, H, D):
+        raise ValueError("q and o must be [B, H, D] for a [B, T_max, H, D] cache")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(lse.shape) != (B, H):
+        raise ValueError("v_cache must match k_cache and lse must be [B, H]")
+    if cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().attn_decode(
+        _ptr(q, "q"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+        _ptr(cache_lens, "cache_lens"), _ptr(o, "o"), _ptr(lse, "lse"),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), B, H, T_max,
+        D, int(window), scale, _dtype_code(q), _stream(stream))
+    check(rc)
+
+
+def decode_attention(q, k_cache, v_cache, cache_lens, scale: float | None = None,
+                     window: int = 0):
+    """attn_decode with freshly allocated o, lse and workspace: returns (o, lse)."""
+    B, T_max, H, D = (int(s) for s in k_cache.shape)
+    o = torch.empty((B, H, D), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    ws = torch.empty(decode_workspace_bytes(B, H, T_max, D), dtype=torch.uint8, device=q.device)
+    attn_decode(q, k_cache, v_cache, cache_lens, o, lse, ws, scale, window)
+    return o, lse
 
 
 def _same_layout(name, t, ref):

@@ -26,12 +26,14 @@ STATUS = {
     8: "ATTN_ERR_ALIAS",
     9: "ATTN_ERR_HIP",
     10: "ATTN_ERR_LAYOUT",
+    11: "ATTN_ERR_WORKSPACE",
 }
 
 # every symbol include/causal_attn.h declares
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
-           "attn_bwd_strided", "attn_status_str", "attn_abi_version")
-ABI_VERSION = (1 << 16) | 1
+           "attn_bwd_strided", "attn_decode", "attn_decode_workspace_bytes", "attn_status_str",
+           "attn_abi_version")
+ABI_VERSION = (1 << 16) | 2
 
 
 class AttnView(ctypes.Structure):
@@ -79,6 +81,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                      [_vp, _int, _int, _int, _int, _int, ctypes.c_float, _int,
                                       _vp])
     lib.attn_bwd_strided.restype = _int
+    lib.attn_decode_workspace_bytes.argtypes = [_int] * 4
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode.argtypes = ([_vp] * 7 + [ctypes.c_size_t] + [_int] * 5 +
+                                [ctypes.c_float, _int, _vp])
+    lib.attn_decode.restype = _int
     lib.attn_status_str.argtypes = [_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []

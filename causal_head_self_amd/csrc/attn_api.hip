@@ -195,6 +195,7 @@ const char* attn_status_str(int st)
     case ATTN_ERR_LAYOUT:
         return "strided views need bf16, D = 64 or 128, strides that are non-negative multiples of 8 "
                "with stride_t >= D, and T * stride_t * 2 < 2^32";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes()";
     default: return "unknown status";
     }
 }
@@ -359,6 +360,61 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     a.sdv = strides_of(dv);
     a.window = window;
     return status(cattn::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int T_max, int D)
+{
+    if (B < 1 || H < 1 || T_max < 1 || D < 1) return 0;
+    return (size_t)B * H * cattn::decode_slices(T_max) * (size_t)(D + 4) * sizeof(float);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_lens,
+                void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int H,
+                int T_max, int D, int window, float scale, int dtype, void* stream)
+{
+    if (!q || !k_cache || !v_cache || !cache_lens || !o || !lse || !workspace)
+        return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || T_max < 1 || window < 0) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED_D;
+    if (!isfinite(scale) || !(scale > 0.0f)) return ATTN_ERR_SCALE;
+    const long long slices = cattn::decode_slices(T_max);
+    if ((long long)B * H * slices > 0x7fffffffLL || (long long)B * T_max * H * D > (1LL << 40))
+        return ATTN_ERR_OVERFLOW;
+    for (const void* p : {q, k_cache, v_cache, (const void*)o, (const void*)workspace})
+        if ((uintptr_t)p % 16) return ATTN_ERR_ALIGN;
+    if ((uintptr_t)lse % 4 || (uintptr_t)cache_lens % 4) return ATTN_ERR_ALIGN;
+    const size_t need = attn_decode_workspace_bytes(B, H, T_max, D);
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t bh = (size_t)B * H;
+    const size_t cache = (size_t)B * T_max * H * D * 2;
+    auto span = [](const void* p, size_t n) {
+        return Span{(uintptr_t)p, (uintptr_t)p + n};
+    };
+    const Span in[4] = {span(q, bh * D * 2), span(k_cache, cache), span(v_cache, cache),
+                        span(cache_lens, (size_t)B * 4)};
+    const Span out[3] = {span(o, bh * D * 2), span(lse, bh * 4), span(workspace, need)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(out[i], in[j])) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(out[i], out[j])) return ATTN_ERR_ALIAS;
+    }
+    cattn::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.lens = cache_lens;
+    a.o = o;
+    a.lse = lse;
+    a.part = (float*)workspace;
+    a.B = B;
+    a.H = H;
+    a.T_max = T_max;
+    a.D = D;
+    a.window = window;
+    a.scale = scale;
+    return status(cattn::launch_decode_bf16(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

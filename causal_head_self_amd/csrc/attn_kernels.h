@@ -34,6 +34,23 @@ struct AttnArgs {
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
 };
 
+// Decode (one query per sequence against a [B][T_max][H][D] KV cache).
+struct DecodeArgs {
+    const void* q;        // [B][H][D]
+    const void* k_cache;  // [B][T_max][H][D]
+    const void* v_cache;
+    const int* lens;      // [B] cached positions per sequence (clamped to [0, T_max])
+    void* o;              // [B][H][D]
+    float* lse;           // [B][H]
+    float* part;          // workspace: [B][H][decode_slices(T_max)][D + 4] fp32
+    int B, H, T_max, D;
+    int window;           // 0: every cached position
+    float scale;
+};
+
+int decode_slices(int T_max);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
+
 // launch_dq_* computes delta (from o and dO) as well as dq.
 hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dq_bf16(const AttnArgs& a, hipStream_t st);

@@ -45,6 +45,8 @@
 #ifndef CAUSAL_ATTN_H
 #define CAUSAL_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -65,7 +67,8 @@ typedef enum {
     ATTN_ERR_SCALE = 7,         /* scale not finite or not > 0              */
     ATTN_ERR_ALIAS = 8,         /* an output overlaps an input or output    */
     ATTN_ERR_HIP = 9,           /* a kernel launch failed                   */
-    ATTN_ERR_LAYOUT = 10        /* strided views: unsupported dtype/D or strides */
+    ATTN_ERR_LAYOUT = 10,       /* strided views: unsupported dtype/D or strides */
+    ATTN_ERR_WORKSPACE = 11     /* decode: workspace smaller than required  */
 } attn_status_t;
 
 /* Forward.  Reads q, k, v; writes o ([B][H][T][D], dtype) and lse
@@ -155,13 +158,48 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
                      attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
                      float scale, int dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Decode against a KV cache.  nanochat, section 8 (inference engine): the
+ * cache is kept in FA3's native (B, T, H, D) layout, a prompt is prefilled
+ * into it, then tokens are produced one at a time, each attending to every
+ * cached position up to and including its own.  One call computes, for every
+ * sequence b and head h, the attention of the new token's query over
+ * positions 0 .. len_b - 1 of the cache (the token's own key and value are
+ * already stored at position len_b - 1): row len_b - 1 of the causal forward
+ * above.  With window W > 0 only the W most recent positions,
+ * max(0, len_b - W) .. len_b - 1, take part.
+ *
+ *   q:        [B][H][D] dtype (the new token of each sequence), 16-byte aligned
+ *   k_cache:  [B][T_max][H][D] dtype, contiguous, 16-byte aligned
+ *   v_cache:  [B][T_max][H][D] dtype, contiguous, 16-byte aligned
+ *   cache_lens: int32 [B] device array, len_b cached positions of sequence b;
+ *             values are clamped to [0, T_max]; len_b = 0 gives o = 0 and
+ *             lse = -inf for that sequence
+ *   o:        [B][H][D] dtype, written
+ *   lse:      fp32 [B][H], written (natural log, as for attn_fwd)
+ *   workspace: device memory of at least attn_decode_workspace_bytes(B, H,
+ *             T_max, D) bytes, 16-byte aligned, owned by the caller; its
+ *             content on entry does not matter and is overwritten
+ *   dtype:    ATTN_BF16 only (else ATTN_ERR_DTYPE); D = 64 or 128 (else
+ *             ATTN_ERR_UNSUPPORTED_D); window >= 0 (else ATTN_ERR_SHAPE)
+ *
+ * All arithmetic after the bf16 loads is fp32.  Two kernel launches on
+ * `stream` (per-slice partial softmax, then their merge); no synchronisation.
+ * Errors: as for attn_fwd, checked before any HIP call, plus
+ * ATTN_ERR_WORKSPACE for a workspace below the required size; outputs and the
+ * workspace must not overlap each other or any input (ATTN_ERR_ALIAS). */
+size_t attn_decode_workspace_bytes(int B, int H, int T_max, int D);
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_lens,
+                void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int H,
+                int T_max, int D, int window, float scale, int dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_str(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 1)
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

@@ -41,11 +41,11 @@ def test_abi_version_and_status_strings():
     lib = cat.load_library()
     assert lib.attn_abi_version() == _lib.ABI_VERSION
     seen = set()
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = cat.attn_status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 11
+    assert len(seen) == 12
     assert cat.attn_status_str(1234) == "unknown status"
     assert cat.attn_status_str(-1) == "unknown status"
 
@@ -306,3 +306,54 @@ def test_strided_alias_rules():
     sb, sh, st = T_ * 3 * C_, D_, 3 * C_
     near = _lib.AttnView(P[6] + 64, sb, sh, st)
     assert _bwd_s(views=[q, k, v, _v(P[3]), _v(P[5]), dq, near, dv]) == 8
+
+
+# ---------------------------------------------------------------------------
+# decode against a KV cache (attn_decode): every call below holds an invalid
+# argument, so it returns during validation
+# ---------------------------------------------------------------------------
+
+DB, DH, DT, DD = 2, 3, 17, 64
+
+
+def _ws(B=DB, H=DH, T=DT, D=DD):
+    return cat.load_library().attn_decode_workspace_bytes(B, H, T, D)
+
+
+def _dec(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], lens=P[3], o=P[4], lse=P[5], ws=P[6], ws_bytes=_ws(),
+             B=DB, H=DH, T=DT, D=DD, window=0, scale=0.125, dtype=1)
+    a.update(kw)
+    return cat.load_library().attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"],
+                                          a["ws"], a["ws_bytes"], a["B"], a["H"], a["T"],
+                                          a["D"], a["window"], a["scale"], a["dtype"], None)
+
+
+def test_decode_workspace_bytes():
+    # one (D + 4)-float partial per (b, h, 64-position slice)
+    assert _ws(8, 12, 1024, 64) == 8 * 12 * 16 * 68 * 4
+    assert _ws(2, 16, 4097, 128) == 2 * 16 * 65 * 132 * 4
+    assert _ws(1, 1, 1, 64) == 68 * 4
+    assert _ws(0, 1, 1, 64) == 0 and _ws(1, 1, 0, 64) == 0
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "lens", "o", "lse", "ws"])
+def test_decode_null_pointer(name):
+    assert _dec(**{name: None}) == 1
+
+
+def test_decode_validation_order_and_codes():
+    assert _dec(B=0) == 2 and _dec(H=0) == 2 and _dec(T=0) == 2 and _dec(window=-1) == 2
+    assert _dec(dtype=0) == 4 and _dec(dtype=5) == 4
+    assert _dec(D=32) == 3 and _dec(D=96) == 3
+    assert _dec(scale=0.0) == 7 and _dec(scale=float("inf")) == 7
+    assert _dec(B=2 ** 16, H=2 ** 10, T=2 ** 12, ws_bytes=2 ** 62) == 6
+    assert _dec(q=P[0] + 8) == 5 and _dec(o=P[4] + 2) == 5 and _dec(ws=P[6] + 4) == 5
+    assert _dec(lse=P[5] + 2) == 5 and _dec(lens=P[3] + 1) == 5
+    assert _dec(ws_bytes=_ws() - 1) == 11 and _dec(ws_bytes=0) == 11
+    assert _dec(o=P[0]) == 8                      # o is q
+    assert _dec(ws=P[1]) == 8                     # workspace is the key cache
+    assert _dec(lse=P[6] + 64) == 8               # lse inside the workspace
+    assert _dec(o=P[3]) == 8                      # o over cache_lens
+    # D = 128 passes the head-dim check (the misaligned q is what fires)
+    assert _dec(D=128, ws_bytes=_ws(D=128), q=P[0] + 8) == 5

@@ -14,7 +14,10 @@ Shapes follow the pages' model configurations:
   * gpt2s_d128 -- the gpt2s width (768) and context in 6 heads of 128, bf16
                  (head dim 128 is not one of the pages' shapes);
   * sublayer  -- the GPT-2-small pre-norm attention sublayer (LayerNorm ->
-                 c_attn -> causal MHA -> c_proj + residual), bf16.
+                 c_attn -> causal MHA -> c_proj + residual), bf16;
+  * decode_*  -- one decode step against a full KV cache in the (B, T, H, D)
+                 layout (nanochat, section 8) at the gpt2s and long head
+                 shapes, bf16.
 
 Seeding follows the set_seed(42) convention of the CS336 tutorial (section
 9.3): tensor number idx is drawn from its own generator seeded 42 + idx, as
@@ -72,6 +75,35 @@ ATTN_CONFIGS = {
     "gpt2s_d128": AttnConfig("gpt2s_d128", B=8, H=6, T=1024, D=128, dtype="bf16"),
 }
 
+@dataclass(frozen=True)
+class DecodeConfig:
+    """One decode step: B sequences, each adding one token to a [T_max] cache
+    of H heads of width D; every sequence holds `fill` cached positions
+    (T_max when fill is None)."""
+    name: str
+    B: int
+    H: int
+    T_max: int
+    D: int
+    fill: int | None = None
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def lens(self):
+        return [self.T_max if self.fill is None else self.fill] * self.B
+
+
+# decode steps at the pages' head shapes with a full cache: GPT-2-small
+# (context 1024) at the training batch and at a serving batch of 64 sequences,
+# and the long-context shape (4096)
+DECODE_CONFIGS = {
+    "decode_gpt2s": DecodeConfig("decode_gpt2s", B=8, H=12, T_max=1024, D=64),
+    "decode_gpt2s_b64": DecodeConfig("decode_gpt2s_b64", B=64, H=12, T_max=1024, D=64),
+    "decode_long": DecodeConfig("decode_long", B=2, H=16, T_max=4096, D=64),
+}
+
 SUBLAYER_CONFIG = SublayerConfig("sublayer", B=8, T=1024, C=768, H=12, n_layer=12, dtype="bf16")
 
 
@@ -96,6 +128,15 @@ def attention_inputs(B: int, H: int, T: int, D: int, dtype="bf16", seed: int = S
 
 def config_inputs(cfg: AttnConfig, seed: int = SEED):
     return attention_inputs(cfg.B, cfg.H, cfg.T, cfg.D, cfg.dtype, seed)
+
+
+def decode_inputs(B: int, H: int, T_max: int, D: int, seed: int = SEED):
+    """q [B, H, D] and k_cache, v_cache [B, T_max, H, D] as bf16 CPU tensors,
+    iid N(0, 1), seeds seed+0..2 (the cache rows past a sequence's length are
+    drawn too; they must not matter)."""
+    dt = torch.bfloat16
+    return (_draw((B, H, D), 0, 1.0, dt, seed), _draw((B, T_max, H, D), 1, 1.0, dt, seed),
+            _draw((B, T_max, H, D), 2, 1.0, dt, seed))
 
 
 def sublayer_inputs(cfg: SublayerConfig = SUBLAYER_CONFIG, seed: int = SEED, B: int | None = None):
