@@ -34,15 +34,20 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["causal_head_self_amd/csrc/attn_bf16.hip",
+# the sources each family of kernels is built from (a profile summary is valid
+# only for the source it was taken on)
+KERNEL_SOURCES = {
+    "attention": ["causal_head_self_amd/csrc/attn_bf16.hip",
                   "causal_head_self_amd/csrc/attn_bf16_d64.hip",
-                  "causal_head_self_amd/csrc/attn_decode.hip",
-                  "causal_head_self_amd/csrc/attn_device.h"]
+                  "causal_head_self_amd/csrc/attn_device.h"],
+    "decode": ["causal_head_self_amd/csrc/attn_decode.hip",
+               "causal_head_self_amd/csrc/attn_device.h"],
+}
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(family: str = "attention") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -274,7 +279,7 @@ def decode_bench(args) -> int:
                      "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": read_traffic("decode", f"{cfg.name}_B{B}_H{H}_T{T_max}_D{D}",
-                                             kernel_source_sha()),
+                                             kernel_source_sha("decode")),
                      "algorithmic_bytes_per_call": alg_bytes},
         "cpu_baseline": cpu,
         "l2_flushed": False,
