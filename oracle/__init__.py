@@ -55,6 +55,12 @@ def _bind(path: str):
     lib.oracle_attn_decode.argtypes = ([_dp] * 3 + [ctypes.POINTER(ctypes.c_int64)] + [_dp] * 2 +
                                        [_i64] * 4 + [ctypes.c_double, _i64, _i64])
     lib.oracle_attn_decode.restype = None
+    lib.oracle_rope_qknorm_fwd.argtypes = [_dp] * 2 + [_i64] * 5 + [ctypes.c_double, _i64, _i64,
+                                                                    ctypes.c_double, ctypes.c_double]
+    lib.oracle_rope_qknorm_fwd.restype = None
+    lib.oracle_rope_qknorm_bwd.argtypes = [_dp] * 3 + [_i64] * 5 + [ctypes.c_double, _i64, _i64,
+                                                                    ctypes.c_double, ctypes.c_double]
+    lib.oracle_rope_qknorm_bwd.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -157,6 +163,31 @@ def attn_decode(q, k_cache, v_cache, lens, scale: float, window: int = 0, nthrea
                                _p(o), _p(lse), B, H, Tmax, D, float(scale), int(window),
                                int(nthreads))
     return o, lse
+
+
+def rope_qknorm_fwd(x, pos0: int = 0, base: float = 10000.0, rope: bool = True,
+                    norm: bool = True, gain: float = 1.0, eps: float = 1e-6,
+                    lib: str | None = None):
+    """RoPE (pairs (i, i + D/2), angle (pos0 + t) * base^(-2i/D)) and QK norm
+    (x / sqrt(mean(x^2) + eps) * gain) of every row of x [B, H, T, D]."""
+    x = _f64(x)
+    B, H, T, D = x.shape
+    y = np.empty_like(x)
+    _load(lib).oracle_rope_qknorm_fwd(_p(x), _p(y), B, H, T, D, int(pos0), float(base),
+                                   int(bool(rope)), int(bool(norm)), float(gain), float(eps))
+    return y
+
+
+def rope_qknorm_bwd(x, dy, pos0: int = 0, base: float = 10000.0, rope: bool = True,
+                    norm: bool = True, gain: float = 1.0, eps: float = 1e-6,
+                    lib: str | None = None):
+    """Gradient with respect to x of sum(dy * rope_qknorm_fwd(x))."""
+    x, dy = _f64(x), _f64(dy)
+    B, H, T, D = x.shape
+    dx = np.empty_like(x)
+    _load(lib).oracle_rope_qknorm_bwd(_p(x), _p(dy), _p(dx), B, H, T, D, int(pos0), float(base),
+                                   int(bool(rope)), int(bool(norm)), float(gain), float(eps))
+    return dx
 
 
 def sublayer_fwd(x, g, bl, Wa, ba, Wp, bp, n_head: int, eps: float = 1e-5,

@@ -235,6 +235,98 @@ void oracle_attn_decode(const double* q, const double* kc, const double* vc,
 }
 
 /* ------------------------------------------------------------------------ */
+/* RoPE and QK-norm on the query and key rows of every head.                 */
+/* nanochat, section 9, lists RoPE position encoding and QK norm (with a     */
+/* factor of 1.2) among the attention's parts; the pages give no formulas,    */
+/* so the standard forms are taken (readings):                                */
+/*  - RoPE rotates the pair of columns (i, i + D/2), i < D/2, of the row at   */
+/*    position p = pos0 + t by the angle p * base^(-2i/D):                    */
+/*        y_i       = x_i cos - x_{i+D/2} sin                                 */
+/*        y_{i+D/2} = x_i sin + x_{i+D/2} cos                                 */
+/*  - QK norm divides the row by its root mean square, sqrt(mean(x^2) + eps), */
+/*    with no learned weight, and multiplies by `gain` (1.2 for queries in    */
+/*    the pages' wording, 1 for keys).                                        */
+/* Rotation keeps the root mean square, so the two commute.                   */
+/* x, y, dy, dx: [B][H][T][D]; use_rope / use_norm switch each part.          */
+/* ------------------------------------------------------------------------ */
+static void rope_angle(int64_t p, int64_t i, int64_t D, double base, double* c, double* s)
+{
+    const double theta = (double)p * pow(base, -2.0 * (double)i / (double)D);
+    *c = cos(theta);
+    *s = sin(theta);
+}
+
+void oracle_rope_qknorm_fwd(const double* x, double* y, int64_t B, int64_t H, int64_t T,
+                            int64_t D, int64_t pos0, double base, int64_t use_rope,
+                            int64_t use_norm, double gain, double eps)
+{
+    const int64_t half = D / 2;
+    for (int64_t row = 0; row < B * H * T; ++row) {
+        const int64_t t = row % T;
+        const double* X = x + row * D;
+        double* Y = y + row * D;
+        double r = 1.0;
+        if (use_norm) {
+            double ss = 0.0;
+            for (int64_t d = 0; d < D; ++d) ss += X[d] * X[d];
+            r = gain / sqrt(ss / (double)D + eps);
+        }
+        for (int64_t i = 0; i < half; ++i) {
+            double c = 1.0, s = 0.0;
+            if (use_rope) rope_angle(pos0 + t, i, D, base, &c, &s);
+            Y[i] = r * (X[i] * c - X[i + half] * s);
+            Y[i + half] = r * (X[i] * s + X[i + half] * c);
+        }
+    }
+}
+
+/* Gradient of sum(dy * y) with respect to x for the map above.  With
+ * z = R x (rotation) and y = gain * z / rms(x), rms(x) = sqrt(mean(x^2) + eps):
+ *   dz = (gain / rms) dy - z * (gain / rms^3) * mean(dy * z)   (norm)
+ *   dx = R^T dz                                                (rotation)
+ * (rotation keeps the norm, so mean(x^2) = mean(z^2)). */
+void oracle_rope_qknorm_bwd(const double* x, const double* dy, double* dx, int64_t B,
+                            int64_t H, int64_t T, int64_t D, int64_t pos0, double base,
+                            int64_t use_rope, int64_t use_norm, double gain, double eps)
+{
+    const int64_t half = D / 2;
+    double* z = (double*)malloc((size_t)D * sizeof(double));
+    double* dz = (double*)malloc((size_t)D * sizeof(double));
+    for (int64_t row = 0; row < B * H * T; ++row) {
+        const int64_t t = row % T;
+        const double* X = x + row * D;
+        const double* G = dy + row * D;
+        double* DX = dx + row * D;
+        for (int64_t i = 0; i < half; ++i) {
+            double c = 1.0, s = 0.0;
+            if (use_rope) rope_angle(pos0 + t, i, D, base, &c, &s);
+            z[i] = X[i] * c - X[i + half] * s;
+            z[i + half] = X[i] * s + X[i + half] * c;
+        }
+        if (use_norm) {
+            double ss = 0.0;
+            for (int64_t d = 0; d < D; ++d) ss += X[d] * X[d];
+            const double rms = sqrt(ss / (double)D + eps);
+            double m = 0.0;
+            for (int64_t d = 0; d < D; ++d) m += G[d] * z[d];
+            m /= (double)D;
+            for (int64_t d = 0; d < D; ++d)
+                dz[d] = gain / rms * G[d] - z[d] * gain / (rms * rms * rms) * m;
+        } else {
+            for (int64_t d = 0; d < D; ++d) dz[d] = G[d];
+        }
+        for (int64_t i = 0; i < half; ++i) {
+            double c = 1.0, s = 0.0;
+            if (use_rope) rope_angle(pos0 + t, i, D, base, &c, &s);
+            DX[i] = dz[i] * c + dz[i + half] * s;
+            DX[i + half] = -dz[i] * s + dz[i + half] * c;
+        }
+    }
+    free(z);
+    free(dz);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Pre-norm attention sublayer:  y = x + c_proj(attn(split(c_attn(LN(x)))))  */
 /* x, y, dx, dy: [N = B*T][C].  LN weight g[C], bias bl[C].                   */
 /* Wa[C][3C], ba[3C] (qkv = u Wa + ba, columns [q | k | v]), Wp[C][C], bp[C]. */

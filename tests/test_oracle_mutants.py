@@ -63,6 +63,19 @@ MUTANTS = {
                                 "acc += exp(s[j] - m) / Z * kc[((b * Tmax + j) * H + h) * D + d];"),
     "decode_scale_missing": ("s[j] = dot * scale;", "s[j] = dot;"),
     "decode_lse_without_max": ("lse[bh] = m + log(Z);", "lse[bh] = log(Z);"),
+    "rope_rotation_sign": ("Y[i] = r * (X[i] * c - X[i + half] * s);",
+                           "Y[i] = r * (X[i] * c + X[i + half] * s);"),
+    "rope_adjacent_pairs": ("Y[i + half] = r * (X[i] * s + X[i + half] * c);",
+                            "Y[i + half] = r * (X[i] * s + X[i + 1] * c);"),
+    "rope_frequency_exponent": ("pow(base, -2.0 * (double)i / (double)D)",
+                                "pow(base, -(double)i / (double)D)"),
+    "qknorm_sum_not_mean": ("r = gain / sqrt(ss / (double)D + eps);", "r = gain / sqrt(ss + eps);"),
+    "qknorm_eps_outside": ("r = gain / sqrt(ss / (double)D + eps);",
+                           "r = gain / (sqrt(ss / (double)D) + eps);"),
+    "qknorm_bwd_drops_projection": ("dz[d] = gain / rms * G[d] - z[d] * gain / (rms * rms * rms) * m;",
+                                    "dz[d] = gain / rms * G[d];"),
+    "rope_bwd_not_transposed": ("DX[i] = dz[i] * c + dz[i + half] * s;",
+                                "DX[i] = dz[i] * c - dz[i + half] * s;"),
     "weight_grad_transposed": ("for (int64_t c = 0; c < C; ++c) dWp[cp * C + c] += av * dy[n * C + c];",
                                "for (int64_t c = 0; c < C; ++c) dWp[c * C + cp] += av * dy[n * C + c];"),
 }
@@ -82,6 +95,10 @@ BATTERY = [
     lambda: pins.test_window_against_torch_sdpa_band_mask(3),
     lambda: pins.test_decode_against_torch_sdpa_single_query(3),
     pins.test_decode_closed_forms,
+    pins.test_rope_two_columns_is_a_plane_rotation_by_the_position,
+    pins.test_rope_four_columns_pairs_and_frequencies,
+    lambda: pins.test_qk_norm_against_torch_rms_norm(1.2, 1e-6),
+    lambda: pins.test_rope_qknorm_backward_finite_differences(True, True),
 ]
 
 

@@ -546,3 +546,87 @@ def test_decode_reads_only_the_visible_cache_rows():
     o3, lse3 = oracle.attn_decode(q, kc[:, perm], vc[:, perm], lens, 0.5, window=W)
     np.testing.assert_allclose(o3[0], o[0], atol=1e-14)
     np.testing.assert_allclose(lse3[0], lse[0], atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# RoPE and QK norm (nanochat, section 9); standard forms as the reading
+# --------------------------------------------------------------------------
+
+def test_rope_two_columns_is_a_plane_rotation_by_the_position():
+    """D = 2: one pair, frequency base^0 = 1, so the row at position p is turned
+    by p radians counter-clockwise: (x0, x1) -> (x0 cos p - x1 sin p,
+    x0 sin p + x1 cos p)."""
+    x = _rand((1, 1, 5, 2), 501)
+    y = oracle.rope_qknorm_fwd(x, pos0=3, norm=False)
+    for t in range(5):
+        p = 3 + t
+        c, s = math.cos(p), math.sin(p)
+        x0, x1 = x[0, 0, t]
+        assert abs(y[0, 0, t, 0] - (x0 * c - x1 * s)) < 1e-15
+        assert abs(y[0, 0, t, 1] - (x0 * s + x1 * c)) < 1e-15
+
+
+def test_rope_four_columns_pairs_and_frequencies():
+    """D = 4, base 100: columns (0, 2) turn by p, columns (1, 3) by p / 10
+    (100^(-2/4) = 0.1)."""
+    x = _rand((1, 1, 4, 4), 503)
+    y = oracle.rope_qknorm_fwd(x, base=100.0, norm=False)
+    for t in range(4):
+        for (a, b), w in (((0, 2), 1.0), ((1, 3), 0.1)):
+            c, s = math.cos(w * t), math.sin(w * t)
+            assert abs(y[0, 0, t, a] - (x[0, 0, t, a] * c - x[0, 0, t, b] * s)) < 1e-14
+            assert abs(y[0, 0, t, b] - (x[0, 0, t, a] * s + x[0, 0, t, b] * c)) < 1e-14
+
+
+def test_rope_scores_depend_only_on_the_relative_position():
+    """q_p . k_s after RoPE is unchanged when both positions move by the same
+    amount (pos0), and position 0 is the identity."""
+    B, H, T, D = 1, 2, 7, 8
+    q, k = _rand((B, H, T, D), 511), _rand((B, H, T, D), 512)
+    s0 = np.einsum("bhid,bhjd->bhij", oracle.rope_qknorm_fwd(q, norm=False),
+                   oracle.rope_qknorm_fwd(k, norm=False))
+    s9 = np.einsum("bhid,bhjd->bhij", oracle.rope_qknorm_fwd(q, pos0=9, norm=False),
+                   oracle.rope_qknorm_fwd(k, pos0=9, norm=False))
+    np.testing.assert_allclose(s9, s0, atol=1e-12)
+    y = oracle.rope_qknorm_fwd(q, norm=False)
+    assert np.array_equal(y[:, :, 0], q[:, :, 0])
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(q, axis=-1), atol=1e-13)
+
+
+@pytest.mark.parametrize("gain,eps", [(1.0, 1e-6), (1.2, 1e-6), (1.2, 0.0), (0.7, 0.5)])
+def test_qk_norm_against_torch_rms_norm(gain, eps):
+    """Norm only: PyTorch's fp64 rms_norm (no weight) times the gain."""
+    x = _rand((2, 3, 5, 16), 521)
+    y = oracle.rope_qknorm_fwd(x, rope=False, gain=gain, eps=eps)
+    ref = torch.nn.functional.rms_norm(torch.tensor(x), (16,), eps=eps).numpy() * gain
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-14)
+    if eps == 0.0:
+        np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), gain, atol=1e-14)
+
+
+def test_rope_and_norm_commute():
+    x = _rand((1, 2, 6, 8), 531)
+    both = oracle.rope_qknorm_fwd(x, pos0=2, gain=1.2)
+    rope_then_norm = oracle.rope_qknorm_fwd(oracle.rope_qknorm_fwd(x, pos0=2, norm=False),
+                                            rope=False, gain=1.2)
+    norm_then_rope = oracle.rope_qknorm_fwd(oracle.rope_qknorm_fwd(x, rope=False, gain=1.2),
+                                            pos0=2, norm=False)
+    np.testing.assert_allclose(both, rope_then_norm, atol=1e-14)
+    np.testing.assert_allclose(both, norm_then_rope, atol=1e-14)
+
+
+@pytest.mark.parametrize("rope,norm", [(True, False), (False, True), (True, True)])
+def test_rope_qknorm_backward_finite_differences(rope, norm):
+    B, H, T, D = 1, 2, 4, 6
+    x = _rand((B, H, T, D), 541)
+    dy = _rand((B, H, T, D), 542)
+    kw = dict(pos0=5, base=50.0, rope=rope, norm=norm, gain=1.2, eps=1e-3)
+    dx = oracle.rope_qknorm_bwd(x, dy, **kw)
+    h = 1e-6
+    for flat in range(x.size):
+        xp, xm = x.copy(), x.copy()
+        xp.flat[flat] += h
+        xm.flat[flat] -= h
+        fd = (np.sum(dy * oracle.rope_qknorm_fwd(xp, **kw)) -
+              np.sum(dy * oracle.rope_qknorm_fwd(xm, **kw))) / (2 * h)
+        assert abs(fd - dx.flat[flat]) < 1e-7 * max(1.0, abs(fd)), (flat, fd, dx.flat[flat])
