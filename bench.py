@@ -288,6 +288,82 @@ def decode_bench(args) -> int:
     return 0
 
 
+def rope_bench(args) -> int:
+    """RoPE + QK norm on q and k of the gpt2s shape, read from the c_attn output
+    layout [B, T, 3C] (as causal_attention_qkv does): the forward launch (read
+    q, k; write the results) and the gradient launch (read q, k and the two
+    incoming gradients; write dq, dk into the q and k thirds of dqkv).  Both are
+    bound by HBM bandwidth; algorithmic bytes per step = 10 * B*H*T*D * 2."""
+    import torch
+    import causal_head_self_amd as cat
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    cat.load_library()
+    c = workloads.ATTN_CONFIGS["gpt2s"]
+    B, H, T, D = c.B, c.H, c.T, c.D
+    dev = torch.device("cuda:0")
+    q, k, v, g = (t.to(dev) for t in workloads.config_inputs(c))
+    qkv = torch.cat([t.permute(0, 2, 1, 3).reshape(B, T, H * D) for t in (q, k, v)], dim=-1)
+    qv, kv, _ = cat.qkv_heads(qkv, H)
+    qo, ko = torch.empty_like(q), torch.empty_like(q)
+    dqkv = torch.empty_like(qkv)
+    dq, dk, _ = cat.qkv_heads(dqkv, H)
+    p = cat.Prologue()
+    stream = torch.cuda.current_stream()
+    names = ["rope_fwd", "rope_bwd"]
+
+    def run(n, evs=None):
+        for i in range(n):
+            if evs:
+                evs[i][0].record(stream)
+            cat.rope_qknorm_fwd(qv, kv, qo, ko, p, stream)
+            if evs:
+                evs[i][1].record(stream)
+            cat.rope_qknorm_bwd(qv, kv, g, g, dq, dk, p, stream)
+            if evs:
+                evs[i][2].record(stream)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    run(args.steps)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    run(args.steps, evs)
+    torch.cuda.synchronize()
+    kern = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+            for i, n in enumerate(names)}
+    elem = B * H * T * D
+    byt = {"rope_fwd": 4.0 * elem * 2, "rope_bwd": 6.0 * elem * 2}
+    gbs = (byt["rope_fwd"] + byt["rope_bwd"]) / (ms * 1e-3) / 1e9
+    dom = max(names, key=lambda n: kern[n])
+    ach = byt[dom] / (kern[dom] * 1e-3) / 1e9
+    out = {
+        "metric": "RoPE + QK-norm prologue (forward + gradient): algorithmic bytes per second",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"rope_gpt2s: RoPE (base 1e4) + QK norm (gain 1.2 / 1.0) on q, k "
+                                f"views of a [B={B}, T={T}, 3C={3 * H * D}] bf16 c_attn output, "
+                                f"H={H} D={D}"),
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "kernel_ms": {n: round(v_, 5) for n, v_ in kern.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": byt[dom]},
+        "cpu_baseline": None,
+        "l2_flushed": False,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,7 +371,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="gpt2s",
                     choices=["tiny", "gpt2s", "gpt400m", "long", "gpt2s_d128", "sublayer",
-                             "decode_gpt2s", "decode_gpt2s_b64", "decode_long"])
+                             "decode_gpt2s", "decode_gpt2s_b64", "decode_long", "rope_gpt2s"])
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window W (bf16, D 64/128): query i sees keys i-W < j <= i")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -313,6 +389,8 @@ def main() -> int:
         return sublayer_bench(args)
     if args.config.startswith("decode_"):
         return decode_bench(args)
+    if args.config == "rope_gpt2s":
+        return rope_bench(args)
 
     import torch
     import causal_head_self_amd as cat

@@ -14,12 +14,15 @@ the computation.  PyTorch supplies device memory and streams.
         fused [B, T, 3C] c_attn output, returning [B, T, C] with no layout copies
     attn_decode / decode_attention                          -- one new token per
         sequence against a [B, T_max, H, D] KV cache
+    rope_qknorm_fwd / rope_qknorm_bwd                       -- RoPE and QK norm on
+        query and key rows (also as causal_attention_qkv(..., prologue=Prologue()))
 
 Tensors are contiguous [B, H, T, D] (D in {32, 64}; 128 in bf16) of float32 or bfloat16 on
 the current GPU; lse and delta are float32 [B, H, T].
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 
 import torch
@@ -30,6 +33,7 @@ from ._lib import (ABI_VERSION, ATTN_BF16, ATTN_F32, EXPORTS, LIB_PATH, AttnErro
 __all__ = [
     "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
     "attn_bwd_strided", "attn_decode", "decode_workspace_bytes", "decode_attention",
+    "rope_qknorm_fwd", "rope_qknorm_bwd", "Prologue",
     "attn_status_str", "causal_attention", "causal_attention_qkv", "qkv_heads", "AttnError",
     "ATTN_F32", "ATTN_BF16", "load_library", "LIB_PATH", "EXPORTS", "ABI_VERSION",
 ]
@@ -159,7 +163,7 @@ def qkv_heads(qkv: torch.Tensor, n_head: int):
 
 class _CausalAttentionQKV(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, qkv, n_head, window):
+    def forward(ctx, qkv, n_head, window, prologue):
         if qkv.dim() != 3 or qkv.shape[-1] % (3 * n_head) != 0 or qkv.stride(-1) != 1:
             raise ValueError("qkv must be [B, T, 3C] with contiguous last dim and C % n_head == 0")
         qkv = qkv if qkv.is_contiguous() else qkv.contiguous()
@@ -169,15 +173,25 @@ class _CausalAttentionQKV(torch.autograd.Function):
         y = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
         o = y.view(B, T, n_head, C // n_head).permute(0, 2, 1, 3)  # [B, H, T, D] view of y
         lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
-        attn_fwd_strided(q, k, v, o, lse, window=window)
-        ctx.save_for_backward(qkv, y, lse)
+        if prologue is not None:  # rotated / normalised q and k, contiguous [B, H, T, D]
+            qa = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+            ka = torch.empty_like(qa)
+            rope_qknorm_fwd(q, k, qa, ka, prologue)
+        else:
+            qa, ka = q, k
+        attn_fwd_strided(qa, ka, v, o, lse, window=window)
+        if prologue is not None:
+            ctx.save_for_backward(qkv, y, lse, qa, ka)
+        else:
+            ctx.save_for_backward(qkv, y, lse)
         ctx.n_head = n_head
         ctx.window = window
+        ctx.prologue = prologue
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        qkv, y, lse = ctx.saved_tensors
+        qkv, y, lse = ctx.saved_tensors[:3]
         n_head = ctx.n_head
         B, T, C3 = qkv.shape
         C = C3 // 3
@@ -190,16 +204,70 @@ class _CausalAttentionQKV(torch.autograd.Function):
         dqkv = torch.empty_like(qkv)
         dq, dk, dv = qkv_heads(dqkv, n_head)
         delta = torch.empty_like(lse)
-        attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, window=ctx.window)
-        return dqkv, None, None
+        if ctx.prologue is None:
+            attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, window=ctx.window)
+        else:
+            qa, ka = ctx.saved_tensors[3:5]
+            dqa, dka = torch.empty_like(qa), torch.empty_like(ka)
+            attn_bwd_strided(qa, ka, v, o, lse, dO, dqa, dka, dv, delta, window=ctx.window)
+            rope_qknorm_bwd(q, k, dqa, dka, dq, dk, ctx.prologue)
+        return dqkv, None, None, None
 
 
-def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0) -> torch.Tensor:
+def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0,
+                         prologue: Prologue | None = None) -> torch.Tensor:
     """Causal attention on the fused c_attn output: qkv [B, T, 3C] (q, k, v
     chunks of C, each [B, T, H, D]) -> y [B, T, C] (heads merged), read and
     written in place through strided views (bf16, head dim 64 or 128).  window W > 0
-    restricts query i to keys i-W < j <= i (sliding window)."""
-    return _CausalAttentionQKV.apply(qkv, n_head, int(window))
+    restricts query i to keys i-W < j <= i (sliding window).  prologue applies
+    RoPE and/or QK norm to q and k first (one extra read and write of q and k
+    each way)."""
+    return _CausalAttentionQKV.apply(qkv, n_head, int(window), prologue)
+
+
+@dataclasses.dataclass(frozen=True)
+class Prologue:
+    """RoPE and/or QK norm applied to q and k before the attention (nanochat,
+    section 9): RoPE turns column pair (i, i + D/2) at position pos0 + t by
+    (pos0 + t) * base^(-2i/D); QK norm divides by sqrt(mean(x^2) + eps) and
+    multiplies by q_gain (queries) or k_gain (keys)."""
+    rope: bool = True
+    qk_norm: bool = True
+    pos0: int = 0
+    base: float = 10000.0
+    q_gain: float = 1.2
+    k_gain: float = 1.0
+    eps: float = 1e-6
+
+    @property
+    def flags(self) -> int:
+        return (1 if self.rope else 0) | (2 if self.qk_norm else 0)
+
+    def args(self):
+        return (int(self.pos0), float(self.base), float(self.q_gain), float(self.k_gain),
+                float(self.eps), self.flags)
+
+
+def rope_qknorm_fwd(q, k, q_out, k_out, prologue: "Prologue" = None, stream=None) -> None:
+    """C ABI attn_rope_qknorm_fwd on [B, H, T, D] views (bf16, D 64 or 128)."""
+    p = prologue or Prologue()
+    B, H, T, D = _shape(q)
+    rc = load_library().attn_rope_qknorm_fwd(
+        _view(q, "q"), _view(k, "k"), _view(q_out, "q_out"), _view(k_out, "k_out"), B, H, T, D,
+        *p.args(), _dtype_code(q), _stream(stream))
+    check(rc)
+
+
+def rope_qknorm_bwd(q, k, dq_out, dk_out, dq, dk, prologue: "Prologue" = None,
+                    stream=None) -> None:
+    """C ABI attn_rope_qknorm_bwd: dq, dk from the gradients dq_out, dk_out of
+    the forward's results."""
+    p = prologue or Prologue()
+    B, H, T, D = _shape(q)
+    rc = load_library().attn_rope_qknorm_bwd(
+        _view(q, "q"), _view(k, "k"), _view(dq_out, "dq_out"), _view(dk_out, "dk_out"),
+        _view(dq, "dq"), _view(dk, "dk"), B, H, T, D, *p.args(), _dtype_code(q), _stream(stream))
+    check(rc)
 
 
 def decode_workspace_bytes(B: int, H: int, T_max: int, D: int) -> int:

@@ -27,13 +27,17 @@ STATUS = {
     9: "ATTN_ERR_HIP",
     10: "ATTN_ERR_LAYOUT",
     11: "ATTN_ERR_WORKSPACE",
+    12: "ATTN_ERR_PARAM",
 }
+
+ATTN_ROPE = 1
+ATTN_QK_NORM = 2
 
 # every symbol include/causal_attn.h declares
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
-           "attn_bwd_strided", "attn_decode", "attn_decode_workspace_bytes", "attn_status_str",
-           "attn_abi_version")
-ABI_VERSION = (1 << 16) | 2
+           "attn_bwd_strided", "attn_decode", "attn_decode_workspace_bytes",
+           "attn_rope_qknorm_fwd", "attn_rope_qknorm_bwd", "attn_status_str", "attn_abi_version")
+ABI_VERSION = (1 << 16) | 3
 
 
 class AttnView(ctypes.Structure):
@@ -86,6 +90,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_decode.argtypes = ([_vp] * 7 + [ctypes.c_size_t] + [_int] * 5 +
                                 [ctypes.c_float, _int, _vp])
     lib.attn_decode.restype = _int
+    _rope_tail = [_int] * 5 + [ctypes.c_float] * 4 + [_int, _int, _vp]
+    lib.attn_rope_qknorm_fwd.argtypes = [AttnView] * 4 + _rope_tail
+    lib.attn_rope_qknorm_fwd.restype = _int
+    lib.attn_rope_qknorm_bwd.argtypes = [AttnView] * 6 + _rope_tail
+    lib.attn_rope_qknorm_bwd.restype = _int
     lib.attn_status_str.argtypes = [_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []

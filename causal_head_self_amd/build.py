@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcausal_attn.so")
-SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_bf16_d64.hip", "attn_decode.hip", "attn_f32.hip"]
+SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_bf16_d64.hip", "attn_decode.hip", "attn_f32.hip",
+           "attn_rope.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

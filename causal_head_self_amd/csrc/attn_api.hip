@@ -175,6 +175,37 @@ cattn::Strides strides_of(const attn_view_t& v)
 
 }  // namespace
 
+namespace {
+
+int rope_params_ok(int T, int pos0, float base, float q_gain, float k_gain, float eps, int flags)
+{
+    if (flags < 0 || flags > 3 || pos0 < 0 || (long long)pos0 + T > (1LL << 24)) return 0;
+    if ((flags & ATTN_ROPE) && (!isfinite(base) || !(base > 0.0f))) return 0;
+    if (!isfinite(q_gain) || !isfinite(k_gain) || !isfinite(eps) || eps < 0.0f) return 0;
+    return 1;
+}
+
+cattn::RopeArgs rope_args(int B, int H, int T, int D, int pos0, float base, float q_gain,
+                          float k_gain, float eps, int flags, bool grad)
+{
+    cattn::RopeArgs a{};
+    a.B = B;
+    a.H = H;
+    a.T = T;
+    a.D = D;
+    a.pos0 = pos0;
+    a.flags = flags;
+    a.q_gain = q_gain;
+    a.k_gain = k_gain;
+    a.eps = eps;
+    a.grad = grad;
+    for (int i = 0; i < D / 2; ++i)  // revolutions per position, base^(-2i/D) / (2 pi)
+        a.freqs.f[i] = pow((double)base, -2.0 * (double)i / (double)D) / 6.283185307179586;
+    return a;
+}
+
+}  // namespace
+
 extern "C" {
 
 int attn_abi_version(void) { return CAUSAL_ATTN_ABI_VERSION; }
@@ -196,6 +227,9 @@ const char* attn_status_str(int st)
         return "strided views need bf16, D = 64 or 128, strides that are non-negative multiples of 8 "
                "with stride_t >= D, and T * stride_t * 2 < 2^32";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes()";
+    case ATTN_ERR_PARAM:
+        return "RoPE / QK norm: flags must be 0..3, 0 <= pos0 and pos0 + T <= 2^24, rope_base "
+               "finite and > 0, gains finite, eps finite and >= 0";
     default: return "unknown status";
     }
 }
@@ -415,6 +449,56 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     a.window = window;
     a.scale = scale;
     return status(cattn::launch_decode_bf16(a, (hipStream_t)stream));
+}
+
+int attn_rope_qknorm_fwd(attn_view_t q, attn_view_t k, attn_view_t q_out, attn_view_t k_out,
+                         int B, int H, int T, int D, int pos0, float rope_base, float q_gain,
+                         float k_gain, float eps, int flags, int dtype, void* stream)
+{
+    const VSpan vs[4] = {{&q, false}, {&k, false}, {&q_out, true}, {&k_out, true}};
+    int st = validate_views(vs, 4, nullptr, 0, B, H, T, D, 1.0f, dtype);
+    if (st != ATTN_OK) return st;
+    if (!rope_params_ok(T, pos0, rope_base, q_gain, k_gain, eps, flags)) return ATTN_ERR_PARAM;
+    cattn::RopeArgs a = rope_args(B, H, T, D, pos0, rope_base, q_gain, k_gain, eps, flags, false);
+    a.q = q.data;
+    a.k = k.data;
+    a.q_out = q_out.data;
+    a.k_out = k_out.data;
+    a.dq_in = q.data;  // unused by the forward
+    a.dk_in = k.data;
+    a.sq = strides_of(q);
+    a.sk = strides_of(k);
+    a.sqo = strides_of(q_out);
+    a.sko = strides_of(k_out);
+    a.sdq = a.sq;
+    a.sdk = a.sk;
+    return status(cattn::launch_rope_qknorm(a, (hipStream_t)stream));
+}
+
+int attn_rope_qknorm_bwd(attn_view_t q, attn_view_t k, attn_view_t dq_out, attn_view_t dk_out,
+                         attn_view_t dq, attn_view_t dk, int B, int H, int T, int D, int pos0,
+                         float rope_base, float q_gain, float k_gain, float eps, int flags,
+                         int dtype, void* stream)
+{
+    const VSpan vs[6] = {{&q, false}, {&k, false}, {&dq_out, false}, {&dk_out, false},
+                         {&dq, true}, {&dk, true}};
+    int st = validate_views(vs, 6, nullptr, 0, B, H, T, D, 1.0f, dtype);
+    if (st != ATTN_OK) return st;
+    if (!rope_params_ok(T, pos0, rope_base, q_gain, k_gain, eps, flags)) return ATTN_ERR_PARAM;
+    cattn::RopeArgs a = rope_args(B, H, T, D, pos0, rope_base, q_gain, k_gain, eps, flags, true);
+    a.q = q.data;
+    a.k = k.data;
+    a.q_out = dq.data;
+    a.k_out = dk.data;
+    a.dq_in = dq_out.data;
+    a.dk_in = dk_out.data;
+    a.sq = strides_of(q);
+    a.sk = strides_of(k);
+    a.sqo = strides_of(dq);
+    a.sko = strides_of(dk);
+    a.sdq = strides_of(dq_out);
+    a.sdk = strides_of(dk_out);
+    return status(cattn::launch_rope_qknorm(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

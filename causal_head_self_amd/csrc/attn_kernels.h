@@ -51,6 +51,29 @@ struct DecodeArgs {
 int decode_slices(int T_max);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
 
+// RoPE / QK norm on query and key rows (forward, or gradient when grad is set).
+struct RopeFreqs {
+    double f[64];  // base^(-2i/D) / (2 pi), i < D/2: revolutions per position
+};
+
+struct RopeArgs {
+    const void* q;       // [B][H][T][D] views (strides sq, sk)
+    const void* k;
+    void* q_out;         // forward: results; gradient: dq, dk (strides sqo, sko)
+    void* k_out;
+    const void* dq_in;   // gradient only: d(loss)/d(forward result)
+    const void* dk_in;
+    Strides sq, sk, sqo, sko, sdq, sdk;
+    RopeFreqs freqs;
+    int B, H, T, D;
+    int pos0;            // position of row t = pos0 + t
+    int flags;           // bit 0: RoPE, bit 1: QK norm
+    float q_gain, k_gain, eps;
+    bool grad;
+};
+
+hipError_t launch_rope_qknorm(const RopeArgs& a, hipStream_t st);
+
 // launch_dq_* computes delta (from o and dO) as well as dq.
 hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dq_bf16(const AttnArgs& a, hipStream_t st);

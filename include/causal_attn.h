@@ -68,7 +68,8 @@ typedef enum {
     ATTN_ERR_ALIAS = 8,         /* an output overlaps an input or output    */
     ATTN_ERR_HIP = 9,           /* a kernel launch failed                   */
     ATTN_ERR_LAYOUT = 10,       /* strided views: unsupported dtype/D or strides */
-    ATTN_ERR_WORKSPACE = 11     /* decode: workspace smaller than required  */
+    ATTN_ERR_WORKSPACE = 11,    /* decode: workspace smaller than required  */
+    ATTN_ERR_PARAM = 12         /* RoPE / QK norm: flags, base, gain, eps or pos0 */
 } attn_status_t;
 
 /* Forward.  Reads q, k, v; writes o ([B][H][T][D], dtype) and lse
@@ -193,13 +194,43 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
                 void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int H,
                 int T_max, int D, int window, float scale, int dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * RoPE and QK norm on the query and key rows.  nanochat, section 9, lists
+ * RoPE position encoding and QK norm (x1.2) among its attention's parts; the
+ * pages print no formulas, so these are the standard forms:
+ *   RoPE (flags & ATTN_ROPE): the column pair (i, i + D/2), i < D/2, of the
+ *     row at position p = pos0 + t is turned by p * rope_base^(-2i/D):
+ *       y_i = x_i cos - x_{i+D/2} sin,   y_{i+D/2} = x_i sin + x_{i+D/2} cos
+ *   QK norm (flags & ATTN_QK_NORM): the row is divided by
+ *     sqrt(mean_d x_d^2 + eps) (no learned weight) and multiplied by q_gain
+ *     for queries, k_gain for keys (the pages quote 1.2).
+ * The two commute (rotation keeps the root mean square).  Queries and keys go
+ * through one launch; attention then runs on the results (q_out, k_out).
+ *
+ * Views as for the strided entry points (bf16, D = 64 or 128).  fwd reads q, k
+ * and writes q_out, k_out; bwd reads q, k (the forward's inputs) and dq_out,
+ * dk_out (gradients with respect to q_out, k_out) and writes dq, dk.  Outputs
+ * must not overlap inputs or each other (ATTN_ERR_ALIAS).  ATTN_ERR_PARAM:
+ * flags outside 0..3, pos0 < 0 or pos0 + T > 2^24, rope_base not finite or
+ * <= 0 (with ATTN_ROPE), gains not finite, eps not finite or < 0.  fp32
+ * arithmetic; one kernel launch each; no synchronisation. */
+#define ATTN_ROPE 1
+#define ATTN_QK_NORM 2
+int attn_rope_qknorm_fwd(attn_view_t q, attn_view_t k, attn_view_t q_out, attn_view_t k_out,
+                         int B, int H, int T, int D, int pos0, float rope_base, float q_gain,
+                         float k_gain, float eps, int flags, int dtype, void* stream);
+int attn_rope_qknorm_bwd(attn_view_t q, attn_view_t k, attn_view_t dq_out, attn_view_t dk_out,
+                         attn_view_t dq, attn_view_t dk, int B, int H, int T, int D, int pos0,
+                         float rope_base, float q_gain, float k_gain, float eps, int flags,
+                         int dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_str(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 2)
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

@@ -41,11 +41,11 @@ def test_abi_version_and_status_strings():
     lib = cat.load_library()
     assert lib.attn_abi_version() == _lib.ABI_VERSION
     seen = set()
-    for code in range(0, 12):
+    for code in range(0, 13):
         s = cat.attn_status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 12
+    assert len(seen) == 13
     assert cat.attn_status_str(1234) == "unknown status"
     assert cat.attn_status_str(-1) == "unknown status"
 
@@ -357,3 +357,38 @@ def test_decode_validation_order_and_codes():
     assert _dec(o=P[3]) == 8                      # o over cache_lens
     # D = 128 passes the head-dim check (the misaligned q is what fires)
     assert _dec(D=128, ws_bytes=_ws(D=128), q=P[0] + 8) == 5
+
+
+# ---------------------------------------------------------------------------
+# RoPE / QK norm (attn_rope_qknorm_fwd / _bwd): invalid arguments only
+# ---------------------------------------------------------------------------
+
+def _rope(fwd=True, views=None, B=B_, H=H_, T=T_, D=D_, pos0=0, base=10000.0, qg=1.2, kg=1.0,
+          eps=1e-6, flags=3, dtype=1):
+    lib = cat.load_library()
+    if fwd:
+        v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3])]
+        return lib.attn_rope_qknorm_fwd(*v, B, H, T, D, pos0, base, qg, kg, eps, flags, dtype, None)
+    v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3]), _v(P[4]), _v(P[5])]
+    return lib.attn_rope_qknorm_bwd(*v, B, H, T, D, pos0, base, qg, kg, eps, flags, dtype, None)
+
+
+@pytest.mark.parametrize("fwd", [True, False])
+def test_rope_qknorm_validation(fwd):
+    n = 4 if fwd else 6
+    for i in range(n):  # a NULL view
+        views = [_v(P[j]) for j in range(n)]
+        views[i] = _v(None)
+        assert _rope(fwd, views=views) == 1
+    assert _rope(fwd, B=0) == 2
+    assert _rope(fwd, dtype=0) == 10 and _rope(fwd, D=32) == 10 and _rope(fwd, D=48) == 3
+    for kw in (dict(flags=4), dict(flags=-1), dict(pos0=-1), dict(pos0=2 ** 24), dict(base=0.0),
+               dict(base=float("inf")), dict(qg=float("nan")), dict(kg=float("inf")),
+               dict(eps=-1e-3), dict(eps=float("nan"))):
+        assert _rope(fwd, **kw) == 12, kw
+    views = [_v(P[j]) for j in range(n)]
+    views[n - 1] = _v(P[0])                       # an output on an input
+    assert _rope(fwd, views=views) == 8
+    views = [_v(P[j]) for j in range(n)]
+    views[n - 1] = _v(P[n - 2])                   # the two outputs on each other
+    assert _rope(fwd, views=views) == 8
