@@ -61,6 +61,17 @@ def _bind(path: str):
     lib.oracle_rope_qknorm_bwd.argtypes = [_dp] * 3 + [_i64] * 5 + [ctypes.c_double, _i64, _i64,
                                                                     ctypes.c_double, ctypes.c_double]
     lib.oracle_rope_qknorm_bwd.restype = None
+    _u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.oracle_philox4x32_10.argtypes = [_u32p, _u32p, _u32p]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_dropout_keep.argtypes = [ctypes.c_uint64, _i64, _i64, _i64, _i64]
+    lib.oracle_dropout_keep.restype = ctypes.c_int
+    lib.oracle_attn_fwd_dropout.argtypes = ([_dp] * 5 + [_i64] * 4 +
+                                            [ctypes.c_double, _i64, _i64, ctypes.c_uint64, _i64])
+    lib.oracle_attn_fwd_dropout.restype = None
+    lib.oracle_attn_bwd_dropout.argtypes = ([_dp] * 8 + [_i64] * 4 +
+                                            [ctypes.c_double, _i64, _i64, ctypes.c_uint64, _i64])
+    lib.oracle_attn_bwd_dropout.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -163,6 +174,53 @@ def attn_decode(q, k_cache, v_cache, lens, scale: float, window: int = 0, nthrea
                                _p(o), _p(lse), B, H, Tmax, D, float(scale), int(window),
                                int(nthreads))
     return o, lse
+
+
+def dropout_threshold(p: float) -> int:
+    """p16 = round(p * 65536), the integer threshold of a 16-bit draw (0 <= p < 1)."""
+    if not 0.0 <= p < 1.0:
+        raise ValueError("dropout p must be in [0, 1)")
+    return min(int(np.floor(p * 65536.0 + 0.5)), 65535)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of a 4-word counter under a 2-word key -> 4 words."""
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    kk = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    _load().oracle_philox4x32_10(c, kk, out)
+    return [int(x) for x in out]
+
+
+def dropout_keep(seed: int, p16: int, bh: int, i: int, j: int) -> bool:
+    return bool(_load().oracle_dropout_keep(int(seed), int(p16), int(bh), int(i), int(j)))
+
+
+def attn_fwd_dropout(q, k, v, scale: float, p: float, seed: int, window: int = 0,
+                     nthreads: int = 0, lib: str | None = None):
+    """Forward with attention dropout (see oracle.c): returns (o, lse)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, D = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    _load(lib).oracle_attn_fwd_dropout(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, T, D,
+                                    float(scale), int(window), dropout_threshold(p),
+                                    int(seed) & (2 ** 64 - 1), int(nthreads))
+    return o, lse
+
+
+def attn_bwd_dropout(q, k, v, dO, scale: float, p: float, seed: int, window: int = 0,
+                     nthreads: int = 0, lib: str | None = None):
+    """Backward with attention dropout: returns (dq, dk, dv, delta)."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, H, T, D = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    delta = np.empty((B, H, T), dtype=np.float64)
+    _load(lib).oracle_attn_bwd_dropout(_p(q), _p(k), _p(v), _p(dO), _p(dq), _p(dk), _p(dv),
+                                    _p(delta), B, H, T, D, float(scale), int(window),
+                                    dropout_threshold(p), int(seed) & (2 ** 64 - 1),
+                                    int(nthreads))
+    return dq, dk, dv, delta
 
 
 def rope_qknorm_fwd(x, pos0: int = 0, base: float = 10000.0, rope: bool = True,

@@ -181,6 +181,148 @@ void oracle_attn_bwd(const double* q, const double* k, const double* v,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Attention dropout.  CS336 tutorial, section 5.1: CausalSelfAttention      */
+/* applies its nn.Dropout to the softmax weights, att = dropout(att), before  */
+/* att @ v (every configuration on the pages sets p = 0).  In training mode   */
+/* that is inverted dropout: each weight is kept with probability 1 - p and  */
+/* scaled by 1 / (1 - p), else zeroed; the softmax normaliser and lse are     */
+/* those of the undropped weights.                                            */
+/* The keep decisions must be the same in the forward and the backward, so   */
+/* they come from a counter-based generator, Philox4x32-10 (Salmon, Moraes,  */
+/* Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011;     */
+/* the Random123 definition), read as follows (this scheme is a choice):     */
+/*   counter (j / 8, i, b * H + h, 0), key (seed mod 2^32, seed / 2^32);      */
+/*   element j % 8 takes 16-bit half (j % 2) of output word (j % 8) / 2;      */
+/*   kept iff that value >= p16, where p16 = round(p * 65536) < 65536;        */
+/*   kept weights are scaled by 65536 / (65536 - p16).                        */
+/* ------------------------------------------------------------------------ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+        const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+        const uint32_t y1 = (uint32_t)p1;
+        const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+        const uint32_t y3 = (uint32_t)p0;
+        x0 = y0;
+        x1 = y1;
+        x2 = y2;
+        x3 = y3;
+        k0 += 0x9E3779B9u;  /* the key schedule (Weyl sequence) */
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = x0;
+    out[1] = x1;
+    out[2] = x2;
+    out[3] = x3;
+}
+
+/* 1 if weight (bh, i, j) is kept. */
+int oracle_dropout_keep(uint64_t seed, int64_t p16, int64_t bh, int64_t i, int64_t j)
+{
+    const uint32_t ctr[4] = {(uint32_t)(j / 8), (uint32_t)i, (uint32_t)bh, 0u};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t r[4];
+    oracle_philox4x32_10(ctr, key, r);
+    const uint32_t u = (r[(j % 8) / 2] >> (16 * (j % 2))) & 0xFFFFu;
+    return (int64_t)u >= p16;
+}
+
+/* Forward with dropout: o_i = sum_j P_ij keep_ij / (1 - p) v_j; lse as without. */
+void oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, double* o,
+                             double* lse, int64_t B, int64_t H, int64_t T, int64_t D,
+                             double scale, int64_t window, int64_t p16, uint64_t seed,
+                             int64_t nthreads)
+{
+    const double keep_scale = 65536.0 / (65536.0 - (double)p16);
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double* Qh = q + bh * T * D;
+        const double* Kh = k + bh * T * D;
+        const double* Vh = v + bh * T * D;
+        double* O = o + bh * T * D;
+        double* s = (double*)malloc((size_t)T * sizeof(double));
+        double* w = (double*)malloc((size_t)T * sizeof(double));
+        for (int64_t i = 0; i < T; ++i) {
+            double m, Z;
+            const int64_t j0 = first_key(i, window);
+            causal_softmax_row(Qh + i * D, Kh, i, j0, D, scale, s, w, &m, &Z);
+            for (int64_t j = j0; j <= i; ++j)  /* the dropped weights */
+                w[j] = oracle_dropout_keep(seed, p16, bh, i, j) ? w[j] * keep_scale : 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                double sum = 0.0;
+                for (int64_t j = j0; j <= i; ++j) sum += w[j] * Vh[j * D + d];
+                O[i * D + d] = sum;
+            }
+            lse[bh * T + i] = m + log(Z);
+        }
+        free(s);
+        free(w);
+    }
+}
+
+/* Backward with dropout, for the forward above (pd = the dropped weights):
+ *   dv_j  = sum_i pd_ij dO_i
+ *   dP_ij = keep_ij / (1 - p) * (dO_i . v_j)     (gradient of the undropped P)
+ *   Delta_i = sum_j P_ij dP_ij  (= dO_i . o_i)
+ *   dS_ij = P_ij (dP_ij - Delta_i);  dq, dk as without dropout. */
+void oracle_attn_bwd_dropout(const double* q, const double* k, const double* v,
+                             const double* dO, double* dq, double* dk, double* dv, double* delta,
+                             int64_t B, int64_t H, int64_t T, int64_t D, double scale,
+                             int64_t window, int64_t p16, uint64_t seed, int64_t nthreads)
+{
+    const double keep_scale = 65536.0 / (65536.0 - (double)p16);
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double* Qh = q + bh * T * D;
+        const double* Kh = k + bh * T * D;
+        const double* Vh = v + bh * T * D;
+        const double* Gh = dO + bh * T * D;
+        double* dQh = dq + bh * T * D;
+        double* dKh = dk + bh * T * D;
+        double* dVh = dv + bh * T * D;
+        double* s = (double*)malloc((size_t)T * sizeof(double));
+        double* w = (double*)malloc((size_t)T * sizeof(double));
+        double* gw = (double*)malloc((size_t)T * sizeof(double));
+        double* mk = (double*)malloc((size_t)T * sizeof(double));
+        memset(dKh, 0, (size_t)(T * D) * sizeof(double));
+        memset(dVh, 0, (size_t)(T * D) * sizeof(double));
+        for (int64_t i = 0; i < T; ++i) {
+            double m, Z;
+            const int64_t j0 = first_key(i, window);
+            causal_softmax_row(Qh + i * D, Kh, i, j0, D, scale, s, w, &m, &Z);
+            double Dl = 0.0;
+            for (int64_t j = j0; j <= i; ++j) {
+                mk[j] = oracle_dropout_keep(seed, p16, bh, i, j) ? keep_scale : 0.0;
+                double sum = 0.0;
+                for (int64_t d = 0; d < D; ++d) sum += Gh[i * D + d] * Vh[j * D + d];
+                gw[j] = mk[j] * sum;
+                Dl += w[j] * gw[j];
+            }
+            delta[bh * T + i] = Dl;
+            for (int64_t d = 0; d < D; ++d) dQh[i * D + d] = 0.0;
+            for (int64_t j = j0; j <= i; ++j) {
+                const double ds = w[j] * (gw[j] - Dl);
+                for (int64_t d = 0; d < D; ++d) {
+                    dQh[i * D + d] += scale * ds * Kh[j * D + d];
+                    dKh[j * D + d] += scale * ds * Qh[i * D + d];
+                    dVh[j * D + d] += w[j] * mk[j] * Gh[i * D + d];
+                }
+            }
+        }
+        free(s);
+        free(w);
+        free(gw);
+        free(mk);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Decode: one new token per sequence against its key/value cache.            */
 /* nanochat, section 8 (inference engine): the KV cache is kept in FA3's      */
 /* native (B, T, H, D) layout; a prompt is prefilled into it, then tokens are */

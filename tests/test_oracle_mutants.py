@@ -76,6 +76,14 @@ MUTANTS = {
                                     "dz[d] = gain / rms * G[d];"),
     "rope_bwd_not_transposed": ("DX[i] = dz[i] * c + dz[i + half] * s;",
                                 "DX[i] = dz[i] * c - dz[i + half] * s;"),
+    "philox_key_schedule": ("k1 += 0xBB67AE85u;", "k1 += 0x9E3779B9u;"),
+    "philox_word_order": ("const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;",
+                          "const uint32_t y0 = (uint32_t)(p0 >> 32) ^ x1 ^ k0;"),
+    "dropout_counter_swapped": ("const uint32_t ctr[4] = {(uint32_t)(j / 8), (uint32_t)i, (uint32_t)bh, 0u};",
+                                "const uint32_t ctr[4] = {(uint32_t)i, (uint32_t)(j / 8), (uint32_t)bh, 0u};"),
+    "dropout_unscaled": ("w[j] = oracle_dropout_keep(seed, p16, bh, i, j) ? w[j] * keep_scale : 0.0;",
+                         "w[j] = oracle_dropout_keep(seed, p16, bh, i, j) ? w[j] : 0.0;"),
+    "dropout_bwd_mask_not_on_dp": ("gw[j] = mk[j] * sum;", "gw[j] = sum;"),
     "weight_grad_transposed": ("for (int64_t c = 0; c < C; ++c) dWp[cp * C + c] += av * dy[n * C + c];",
                                "for (int64_t c = 0; c < C; ++c) dWp[c * C + cp] += av * dy[n * C + c];"),
 }
@@ -99,6 +107,9 @@ BATTERY = [
     pins.test_rope_four_columns_pairs_and_frequencies,
     lambda: pins.test_qk_norm_against_torch_rms_norm(1.2, 1e-6),
     lambda: pins.test_rope_qknorm_backward_finite_differences(True, True),
+    pins.test_philox_known_answer_vectors,
+    pins.test_dropout_keep_follows_the_stated_draw_and_rate,
+    lambda: pins.test_dropout_against_torch_ops_with_the_same_mask(0.3, 3),
 ]
 
 

@@ -630,3 +630,113 @@ def test_rope_qknorm_backward_finite_differences(rope, norm):
         fd = (np.sum(dy * oracle.rope_qknorm_fwd(xp, **kw)) -
               np.sum(dy * oracle.rope_qknorm_fwd(xm, **kw))) / (2 * h)
         assert abs(fd - dx.flat[flat]) < 1e-7 * max(1.0, abs(fd)), (flat, fd, dx.flat[flat])
+
+
+# --------------------------------------------------------------------------
+# attention dropout (CS336 section 5.1: att = dropout(att) before att @ v)
+# with keep decisions from Philox4x32-10
+# --------------------------------------------------------------------------
+
+# Published known-answer vectors of Philox4x32-10 (Random123's kat_vectors,
+# the reference implementation of Salmon et al., SC 2011):
+# (counter, key) -> output
+PHILOX_KAT = [
+    ((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+
+
+def test_philox_known_answer_vectors():
+    for ctr, key, out in PHILOX_KAT:
+        assert tuple(oracle.philox4x32_10(ctr, key)) == out
+
+
+def test_dropout_keep_follows_the_stated_draw_and_rate():
+    """Element (bh, i, j) reads 16-bit half j % 2 of word (j % 8) / 2 of
+    Philox(counter (j/8, i, bh, 0), key = the seed's two halves); over many
+    elements the kept fraction is 1 - p16 / 65536 within 5 sigma."""
+    seed = 0x0123456789ABCDEF
+    p16 = oracle.dropout_threshold(0.3)
+    assert p16 == 19661
+    kept = n = 0
+    for bh in range(3):
+        for i in range(0, 40, 7):
+            for j in range(0, 64):
+                r = oracle.philox4x32_10((j // 8, i, bh, 0), (seed & 0xFFFFFFFF, seed >> 32))
+                u = (r[(j % 8) // 2] >> (16 * (j % 2))) & 0xFFFF
+                k = oracle.dropout_keep(seed, p16, bh, i, j)
+                assert k == (u >= p16)
+                kept += k
+                n += 1
+    rate = 1 - p16 / 65536
+    assert abs(kept - n * rate) < 5 * math.sqrt(n * rate * (1 - rate))
+
+
+def test_dropout_zero_is_the_plain_attention():
+    shape = (2, 2, 9, 4)
+    q, k, v = _qkv(shape, seed=601)
+    dO = _rand(shape, 602)
+    o, lse = oracle.attn_fwd(q, k, v, 0.5, window=4)
+    od, lsed = oracle.attn_fwd_dropout(q, k, v, 0.5, 0.0, seed=7, window=4)
+    assert np.array_equal(o, od) and np.array_equal(lse, lsed)
+    g = oracle.attn_bwd(q, k, v, dO, 0.5, window=4)
+    gd = oracle.attn_bwd_dropout(q, k, v, dO, 0.5, 0.0, seed=7, window=4)
+    for a, b in zip(g, gd):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("p,window", [(0.1, 0), (0.5, 0), (0.3, 3)])
+def test_dropout_against_torch_ops_with_the_same_mask(p, window):
+    """PyTorch fp64 ops with autograd: masked softmax, times keep / (1 - p16 /
+    65536), times v.  lse is that of the undropped weights; Delta equals
+    dO . o of the dropped output."""
+    B, H, T, D = 2, 2, 10, 3
+    q, k, v = _qkv((B, H, T, D), seed=611)
+    dO = _rand((B, H, T, D), 612)
+    s, seed = 0.6, 0xDEADBEEF12345
+    p16 = oracle.dropout_threshold(p)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    vis = (j <= i) & ((j > i - window) if window else True)
+    keep = np.array([[[[oracle.dropout_keep(seed, p16, b * H + h, a, c) for c in range(T)]
+                       for a in range(T)] for h in range(H)] for b in range(B)], dtype=np.float64)
+    mult = torch.tensor(keep * (65536.0 / (65536 - p16)))
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    sc = s * tq @ tk.transpose(-1, -2)
+    sc = sc.masked_fill(~torch.tensor(vis), float("-inf"))
+    to = (torch.softmax(sc, dim=-1) * mult) @ tv
+    to.backward(torch.tensor(dO))
+    o, lse = oracle.attn_fwd_dropout(q, k, v, s, p, seed, window=window)
+    dq, dk, dv, delta = oracle.attn_bwd_dropout(q, k, v, dO, s, p, seed, window=window)
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(sc, dim=-1).detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(delta, np.sum(dO * o, axis=-1), atol=1e-12)
+    assert 0 < keep[vis[None, None].repeat(B, 0).repeat(H, 1)].mean() < 1
+
+
+def test_dropout_backward_finite_differences():
+    shape = (1, 2, 7, 3)
+    q, k, v = _qkv(shape, seed=621)
+    dO = _rand(shape, 622)
+    kw = dict(p=0.4, seed=99, window=0)
+    dq, dk, dv, _ = oracle.attn_bwd_dropout(q, k, v, dO, 0.5, **kw)
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for flat in range(x.size):
+            xp, xm = x.copy(), x.copy()
+            xp.flat[flat] += h
+            xm.flat[flat] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            fp = np.sum(dO * oracle.attn_fwd_dropout(args_p["q"], args_p["k"], args_p["v"], 0.5,
+                                                     **kw)[0])
+            fm = np.sum(dO * oracle.attn_fwd_dropout(args_m["q"], args_m["k"], args_m["v"], 0.5,
+                                                     **kw)[0])
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - g.flat[flat]) < 1e-7 * max(1.0, abs(fd)), (name, flat)
