@@ -374,6 +374,8 @@ def main() -> int:
                              "decode_gpt2s", "decode_gpt2s_b64", "decode_long", "rope_gpt2s"])
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window W (bf16, D 64/128): query i sees keys i-W < j <= i")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="attention dropout probability (bf16, D 64/128; Philox seed 42)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
@@ -413,21 +415,23 @@ def main() -> int:
     scale = cfg.scale
     stream = torch.cuda.current_stream()
 
-    W = args.window
-    if W < 0 or (W and (cfg.dtype != "bf16" or D not in (64, 128))):
-        print("bench.py: --window needs W >= 0 and a bf16 workload with D 64 or 128",
-              file=sys.stderr)
+    W, P = args.window, args.dropout
+    if W < 0 or not 0.0 <= P < 1.0 or ((W or P) and (cfg.dtype != "bf16" or D not in (64, 128))):
+        print("bench.py: --window needs W >= 0, --dropout 0 <= p < 1, and either a bf16 "
+              "workload with D 64 or 128", file=sys.stderr)
         return 2
+    strided = bool(W or P)
 
     def fwd():
-        if W:
-            cat.attn_fwd_strided(q, k, v, o, lse, scale, stream, window=W)
+        if strided:
+            cat.attn_fwd_strided(q, k, v, o, lse, scale, stream, window=W, dropout_p=P, seed=42)
         else:
             cat.attn_fwd(q, k, v, o, lse, scale, stream)
 
     def bwd():
-        if W:
-            cat.attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream, window=W)
+        if strided:
+            cat.attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream, window=W,
+                                 dropout_p=P, seed=42)
         else:
             cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream)
 
@@ -483,7 +487,8 @@ def main() -> int:
     dominant = max(names, key=lambda n: kern_ms[n])
     achieved = work[dominant]["flops"] / (kern_ms[dominant] * 1e-3) / 1e12
     sha = kernel_source_sha()
-    workload_name = f"{cfg.name}_B{B}_H{H}_T{T}_D{D}_{cfg.dtype}" + (f"_W{W}" if W else "")
+    workload_name = (f"{cfg.name}_B{B}_H{H}_T{T}_D{D}_{cfg.dtype}" + (f"_W{W}" if W else "")
+                     + (f"_drop{P:g}" if P else ""))
     roofline = {
         "bound": "mfma",
         "kernel": dominant,
@@ -501,7 +506,7 @@ def main() -> int:
             threads = min(16, len(os.sched_getaffinity(0)))
         except AttributeError:
             threads = min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(cfg, host_inputs, threads, W)
+        cpu = cpu_baseline(cfg, host_inputs, threads, W) if not P else None
 
     fwd_tflops = flops_f / (kern_ms["fwd"] * 1e-3) / 1e12
     out = {
@@ -520,8 +525,10 @@ def main() -> int:
         "config": {
             "workload": (f"causal MHA fwd+bwd, {cfg.name}: B={B} H={H} T={T} D={D} {cfg.dtype} "
                          "storage / fp32 accumulate, q,k,v,dO iid N(0,1) seeds 42+idx"
-                         + (f", sliding window W={W}" if W else "")),
-            "B": B, "H": H, "T": T, "D": D, "window": W, "global_batch": B, "seq_len": T,
+                         + (f", sliding window W={W}" if W else "")
+                         + (f", attention dropout p={P:g} (Philox seed 42)" if P else "")),
+            "B": B, "H": H, "T": T, "D": D, "window": W, "dropout": P, "global_batch": B,
+            "seq_len": T,
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100.0 * value / peak, 2),

@@ -129,26 +129,30 @@ def _view(t: torch.Tensor, name: str) -> AttnView:
 
 
 def attn_fwd_strided(q, k, v, o, lse, scale: float | None = None, stream=None,
-                     window: int = 0) -> None:
+                     window: int = 0, dropout_p: float = 0.0, seed: int = 0) -> None:
     """C ABI attn_fwd_strided: q, k, v, o are [B, H, T, D] views (D contiguous);
-    window W > 0 keeps keys i-W < j <= i (0 = plain causal)."""
+    window W > 0 keeps keys i-W < j <= i (0 = plain causal); dropout_p > 0
+    drops attention weights with the Philox draws of `seed`."""
     B, H, T, D = _shape(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rc = load_library().attn_fwd_strided(
         _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
-        B, H, T, D, int(window), scale, _dtype_code(q), _stream(stream))
+        B, H, T, D, int(window), float(dropout_p), int(seed) & (2 ** 64 - 1), scale,
+        _dtype_code(q), _stream(stream))
     check(rc)
 
 
 def attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale: float | None = None,
-                     stream=None, window: int = 0) -> None:
-    """C ABI attn_bwd_strided: every [B, H, T, D] argument is a view."""
+                     stream=None, window: int = 0, dropout_p: float = 0.0, seed: int = 0) -> None:
+    """C ABI attn_bwd_strided: every [B, H, T, D] argument is a view; window,
+    dropout_p and seed as in the forward call."""
     B, H, T, D = _shape(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rc = load_library().attn_bwd_strided(
         _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
         _view(dO, "dO"), _view(dq, "dq"), _view(dk, "dk"), _view(dv, "dv"),
-        _ptr(delta, "delta"), B, H, T, D, int(window), scale, _dtype_code(q), _stream(stream))
+        _ptr(delta, "delta"), B, H, T, D, int(window), float(dropout_p),
+        int(seed) & (2 ** 64 - 1), scale, _dtype_code(q), _stream(stream))
     check(rc)
 
 
@@ -163,7 +167,7 @@ def qkv_heads(qkv: torch.Tensor, n_head: int):
 
 class _CausalAttentionQKV(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, qkv, n_head, window, prologue):
+    def forward(ctx, qkv, n_head, window, prologue, dropout_p, seed):
         if qkv.dim() != 3 or qkv.shape[-1] % (3 * n_head) != 0 or qkv.stride(-1) != 1:
             raise ValueError("qkv must be [B, T, 3C] with contiguous last dim and C % n_head == 0")
         qkv = qkv if qkv.is_contiguous() else qkv.contiguous()
@@ -179,7 +183,7 @@ class _CausalAttentionQKV(torch.autograd.Function):
             rope_qknorm_fwd(q, k, qa, ka, prologue)
         else:
             qa, ka = q, k
-        attn_fwd_strided(qa, ka, v, o, lse, window=window)
+        attn_fwd_strided(qa, ka, v, o, lse, window=window, dropout_p=dropout_p, seed=seed)
         if prologue is not None:
             ctx.save_for_backward(qkv, y, lse, qa, ka)
         else:
@@ -187,6 +191,7 @@ class _CausalAttentionQKV(torch.autograd.Function):
         ctx.n_head = n_head
         ctx.window = window
         ctx.prologue = prologue
+        ctx.dropout = (dropout_p, seed)
         return y
 
     @staticmethod
@@ -205,24 +210,32 @@ class _CausalAttentionQKV(torch.autograd.Function):
         dq, dk, dv = qkv_heads(dqkv, n_head)
         delta = torch.empty_like(lse)
         if ctx.prologue is None:
-            attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, window=ctx.window)
+            attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, window=ctx.window,
+                             dropout_p=ctx.dropout[0], seed=ctx.dropout[1])
         else:
             qa, ka = ctx.saved_tensors[3:5]
             dqa, dka = torch.empty_like(qa), torch.empty_like(ka)
-            attn_bwd_strided(qa, ka, v, o, lse, dO, dqa, dka, dv, delta, window=ctx.window)
+            attn_bwd_strided(qa, ka, v, o, lse, dO, dqa, dka, dv, delta, window=ctx.window,
+                             dropout_p=ctx.dropout[0], seed=ctx.dropout[1])
             rope_qknorm_bwd(q, k, dqa, dka, dq, dk, ctx.prologue)
-        return dqkv, None, None, None
+        return dqkv, None, None, None, None, None
 
 
 def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0,
-                         prologue: Prologue | None = None) -> torch.Tensor:
+                         prologue: Prologue | None = None, dropout_p: float = 0.0,
+                         seed: int | None = None) -> torch.Tensor:
     """Causal attention on the fused c_attn output: qkv [B, T, 3C] (q, k, v
     chunks of C, each [B, T, H, D]) -> y [B, T, C] (heads merged), read and
     written in place through strided views (bf16, head dim 64 or 128).  window W > 0
     restricts query i to keys i-W < j <= i (sliding window).  prologue applies
     RoPE and/or QK norm to q and k first (one extra read and write of q and k
-    each way)."""
-    return _CausalAttentionQKV.apply(qkv, n_head, int(window), prologue)
+    each way).  dropout_p > 0 drops attention weights (training mode); the
+    Philox seed is drawn from torch's default generator unless given, and the
+    backward reuses it."""
+    if dropout_p > 0.0 and seed is None:
+        seed = int(torch.randint(0, 2 ** 62, (1,)).item())
+    return _CausalAttentionQKV.apply(qkv, n_head, int(window), prologue, float(dropout_p),
+                                     int(seed or 0))
 
 
 @dataclasses.dataclass(frozen=True)

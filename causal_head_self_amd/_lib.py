@@ -37,7 +37,7 @@ ATTN_QK_NORM = 2
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
            "attn_bwd_strided", "attn_decode", "attn_decode_workspace_bytes",
            "attn_rope_qknorm_fwd", "attn_rope_qknorm_bwd", "attn_status_str", "attn_abi_version")
-ABI_VERSION = (1 << 16) | 3
+ABI_VERSION = (1 << 16) | 4
 
 
 class AttnView(ctypes.Structure):
@@ -79,11 +79,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_dkdv.argtypes = [_vp] * 8 + [_int] * 4 + [ctypes.c_float, _int, _vp]
     lib.attn_bwd_dkdv.restype = _int
     lib.attn_fwd_strided.argtypes = [AttnView] * 4 + [_vp, _int, _int, _int, _int, _int,
+                                                      ctypes.c_float, ctypes.c_ulonglong,
                                                       ctypes.c_float, _int, _vp]
     lib.attn_fwd_strided.restype = _int
     lib.attn_bwd_strided.argtypes = ([AttnView] * 4 + [_vp] + [AttnView] * 4 +
-                                     [_vp, _int, _int, _int, _int, _int, ctypes.c_float, _int,
-                                      _vp])
+                                     [_vp, _int, _int, _int, _int, _int, ctypes.c_float,
+                                      ctypes.c_ulonglong, ctypes.c_float, _int, _vp])
     lib.attn_bwd_strided.restype = _int
     lib.attn_decode_workspace_bytes.argtypes = [_int] * 4
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t

@@ -168,6 +168,15 @@ int validate_views(const VSpan* vs, int n, const float* const* rows, int nrows, 
     return ATTN_OK;
 }
 
+// round(p * 65536) for a dropout probability 0 <= p < 1, capped at 65535;
+// -1 for anything else.
+int dropout_threshold(float p)
+{
+    if (!isfinite(p) || p < 0.0f || !(p < 1.0f)) return -1;
+    const double t = floor((double)p * 65536.0 + 0.5);
+    return t > 65535.0 ? 65535 : (int)t;
+}
+
 cattn::Strides strides_of(const attn_view_t& v)
 {
     return cattn::Strides{v.stride_b, v.stride_h, (int)v.stride_t};
@@ -229,7 +238,7 @@ const char* attn_status_str(int st)
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes()";
     case ATTN_ERR_PARAM:
         return "RoPE / QK norm: flags must be 0..3, 0 <= pos0 and pos0 + T <= 2^24, rope_base "
-               "finite and > 0, gains finite, eps finite and >= 0";
+               "finite and > 0, gains finite, eps finite and >= 0; dropout_p must be in [0, 1)";
     default: return "unknown status";
     }
 }
@@ -323,14 +332,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 }
 
 int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
-                     int B, int H, int T, int D, int window, float scale, int dtype,
-                     void* stream)
+                     int B, int H, int T, int D, int window, float dropout_p,
+                     unsigned long long seed, float scale, int dtype, void* stream)
 {
     const VSpan vs[4] = {{&q, false}, {&k, false}, {&v, false}, {&o, true}};
     const float* rows[1] = {lse};
     int st = validate_views(vs, 4, rows, 1, B, H, T, D, scale, dtype);
     if (st != ATTN_OK) return st;
     if (window < 0) return ATTN_ERR_SHAPE;
+    const int p16 = dropout_threshold(dropout_p);
+    if (p16 < 0) return ATTN_ERR_PARAM;
     // lse (an output) must not overlap an input view either
     const uintptr_t rlo = (uintptr_t)lse, rhi = rlo + (size_t)B * H * T * sizeof(float);
     for (int i = 0; i < 3; ++i) {
@@ -350,13 +361,16 @@ int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     a.sv = strides_of(v);
     a.so = strides_of(o);
     a.window = window;
+    a.dropout_p16 = p16;
+    a.dropout_seed = seed;
     return status(cattn::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
 int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
                      const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
                      attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
-                     float scale, int dtype, void* stream)
+                     float dropout_p, unsigned long long seed, float scale, int dtype,
+                     void* stream)
 {
     const VSpan vs[8] = {{&q, false}, {&k, false}, {&v, false}, {&o, false},
                          {&dO, false}, {&dq, true}, {&dk, true}, {&dv, true}};
@@ -364,6 +378,8 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     int st = validate_views(vs, 8, rows, 2, B, H, T, D, scale, dtype);
     if (st != ATTN_OK) return st;
     if (window < 0) return ATTN_ERR_SHAPE;
+    const int p16 = dropout_threshold(dropout_p);
+    if (p16 < 0) return ATTN_ERR_PARAM;
     // delta (an output) must not overlap lse or an input view
     const size_t rb = (size_t)B * H * T * sizeof(float);
     const uintptr_t dlo = (uintptr_t)delta, dhi = dlo + rb;
@@ -393,6 +409,8 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     a.sdk = strides_of(dk);
     a.sdv = strides_of(dv);
     a.window = window;
+    a.dropout_p16 = p16;
+    a.dropout_seed = seed;
     return status(cattn::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 

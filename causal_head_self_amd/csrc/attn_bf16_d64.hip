@@ -45,6 +45,50 @@ template <int NP>
 constexpr int kWavesPerEU = NP == 1 ? 3 : 2;
 constexpr float kLazyRescale = 8.0f;  // log2 growth of the running max that forces a rescale
 
+// Attention dropout (the softmax weights go through dropout before the product
+// with V, CS336 tutorial section 5.1; inverted dropout in training mode).  The
+// keep decision of weight (bh, query i, key j) is a Philox4x32-10 draw (Salmon
+// et al., SC 2011): counter (j / 8, i, bh, 0) under the 64-bit seed as the key;
+// key j takes the 16-bit half j % 2 of output word (j % 8) / 2 and is kept iff
+// that value is >= p16.  Kept weights are scaled by 65536 / (65536 - p16),
+// which the kernels apply once to their fp32 accumulators.
+struct Dropout {
+    uint32_t seed_lo, seed_hi;
+    uint32_t p16;       // 0: no dropout
+    float keep_scale;   // 65536 / (65536 - p16)
+};
+
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                              uint32_t k0, uint32_t k1, uint32_t (&r)[4])
+{
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    r[0] = c0;
+    r[1] = c1;
+    r[2] = c2;
+    r[3] = c3;
+}
+
+// Draws of the 8-key block `blk` for query i: word w, half h is key 8 blk + 2w + h.
+__device__ __forceinline__ void drop_block(const Dropout& dr, int bh, int i, int blk, uint32_t (&r)[4])
+{
+    philox4x32_10((uint32_t)blk, (uint32_t)i, (uint32_t)bh, 0u, dr.seed_lo, dr.seed_hi, r);
+}
+
+__device__ __forceinline__ bool drop_kept(const Dropout& dr, const uint32_t (&r)[4], int w, int h)
+{
+    return ((r[w] >> (16 * h)) & 0xFFFFu) >= dr.p16;
+}
+
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -281,10 +325,10 @@ __device__ __forceinline__ bf16* head_of(const View& v, int bh, int H)
 // three waves that share a SIMD overlap each other's LDS latency.  Every wave
 // needs tiles 0..last_w; only the last one crosses its diagonal and is masked.
 // ---------------------------------------------------------------------------
-template <int NP>
+template <int NP, bool kDrop>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_fwd_d64_kernel(
     View Q, View K, View V, View O, float* __restrict__ LSE, int BH, int H, int T, int W,
-    int n_qtiles, float scale, float scale_log2, int n_cu)
+    int n_qtiles, float scale, float scale_log2, int n_cu, Dropout dr)
 {
     // Separate arrays per buffer (not one indexed array): with the buffer of every
     // access known at compile time, the compiler can tell that an LDS read does not
@@ -384,7 +428,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             bf16x8 pb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) pb[e] = (bf16)fast_exp2(fmaf(sc[b + e], scale_log2, -mc));
-            l = sum8(pb, l);
+            l = sum8(pb, l);  // the normaliser is that of the undropped weights
+            if constexpr (kDrop) {
+                // elements e < 4 are keys 4hi + e of 8-key block blk, e >= 4 of blk + 1
+                const int blk = 8 * j + 4 * (c >> 1) + 2 * (c & 1);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    uint32_t r[4];
+                    drop_block(dr, bh, qrow, blk + half, r);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (!drop_kept(dr, r, 2 * hi + (e >> 1), e & 1)) pb[4 * half + e] = (bf16)0.0f;
+                }
+            }
 #pragma unroll
             for (int dt = 0; dt < 2 * NP; ++dt) oacc[dt] = mfma32x32x16(tv[c][dt], pb, oacc[dt]);
         }
@@ -411,7 +467,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
     l = halves_sum(l);
     if (qrow < T) {
-        const float inv = 1.0f / l;
+        const float inv = (kDrop ? dr.keep_scale : 1.0f) / l;
         bf16* orow = head_of(O, bh, H) + (size_t)qrow * O.st;
 #pragma unroll
         for (int dt = 0; dt < 2 * NP; ++dt)
@@ -433,6 +489,7 @@ struct BwdParams {
     int BH, H, T;
     int W;  // window: query q sees keys q-W < k <= q (W >= T: the plain causal mask)
     float scale, scale_log2;
+    Dropout dr;
 };
 
 // ---------------------------------------------------------------------------
@@ -444,7 +501,7 @@ struct BwdParams {
 // Delta_i = sum_d dO_id O_id is formed from the rows the wave holds as MFMA
 // operands and written out.
 // ---------------------------------------------------------------------------
-template <int NP>
+template <int NP, bool kDrop>
 __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char* sK0, char* sK1,
                                         char* sV0, char* sV1)
 {
@@ -500,7 +557,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
 
     // keys 32h .. 32h+31 of tile j: S^T, dP^T - Delta, dS^T, dQ^T += K^T dS^T
     auto half = [&](int h, bool diag, int k0, const char* kc, const char* vc) {
-        f32x16 sv = f32x16{}, pv = ndl;
+        // dP^T - Delta (without dropout), or dP^T alone, to be masked first
+        f32x16 sv = f32x16{}, pv = kDrop ? f32x16{} : ndl;
 #pragma unroll
         for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -518,8 +576,26 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
                 sv[r] = kk <= lim && kk > lim - W ? sv[r] : -INFINITY;
             }
         }
+        if constexpr (kDrop) {
+            // dS = P (keep * keep_scale * dP - Delta); register group g holds keys
+            // 4hi .. 4hi+3 of 8-key block (k0 + 32h) / 8 + g
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(fmaf(sv[r], scale_log2, nlse2)) * pv[r];  // dS^T
+            for (int g = 0; g < 4; ++g) {
+                uint32_t rr[4];
+                drop_block(a.dr, bh, qrow, (k0 + 32 * h) / 8 + g, rr);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    const float pr = fast_exp2(fmaf(sv[r], scale_log2, nlse2));
+                    const float t = drop_kept(a.dr, rr, 2 * hi + (e >> 1), e & 1)
+                                        ? fmaf(pv[r], a.dr.keep_scale, -dlt) : -dlt;
+                    sv[r] = pr * t;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(fmaf(sv[r], scale_log2, nlse2)) * pv[r];  // dS^T
+        }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const int c = 2 * h + cc;
@@ -586,7 +662,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
 // leaves -Delta in the row buffer, which the next step's barrier publishes.
 // Otherwise Delta is read from memory (written by a dQ pass).
 // ---------------------------------------------------------------------------
-template <int NP, bool kDeltaFromO>
+template <int NP, bool kDeltaFromO, bool kDrop>
 __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, char* sQ0, char* sQ1,
                                           char* sG0, char* sG1, char* sO0, char* sO1,
                                           float (*sR0)[kTile], float (*sR1)[kTile])
@@ -683,11 +759,15 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     auto half = [&](int h, bool diag, int q0, const char* qc, const char* gc,
                     const float (*rc)[kTile]) {
         f32x16 sv = f32x16{}, dp;
+        if constexpr (kDrop) {
+            dp = f32x16{};  // dP alone: the keep mask applies before Delta is taken off
+        } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {  // dP starts from -Delta of its row
-            const f32x4 nd = *(const f32x4*)(rc[1] + 32 * h + 8 * g + 4 * hi);
+            for (int g = 0; g < 4; ++g) {  // dP starts from -Delta of its row
+                const f32x4 nd = *(const f32x4*)(rc[1] + 32 * h + 8 * g + 4 * hi);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
+                for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
+            }
         }
 #pragma unroll
         for (int p = 0; p < NP; ++p)
@@ -710,12 +790,28 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 nl = *(const f32x4*)(rc[0] + 32 * h + 8 * g + 4 * hi);
+            if constexpr (kDrop) {
+                // each register is another query: one draw per weight (key % 8 of
+                // this lane's key picks the word and half)
+                const f32x4 nd = *(const f32x4*)(rc[1] + 32 * h + 8 * g + 4 * hi);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g + e;
-                const float pr = fast_exp2(fmaf(sv[r], scale_log2, nl[e]));
-                sv[r] = pr;
-                dp[r] *= pr;  // dS
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    const float pr = fast_exp2(fmaf(sv[r], scale_log2, nl[e]));
+                    uint32_t rr[4];
+                    drop_block(a.dr, bh, q0 + 32 * h + 8 * g + 4 * hi + e, key >> 3, rr);
+                    const bool kept = drop_kept(a.dr, rr, (key & 7) >> 1, key & 1);
+                    sv[r] = kept ? pr : 0.f;  // dropped weight (times keep_scale at the end)
+                    dp[r] = pr * (kept ? fmaf(dp[r], a.dr.keep_scale, nd[e]) : nd[e]);  // dS
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    const float pr = fast_exp2(fmaf(sv[r], scale_log2, nl[e]));
+                    sv[r] = pr;
+                    dp[r] *= pr;  // dS
+                }
             }
         }
 #pragma unroll
@@ -777,14 +873,15 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
                 const int d = 32 * dt + 8 * g + 4 * hi;
                 store_bf16x4(krow + d, dkacc[dt][4 * g] * scale, dkacc[dt][4 * g + 1] * scale,
                              dkacc[dt][4 * g + 2] * scale, dkacc[dt][4 * g + 3] * scale);
-                store_bf16x4(vrow + d, dvacc[dt][4 * g], dvacc[dt][4 * g + 1],
-                             dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]);
+                const float vs = kDrop ? a.dr.keep_scale : 1.0f;
+                store_bf16x4(vrow + d, dvacc[dt][4 * g] * vs, dvacc[dt][4 * g + 1] * vs,
+                             dvacc[dt][4 * g + 2] * vs, dvacc[dt][4 * g + 3] * vs);
             }
     }
 }
 
 // dQ alone (also writes Delta).
-template <int NP>
+template <int NP, bool kDrop>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dq_d64_kernel(
     BwdParams a, int n_qtiles, int n_cu)
 {
@@ -794,11 +891,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char sV0[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV1[NP * kTileBytes];
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    dq_item<NP>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1);
+    dq_item<NP, kDrop>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1);
 }
 
 // dK, dV alone, from a Delta in memory.
-template <int NP>
+template <int NP, bool kDrop>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dkdv_d64_kernel(
     BwdParams a, int n_cu)
 {
@@ -809,7 +906,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
     __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    dkdv_item<NP, false>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1, nullptr, nullptr, sR0, sR1);
+    dkdv_item<NP, false, kDrop>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1, nullptr, nullptr,
+                                sR0, sR1);
 }
 
 // ---------------------------------------------------------------------------
@@ -821,6 +919,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 // count (a dK/dV tile costs more): level v holds the dK/dV items of key block v
 // and the dQ items of query block n - 1 - v, BH of each.
 // ---------------------------------------------------------------------------
+template <bool kDrop>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_d64_kernel(
     BwdParams a, int n_blocks, int n_cu)
 {
@@ -836,9 +935,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int BH = a.BH;
     const int level = item / (2 * BH), r = item - level * 2 * BH;
     if (r < BH)
-        dkdv_item<1, true>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1);
+        dkdv_item<1, true, kDrop>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1);
     else
-        dq_item<1>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
+        dq_item<1, kDrop>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
 }
 
 }  // namespace d64
@@ -851,14 +950,27 @@ static d64::View view(const void* p, const Strides& s)
 // the window the kernels use: W >= T (no lower edge) for the plain causal mask
 static int window_of(const AttnArgs& a) { return a.window > 0 && a.window < a.T ? a.window : a.T; }
 
+static d64::Dropout dropout_of(const AttnArgs& a)
+{
+    d64::Dropout d{};
+    d.seed_lo = (uint32_t)a.dropout_seed;
+    d.seed_hi = (uint32_t)(a.dropout_seed >> 32);
+    d.p16 = (uint32_t)a.dropout_p16;
+    d.keep_scale = (float)(65536.0 / (65536.0 - (double)a.dropout_p16));
+    return d;
+}
+
 hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
-    auto k = a.D == 128 ? d64::attn_fwd_d64_kernel<2> : d64::attn_fwd_d64_kernel<1>;
+    const bool drop = a.dropout_p16 > 0;
+    auto k = a.D == 128 ? (drop ? d64::attn_fwd_d64_kernel<2, true> : d64::attn_fwd_d64_kernel<2, false>)
+                        : (drop ? d64::attn_fwd_d64_kernel<1, true> : d64::attn_fwd_d64_kernel<1, false>);
     hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
                        view(a.q, a.sq), view(a.k, a.sk), view(a.v, a.sv), view(a.o_out, a.so),
-                       a.lse, BH, a.H, a.T, window_of(a), nqt, a.scale, a.scale * kLog2e, a.n_cu);
+                       a.lse, BH, a.H, a.T, window_of(a), nqt, a.scale, a.scale * kLog2e, a.n_cu,
+                       dropout_of(a));
     return hipGetLastError();
 }
 
@@ -881,6 +993,7 @@ static d64::BwdParams bwd_params(const AttnArgs& a)
     p.W = window_of(a);
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;
+    p.dr = dropout_of(a);
     return p;
 }
 
@@ -888,7 +1001,9 @@ hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
-    auto k = a.D == 128 ? d64::attn_bwd_dq_d64_kernel<2> : d64::attn_bwd_dq_d64_kernel<1>;
+    const bool drop = a.dropout_p16 > 0;
+    auto k = a.D == 128 ? (drop ? d64::attn_bwd_dq_d64_kernel<2, true> : d64::attn_bwd_dq_d64_kernel<2, false>)
+                        : (drop ? d64::attn_bwd_dq_d64_kernel<1, true> : d64::attn_bwd_dq_d64_kernel<1, false>);
     hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nqt, a.n_cu);
     return hipGetLastError();
 }
@@ -897,7 +1012,9 @@ hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
     const int BH = a.B * a.H;
     const int nkt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
-    auto k = a.D == 128 ? d64::attn_bwd_dkdv_d64_kernel<2> : d64::attn_bwd_dkdv_d64_kernel<1>;
+    const bool drop = a.dropout_p16 > 0;
+    auto k = a.D == 128 ? (drop ? d64::attn_bwd_dkdv_d64_kernel<2, true> : d64::attn_bwd_dkdv_d64_kernel<2, false>)
+                        : (drop ? d64::attn_bwd_dkdv_d64_kernel<1, true> : d64::attn_bwd_dkdv_d64_kernel<1, false>);
     hipLaunchKernelGGL(k, dim3(nkt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), a.n_cu);
     return hipGetLastError();
 }
@@ -910,8 +1027,8 @@ hipError_t launch_bwd_bf16_d64(const AttnArgs& a, hipStream_t st)
     }
     const int BH = a.B * a.H;
     const int nb = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
-    hipLaunchKernelGGL(d64::attn_bwd_d64_kernel, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st,
-                       bwd_params(a), nb, a.n_cu);
+    auto k = a.dropout_p16 > 0 ? d64::attn_bwd_d64_kernel<true> : d64::attn_bwd_d64_kernel<false>;
+    hipLaunchKernelGGL(k, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nb, a.n_cu);
     return hipGetLastError();
 }
 

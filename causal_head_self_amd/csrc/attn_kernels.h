@@ -30,6 +30,8 @@ struct AttnArgs {
     int window;      // sliding window W (query q sees keys q-W < k <= q); 0 = plain causal.
                      // Only the bf16 D=64/128 kernels take it; the entry points with a
                      // window argument accept no other case.
+    int dropout_p16;                  // attention dropout: round(p * 65536); 0 = none
+    unsigned long long dropout_seed;  // Philox key
     // strides of q, k, v, o, dO, dq, dk, dv (contiguous unless a strided entry point set them)
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
 };

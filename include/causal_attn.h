@@ -69,7 +69,7 @@ typedef enum {
     ATTN_ERR_HIP = 9,           /* a kernel launch failed                   */
     ATTN_ERR_LAYOUT = 10,       /* strided views: unsupported dtype/D or strides */
     ATTN_ERR_WORKSPACE = 11,    /* decode: workspace smaller than required  */
-    ATTN_ERR_PARAM = 12         /* RoPE / QK norm: flags, base, gain, eps or pos0 */
+    ATTN_ERR_PARAM = 12         /* RoPE / QK norm parameters, or dropout_p    */
 } attn_status_t;
 
 /* Forward.  Reads q, k, v; writes o ([B][H][T][D], dtype) and lse
@@ -147,17 +147,33 @@ typedef struct {
  * mask.  window < 0 is rejected with ATTN_ERR_SHAPE.  lse is then the
  * log-sum-exp over the window. */
 
-/* attn_fwd on strided views (q, k, v read; o written), with a window. */
-int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
-                     int B, int H, int T, int D, int window, float scale, int dtype,
-                     void* stream);
+/* Attention dropout (dropout_p > 0).  The CS336 tutorial (section 5.1)
+ * passes the softmax weights through nn.Dropout before the product with v;
+ * every configuration on the pages uses p = 0.  In training mode that is
+ * inverted dropout: each weight P[i][j] is kept with probability 1 - p and
+ * scaled by 1 / (1 - p), or zeroed; lse stays that of the undropped weights.
+ * The decisions are reproducible: weight (b, h, i, j) is kept iff the 16-bit
+ * half (j % 2) of word (j % 8) / 2 of Philox4x32-10(counter = (j / 8, i,
+ * b * H + h, 0), key = (seed mod 2^32, seed / 2^32)) is >= p16, with
+ * p16 = round(p * 65536) (p is quantised to 1/65536) and kept weights scaled by
+ * 65536 / (65536 - p16).  The backward must get the same dropout_p and seed
+ * as the forward.  dropout_p must be finite with 0 <= p < 1
+ * (ATTN_ERR_PARAM otherwise); p = 0 runs the kernels without dropout. */
 
-/* attn_bwd on strided views (q, k, v, o, dO read; dq, dk, dv written), in one
- * kernel launch; delta as in attn_bwd; window as in the forward call. */
+/* attn_fwd on strided views (q, k, v read; o written), with a window and
+ * dropout. */
+int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                     int B, int H, int T, int D, int window, float dropout_p,
+                     unsigned long long seed, float scale, int dtype, void* stream);
+
+/* attn_bwd on strided views (q, k, v, o, dO read; dq, dk, dv written); delta as
+ * in attn_bwd; window, dropout_p and seed as in the forward call.  One kernel
+ * launch at D = 64, two at D = 128. */
 int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
                      const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
                      attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
-                     float scale, int dtype, void* stream);
+                     float dropout_p, unsigned long long seed, float scale, int dtype,
+                     void* stream);
 
 /* ---------------------------------------------------------------------------
  * Decode against a KV cache.  nanochat, section 8 (inference engine): the
@@ -230,7 +246,7 @@ const char* attn_status_str(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 3)
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 4)
 
 #ifdef __cplusplus
 }

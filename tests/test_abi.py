@@ -9,6 +9,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import causal_head_self_amd as cat
 from causal_head_self_amd import _lib
@@ -237,19 +238,20 @@ def _qkv_views(base, elem=2):
     return [_v(base + i * C_ * elem, sb, sh, st) for i in range(3)]
 
 
-def _fwd_s(views=None, lse=P[4], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1, window=0):
+def _fwd_s(views=None, lse=P[4], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1, window=0,
+           dropout_p=0.0):
     v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3])]
     return cat.load_library().attn_fwd_strided(v[0], v[1], v[2], v[3], lse, B, H, T, D, window,
-                                               scale, dtype, None)
+                                               dropout_p, 0, scale, dtype, None)
 
 
 def _bwd_s(views=None, lse=P[4], delta=P[9], B=B_, H=H_, T=T_, D=D_, scale=0.125, dtype=1,
-           window=0):
+           window=0, dropout_p=0.0):
     v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3]), _v(P[5]), _v(P[6]), _v(P[7]),
                   _v(P[8])]
     return cat.load_library().attn_bwd_strided(v[0], v[1], v[2], v[3], lse, v[4], v[5], v[6],
-                                               v[7], delta, B, H, T, D, window, scale, dtype,
-                                               None)
+                                               v[7], delta, B, H, T, D, window, dropout_p, 0,
+                                               scale, dtype, None)
 
 
 def test_strided_null_shape_scale():
@@ -260,10 +262,27 @@ def test_strided_null_shape_scale():
     assert _bwd_s(H=0) == 2
     assert _fwd_s(scale=0.0) == 7
     assert _bwd_s(scale=float("nan")) == 7
-    # a negative window is a shape error; it is checked after the views (here a
-    # misaligned lse keeps the call from reaching any launch)
+
+
+# The window and dropout_p checks come after every other check, so a call whose
+# only fault is one of them would reach a kernel launch (with the fake pointers
+# above) if that check were missing.  Without a GPU such a launch can only fail;
+# with one it must not be attempted, so these run on GPU-less hosts only.
+_last_check = pytest.mark.skipif(torch.cuda.is_available(),
+                                 reason="would launch with fake pointers if the check were missing")
+
+
+@_last_check
+def test_strided_negative_window_is_a_shape_error():
     assert _fwd_s(window=-1) == 2
     assert _bwd_s(window=-5) == 2
+
+
+@_last_check
+def test_strided_dropout_probability_range():
+    for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert _fwd_s(dropout_p=p) == 12, p
+        assert _bwd_s(dropout_p=p) == 12, p
 
 
 def test_strided_supports_only_bf16_d64_d128():
@@ -342,6 +361,7 @@ def test_decode_null_pointer(name):
     assert _dec(**{name: None}) == 1
 
 
+@_last_check
 def test_decode_validation_order_and_codes():
     assert _dec(B=0) == 2 and _dec(H=0) == 2 and _dec(T=0) == 2 and _dec(window=-1) == 2
     assert _dec(dtype=0) == 4 and _dec(dtype=5) == 4
@@ -373,6 +393,7 @@ def _rope(fwd=True, views=None, B=B_, H=H_, T=T_, D=D_, pos0=0, base=10000.0, qg
     return lib.attn_rope_qknorm_bwd(*v, B, H, T, D, pos0, base, qg, kg, eps, flags, dtype, None)
 
 
+@_last_check
 @pytest.mark.parametrize("fwd", [True, False])
 def test_rope_qknorm_validation(fwd):
     n = 4 if fwd else 6
