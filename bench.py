@@ -231,8 +231,8 @@ def decode_bench(args) -> int:
     ws = torch.empty(cat.decode_workspace_bytes(B, H, T_max, D), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        cat.attn_decode(q, kc, vc, ln, o, lse, ws, cfg.scale, 0, stream)
+    def step(s=stream):
+        cat.attn_decode(q, kc, vc, ln, o, lse, ws, cfg.scale, 0, s)
 
     for _ in range(args.warmup):
         step()
@@ -244,6 +244,33 @@ def decode_bench(args) -> int:
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+
+    # the same steps captured once in a HIP graph and replayed (launch cost of
+    # the two small kernels per step amortised by the graph)
+    graph_ms = None
+    if args.graph:
+        per = 16
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()  # the capturing stream
+            for _ in range(per):
+                step(cap)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // per)
+        t0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = t0.elapsed_time(t1) / (reps * per)
 
     kv_bytes = 2.0 * sum(lens) * H * D * 2
     alg_bytes = kv_bytes + 2.0 * B * H * D * 2 + B * H * 4 + B * 4
@@ -284,6 +311,10 @@ def decode_bench(args) -> int:
         "cpu_baseline": cpu,
         "l2_flushed": False,
     }
+    if graph_ms is not None:
+        out["graph"] = {"ms_per_step": round(graph_ms, 6),
+                        "GB_per_s": round(alg_bytes / (graph_ms * 1e-3) / 1e9, 2),
+                        "note": "16 decode steps per captured graph, replayed"}
     print(json.dumps(out), flush=True)
     return 0
 
@@ -377,6 +408,8 @@ def main() -> int:
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="attention dropout probability (bf16, D 64/128; Philox seed 42)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode configs: also time the steps replayed from a captured HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
     args = ap.parse_args()

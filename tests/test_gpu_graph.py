@@ -1,0 +1,96 @@
+"""The attention step and the decode step captured in HIP graphs (through
+torch.cuda.CUDAGraph, which captures the launches the C ABI enqueues on the
+current stream) and replayed.  Every replay is compared with the eager result,
+bit for bit (the kernels are deterministic), with eager work and
+synchronisations between the replays.  The kernels record no memset and
+allocate nothing, so they are capturable."""
+import sys
+
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def test_attention_step_graph_replays_match_eager():
+    import causal_head_self_amd as cat
+    B, H, T, D = 2, 3, 300, 64
+    _note(f"[graph] attention fwd+bwd B={B} H={H} T={T} D={D}")
+    dev = torch.device("cuda")
+    q, k, v, dO = (t.to(dev) for t in workloads.attention_inputs(B, H, T, D, "bf16", 501))
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+
+    def step():
+        cat.attn_fwd(q, k, v, o, lse)
+        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, lse, dq, dk, dv, delta)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm the stream before capture
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (o, lse, dq, dk, dv, delta):
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, r in zip(("o", "lse", "dq", "dk", "dv", "delta"),
+                              (o, lse, dq, dk, dv, delta), ref):
+            assert torch.equal(a, r), f"replay {rep}: {name}"
+
+
+def test_decode_graph_replays_match_eager():
+    import causal_head_self_amd as cat
+    B, H, T_max, D = 4, 6, 700, 64
+    _note(f"[graph] decode B={B} H={H} T_max={T_max} D={D}")
+    dev = torch.device("cuda")
+    q, kc, vc = (t.to(dev) for t in workloads.decode_inputs(B, H, T_max, D, seed=777))
+    lens = torch.tensor([700, 1, 350, 64], dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(cat.decode_workspace_bytes(B, H, T_max, D), dtype=torch.uint8, device=dev)
+    cat.attn_decode(q, kc, vc, lens, o, lse, ws)
+    torch.cuda.synchronize()
+    ref_o, ref_l = o.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        cat.attn_decode(q, kc, vc, lens, o, lse, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cat.attn_decode(q, kc, vc, lens, o, lse, ws)
+    for rep in range(3):
+        o.fill_(0)
+        lse.fill_(0)
+        ws.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), f"replay {rep}"
+    # the lengths are read on the device at run time: a replay after they change
+    # computes the new step (the next token of each sequence)
+    lens.add_(torch.tensor([0, 1, 1, 1], dtype=torch.int32, device=dev))
+    cat.attn_decode(q, kc, vc, lens, ref_o, ref_l, ws)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
