@@ -67,10 +67,12 @@ def _bind(path: str):
     lib.oracle_dropout_keep.argtypes = [ctypes.c_uint64, _i64, _i64, _i64, _i64]
     lib.oracle_dropout_keep.restype = ctypes.c_int
     lib.oracle_attn_fwd_dropout.argtypes = ([_dp] * 5 + [_i64] * 4 +
-                                            [ctypes.c_double, _i64, _i64, ctypes.c_uint64, _i64])
+                                            [ctypes.c_double, _i64, _i64, ctypes.c_uint64, _i64,
+                                             _i64])
     lib.oracle_attn_fwd_dropout.restype = None
     lib.oracle_attn_bwd_dropout.argtypes = ([_dp] * 8 + [_i64] * 4 +
-                                            [ctypes.c_double, _i64, _i64, ctypes.c_uint64, _i64])
+                                            [ctypes.c_double, _i64, _i64, ctypes.c_uint64, _i64,
+                                             _i64])
     lib.oracle_attn_bwd_dropout.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -197,20 +199,21 @@ def dropout_keep(seed: int, p16: int, bh: int, i: int, j: int) -> bool:
 
 
 def attn_fwd_dropout(q, k, v, scale: float, p: float, seed: int, window: int = 0,
-                     nthreads: int = 0, lib: str | None = None):
-    """Forward with attention dropout (see oracle.c): returns (o, lse)."""
+                     nthreads: int = 0, lib: str | None = None, bh0: int = 0):
+    """Forward with attention dropout (see oracle.c): returns (o, lse).  bh0 is
+    the global (batch, head) index of the first pair given."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, T, D = q.shape
     o = np.empty_like(q)
     lse = np.empty((B, H, T), dtype=np.float64)
     _load(lib).oracle_attn_fwd_dropout(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, T, D,
                                     float(scale), int(window), dropout_threshold(p),
-                                    int(seed) & (2 ** 64 - 1), int(nthreads))
+                                    int(seed) & (2 ** 64 - 1), int(bh0), int(nthreads))
     return o, lse
 
 
 def attn_bwd_dropout(q, k, v, dO, scale: float, p: float, seed: int, window: int = 0,
-                     nthreads: int = 0, lib: str | None = None):
+                     nthreads: int = 0, lib: str | None = None, bh0: int = 0):
     """Backward with attention dropout: returns (dq, dk, dv, delta)."""
     q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
     B, H, T, D = q.shape
@@ -218,7 +221,7 @@ def attn_bwd_dropout(q, k, v, dO, scale: float, p: float, seed: int, window: int
     delta = np.empty((B, H, T), dtype=np.float64)
     _load(lib).oracle_attn_bwd_dropout(_p(q), _p(k), _p(v), _p(dO), _p(dq), _p(dk), _p(dv),
                                     _p(delta), B, H, T, D, float(scale), int(window),
-                                    dropout_threshold(p), int(seed) & (2 ** 64 - 1),
+                                    dropout_threshold(p), int(seed) & (2 ** 64 - 1), int(bh0),
                                     int(nthreads))
     return dq, dk, dv, delta
 

@@ -231,11 +231,13 @@ int oracle_dropout_keep(uint64_t seed, int64_t p16, int64_t bh, int64_t i, int64
     return (int64_t)u >= p16;
 }
 
-/* Forward with dropout: o_i = sum_j P_ij keep_ij / (1 - p) v_j; lse as without. */
+/* Forward with dropout: o_i = sum_j P_ij keep_ij / (1 - p) v_j; lse as without.
+ * bh0: the global (batch, head) index of the first pair given (the draws are
+ * indexed by it), so that a slice of a larger batch can be checked alone. */
 void oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, double* o,
                              double* lse, int64_t B, int64_t H, int64_t T, int64_t D,
                              double scale, int64_t window, int64_t p16, uint64_t seed,
-                             int64_t nthreads)
+                             int64_t bh0, int64_t nthreads)
 {
     const double keep_scale = 65536.0 / (65536.0 - (double)p16);
     set_threads(nthreads);
@@ -252,7 +254,7 @@ void oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, 
             const int64_t j0 = first_key(i, window);
             causal_softmax_row(Qh + i * D, Kh, i, j0, D, scale, s, w, &m, &Z);
             for (int64_t j = j0; j <= i; ++j)  /* the dropped weights */
-                w[j] = oracle_dropout_keep(seed, p16, bh, i, j) ? w[j] * keep_scale : 0.0;
+                w[j] = oracle_dropout_keep(seed, p16, bh0 + bh, i, j) ? w[j] * keep_scale : 0.0;
             for (int64_t d = 0; d < D; ++d) {
                 double sum = 0.0;
                 for (int64_t j = j0; j <= i; ++j) sum += w[j] * Vh[j * D + d];
@@ -273,7 +275,8 @@ void oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, 
 void oracle_attn_bwd_dropout(const double* q, const double* k, const double* v,
                              const double* dO, double* dq, double* dk, double* dv, double* delta,
                              int64_t B, int64_t H, int64_t T, int64_t D, double scale,
-                             int64_t window, int64_t p16, uint64_t seed, int64_t nthreads)
+                             int64_t window, int64_t p16, uint64_t seed, int64_t bh0,
+                             int64_t nthreads)
 {
     const double keep_scale = 65536.0 / (65536.0 - (double)p16);
     set_threads(nthreads);
@@ -298,7 +301,7 @@ void oracle_attn_bwd_dropout(const double* q, const double* k, const double* v,
             causal_softmax_row(Qh + i * D, Kh, i, j0, D, scale, s, w, &m, &Z);
             double Dl = 0.0;
             for (int64_t j = j0; j <= i; ++j) {
-                mk[j] = oracle_dropout_keep(seed, p16, bh, i, j) ? keep_scale : 0.0;
+                mk[j] = oracle_dropout_keep(seed, p16, bh0 + bh, i, j) ? keep_scale : 0.0;
                 double sum = 0.0;
                 for (int64_t d = 0; d < D; ++d) sum += Gh[i * D + d] * Vh[j * D + d];
                 gw[j] = mk[j] * sum;

@@ -447,3 +447,40 @@ def test_qkv_autograd_window_matches_oracle():
     got = {"o": got_o, "dq": as_np(g[0]), "dk": as_np(g[1]), "dv": as_np(g[2])}
     assert_close(got, {n: ref[n] for n in got}, TOL["bf16"], f"qkv window {W}", None,
                  scaled_tol(D))
+
+
+@pytest.mark.parametrize("name,window,p", [("long", 1024, 0.0), ("gpt2s", 0, 0.1),
+                                           ("gpt2s_d128", 256, 0.0)])
+def test_full_size_window_and_dropout_sampled_heads(name, window, p):
+    """The bench launches with a window or dropout, at the full workload size:
+    two sampled (b, h) pairs against the oracle."""
+    import causal_head_self_amd as cat
+    c = ATTN_CONFIGS[name]
+    _note(f"[parity] {name} B={c.B} H={c.H} T={c.T} D={c.D} window={window} p={p} (sampled)")
+    q, k, v, dO = workloads.config_inputs(c)
+    dev = torch.device("cuda")
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, dO))
+    o = torch.empty_like(qd)
+    lse = torch.empty((c.B, c.H, c.T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    delta = torch.empty_like(lse)
+    cat.attn_fwd_strided(qd, kd, vd, o, lse, c.scale, window=window, dropout_p=p, seed=42)
+    cat.attn_bwd_strided(qd, kd, vd, o, lse, gd, dq, dk, dv, delta, c.scale, window=window,
+                         dropout_p=p, seed=42)
+    torch.cuda.synchronize()
+    s = oracle.widen_scale(c.scale)
+    for b, h in ((0, 1), (c.B - 1, c.H - 1)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        qs, ks, vs, gs = q[sl], k[sl], v[sl], dO[sl]
+        if p > 0:  # the draws are indexed by the global (b, h) pair
+            ro, rlse = oracle.attn_fwd_dropout(qs, ks, vs, s, p, 42, window=window, bh0=b * c.H + h)
+            rdq, rdk, rdv, rdl = oracle.attn_bwd_dropout(qs, ks, vs, gs, s, p, 42, window=window,
+                                                         bh0=b * c.H + h)
+        else:
+            ro, rlse = oracle.attn_fwd(qs, ks, vs, s, window=window)
+            rdq, rdk, rdv, rdl = oracle.attn_bwd(qs, ks, vs, gs, s, window=window)
+        ref = dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv, delta=rdl)
+        got = {n: t[sl].float().cpu().numpy().astype(np.float64)
+               for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta).items()}
+        assert_close(got, ref, TOL["bf16"], f"{name} W{window} head ({b},{h})",
+                     delta_bound(ref, gs), scaled_tol(c.D))

@@ -81,8 +81,8 @@ MUTANTS = {
                           "const uint32_t y0 = (uint32_t)(p0 >> 32) ^ x1 ^ k0;"),
     "dropout_counter_swapped": ("const uint32_t ctr[4] = {(uint32_t)(j / 8), (uint32_t)i, (uint32_t)bh, 0u};",
                                 "const uint32_t ctr[4] = {(uint32_t)i, (uint32_t)(j / 8), (uint32_t)bh, 0u};"),
-    "dropout_unscaled": ("w[j] = oracle_dropout_keep(seed, p16, bh, i, j) ? w[j] * keep_scale : 0.0;",
-                         "w[j] = oracle_dropout_keep(seed, p16, bh, i, j) ? w[j] : 0.0;"),
+    "dropout_unscaled": ("w[j] = oracle_dropout_keep(seed, p16, bh0 + bh, i, j) ? w[j] * keep_scale : 0.0;",
+                         "w[j] = oracle_dropout_keep(seed, p16, bh0 + bh, i, j) ? w[j] : 0.0;"),
     "dropout_bwd_mask_not_on_dp": ("gw[j] = mk[j] * sum;", "gw[j] = sum;"),
     "weight_grad_transposed": ("for (int64_t c = 0; c < C; ++c) dWp[cp * C + c] += av * dy[n * C + c];",
                                "for (int64_t c = 0; c < C; ++c) dWp[c * C + cp] += av * dy[n * C + c];"),

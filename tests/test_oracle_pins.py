@@ -740,3 +740,20 @@ def test_dropout_backward_finite_differences():
                                                      **kw)[0])
             fd = (fp - fm) / (2 * h)
             assert abs(fd - g.flat[flat]) < 1e-7 * max(1.0, abs(fd)), (name, flat)
+
+
+def test_dropout_head_offset_matches_the_full_batch():
+    """A (b, h) slice checked alone with bh0 = its global index gets the same
+    result as inside the full batch."""
+    B, H, T, D = 2, 3, 12, 4
+    q, k, v = _qkv((B, H, T, D), seed=631)
+    dO = _rand((B, H, T, D), 632)
+    o, lse = oracle.attn_fwd_dropout(q, k, v, 0.5, 0.3, 11)
+    g = oracle.attn_bwd_dropout(q, k, v, dO, 0.5, 0.3, 11)
+    b, h = 1, 2
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    os_, ls_ = oracle.attn_fwd_dropout(q[sl], k[sl], v[sl], 0.5, 0.3, 11, bh0=b * H + h)
+    gs = oracle.attn_bwd_dropout(q[sl], k[sl], v[sl], dO[sl], 0.5, 0.3, 11, bh0=b * H + h)
+    assert np.array_equal(os_, o[sl]) and np.array_equal(ls_, lse[sl])
+    for a, r in zip(gs, g):
+        assert np.array_equal(a, r[sl])
