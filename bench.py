@@ -272,6 +272,14 @@ def decode_bench(args) -> int:
         torch.cuda.synchronize()
         graph_ms = t0.elapsed_time(t1) / (reps * per)
 
+    if args.copy_calibration_mib > 0:  # a plain device copy of known size (counter scaling)
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
     kv_bytes = 2.0 * sum(lens) * H * D * 2
     alg_bytes = kv_bytes + 2.0 * B * H * D * 2 + B * H * 4 + B * 4
     gbs = alg_bytes / (ms * 1e-3) / 1e9
