@@ -1,11 +1,13 @@
 // attn_bf16_d64.hip -- gfx950 kernels for causal multi-head self-attention
-// at head dim 64, bf16 storage / fp32 accumulation: forward, dQ and dK/dV.
+// at head dims 64 and 128 (tiles of 64-column panels), bf16 storage / fp32
+// accumulation: forward, dQ and dK/dV, with optional sliding window and
+// attention dropout, on strided [B][H][T][D] views.
 //
 // Same operation as attn_bf16.hip (CS336 from-scratch tutorial, lmnt.cn,
 // section 5.1 CausalSelfAttention.forward; the tril mask keeps the diagonal,
 // "Train Your Own LLM from Scratch", section 1; the backward is the exact
-// gradient the pages train through, tutorial section 5.2).  This file is the
-// head-dim-64 specialisation that the GPT-2-small and ~400M shapes run:
+// gradient the pages train through, tutorial section 5.2).  The GPT-2-small,
+// ~400M and long-context shapes run here:
 //
 //  * Streamed tiles (64 rows x 128 bytes) travel HBM -> LDS with the
 //    asynchronous global_load_lds (16 bytes per lane; one wave instruction
