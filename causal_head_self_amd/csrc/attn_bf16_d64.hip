@@ -86,9 +86,25 @@ __device__ __forceinline__ void drop_block(const Dropout& dr, int bh, int i, int
     philox4x32_10((uint32_t)blk, (uint32_t)i, (uint32_t)bh, 0u, dr.seed_lo, dr.seed_hi, r);
 }
 
-__device__ __forceinline__ bool drop_kept(const Dropout& dr, const uint32_t (&r)[4], int w, int h)
+// Keep bits of the 8-key block `blk` for query i: bit t is key 8 blk + t.  Lanes
+// draw only the blocks assigned to them and pass the bit words to the lanes
+// whose accumulators hold those weights (one Philox call per 8 weights).
+__device__ __forceinline__ uint32_t drop_bits8(const Dropout& dr, int bh, int i, int blk)
 {
-    return ((r[w] >> (16 * h)) & 0xFFFFu) >= dr.p16;
+    uint32_t r[4];
+    drop_block(dr, bh, i, blk, r);
+    uint32_t b = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) b |= (uint32_t)(((r[t >> 1] >> (16 * (t & 1))) & 0xFFFFu) >= dr.p16) << t;
+    return b;
+}
+
+// The value of x held by lane l ^ 32 (v_permlane32_swap; which of the two
+// results is the other lane's is told apart by comparing with x itself).
+__device__ __forceinline__ uint32_t other_half_u32(uint32_t x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return r[0] == x ? r[1] : r[0];
 }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -406,6 +422,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // One code path for both cases: two separately inlined variants of this body
     // made the register allocator spill.
     auto tile = [&](bool diag, int j, const char* kc, const char* vc) {
+        // dropout keep bits of this tile for the lane's query: kw_lo for keys
+        // 0..31, kw_hi for 32..63 (lane half hi draws keys 32hi .. 32hi+31).
+        // Drawn before the S product: later, with S live, the draws spill.
+        uint32_t kw_lo = 0, kw_hi = 0;
+        if constexpr (kDrop) {
+            uint32_t own = 0;
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4) own |= drop_bits8(dr, bh, qrow, 8 * j + 4 * hi + m4) << (8 * m4);
+            const uint32_t oth = other_half_u32(own);
+            kw_lo = hi ? oth : own;
+            kw_hi = hi ? own : oth;
+        }
         f32x16 s0, s1;
         tile_product<NP>(kc, off, qreg, s0, s1);
         bf16x8 tv[4][2 * NP];
@@ -432,16 +460,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             for (int e = 0; e < 8; ++e) pb[e] = (bf16)fast_exp2(fmaf(sc[b + e], scale_log2, -mc));
             l = sum8(pb, l);  // the normaliser is that of the undropped weights
             if constexpr (kDrop) {
-                // elements e < 4 are keys 4hi + e of 8-key block blk, e >= 4 of blk + 1
-                const int blk = 8 * j + 4 * (c >> 1) + 2 * (c & 1);
+                // element e of chunk c is key 32(c/2) + 16(c%2) + 4hi + e (+ 4 for e >= 4)
+                const uint32_t w = (c >> 1) ? kw_hi : kw_lo;
+                const int base = 16 * (c & 1) + 4 * hi;
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    uint32_t r[4];
-                    drop_block(dr, bh, qrow, blk + half, r);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (!drop_kept(dr, r, 2 * hi + (e >> 1), e & 1)) pb[4 * half + e] = (bf16)0.0f;
-                }
+                for (int e = 0; e < 8; ++e)
+                    if (!((w >> (base + e + (e >> 2) * 4)) & 1u)) pb[e] = (bf16)0.0f;
             }
 #pragma unroll
             for (int dt = 0; dt < 2 * NP; ++dt) oacc[dt] = mfma32x32x16(tv[c][dt], pb, oacc[dt]);
@@ -579,20 +603,18 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
             }
         }
         if constexpr (kDrop) {
-            // dS = P (keep * keep_scale * dP - Delta); register group g holds keys
-            // 4hi .. 4hi+3 of 8-key block (k0 + 32h) / 8 + g
+            // dS = P (keep * keep_scale * dP - Delta).  Lane half hi draws keys
+            // 16hi .. 16hi+15 of the half; w has bit b for key 32h + b.
+            const int blk0 = (k0 + 32 * h) / 8 + 2 * hi;
+            const uint32_t own = drop_bits8(a.dr, bh, qrow, blk0) |
+                                 (drop_bits8(a.dr, bh, qrow, blk0 + 1) << 8);
+            const uint32_t oth = other_half_u32(own);
+            const uint32_t w = hi ? (oth | (own << 16)) : (own | (oth << 16));
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint32_t rr[4];
-                drop_block(a.dr, bh, qrow, (k0 + 32 * h) / 8 + g, rr);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e;
-                    const float pr = fast_exp2(fmaf(sv[r], scale_log2, nlse2));
-                    const float t = drop_kept(a.dr, rr, 2 * hi + (e >> 1), e & 1)
-                                        ? fmaf(pv[r], a.dr.keep_scale, -dlt) : -dlt;
-                    sv[r] = pr * t;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const float pr = fast_exp2(fmaf(sv[r], scale_log2, nlse2));
+                const bool kept = (w >> (8 * (r >> 2) + 4 * hi + (r & 3))) & 1u;
+                sv[r] = pr * (kept ? fmaf(pv[r], a.dr.keep_scale, -dlt) : -dlt);
             }
         } else {
 #pragma unroll
@@ -789,20 +811,26 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
                 sv[r] = qq >= lim && qq < lim + W ? sv[r] : -INFINITY;
             }
         }
+        // dropout: this lane draws for query q0 + 32h + li and the keys 16hi ..
+        // 16hi+15 of the wave's 32 (bit t = key k0w + 16hi + t)
+        uint32_t dbits = 0;
+        if constexpr (kDrop) {
+            const int blk0 = k0w / 8 + 2 * hi, qd = q0 + 32 * h + li;
+            dbits = drop_bits8(a.dr, bh, qd, blk0) | (drop_bits8(a.dr, bh, qd, blk0 + 1) << 8);
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 nl = *(const f32x4*)(rc[0] + 32 * h + 8 * g + 4 * hi);
             if constexpr (kDrop) {
-                // each register is another query: one draw per weight (key % 8 of
-                // this lane's key picks the word and half)
+                // register r is query 8g + 4hi + e of the half for this lane's key
+                // li: bit li % 16 of the word drawn by lane (8g + 4hi + e) + 32 (li / 16)
                 const f32x4 nd = *(const f32x4*)(rc[1] + 32 * h + 8 * g + 4 * hi);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
                     const float pr = fast_exp2(fmaf(sv[r], scale_log2, nl[e]));
-                    uint32_t rr[4];
-                    drop_block(a.dr, bh, q0 + 32 * h + 8 * g + 4 * hi + e, key >> 3, rr);
-                    const bool kept = drop_kept(a.dr, rr, (key & 7) >> 1, key & 1);
+                    const uint32_t wsrc = (uint32_t)__shfl((int)dbits, 8 * g + 4 * hi + e + 32 * (li >> 4), 64);
+                    const bool kept = (wsrc >> (li & 15)) & 1u;
                     sv[r] = kept ? pr : 0.f;  // dropped weight (times keep_scale at the end)
                     dp[r] = pr * (kept ? fmaf(dp[r], a.dr.keep_scale, nd[e]) : nd[e]);  // dS
                 }
