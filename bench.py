@@ -205,12 +205,14 @@ def sublayer_bench(args) -> int:
 
 def decode_bench(args) -> int:
     """One decode step against a full KV cache (nanochat, section 8: (B, T, H, D)
-    cache, one new token per sequence): attn_decode, its per-slice partial and
-    merge launches together.  The op streams the visible cache once, so the
-    metric is bytes per second against the HBM peak.  Algorithmic bytes per
-    call: the visible K and V rows (2 * sum_b len_b * H * D * 2), q and o
-    (B * H * D * 2 each), lse (B * H * 4) and the lengths (B * 4); the
-    workspace round trip (B * H * slices * (D + 4) * 4 twice) is not counted."""
+    cache, one new token per sequence): one attn_decode call, which is one
+    launch (a workgroup per head) or, for few heads with long caches, a
+    per-slice partial launch and a merge launch.  The op streams the visible
+    cache once, so the metric is bytes per second against the HBM peak.
+    Algorithmic bytes per call: the visible K and V rows
+    (2 * sum_b len_b * H * D * 2), q and o (B * H * D * 2 each), lse (B * H * 4)
+    and the lengths (B * 4); the workspace round trip of the two-launch path
+    (B * H * slices * (D + 4) * 4 twice) is not counted."""
     import torch
     import causal_head_self_amd as cat
     import workloads
@@ -280,6 +282,13 @@ def decode_bench(args) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # the path attn_decode takes (the library's rule): one launch when every wave
+    # of a workgroup has at most one 64-position slice, or when B*H reaches half
+    # the compute units
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    one_launch = -(-T_max // 64) <= (8 if D == 128 else 16) or 2 * B * H >= n_cu
+    kernel_name = ("attn_decode (one launch: decode_fused_kernel)" if one_launch else
+                   "attn_decode (decode_partial_kernel + decode_combine_kernel launches)")
     kv_bytes = 2.0 * sum(lens) * H * D * 2
     alg_bytes = kv_bytes + 2.0 * B * H * D * 2 + B * H * 4 + B * 4
     gbs = alg_bytes / (ms * 1e-3) / 1e9
@@ -310,7 +319,7 @@ def decode_bench(args) -> int:
                                 "q, k, v iid N(0,1) seeds 42+idx"),
                    "B": B, "H": H, "T_max": T_max, "D": D, "cached_positions": lens,
                    "global_batch": B, "seq_len": T_max, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "attn_decode (partial + combine launches)",
+        "roofline": {"bound": "hbm", "kernel": kernel_name,
                      "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": read_traffic("decode", f"{cfg.name}_B{B}_H{H}_T{T_max}_D{D}",

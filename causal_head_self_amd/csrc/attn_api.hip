@@ -466,6 +466,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     a.D = D;
     a.window = window;
     a.scale = scale;
+    a.n_cu = cu_count();
     return status(cattn::launch_decode_bf16(a, (hipStream_t)stream));
 }
 

@@ -9,7 +9,9 @@
 // so the op is bound by HBM bandwidth, not by the matrix cores; it runs on the
 // vector ALUs and is built to stream the cache once at full width.
 //
-// Split-K in two launches:
+// Two paths.  One launch (decode_fused_kernel, below): a workgroup per (b, h)
+// whose waves split the cache and merge through LDS.  Split-K in two launches,
+// for few heads with long caches:
 //   decode_partial_kernel: one wave per (sequence, slice of 64 cached
 //     positions, head).  Workgroups are numbered (b, slice, h), h fastest, so
 //     neighbouring waves stream neighbouring bytes of the same cache rows.
@@ -213,6 +215,147 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     if (lane == 0) lse[bh] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
 }
 
+// Whole decode of one (b, h) in one workgroup of NW waves: wave w takes the
+// slices w, w + NW, ... of 64 cached positions with the loads and scores of
+// decode_partial_kernel, and keeps a running max, normaliser and output across
+// its slices (online softmax, base 2).  The waves then meet in LDS, where wave
+// 0 merges their states as decode_combine_kernel merges slices.  No workspace
+// and no second launch.
+template <int NL, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_fused_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    const int* __restrict__ lens, bf16* __restrict__ o, float* __restrict__ lse, int H, int Tmax,
+    int n_slice, int window, float scale_log2)
+{
+    constexpr int D = 64 * NL;
+    __shared__ float s_o[NW][D];
+    __shared__ float s_m[NW], s_l[NW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    const int g = lane >> 3, sub = lane & 7;
+    const int bh = blockIdx.x;
+    const int h = bh % H, b = bh / H;
+    const int len = min(max(lens[b], 0), Tmax);
+    const int first = window > 0 ? max(0, len - window) : 0;
+
+    const size_t row = (size_t)H * D;
+    const bf16* kb = kc + (size_t)b * Tmax * row + (size_t)h * D + 8 * sub;
+    const bf16* vb = vc + (size_t)b * Tmax * row + (size_t)h * D + 8 * sub;
+    float qf[NL][8];
+    const bf16* qr = q + (size_t)bh * D + 8 * sub;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+        const bf16x8 qv = *(const bf16x8*)(qr + 64 * n);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[n][e] = (float)qv[e] * scale_log2;
+    }
+
+    float m = -INFINITY, l = 0.f;  // running state of this lane group
+    float acc[NL][8];
+#pragma unroll
+    for (int n = 0; n < NL; ++n)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[n][e] = 0.f;
+
+    for (int slice = wave; slice < n_slice; slice += nw) {
+        const int p0 = slice * kPos;
+        const int lo = max(first, p0), hi = min(len, p0 + kPos);
+        if (lo >= hi) continue;  // wave-uniform
+        bf16x8 kr[kSteps][NL], vr[kSteps][NL];
+#pragma unroll
+        for (int it = 0; it < kSteps; ++it) {
+            const int p = p0 + 8 * it + g;
+            const bool in = p >= lo && p < hi;
+#pragma unroll
+            for (int n = 0; n < NL; ++n) {
+                kr[it][n] = in ? *(const bf16x8*)(kb + (size_t)p * row + 64 * n) : zero_bf16x8();
+                vr[it][n] = in ? *(const bf16x8*)(vb + (size_t)p * row + 64 * n) : zero_bf16x8();
+            }
+        }
+        float sc[kSteps];
+        float mx = m;
+#pragma unroll
+        for (int it = 0; it < kSteps; ++it) {
+            float d = 0.f;
+#pragma unroll
+            for (int n = 0; n < NL; ++n)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d = fmaf(qf[n][e], (float)kr[it][n][e], d);
+            d = group8_sum(d);
+            const int p = p0 + 8 * it + g;
+            sc[it] = (p >= lo && p < hi) ? d : -INFINITY;
+            mx = fmaxf(mx, sc[it]);
+        }
+        if (mx == -INFINITY) continue;  // no visible position for this group yet
+        const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mx);
+        l *= alpha;
+#pragma unroll
+        for (int n = 0; n < NL; ++n)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[n][e] *= alpha;
+#pragma unroll
+        for (int it = 0; it < kSteps; ++it) {
+            const float pr = fast_exp2(sc[it] - mx);  // 0 for a masked position
+            l += pr;
+#pragma unroll
+            for (int n = 0; n < NL; ++n)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[n][e] = fmaf(pr, (float)vr[it][n][e], acc[n][e]);
+        }
+        m = mx;
+    }
+
+    // the wave's 8 groups (lanes l, l ^ 8, l ^ 16, l ^ 32 hold the same columns)
+    float M = m;
+#pragma unroll
+    for (int k = 8; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
+    const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    l *= f;
+#pragma unroll
+    for (int k = 8; k < 64; k <<= 1) l += __shfl_xor(l, k, 64);
+#pragma unroll
+    for (int n = 0; n < NL; ++n)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = acc[n][e] * f;
+#pragma unroll
+            for (int k = 8; k < 64; k <<= 1) x += __shfl_xor(x, k, 64);
+            acc[n][e] = x;
+        }
+    if (g == 0) {
+#pragma unroll
+        for (int n = 0; n < NL; ++n)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_o[wave][64 * n + 8 * sub + e] = acc[n][e];
+    }
+    if (lane == 0) {
+        s_m[wave] = M;
+        s_l[wave] = l;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+
+    // wave 0: lane c owns columns c + 64 n
+    float Mx = -INFINITY;
+    for (int w = 0; w < nw; ++w) Mx = fmaxf(Mx, s_m[w]);
+    float L = 0.f, out[NL];
+#pragma unroll
+    for (int n = 0; n < NL; ++n) out[n] = 0.f;
+    if (Mx != -INFINITY) {
+        for (int w = 0; w < nw; ++w) {
+            const float mw = s_m[w];
+            const float ww = mw == -INFINITY ? 0.f : fast_exp2(mw - Mx);
+            L = fmaf(ww, s_l[w], L);
+#pragma unroll
+            for (int n = 0; n < NL; ++n) out[n] = fmaf(ww, s_o[w][lane + 64 * n], out[n]);
+        }
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) o[(size_t)bh * D + lane + 64 * n] = (bf16)(out[n] * inv);
+    if (lane == 0) lse[bh] = Mx == -INFINITY ? -INFINITY : (Mx + log2f(L)) * kLn2;
+}
+
 }  // namespace dec
 
 int decode_slices(int T_max) { return (T_max + dec::kPos - 1) / dec::kPos; }
@@ -220,8 +363,27 @@ int decode_slices(int T_max) { return (T_max + dec::kPos - 1) / dec::kPos; }
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st)
 {
     const int n_slice = decode_slices(a.T_max);
-    const dim3 grid_p((unsigned)(a.B * n_slice * a.H)), grid_c((unsigned)(a.B * a.H));
     const float sl2 = a.scale * kLog2e;
+    const int nw = a.D == 128 ? 8 : 16;  // waves of a one-launch workgroup
+    const long long heads = (long long)a.B * a.H;
+    // One launch when every wave has at most one slice, or when the heads alone
+    // spread over half the compute units or more.  Otherwise (few heads, long
+    // caches) one workgroup per head would leave most compute units idle and
+    // each streaming its whole cache; the split path spreads the slices over
+    // the machine and pays a second launch for the merge.
+    if (n_slice <= nw || heads * 2 >= a.n_cu) {
+        const dim3 grid((unsigned)heads);
+        if (a.D == 128)
+            hipLaunchKernelGGL((dec::decode_fused_kernel<2, 8>), grid, dim3(64 * min(8, n_slice)), 0, st,
+                               (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.lens,
+                               (bf16*)a.o, a.lse, a.H, a.T_max, n_slice, a.window, sl2);
+        else
+            hipLaunchKernelGGL((dec::decode_fused_kernel<1, 16>), grid, dim3(64 * min(16, n_slice)), 0, st,
+                               (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.lens,
+                               (bf16*)a.o, a.lse, a.H, a.T_max, n_slice, a.window, sl2);
+        return hipGetLastError();
+    }
+    const dim3 grid_p((unsigned)(a.B * n_slice * a.H)), grid_c((unsigned)(a.B * a.H));
     if (a.D == 128) {
         hipLaunchKernelGGL(dec::decode_partial_kernel<2>, grid_p, dim3(64), 0, st, (const bf16*)a.q,
                            (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.lens, a.part, a.H,

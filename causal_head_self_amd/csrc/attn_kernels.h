@@ -48,6 +48,7 @@ struct DecodeArgs {
     int B, H, T_max, D;
     int window;           // 0: every cached position
     float scale;
+    int n_cu;             // compute units of the device (picks one launch or split-K)
 };
 
 int decode_slices(int T_max);

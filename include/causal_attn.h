@@ -196,12 +196,16 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
  *   lse:      fp32 [B][H], written (natural log, as for attn_fwd)
  *   workspace: device memory of at least attn_decode_workspace_bytes(B, H,
  *             T_max, D) bytes, 16-byte aligned, owned by the caller; its
- *             content on entry does not matter and is overwritten
+ *             content on entry does not matter, and it may be overwritten
+ *             (the one-launch path below leaves it untouched)
  *   dtype:    ATTN_BF16 only (else ATTN_ERR_DTYPE); D = 64 or 128 (else
  *             ATTN_ERR_UNSUPPORTED_D); window >= 0 (else ATTN_ERR_SHAPE)
  *
- * All arithmetic after the bf16 loads is fp32.  Two kernel launches on
- * `stream` (per-slice partial softmax, then their merge); no synchronisation.
+ * All arithmetic after the bf16 loads is fp32.  One kernel launch on `stream`
+ * (a workgroup per head, merging its waves' partial softmaxes in LDS) when
+ * T_max <= 1024 at D = 64 (512 at D = 128) or when B*H is at least half the
+ * device's compute units; otherwise two (per-slice partial softmax into the
+ * workspace, then their merge).  No synchronisation.
  * Errors: as for attn_fwd, checked before any HIP call, plus
  * ATTN_ERR_WORKSPACE for a workspace below the required size; outputs and the
  * workspace must not overlap each other or any input (ATTN_ERR_ALIAS). */

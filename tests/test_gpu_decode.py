@@ -5,7 +5,9 @@ Decode follows nanochat, section 8: a (B, T, H, D) cache, prefilled, then one
 token at a time; the token at position len-1 attends to positions 0..len-1
 (the W most recent with a window).  All arithmetic after the bf16 loads is
 fp32, so the 2e-2 bar of the bf16 configurations is met with a wide margin;
-the largest error is printed for each case.
+the largest error is printed for each case.  The cases cover both paths of the
+library: one launch (T_max <= 1024 at D = 64, 512 at D = 128, or B*H at least
+half the compute units) and the two-launch split (few heads, longer caches).
 """
 import math
 import sys
@@ -67,6 +69,12 @@ def check(q, kc, vc, lens, window, label):
     (1, 1, 1, 64, [1], 0),
     (4, 2, 130, 64, [0, 130, 500, -3], 0),   # nothing cached, full, clamped above and below
     (1, 12, 1024, 64, [1024], 0),
+    # two launches (few heads, more slices than waves in a one-launch workgroup)
+    (2, 2, 1500, 64, [1500, 1100], 300),
+    (2, 3, 700, 128, [700, 65], 0),
+    # one launch with two slices for some waves (many heads, long caches)
+    (1, 130, 1100, 64, [1100], 0),
+    (1, 130, 600, 128, [600], 200),
 ])
 def test_decode_matches_oracle(B, H, T_max, D, lens, window):
     _note(f"[decode] B={B} H={H} T_max={T_max} D={D} lens={lens} window={window}")
