@@ -60,13 +60,28 @@ struct Dropout {
     float keep_scale;   // 65536 / (65536 - p16)
 };
 
+// kWide: each 32 x 32 -> 64-bit product as one v_mad_u64_u32 (about the cost
+// of a v_mul_hi_u32 alone), else as v_mul_hi_u32 + v_mul_lo_u32, which need no
+// aligned register pair (the dK/dV items are at their register limit).
+template <bool kWide>
 __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                               uint32_t k0, uint32_t k1, uint32_t (&r)[4])
 {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        uint32_t hi0, lo0, hi1, lo1;
+        if constexpr (kWide) {
+            const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+            hi0 = (uint32_t)(p0 >> 32);
+            lo0 = (uint32_t)p0;
+            hi1 = (uint32_t)(p1 >> 32);
+            lo1 = (uint32_t)p1;
+        } else {
+            hi0 = __umulhi(0xD2511F53u, c0);
+            lo0 = 0xD2511F53u * c0;
+            hi1 = __umulhi(0xCD9E8D57u, c2);
+            lo1 = 0xCD9E8D57u * c2;
+        }
         c0 = hi1 ^ c1 ^ k0;
         c1 = lo1;
         c2 = hi0 ^ c3 ^ k1;
@@ -81,18 +96,20 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
 }
 
 // Draws of the 8-key block `blk` for query i: word w, half h is key 8 blk + 2w + h.
+template <bool kWide>
 __device__ __forceinline__ void drop_block(const Dropout& dr, int bh, int i, int blk, uint32_t (&r)[4])
 {
-    philox4x32_10((uint32_t)blk, (uint32_t)i, (uint32_t)bh, 0u, dr.seed_lo, dr.seed_hi, r);
+    philox4x32_10<kWide>((uint32_t)blk, (uint32_t)i, (uint32_t)bh, 0u, dr.seed_lo, dr.seed_hi, r);
 }
 
 // Keep bits of the 8-key block `blk` for query i: bit t is key 8 blk + t.  Lanes
 // draw only the blocks assigned to them and pass the bit words to the lanes
 // whose accumulators hold those weights (one Philox call per 8 weights).
+template <bool kWide = true>
 __device__ __forceinline__ uint32_t drop_bits8(const Dropout& dr, int bh, int i, int blk)
 {
     uint32_t r[4];
-    drop_block(dr, bh, i, blk, r);
+    drop_block<kWide>(dr, bh, i, blk, r);
     uint32_t b = 0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) b |= (uint32_t)(((r[t >> 1] >> (16 * (t & 1))) & 0xFFFFu) >= dr.p16) << t;
@@ -816,7 +833,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         uint32_t dbits = 0;
         if constexpr (kDrop) {
             const int blk0 = k0w / 8 + 2 * hi, qd = q0 + 32 * h + li;
-            dbits = drop_bits8(a.dr, bh, qd, blk0) | (drop_bits8(a.dr, bh, qd, blk0 + 1) << 8);
+            dbits = drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
