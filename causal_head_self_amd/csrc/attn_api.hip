@@ -1,5 +1,6 @@
 // attn_api.hip -- the C ABI declared in include/causal_attn.h: argument
 // validation (all of it before any HIP call) and dispatch to the kernels.
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 
@@ -60,18 +61,21 @@ int validate(const Buf (&in)[NI], const Buf (&out)[NO], int B, int H, int T, int
     return ATTN_OK;
 }
 
-// Compute units of the current device, queried once per device.
+// Compute units of the current device, queried once per device (callers on
+// several threads may race to fill the cache; they store the same value).
 int cu_count()
 {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
+    int c = cached[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-        cached[dev] = n > 0 ? n : -1;
+        c = n > 0 ? n : -1;
+        cached[dev].store(c, std::memory_order_relaxed);
     }
-    return cached[dev] > 0 ? cached[dev] : 0;
+    return c > 0 ? c : 0;
 }
 
 cattn::AttnArgs make_args(int B, int H, int T, int D, float scale)
