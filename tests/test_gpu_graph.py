@@ -3,7 +3,9 @@ torch.cuda.CUDAGraph, which captures the launches the C ABI enqueues on the
 current stream) and replayed.  Every replay is compared with the eager result,
 bit for bit (the kernels are deterministic), with eager work and
 synchronisations between the replays.  The kernels record no memset and
-allocate nothing, so they are capturable."""
+allocate nothing, so they are capturable.  The cases cover the plain and the
+strided entry points (with a window and dropout, and the two-launch backward at
+D = 128) and both decode paths."""
 import sys
 
 import pytest
@@ -19,10 +21,14 @@ def _note(msg):
     sys.stdout.flush()
 
 
-def test_attention_step_graph_replays_match_eager():
+@pytest.mark.parametrize("B,H,T,D,window,p", [
+    (2, 3, 300, 64, 0, 0.0),      # attn_fwd / attn_bwd (one backward launch)
+    (2, 2, 300, 128, 100, 0.1),   # strided entry points: window, dropout, two backward launches
+    (1, 3, 200, 64, 70, 0.2),     # strided, window and dropout at D = 64
+])
+def test_attention_step_graph_replays_match_eager(B, H, T, D, window, p):
     import causal_head_self_amd as cat
-    B, H, T, D = 2, 3, 300, 64
-    _note(f"[graph] attention fwd+bwd B={B} H={H} T={T} D={D}")
+    _note(f"[graph] attention fwd+bwd B={B} H={H} T={T} D={D} window={window} p={p}")
     dev = torch.device("cuda")
     q, k, v, dO = (t.to(dev) for t in workloads.attention_inputs(B, H, T, D, "bf16", 501))
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
@@ -30,8 +36,13 @@ def test_attention_step_graph_replays_match_eager():
     delta = torch.empty_like(lse)
 
     def step():
-        cat.attn_fwd(q, k, v, o, lse)
-        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta)
+        if window == 0 and p == 0.0:
+            cat.attn_fwd(q, k, v, o, lse)
+            cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta)
+        else:
+            cat.attn_fwd_strided(q, k, v, o, lse, window=window, dropout_p=p, seed=99)
+            cat.attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, window=window,
+                                 dropout_p=p, seed=99)
 
     step()
     torch.cuda.synchronize()
@@ -56,13 +67,16 @@ def test_attention_step_graph_replays_match_eager():
             assert torch.equal(a, r), f"replay {rep}: {name}"
 
 
-def test_decode_graph_replays_match_eager():
+@pytest.mark.parametrize("B,H,T_max,D,lens,step", [
+    (4, 6, 700, 64, [700, 1, 350, 64], [0, 1, 1, 1]),   # one launch
+    (2, 2, 1500, 64, [1500, 700], [0, 1]),              # two launches (split-K and merge)
+])
+def test_decode_graph_replays_match_eager(B, H, T_max, D, lens, step):
     import causal_head_self_amd as cat
-    B, H, T_max, D = 4, 6, 700, 64
-    _note(f"[graph] decode B={B} H={H} T_max={T_max} D={D}")
+    _note(f"[graph] decode B={B} H={H} T_max={T_max} D={D} lens={lens}")
     dev = torch.device("cuda")
     q, kc, vc = (t.to(dev) for t in workloads.decode_inputs(B, H, T_max, D, seed=777))
-    lens = torch.tensor([700, 1, 350, 64], dtype=torch.int32, device=dev)
+    lens = torch.tensor(lens, dtype=torch.int32, device=dev)
     o = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     ws = torch.empty(cat.decode_workspace_bytes(B, H, T_max, D), dtype=torch.uint8, device=dev)
@@ -88,7 +102,7 @@ def test_decode_graph_replays_match_eager():
         assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), f"replay {rep}"
     # the lengths are read on the device at run time: a replay after they change
     # computes the new step (the next token of each sequence)
-    lens.add_(torch.tensor([0, 1, 1, 1], dtype=torch.int32, device=dev))
+    lens.add_(torch.tensor(step, dtype=torch.int32, device=dev))
     cat.attn_decode(q, kc, vc, lens, ref_o, ref_l, ws)
     torch.cuda.synchronize()
     g.replay()
