@@ -519,6 +519,8 @@ def main() -> int:
     torch.cuda.synchronize()
     kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                for i, n in enumerate(names)}
+    per_iter = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
+    step_iter = sorted(e[0].elapsed_time(e[2]) for e in evs)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -585,6 +587,11 @@ def main() -> int:
         "fwd_tflops": round(fwd_tflops, 3),
         "fwd_pct_of_peak": round(100.0 * fwd_tflops / peak, 2),
         "kernel_ms": {n: round(v_, 5) for n, v_ in kern_ms.items()},
+        # per-iteration spread of the per-kernel pass (events between the calls)
+        "kernel_ms_median": {n: round(v_[len(v_) // 2], 5) for n, v_ in per_iter.items()},
+        "kernel_ms_min": {n: round(v_[0], 5) for n, v_ in per_iter.items()},
+        "step_ms_median": round(step_iter[len(step_iter) // 2], 5),
+        "step_ms_min": round(step_iter[0], 5),
         "kernel_src_sha": sha,
         "roofline": roofline,
         "cpu_baseline": cpu,
