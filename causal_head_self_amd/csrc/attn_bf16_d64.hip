@@ -796,6 +796,24 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     rows_finish(i_hi, sG0, sO0, sR0);
     f32x16 dkacc[2 * NP] = {}, dvacc[2 * NP] = {};
 
+    // Dropout: the keep bits of a half are drawn at the end of the half before
+    // it (and those of the first half before the loop), when its S and dP
+    // accumulators are dead: drawn later, with them live, the draws spilled.
+    // Halves run in this order: tiles from min(i_hi, last_w) down to first_w,
+    // in each tile half 0 (if some query of it reaches a key of the wave) and
+    // then half 1.  This lane draws for query 32h + li of the half and the
+    // keys 16hi .. 16hi+15 of the wave's 32 (bit t = key k0w + 16hi + t).
+    auto runs_half0 = [&](int i) { return i > first_w || i * kTile + 31 >= k0w; };
+    auto draw_half = [&](int i, int h) -> uint32_t {
+        const int blk0 = k0w / 8 + 2 * hi, qd = i * kTile + 32 * h + li;
+        return drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
+    };
+    uint32_t dbits = 0;  // keep bits of the half about to run
+    if constexpr (kDrop) {
+        const int i_first = min(i_hi, last_w);
+        if (i_first >= first_w) dbits = draw_half(i_first, runs_half0(i_first) ? 0 : 1);
+    }
+
     // queries 32h .. 32h+31 of the tile in qc / gc / rc
     auto half = [&](int h, bool diag, int q0, const char* qc, const char* gc,
                     const float (*rc)[kTile]) {
@@ -827,13 +845,6 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
                 const int qq = 8 * (r >> 2) + (r & 3);
                 sv[r] = qq >= lim && qq < lim + W ? sv[r] : -INFINITY;
             }
-        }
-        // dropout: this lane draws for query q0 + 32h + li and the keys 16hi ..
-        // 16hi+15 of the wave's 32 (bit t = key k0w + 16hi + t)
-        uint32_t dbits = 0;
-        if constexpr (kDrop) {
-            const int blk0 = k0w / 8 + 2 * hi, qd = q0 + 32 * h + li;
-            dbits = drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -876,6 +887,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
                     dkacc[2 * p + dt] = mfma32x32x16(lds_tr_read(qc, o0, o1), sb, dkacc[2 * p + dt]);
                 }
         }
+        if constexpr (kDrop) {  // the bits of the next half to run (if any)
+            const int i = q0 / kTile;
+            if (h == 0)
+                dbits = draw_half(i, 1);
+            else if (i - 1 >= first_w)
+                dbits = draw_half(i - 1, runs_half0(i - 1) ? 0 : 1);
+        }
     };
 
     // after the barrier tile i sits in qc, gc, (oc,) rc; every wave is done with tile
@@ -896,7 +914,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
             // masked: the diagonal tile and tiles reaching past the window of a key
             const bool diag = i == first_w || q0 + kTile - 1 >= k0w + W;
             // on the diagonal tile, queries 0..31 matter only if one of them is >= a key
-            if (i > first_w || q0 + 31 >= k0w) half(0, diag, q0, qc, gc, rc);
+            if (runs_half0(i)) half(0, diag, q0, qc, gc, rc);
             half(1, diag, q0, qc, gc, rc);
         }
         if (more) {
