@@ -297,10 +297,9 @@ __device__ __forceinline__ void tile_product(const char* tile, const Offsets& of
 }
 
 // Causal mask of a (key-subtile, query-lane) score tile: element r of s0
-// holds row 8(r/4) + 4hi + r%4 of the tile (+32 in s1); it stays iff that
-// row offset is <= lim, otherwise it becomes -inf.
-// Band version: element kept iff lo < its row offset <= lim (the causal window
-// i - W < j <= i seen from the tile).
+// holds row 8(r/4) + 4hi + r%4 of the tile (+32 in s1); it stays iff
+// lo < that row offset <= lim (the causal window i - W < j <= i seen from the
+// tile), otherwise it becomes -inf.
 __device__ __forceinline__ void mask_band(f32x16& s0, f32x16& s1, int lim, int lo)
 {
 #pragma unroll
@@ -308,16 +307,6 @@ __device__ __forceinline__ void mask_band(f32x16& s0, f32x16& s1, int lim, int l
         const int kk = 8 * (r >> 2) + (r & 3);
         s0[r] = kk <= lim && kk > lo ? s0[r] : -INFINITY;
         s1[r] = kk + 32 <= lim && kk + 32 > lo ? s1[r] : -INFINITY;
-    }
-}
-
-__device__ __forceinline__ void mask_upto(f32x16& s0, f32x16& s1, int lim)
-{
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int kk = 8 * (r >> 2) + (r & 3);
-        s0[r] = kk <= lim ? s0[r] : -INFINITY;
-        s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
     }
 }
 
