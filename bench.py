@@ -424,6 +424,9 @@ def main() -> int:
                     help="sliding window W (bf16, D 64/128): query i sees keys i-W < j <= i")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="attention dropout probability (bf16, D 64/128; Philox seed 42)")
+    ap.add_argument("--keep-bits", action="store_true",
+                    help="with --dropout: the forward stores its keep bits and the backward "
+                         "loads them (attn_*_strided_keep) instead of drawing them again")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="decode configs: also time the steps replayed from a captured HIP graph")
@@ -471,15 +474,24 @@ def main() -> int:
               "workload with D 64 or 128", file=sys.stderr)
         return 2
     strided = bool(W or P)
+    keep = None
+    if args.keep_bits and P > 0:
+        keep = torch.empty((cat.dropout_keep_bytes(B, H, T) // 4,), dtype=torch.int32, device=dev)
 
     def fwd():
-        if strided:
+        if keep is not None:
+            cat.attn_fwd_strided_keep(q, k, v, o, lse, keep, scale, stream, window=W, dropout_p=P,
+                                      seed=42)
+        elif strided:
             cat.attn_fwd_strided(q, k, v, o, lse, scale, stream, window=W, dropout_p=P, seed=42)
         else:
             cat.attn_fwd(q, k, v, o, lse, scale, stream)
 
     def bwd():
-        if strided:
+        if keep is not None:
+            cat.attn_bwd_strided_keep(q, k, v, o, lse, dO, dq, dk, dv, delta, keep, scale, stream,
+                                      window=W, dropout_p=P)
+        elif strided:
             cat.attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream, window=W,
                                  dropout_p=P, seed=42)
         else:
@@ -578,8 +590,10 @@ def main() -> int:
             "workload": (f"causal MHA fwd+bwd, {cfg.name}: B={B} H={H} T={T} D={D} {cfg.dtype} "
                          "storage / fp32 accumulate, q,k,v,dO iid N(0,1) seeds 42+idx"
                          + (f", sliding window W={W}" if W else "")
-                         + (f", attention dropout p={P:g} (Philox seed 42)" if P else "")),
-            "B": B, "H": H, "T": T, "D": D, "window": W, "dropout": P, "global_batch": B,
+                         + (f", attention dropout p={P:g} (Philox seed 42)" if P else "")
+                         + (", keep bits stored by the forward" if keep is not None else "")),
+            "B": B, "H": H, "T": T, "D": D, "window": W, "dropout": P,
+            "keep_bits": keep is not None, "global_batch": B,
             "seq_len": T,
             "parallelism": "single GPU",
         },

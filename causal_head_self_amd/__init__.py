@@ -156,6 +156,47 @@ def attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale: float | None
     check(rc)
 
 
+def dropout_keep_bytes(B: int, H: int, T: int) -> int:
+    """C ABI attn_dropout_keep_bytes: size of the stored keep bits of one call."""
+    return int(load_library().attn_dropout_keep_bytes(int(B), int(H), int(T)))
+
+
+def _keep_buf(keep: torch.Tensor, name: str = "keep") -> tuple[int, int]:
+    if not keep.is_cuda or not keep.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return keep.data_ptr(), keep.numel() * keep.element_size()
+
+
+def attn_fwd_strided_keep(q, k, v, o, lse, keep, scale: float | None = None, stream=None,
+                          window: int = 0, dropout_p: float = 0.0, seed: int = 0) -> None:
+    """C ABI attn_fwd_strided_keep: attn_fwd_strided that also stores its keep
+    bits in `keep` (a GPU tensor of at least dropout_keep_bytes(B, H, T) bytes)."""
+    B, H, T, D = _shape(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    kp, kb = _keep_buf(keep)
+    rc = load_library().attn_fwd_strided_keep(
+        _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
+        B, H, T, D, int(window), float(dropout_p), int(seed) & (2 ** 64 - 1), scale,
+        _dtype_code(q), kp, kb, _stream(stream))
+    check(rc)
+
+
+def attn_bwd_strided_keep(q, k, v, o, lse, dO, dq, dk, dv, delta, keep,
+                          scale: float | None = None, stream=None, window: int = 0,
+                          dropout_p: float = 0.0) -> None:
+    """C ABI attn_bwd_strided_keep: attn_bwd_strided with the keep bits loaded
+    from `keep` (written by attn_fwd_strided_keep) instead of drawn."""
+    B, H, T, D = _shape(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    kp, kb = _keep_buf(keep)
+    rc = load_library().attn_bwd_strided_keep(
+        _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
+        _view(dO, "dO"), _view(dq, "dq"), _view(dk, "dk"), _view(dv, "dv"),
+        _ptr(delta, "delta"), B, H, T, D, int(window), float(dropout_p), scale,
+        _dtype_code(q), kp, kb, _stream(stream))
+    check(rc)
+
+
 def qkv_heads(qkv: torch.Tensor, n_head: int):
     """q, k, v as [B, H, T, D] views of a [B, T, 3C] tensor (no copies)."""
     B, T, C3 = qkv.shape
@@ -167,7 +208,7 @@ def qkv_heads(qkv: torch.Tensor, n_head: int):
 
 class _CausalAttentionQKV(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, qkv, n_head, window, prologue, dropout_p, seed):
+    def forward(ctx, qkv, n_head, window, prologue, dropout_p, seed, keep_bits):
         if qkv.dim() != 3 or qkv.shape[-1] % (3 * n_head) != 0 or qkv.stride(-1) != 1:
             raise ValueError("qkv must be [B, T, 3C] with contiguous last dim and C % n_head == 0")
         qkv = qkv if qkv.is_contiguous() else qkv.contiguous()
@@ -183,11 +224,17 @@ class _CausalAttentionQKV(torch.autograd.Function):
             rope_qknorm_fwd(q, k, qa, ka, prologue)
         else:
             qa, ka = q, k
-        attn_fwd_strided(qa, ka, v, o, lse, window=window, dropout_p=dropout_p, seed=seed)
-        if prologue is not None:
-            ctx.save_for_backward(qkv, y, lse, qa, ka)
+        keep = None
+        if dropout_p > 0.0 and keep_bits:  # the forward's keep decisions, for the backward
+            keep = torch.empty((dropout_keep_bytes(B, n_head, T) // 4,), dtype=torch.int32,
+                               device=qkv.device)
+            attn_fwd_strided_keep(qa, ka, v, o, lse, keep, window=window, dropout_p=dropout_p,
+                                  seed=seed)
         else:
-            ctx.save_for_backward(qkv, y, lse)
+            attn_fwd_strided(qa, ka, v, o, lse, window=window, dropout_p=dropout_p, seed=seed)
+        saved = [qkv, y, lse] + ([qa, ka] if prologue is not None else [])
+        ctx.has_keep = keep is not None
+        ctx.save_for_backward(*saved, *([keep] if keep is not None else []))
         ctx.n_head = n_head
         ctx.window = window
         ctx.prologue = prologue
@@ -209,21 +256,29 @@ class _CausalAttentionQKV(torch.autograd.Function):
         dqkv = torch.empty_like(qkv)
         dq, dk, dv = qkv_heads(dqkv, n_head)
         delta = torch.empty_like(lse)
+        keep = ctx.saved_tensors[-1] if ctx.has_keep else None
+
+        def bwd(qx, kx, dqx, dkx):
+            if keep is not None:
+                attn_bwd_strided_keep(qx, kx, v, o, lse, dO, dqx, dkx, dv, delta, keep,
+                                      window=ctx.window, dropout_p=ctx.dropout[0])
+            else:
+                attn_bwd_strided(qx, kx, v, o, lse, dO, dqx, dkx, dv, delta, window=ctx.window,
+                                 dropout_p=ctx.dropout[0], seed=ctx.dropout[1])
+
         if ctx.prologue is None:
-            attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, window=ctx.window,
-                             dropout_p=ctx.dropout[0], seed=ctx.dropout[1])
+            bwd(q, k, dq, dk)
         else:
             qa, ka = ctx.saved_tensors[3:5]
             dqa, dka = torch.empty_like(qa), torch.empty_like(ka)
-            attn_bwd_strided(qa, ka, v, o, lse, dO, dqa, dka, dv, delta, window=ctx.window,
-                             dropout_p=ctx.dropout[0], seed=ctx.dropout[1])
+            bwd(qa, ka, dqa, dka)
             rope_qknorm_bwd(q, k, dqa, dka, dq, dk, ctx.prologue)
-        return dqkv, None, None, None, None, None
+        return dqkv, None, None, None, None, None, None
 
 
 def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0,
                          prologue: Prologue | None = None, dropout_p: float = 0.0,
-                         seed: int | None = None) -> torch.Tensor:
+                         seed: int | None = None, keep_bits: bool = True) -> torch.Tensor:
     """Causal attention on the fused c_attn output: qkv [B, T, 3C] (q, k, v
     chunks of C, each [B, T, H, D]) -> y [B, T, C] (heads merged), read and
     written in place through strided views (bf16, head dim 64 or 128).  window W > 0
@@ -231,11 +286,14 @@ def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0,
     RoPE and/or QK norm to q and k first (one extra read and write of q and k
     each way).  dropout_p > 0 drops attention weights (training mode); the
     Philox seed is drawn from torch's default generator unless given, and the
-    backward reuses it."""
+    backward reuses it.  With keep_bits (the default) the forward stores its
+    keep decisions (dropout_keep_bytes(B, H, T) bytes, held for the backward)
+    and the backward loads them instead of drawing them again; the results are
+    the same bits either way."""
     if dropout_p > 0.0 and seed is None:
         seed = int(torch.randint(0, 2 ** 62, (1,)).item())
     return _CausalAttentionQKV.apply(qkv, n_head, int(window), prologue, float(dropout_p),
-                                     int(seed or 0))
+                                     int(seed or 0), bool(keep_bits))
 
 
 @dataclasses.dataclass(frozen=True)

@@ -35,9 +35,10 @@ ATTN_QK_NORM = 2
 
 # every symbol include/causal_attn.h declares
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
-           "attn_bwd_strided", "attn_decode", "attn_decode_workspace_bytes",
+           "attn_bwd_strided", "attn_dropout_keep_bytes", "attn_fwd_strided_keep",
+           "attn_bwd_strided_keep", "attn_decode", "attn_decode_workspace_bytes",
            "attn_rope_qknorm_fwd", "attn_rope_qknorm_bwd", "attn_status_str", "attn_abi_version")
-ABI_VERSION = (1 << 16) | 4
+ABI_VERSION = (1 << 16) | 5
 
 
 class AttnView(ctypes.Structure):
@@ -86,6 +87,16 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                      [_vp, _int, _int, _int, _int, _int, ctypes.c_float,
                                       ctypes.c_ulonglong, ctypes.c_float, _int, _vp])
     lib.attn_bwd_strided.restype = _int
+    lib.attn_dropout_keep_bytes.argtypes = [_int] * 3
+    lib.attn_dropout_keep_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_strided_keep.argtypes = ([AttnView] * 4 + [_vp, _int, _int, _int, _int, _int,
+                                           ctypes.c_float, ctypes.c_ulonglong, ctypes.c_float,
+                                           _int, _vp, ctypes.c_size_t, _vp])
+    lib.attn_fwd_strided_keep.restype = _int
+    lib.attn_bwd_strided_keep.argtypes = ([AttnView] * 4 + [_vp] + [AttnView] * 4 +
+                                          [_vp, _int, _int, _int, _int, _int, ctypes.c_float,
+                                           ctypes.c_float, _int, _vp, ctypes.c_size_t, _vp])
+    lib.attn_bwd_strided_keep.restype = _int
     lib.attn_decode_workspace_bytes.argtypes = [_int] * 4
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode.argtypes = ([_vp] * 7 + [ctypes.c_size_t] + [_int] * 5 +

@@ -335,17 +335,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     return status(e);
 }
 
-int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
-                     int B, int H, int T, int D, int window, float dropout_p,
-                     unsigned long long seed, float scale, int dtype, void* stream)
+// Argument checks of the strided forward (in the documented order).
+static int fwd_strided_check(const attn_view_t& q, const attn_view_t& k, const attn_view_t& v,
+                             const attn_view_t& o, const float* lse, int B, int H, int T, int D,
+                             int window, float dropout_p, float scale, int dtype)
 {
     const VSpan vs[4] = {{&q, false}, {&k, false}, {&v, false}, {&o, true}};
     const float* rows[1] = {lse};
     int st = validate_views(vs, 4, rows, 1, B, H, T, D, scale, dtype);
     if (st != ATTN_OK) return st;
     if (window < 0) return ATTN_ERR_SHAPE;
-    const int p16 = dropout_threshold(dropout_p);
-    if (p16 < 0) return ATTN_ERR_PARAM;
+    if (dropout_threshold(dropout_p) < 0) return ATTN_ERR_PARAM;
     // lse (an output) must not overlap an input view either
     const uintptr_t rlo = (uintptr_t)lse, rhi = rlo + (size_t)B * H * T * sizeof(float);
     for (int i = 0; i < 3; ++i) {
@@ -353,6 +353,17 @@ int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
         const uintptr_t hi = lo + (uintptr_t)view_extent(*vs[i].v, B, H, T, D) * 2;
         if (lo < rhi && rlo < hi) return ATTN_ERR_ALIAS;
     }
+    return ATTN_OK;
+}
+
+static int fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                       int B, int H, int T, int D, int window, float dropout_p,
+                       unsigned long long seed, float scale, int dtype, unsigned int* keep,
+                       void* stream)
+{
+    const int st = fwd_strided_check(q, k, v, o, lse, B, H, T, D, window, dropout_p, scale, dtype);
+    if (st != ATTN_OK) return st;
+    const int p16 = dropout_threshold(dropout_p);
     cattn::AttnArgs a = make_args(B, H, T, D, scale);
     a.q = q.data;
     a.k = k.data;
@@ -367,14 +378,16 @@ int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     a.window = window;
     a.dropout_p16 = p16;
     a.dropout_seed = seed;
+    a.keep = keep;
     return status(cattn::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
-int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
-                     const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
-                     attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
-                     float dropout_p, unsigned long long seed, float scale, int dtype,
-                     void* stream)
+// Argument checks of the strided backward (in the documented order).
+static int bwd_strided_check(const attn_view_t& q, const attn_view_t& k, const attn_view_t& v,
+                             const attn_view_t& o, const float* lse, const attn_view_t& dO,
+                             const attn_view_t& dq, const attn_view_t& dk, const attn_view_t& dv,
+                             const float* delta, int B, int H, int T, int D, int window,
+                             float dropout_p, float scale, int dtype)
 {
     const VSpan vs[8] = {{&q, false}, {&k, false}, {&v, false}, {&o, false},
                          {&dO, false}, {&dq, true}, {&dk, true}, {&dv, true}};
@@ -382,8 +395,7 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     int st = validate_views(vs, 8, rows, 2, B, H, T, D, scale, dtype);
     if (st != ATTN_OK) return st;
     if (window < 0) return ATTN_ERR_SHAPE;
-    const int p16 = dropout_threshold(dropout_p);
-    if (p16 < 0) return ATTN_ERR_PARAM;
+    if (dropout_threshold(dropout_p) < 0) return ATTN_ERR_PARAM;
     // delta (an output) must not overlap lse or an input view
     const size_t rb = (size_t)B * H * T * sizeof(float);
     const uintptr_t dlo = (uintptr_t)delta, dhi = dlo + rb;
@@ -393,6 +405,19 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
         const uintptr_t hi = lo + (uintptr_t)view_extent(*vs[i].v, B, H, T, D) * 2;
         if (lo < dhi && dlo < hi) return ATTN_ERR_ALIAS;
     }
+    return ATTN_OK;
+}
+
+static int bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
+                       const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
+                       attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
+                       float dropout_p, unsigned long long seed, float scale, int dtype,
+                       const unsigned int* keep, void* stream)
+{
+    const int st = bwd_strided_check(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, D, window,
+                                     dropout_p, scale, dtype);
+    if (st != ATTN_OK) return st;
+    const int p16 = dropout_threshold(dropout_p);
     cattn::AttnArgs a = make_args(B, H, T, D, scale);
     a.q = q.data;
     a.k = k.data;
@@ -415,7 +440,87 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
     a.window = window;
     a.dropout_p16 = p16;
     a.dropout_seed = seed;
+    a.keep = const_cast<unsigned int*>(keep);
     return status(cattn::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+int attn_fwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                     int B, int H, int T, int D, int window, float dropout_p,
+                     unsigned long long seed, float scale, int dtype, void* stream)
+{
+    return fwd_strided(q, k, v, o, lse, B, H, T, D, window, dropout_p, seed, scale, dtype, nullptr,
+                       stream);
+}
+
+int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
+                     const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
+                     attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
+                     float dropout_p, unsigned long long seed, float scale, int dtype,
+                     void* stream)
+{
+    return bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, D, window, dropout_p, seed,
+                       scale, dtype, nullptr, stream);
+}
+
+size_t attn_dropout_keep_bytes(int B, int H, int T)
+{
+    if (B < 1 || H < 1 || T < 1) return 0;
+    return (size_t)B * H * (size_t)((T + 31) / 32) * T * sizeof(unsigned int);
+}
+
+// The keep-bit buffer: present, aligned, large enough, and apart from every
+// other buffer of the call (views given with their element extents).
+static int check_keep(const void* keep, size_t keep_bytes, int B, int H, int T, int D,
+                      const attn_view_t* const* views, int n_views, const float* const* rows,
+                      int n_rows)
+{
+    if (!keep) return ATTN_ERR_NULL;
+    if ((uintptr_t)keep % 4) return ATTN_ERR_ALIGN;
+    const size_t need = attn_dropout_keep_bytes(B, H, T);
+    if (keep_bytes < need) return ATTN_ERR_WORKSPACE;
+    const uintptr_t klo = (uintptr_t)keep, khi = klo + need;
+    for (int i = 0; i < n_views; ++i) {
+        const uintptr_t lo = (uintptr_t)views[i]->data;
+        const uintptr_t hi = lo + (uintptr_t)view_extent(*views[i], B, H, T, D) * 2;
+        if (lo < khi && klo < hi) return ATTN_ERR_ALIAS;
+    }
+    const size_t rb = (size_t)B * H * T * sizeof(float);
+    for (int i = 0; i < n_rows; ++i)
+        if ((uintptr_t)rows[i] < khi && klo < (uintptr_t)rows[i] + rb) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+int attn_fwd_strided_keep(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                          int B, int H, int T, int D, int window, float dropout_p,
+                          unsigned long long seed, float scale, int dtype, unsigned int* keep,
+                          size_t keep_bytes, void* stream)
+{
+    // the checks of attn_fwd_strided first, then those of the keep buffer
+    const int st = fwd_strided_check(q, k, v, o, lse, B, H, T, D, window, dropout_p, scale, dtype);
+    if (st != ATTN_OK) return st;
+    const attn_view_t* views[4] = {&q, &k, &v, &o};
+    const float* rows[1] = {lse};
+    const int ks = check_keep(keep, keep_bytes, B, H, T, D, views, 4, rows, 1);
+    if (ks != ATTN_OK) return ks;
+    return fwd_strided(q, k, v, o, lse, B, H, T, D, window, dropout_p, seed, scale, dtype, keep,
+                       stream);
+}
+
+int attn_bwd_strided_keep(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
+                          const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
+                          attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
+                          float dropout_p, float scale, int dtype, const unsigned int* keep,
+                          size_t keep_bytes, void* stream)
+{
+    const int st = bwd_strided_check(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, D, window,
+                                     dropout_p, scale, dtype);
+    if (st != ATTN_OK) return st;
+    const attn_view_t* views[8] = {&q, &k, &v, &o, &dO, &dq, &dk, &dv};
+    const float* rows[2] = {lse, delta};
+    const int ks = check_keep(keep, keep_bytes, B, H, T, D, views, 8, rows, 2);
+    if (ks != ATTN_OK) return ks;
+    return bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, D, window, dropout_p, 0,
+                       scale, dtype, keep, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int T_max, int D)

@@ -58,7 +58,17 @@ struct Dropout {
     uint32_t seed_lo, seed_hi;
     uint32_t p16;       // 0: no dropout
     float keep_scale;   // 65536 / (65536 - p16)
+    // Stored keep bits (nullptr: none): word (bh, w, i) of [BH][ceil(T/32)][T] holds
+    // bit t = keep decision of query i and key 32w + t.  The forward writes the
+    // words it draws; the backward items then load them instead of drawing.
+    uint32_t* keep;
 };
+
+// Word of the stored keep bits for query i and keys 32w .. 32w + 31.
+__device__ __forceinline__ size_t keep_index(int bh, int w, int i, int T)
+{
+    return ((size_t)bh * ((T + 31) / 32) + w) * T + i;
+}
 
 // kWide: each 32 x 32 -> 64-bit product as one v_mad_u64_u32 (about the cost
 // of a v_mul_hi_u32 alone), else as v_mul_hi_u32 + v_mul_lo_u32, which need no
@@ -349,7 +359,7 @@ __device__ __forceinline__ bf16* head_of(const View& v, int bh, int H)
 // three waves that share a SIMD overlap each other's LDS latency.  Every wave
 // needs tiles 0..last_w; only the last one crosses its diagonal and is masked.
 // ---------------------------------------------------------------------------
-template <int NP, bool kDrop>
+template <int NP, bool kDrop, bool kKeep = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_fwd_d64_kernel(
     View Q, View K, View V, View O, float* __restrict__ LSE, int BH, int H, int T, int W,
     int n_qtiles, float scale, float scale_log2, int n_cu, Dropout dr)
@@ -439,6 +449,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             const uint32_t oth = other_half_u32(own);
             kw_lo = hi ? oth : own;
             kw_hi = hi ? own : oth;
+            // own: keys 64j + 32hi .. +31 of this lane's query (word 2j + hi); a
+            // wave-uniform base and a 32-bit lane offset keep the address cheap
+            if constexpr (kKeep) {
+                uint32_t* const words = dr.keep + ((size_t)bh * ((T + 31) / 32) + 2 * j) * T;
+                if (qrow < T && 64 * j + 32 * hi < T) words[(uint32_t)(hi * T + qrow)] = own;
+            }
         }
         f32x16 s0, s1;
         tile_product<NP>(kc, off, qreg, s0, s1);
@@ -533,7 +549,7 @@ struct BwdParams {
 // Delta_i = sum_d dO_id O_id is formed from the rows the wave holds as MFMA
 // operands and written out.
 // ---------------------------------------------------------------------------
-template <int NP, bool kDrop>
+template <int NP, bool kDrop, bool kKeep = false>
 __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char* sK0, char* sK1,
                                         char* sV0, char* sV1)
 {
@@ -611,11 +627,17 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
         if constexpr (kDrop) {
             // dS = P (keep * keep_scale * dP - Delta).  Lane half hi draws keys
             // 16hi .. 16hi+15 of the half; w has bit b for key 32h + b.
-            const int blk0 = (k0 + 32 * h) / 8 + 2 * hi;
-            const uint32_t own = drop_bits8(a.dr, bh, qrow, blk0) |
-                                 (drop_bits8(a.dr, bh, qrow, blk0 + 1) << 8);
-            const uint32_t oth = other_half_u32(own);
-            const uint32_t w = hi ? (oth | (own << 16)) : (own | (oth << 16));
+            uint32_t w;
+            if constexpr (kKeep) {  // stored by the forward
+                const uint32_t* words = a.dr.keep + keep_index(bh, (k0 + 32 * h) / 32, 0, T);
+                w = valid ? words[(uint32_t)qrow] : 0u;
+            } else {
+                const int blk0 = (k0 + 32 * h) / 8 + 2 * hi;
+                const uint32_t own = drop_bits8(a.dr, bh, qrow, blk0) |
+                                     (drop_bits8(a.dr, bh, qrow, blk0 + 1) << 8);
+                const uint32_t oth = other_half_u32(own);
+                w = hi ? (oth | (own << 16)) : (own | (oth << 16));
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float pr = fast_exp2(fmaf(sv[r], scale_log2, nlse2));
@@ -692,7 +714,7 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
 // leaves -Delta in the row buffer, which the next step's barrier publishes.
 // Otherwise Delta is read from memory (written by a dQ pass).
 // ---------------------------------------------------------------------------
-template <int NP, bool kDeltaFromO, bool kDrop>
+template <int NP, bool kDeltaFromO, bool kDrop, bool kKeep = false>
 __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, char* sQ0, char* sQ1,
                                           char* sG0, char* sG1, char* sO0, char* sO1,
                                           float (*sR0)[kTile], float (*sR1)[kTile])
@@ -795,7 +817,11 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     auto runs_half0 = [&](int i) { return i > first_w || i * kTile + 31 >= k0w; };
     auto draw_half = [&](int i, int h) -> uint32_t {
         const int blk0 = k0w / 8 + 2 * hi, qd = i * kTile + 32 * h + li;
-        return drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
+        if constexpr (kKeep)  // stored by the forward: this lane half's 16 keys of the word
+            return qd < T ? (a.dr.keep[keep_index(bh, k0w / 32, 0, T) + (uint32_t)qd] >> (16 * hi)) & 0xFFFFu
+                          : 0u;
+        else
+            return drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
     };
     uint32_t dbits = 0;  // keep bits of the half about to run
     if constexpr (kDrop) {
@@ -935,7 +961,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
 }
 
 // dQ alone (also writes Delta).
-template <int NP, bool kDrop>
+template <int NP, bool kDrop, bool kKeep = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dq_d64_kernel(
     BwdParams a, int n_qtiles, int n_cu)
 {
@@ -945,11 +971,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char sV0[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV1[NP * kTileBytes];
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    dq_item<NP, kDrop>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1);
+    dq_item<NP, kDrop, kKeep>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1);
 }
 
 // dK, dV alone, from a Delta in memory.
-template <int NP, bool kDrop>
+template <int NP, bool kDrop, bool kKeep = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dkdv_d64_kernel(
     BwdParams a, int n_cu)
 {
@@ -960,7 +986,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
     __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    dkdv_item<NP, false, kDrop>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1, nullptr, nullptr,
+    dkdv_item<NP, false, kDrop, kKeep>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1, nullptr, nullptr,
                                 sR0, sR1);
 }
 
@@ -973,7 +999,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 // count (a dK/dV tile costs more): level v holds the dK/dV items of key block v
 // and the dQ items of query block n - 1 - v, BH of each.
 // ---------------------------------------------------------------------------
-template <bool kDrop>
+template <bool kDrop, bool kKeep = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_d64_kernel(
     BwdParams a, int n_blocks, int n_cu)
 {
@@ -989,9 +1015,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int BH = a.BH;
     const int level = item / (2 * BH), r = item - level * 2 * BH;
     if (r < BH)
-        dkdv_item<1, true, kDrop>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1);
+        dkdv_item<1, true, kDrop, kKeep>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1);
     else
-        dq_item<1, kDrop>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
+        dq_item<1, kDrop, kKeep>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
 }
 
 }  // namespace d64
@@ -1011,6 +1037,7 @@ static d64::Dropout dropout_of(const AttnArgs& a)
     d.seed_hi = (uint32_t)(a.dropout_seed >> 32);
     d.p16 = (uint32_t)a.dropout_p16;
     d.keep_scale = (float)(65536.0 / (65536.0 - (double)a.dropout_p16));
+    d.keep = a.keep;
     return d;
 }
 
@@ -1019,8 +1046,11 @@ hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     const bool drop = a.dropout_p16 > 0;
-    auto k = a.D == 128 ? (drop ? d64::attn_fwd_d64_kernel<2, true> : d64::attn_fwd_d64_kernel<2, false>)
-                        : (drop ? d64::attn_fwd_d64_kernel<1, true> : d64::attn_fwd_d64_kernel<1, false>);
+    const bool keep = drop && a.keep;  // also store the keep bits
+    auto k = a.D == 128 ? (keep ? d64::attn_fwd_d64_kernel<2, true, true>
+                                : drop ? d64::attn_fwd_d64_kernel<2, true> : d64::attn_fwd_d64_kernel<2, false>)
+                        : (keep ? d64::attn_fwd_d64_kernel<1, true, true>
+                                : drop ? d64::attn_fwd_d64_kernel<1, true> : d64::attn_fwd_d64_kernel<1, false>);
     hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
                        view(a.q, a.sq), view(a.k, a.sk), view(a.v, a.sv), view(a.o_out, a.so),
                        a.lse, BH, a.H, a.T, window_of(a), nqt, a.scale, a.scale * kLog2e, a.n_cu,
@@ -1056,8 +1086,11 @@ hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st)
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     const bool drop = a.dropout_p16 > 0;
-    auto k = a.D == 128 ? (drop ? d64::attn_bwd_dq_d64_kernel<2, true> : d64::attn_bwd_dq_d64_kernel<2, false>)
-                        : (drop ? d64::attn_bwd_dq_d64_kernel<1, true> : d64::attn_bwd_dq_d64_kernel<1, false>);
+    const bool keep = drop && a.keep;  // load the stored keep bits
+    auto k = a.D == 128 ? (keep ? d64::attn_bwd_dq_d64_kernel<2, true, true>
+                                : drop ? d64::attn_bwd_dq_d64_kernel<2, true> : d64::attn_bwd_dq_d64_kernel<2, false>)
+                        : (keep ? d64::attn_bwd_dq_d64_kernel<1, true, true>
+                                : drop ? d64::attn_bwd_dq_d64_kernel<1, true> : d64::attn_bwd_dq_d64_kernel<1, false>);
     hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nqt, a.n_cu);
     return hipGetLastError();
 }
@@ -1067,8 +1100,11 @@ hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st)
     const int BH = a.B * a.H;
     const int nkt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     const bool drop = a.dropout_p16 > 0;
-    auto k = a.D == 128 ? (drop ? d64::attn_bwd_dkdv_d64_kernel<2, true> : d64::attn_bwd_dkdv_d64_kernel<2, false>)
-                        : (drop ? d64::attn_bwd_dkdv_d64_kernel<1, true> : d64::attn_bwd_dkdv_d64_kernel<1, false>);
+    const bool keep = drop && a.keep;
+    auto k = a.D == 128 ? (keep ? d64::attn_bwd_dkdv_d64_kernel<2, true, true>
+                                : drop ? d64::attn_bwd_dkdv_d64_kernel<2, true> : d64::attn_bwd_dkdv_d64_kernel<2, false>)
+                        : (keep ? d64::attn_bwd_dkdv_d64_kernel<1, true, true>
+                                : drop ? d64::attn_bwd_dkdv_d64_kernel<1, true> : d64::attn_bwd_dkdv_d64_kernel<1, false>);
     hipLaunchKernelGGL(k, dim3(nkt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), a.n_cu);
     return hipGetLastError();
 }
@@ -1081,7 +1117,8 @@ hipError_t launch_bwd_bf16_d64(const AttnArgs& a, hipStream_t st)
     }
     const int BH = a.B * a.H;
     const int nb = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
-    auto k = a.dropout_p16 > 0 ? d64::attn_bwd_d64_kernel<true> : d64::attn_bwd_d64_kernel<false>;
+    auto k = a.dropout_p16 > 0 ? (a.keep ? d64::attn_bwd_d64_kernel<true, true> : d64::attn_bwd_d64_kernel<true>)
+                               : d64::attn_bwd_d64_kernel<false>;
     hipLaunchKernelGGL(k, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nb, a.n_cu);
     return hipGetLastError();
 }

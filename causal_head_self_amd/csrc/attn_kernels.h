@@ -32,6 +32,10 @@ struct AttnArgs {
                      // window argument accept no other case.
     int dropout_p16;                  // attention dropout: round(p * 65536); 0 = none
     unsigned long long dropout_seed;  // Philox key
+    // stored keep bits, [B*H][ceil(T/32)][T] words (bit t of word (bh, w, i): query i,
+    // key 32w + t): the forward writes them when set, the backward reads them
+    // instead of drawing; nullptr: the backward draws them again
+    unsigned int* keep;
     // strides of q, k, v, o, dO, dq, dk, dv (contiguous unless a strided entry point set them)
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
 };

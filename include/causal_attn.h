@@ -175,6 +175,37 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
                      float dropout_p, unsigned long long seed, float scale, int dtype,
                      void* stream);
 
+/* Stored keep bits: the dropout forward's keep decisions kept for its backward.
+ * With dropout the forward and both backward stages each draw the keep bits of
+ * the weights they touch (Philox, as above).  These two entry points let the
+ * forward store its draws in a caller-owned buffer and the backward load them
+ * instead of drawing again; the results are bit for bit those of
+ * attn_fwd_strided / attn_bwd_strided with the same dropout_p and seed.
+ *
+ *   keep:       uint32 words, [B*H][ceil(T/32)][T]: bit t of word (b*H + h, w, i)
+ *               is the keep decision of query i and key 32 w + t (1 = kept).  The
+ *               forward writes the words of the (query, 32-key block) pairs it
+ *               visits; the rest of the buffer is neither written nor read.  The
+ *               caller owns it; 4-byte aligned; it must not overlap any other
+ *               buffer of the call (ATTN_ERR_ALIAS).
+ *   keep_bytes: its size, at least attn_dropout_keep_bytes(B, H, T)
+ *               (ATTN_ERR_WORKSPACE otherwise; 0 for a non-positive size).
+ *
+ * The backward takes the forward's dropout_p (the keep scale) but no seed.
+ * With dropout_p = 0 the buffer is neither written nor read.  Errors: those of
+ * the strided call first, then ATTN_ERR_NULL, ATTN_ERR_ALIGN,
+ * ATTN_ERR_WORKSPACE and ATTN_ERR_ALIAS for the keep buffer. */
+size_t attn_dropout_keep_bytes(int B, int H, int T);
+int attn_fwd_strided_keep(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                          int B, int H, int T, int D, int window, float dropout_p,
+                          unsigned long long seed, float scale, int dtype, unsigned int* keep,
+                          size_t keep_bytes, void* stream);
+int attn_bwd_strided_keep(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
+                          const float* lse, attn_view_t dO, attn_view_t dq, attn_view_t dk,
+                          attn_view_t dv, float* delta, int B, int H, int T, int D, int window,
+                          float dropout_p, float scale, int dtype, const unsigned int* keep,
+                          size_t keep_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Decode against a KV cache.  nanochat, section 8 (inference engine): the
  * cache is kept in FA3's native (B, T, H, D) layout, a prompt is prefilled
@@ -250,7 +281,7 @@ const char* attn_status_str(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 4)
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 5)
 
 #ifdef __cplusplus
 }

@@ -285,6 +285,49 @@ def test_strided_dropout_probability_range():
         assert _bwd_s(dropout_p=p) == 12, p
 
 
+def test_dropout_keep_bytes():
+    kb = cat.load_library().attn_dropout_keep_bytes
+    assert kb(2, 3, 17) == 2 * 3 * 1 * 17 * 4
+    assert kb(8, 12, 1024) == 8 * 12 * 32 * 1024 * 4
+    assert kb(1, 1, 33) == 2 * 33 * 4
+    assert kb(0, 1, 1) == 0 and kb(1, 0, 1) == 0 and kb(1, 1, 0) == 0 and kb(-1, 2, 3) == 0
+
+
+KEEP = P[11]
+KEEP_BYTES = 2 * 3 * 1 * 17 * 4
+
+
+def _fwd_k(keep=KEEP, keep_bytes=KEEP_BYTES, T=T_, dropout_p=0.1, views=None):
+    v = views or [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3])]
+    return cat.load_library().attn_fwd_strided_keep(v[0], v[1], v[2], v[3], P[4], B_, H_, T, D_, 0,
+                                                    dropout_p, 0, 0.125, 1, keep, keep_bytes, None)
+
+
+def _bwd_k(keep=KEEP, keep_bytes=KEEP_BYTES, T=T_, dropout_p=0.1):
+    v = [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3]), _v(P[5]), _v(P[6]), _v(P[7]), _v(P[8])]
+    return cat.load_library().attn_bwd_strided_keep(v[0], v[1], v[2], v[3], P[4], v[4], v[5], v[6],
+                                                    v[7], P[9], B_, H_, T, D_, 0, dropout_p, 0.125,
+                                                    1, keep, keep_bytes, None)
+
+
+def test_keep_entry_points_check_the_strided_arguments_first():
+    assert _fwd_k(T=0, keep=0) == 2        # shape before the keep buffer
+    assert _bwd_k(T=0, keep=0) == 2
+    assert _fwd_k(dropout_p=1.5, keep=0) == 12
+    assert _bwd_k(dropout_p=-1.0, keep=0) == 12
+
+
+@_last_check
+def test_keep_buffer_checks():
+    for call in (_fwd_k, _bwd_k):
+        assert call(keep=0) == 1                               # null
+        assert call(keep=KEEP + 2) == 5                        # not 4-byte aligned
+        assert call(keep_bytes=KEEP_BYTES - 4) == 11           # too small
+        assert call(keep=P[1] + 64) == 8                       # inside k
+        assert call(keep=P[4]) == 8                            # on lse
+    assert _bwd_k(keep=P[9] - 4, keep_bytes=KEEP_BYTES) == 8   # overlaps delta
+
+
 def test_strided_supports_only_bf16_d64_d128():
     assert _fwd_s(dtype=0) == 10
     assert _bwd_s(dtype=0) == 10

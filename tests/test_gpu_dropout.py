@@ -126,3 +126,54 @@ def test_qkv_autograd_with_dropout():
     got = dict(o=as_np(y.view(B, T, H, D).permute(0, 2, 1, 3)), dq=as_np(g[0]), dk=as_np(g[1]),
                dv=as_np(g[2]))
     check(got, dict(o=o, dq=dq, dk=dk, dv=dv), "qkv dropout")
+
+
+@pytest.mark.parametrize("shape,p,window", [
+    ((2, 3, 200, 64), 0.2, 0), ((1, 2, 130, 128), 0.3, 50), ((2, 2, 257, 64), 0.1, 0),
+    ((1, 1, 33, 64), 0.5, 0), ((1, 2, 300, 64), 0.25, 64)])
+def test_stored_keep_bits(shape, p, window):
+    """attn_fwd_strided_keep / attn_bwd_strided_keep give the same bits as the
+    entry points that draw, and every stored word of a visible (query, key)
+    pair holds the oracle's keep decision (bit t of word (bh, w, i) is key
+    32w + t)."""
+    import causal_head_self_amd as cat
+    B, H, T, D = shape
+    seed = 0xC0FFEE + T
+    _note(f"[dropout] stored keep bits B={B} H={H} T={T} D={D} p={p} window={window}")
+    dev = torch.device("cuda")
+    q, k, v, dO = (t.to(dev).contiguous()
+                   for t in workloads.attention_inputs(B, H, T, D, "bf16", 1500 + T))
+
+    def run(keep):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        delta = torch.empty_like(lse)
+        if keep is None:
+            cat.attn_fwd_strided(q, k, v, o, lse, window=window, dropout_p=p, seed=seed)
+            cat.attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, window=window,
+                                 dropout_p=p, seed=seed)
+        else:
+            cat.attn_fwd_strided_keep(q, k, v, o, lse, keep, window=window, dropout_p=p,
+                                      seed=seed)
+            cat.attn_bwd_strided_keep(q, k, v, o, lse, dO, dq, dk, dv, delta, keep,
+                                      window=window, dropout_p=p)
+        torch.cuda.synchronize()
+        return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
+
+    ref = run(None)
+    keep = torch.full((cat.dropout_keep_bytes(B, H, T) // 4,), -1, dtype=torch.int32, device=dev)
+    got = run(keep)
+    for n in ref:
+        assert torch.equal(got[n], ref[n]), n
+    words = keep.cpu().numpy().astype(np.uint32).reshape(B * H, (T + 31) // 32, T)
+    p16 = oracle.dropout_threshold(p)
+    checked = 0
+    for bh in range(B * H):
+        for i in range(T):
+            lo = max(0, i - window + 1) if window else 0
+            for j in range(lo, i + 1):
+                bit = (int(words[bh, j // 32, i]) >> (j % 32)) & 1
+                assert bit == int(oracle.dropout_keep(seed, p16, bh, i, j)), (bh, i, j)
+                checked += 1
+    _note(f"    {checked} keep decisions checked")
