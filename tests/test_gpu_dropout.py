@@ -177,3 +177,54 @@ def test_stored_keep_bits(shape, p, window):
                 assert bit == int(oracle.dropout_keep(seed, p16, bh, i, j)), (bh, i, j)
                 checked += 1
     _note(f"    {checked} keep decisions checked")
+
+
+def test_stored_keep_bits_past_2_32_bytes():
+    """Dropout p = 0.1 with stored keep bits at B=2 H=17000 T=1000 D=64: every
+    tensor holds 2.18e9 elements and the keep buffer takes 4.35 GB, so the keep
+    words of the last heads sit past 2^32 bytes.  The sampled heads (the first,
+    those that straddle 2^30 and 2^31 tensor elements, and the last) match the
+    oracle, given each head's global index, element by element, and 4000 sampled
+    stored words of each hold the oracle's keep decisions."""
+    import causal_head_self_amd as cat
+    B, H, T, D = 2, 17000, 1000, 64
+    p, seed = 0.1, 0xBEEF
+    per_head, n_words = T * D, (T + 31) // 32
+    _note(f"[dropout] stored keep bits B={B} H={H} T={T} D={D} p={p}: "
+          f"keep buffer {cat.dropout_keep_bytes(B, H, T)} bytes")
+    dev = torch.device("cuda")
+    q, k, v, dO = workloads.device_attention_inputs(B, H, T, D, dev, seed=77)
+    scale = 1.0 / math.sqrt(D)
+    keep = torch.full((cat.dropout_keep_bytes(B, H, T) // 4,), -1, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty_like(lse)
+    cat.attn_fwd_strided_keep(q, k, v, o, lse, keep, scale=scale, dropout_p=p, seed=seed)
+    cat.attn_bwd_strided_keep(q, k, v, o, lse, dO, dq, dk, dv, delta, keep, scale=scale,
+                              dropout_p=p)
+    torch.cuda.synchronize()
+    p16 = oracle.dropout_threshold(p)
+    rng = np.random.default_rng(5)
+    for bh in [0, 2 ** 30 // per_head, 2 ** 31 // per_head, B * H - 1]:
+        b, h = divmod(bh, H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        cpu = lambda t: t[sl].cpu()
+        got = {n: t[sl].float().cpu().numpy().astype(np.float64)
+               for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv),
+                            ("delta", delta))}
+        ro, rl = oracle.attn_fwd_dropout(cpu(q), cpu(k), cpu(v), scale, p, seed, bh0=bh)
+        rq, rk, rv, rd = oracle.attn_bwd_dropout(cpu(q), cpu(k), cpu(v), cpu(dO), scale, p,
+                                                 seed, bh0=bh)
+        _note(f"  head {bh}: keep words from byte {bh * n_words * T * 4}")
+        check(got, dict(o=ro, lse=rl, dq=rq, dk=rk, dv=rv, delta=rd), f"head {bh}",
+              cpu(dO).double().numpy())
+        words = keep[bh * n_words * T:(bh + 1) * n_words * T].cpu().numpy().astype(np.uint32)
+        words = words.reshape(n_words, T)
+        for _ in range(4000):
+            i = int(rng.integers(0, T))
+            j = int(rng.integers(0, i + 1))
+            bit = (int(words[j // 32, i]) >> (j % 32)) & 1
+            assert bit == int(oracle.dropout_keep(seed, p16, bh, i, j)), (bh, i, j)
+    del q, k, v, dO, o, dq, dk, dv, keep
+    torch.cuda.empty_cache()

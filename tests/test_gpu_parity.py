@@ -197,6 +197,48 @@ def test_full_config_sampled_heads(name):
                      delta_bound(ref, dO[sl]), scaled_tol(c.D))
 
 
+def test_tensors_past_2_31_elements():
+    """Every tensor of B=2 H=17000 T=1000 D=64 holds 2.18e9 elements (4.35 GB
+    in bf16), past 2^31 bytes and 2^31 elements, with a ragged last tile (T %
+    64 = 40).  Offsets past those boundaries must be formed in 64 bits.  Pinned
+    on the whole tensors: row 0 of every head sees only key 0, so o[.., 0, :]
+    equals v[.., 0, :] bit for bit, and every output is finite.  Pinned element
+    by element against the oracle: the first head, the heads that straddle
+    2^30 and 2^31 elements, and the last head."""
+    import causal_head_self_amd as cat
+    B, H, T, D = 2, 17000, 1000, 64
+    per_head = T * D
+    assert B * H * per_head > 2 ** 31
+    _note(f"[parity] B={B} H={H} T={T} D={D} bf16: tensors of {B * H * per_head} elements")
+    dev = torch.device("cuda")
+    q, k, v, dO = workloads.device_attention_inputs(B, H, T, D, dev)
+    scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    cat.attn_fwd(q, k, v, o, lse, scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty_like(lse)
+    cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0, :], v[:, :, 0, :])
+    for name, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv), ("delta", delta)):
+        assert bool(torch.isfinite(t).all()), name
+    heads = [0, 2 ** 30 // per_head, 2 ** 31 // per_head, B * H - 1]
+    for bh in heads:
+        b, h = divmod(bh, H)
+        first, last = bh * per_head, (bh + 1) * per_head - 1
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        cpu = lambda t: t[sl].cpu()
+        got = {n: t[sl].float().cpu().numpy().astype(np.float64)
+               for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv),
+                            ("delta", delta))}
+        ref = oracle_attention(cpu(q), cpu(k), cpu(v), cpu(dO), scale)
+        assert_close(got, ref, TOL["bf16"], f"head {bh} (elements {first}..{last})",
+                     delta_bound(ref, cpu(dO)))
+    del q, k, v, dO, o, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # exactness pins and invariants on the GPU
 # ---------------------------------------------------------------------------

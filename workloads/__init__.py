@@ -126,6 +126,21 @@ def attention_inputs(B: int, H: int, T: int, D: int, dtype="bf16", seed: int = S
     return tuple(_draw(shape, i, 1.0, dt, seed) for i in range(4))
 
 
+def device_attention_inputs(B: int, H: int, T: int, D: int, device, seed: int = SEED):
+    """q, k, v, dO as bf16 [B, H, T, D] tensors drawn on `device` (for shapes too
+    large to draw on the host): the same recipe as attention_inputs (float32
+    N(0, 1) from a generator seeded seed + idx, rounded to bf16), but from the
+    device generator, so the values differ from the host draws of that shape."""
+    out = []
+    for idx in range(4):
+        g = torch.Generator(device=device).manual_seed(seed + idx)
+        x = torch.empty((B, H, T, D), dtype=torch.bfloat16, device=device)
+        for b in range(B):  # one batch at a time keeps the float32 temporary small
+            x[b] = torch.randn((H, T, D), generator=g, dtype=torch.float32, device=device)
+        out.append(x)
+    return tuple(out)
+
+
 def config_inputs(cfg: AttnConfig, seed: int = SEED):
     return attention_inputs(cfg.B, cfg.H, cfg.T, cfg.D, cfg.dtype, seed)
 
