@@ -150,3 +150,41 @@ def test_decode_equals_last_row_of_prefill_forward():
         o, _ = gpu_decode(q[:, :, n - 1].contiguous(), kc, vc, [n] * B)
         full = o_full[:, :, n - 1].float().cpu().numpy()
         assert np.abs(o - full).max() <= 2 * TOL
+
+
+@pytest.mark.parametrize("B,H,T_max,D,one_launch", [
+    (66, 16, 32768, 64, True),       # 1056 heads: one launch
+    (1, 100, 336544, 64, False),     # 100 heads, 5259 slices each: two launches
+])
+def test_decode_caches_past_2_31_elements(B, H, T_max, D, one_launch):
+    """K/V caches of more than 2^31 elements (4.3-4.4 GB each in bf16), so the
+    positions of the last sequences and heads lie past 2^31 elements.  Each
+    case takes the path named (the library's rule: one launch when every wave
+    of a workgroup has at most one 64-position slice or when B*H reaches half
+    the compute units).  Sampled (sequence, head) pairs, the last one included,
+    are compared with the oracle on that head alone."""
+    import causal_head_self_amd as cat
+    assert B * T_max * H * D > 2 ** 31
+    dev = torch.device("cuda")
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    assert (-(-T_max // 64) <= 16 or 2 * B * H >= n_cu) == one_launch
+    _note(f"[decode] B={B} H={H} T_max={T_max} D={D}: caches of {B * T_max * H * D} elements, "
+          f"{'one launch' if one_launch else 'two launches'}")
+    q, kc, vc = workloads.device_decode_inputs(B, H, T_max, D, dev, seed=91)
+    lens = [T_max - 37 * b for b in range(B)]
+    ln = torch.tensor(lens, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = cat.decode_attention(q, kc, vc, ln, scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    for b, h in [(0, 0), (B // 2, H // 3), (B - 1, H - 1)]:
+        n = lens[b]
+        ro, rlse = oracle.attn_decode(q[b:b + 1, h:h + 1].cpu(), kc[b:b + 1, :n, h:h + 1].cpu(),
+                                      vc[b:b + 1, :n, h:h + 1].cpu(), [n],
+                                      oracle.widen_scale(scale))
+        eo = float(np.abs(o[b, h].float().cpu().numpy() - ro[0, 0]).max())
+        el = abs(float(lse[b, h]) - float(rlse[0, 0]))
+        _note(f"    (b={b}, h={h}) len {n}: max |o - ref| {eo:.2e}, |lse - ref| {el:.2e}")
+        assert eo <= TOL and el <= TOL, (b, h, eo, el)
+    del q, kc, vc
+    torch.cuda.empty_cache()

@@ -141,6 +141,21 @@ def device_attention_inputs(B: int, H: int, T: int, D: int, device, seed: int = 
     return tuple(out)
 
 
+def device_decode_inputs(B: int, H: int, T_max: int, D: int, device, seed: int = SEED):
+    """q [B, H, D] and k_cache, v_cache [B, T_max, H, D] as bf16 tensors drawn on
+    `device`: the decode_inputs recipe from the device generator."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    q = torch.randn((B, H, D), generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+    out = [q]
+    for idx in (1, 2):
+        g = torch.Generator(device=device).manual_seed(seed + idx)
+        x = torch.empty((B, T_max, H, D), dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            x[b] = torch.randn((T_max, H, D), generator=g, dtype=torch.float32, device=device)
+        out.append(x)
+    return tuple(out)
+
+
 def config_inputs(cfg: AttnConfig, seed: int = SEED):
     return attention_inputs(cfg.B, cfg.H, cfg.T, cfg.D, cfg.dtype, seed)
 
