@@ -1,10 +1,11 @@
 """Host-side logic of bench.py (no GPU): the work convention and the refusal
-of multi-GPU runs."""
+of multi-GPU runs, and the seeded input generators."""
 import os
 import subprocess
 import sys
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -42,3 +43,25 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_device_input_generators_follow_the_host_recipe():
+    """The device-side generators (used for tensors too large to draw on the
+    host) give bf16 tensors of the stated shapes, reproducible per seed, with
+    q, k, v, dO drawn from different streams and unit-variance values.  Run
+    here on the CPU device."""
+    q, k, v, dO = workloads.device_attention_inputs(2, 3, 40, 64, "cpu", seed=5)
+    again = workloads.device_attention_inputs(2, 3, 40, 64, "cpu", seed=5)
+    for a, b in zip((q, k, v, dO), again):
+        assert a.shape == (2, 3, 40, 64) and a.dtype == torch.bfloat16
+        assert torch.equal(a, b)
+    assert not torch.equal(q, k) and not torch.equal(v, dO)
+    x = torch.cat([t.float().flatten() for t in (q, k, v, dO)])
+    assert abs(float(x.mean())) < 0.05 and abs(float(x.std()) - 1.0) < 0.05
+    # with one batch the device recipe is the host recipe on the CPU device
+    q1, _, _, _ = workloads.device_attention_inputs(1, 3, 40, 64, "cpu", seed=5)
+    assert torch.equal(q1, workloads.attention_inputs(1, 3, 40, 64, "bf16", 5)[0])
+    qd, kc, vc = workloads.device_decode_inputs(3, 2, 50, 64, "cpu", seed=9)
+    assert qd.shape == (3, 2, 64) and kc.shape == vc.shape == (3, 50, 2, 64)
+    assert qd.dtype == kc.dtype == vc.dtype == torch.bfloat16
+    assert torch.equal(kc, workloads.device_decode_inputs(3, 2, 50, 64, "cpu", seed=9)[1])
