@@ -42,6 +42,8 @@ KERNEL_SOURCES = {
                   "causal_head_self_amd/csrc/attn_device.h"],
     "decode": ["causal_head_self_amd/csrc/attn_decode.hip",
                "causal_head_self_amd/csrc/attn_device.h"],
+    "rope": ["causal_head_self_amd/csrc/attn_rope.hip",
+             "causal_head_self_amd/csrc/attn_device.h"],
 }
 
 
@@ -363,35 +365,65 @@ def rope_bench(args) -> int:
     stream = torch.cuda.current_stream()
     names = ["rope_fwd", "rope_bwd"]
 
-    def run(n, evs=None):
-        for i in range(n):
-            if evs:
-                evs[i][0].record(stream)
-            cat.rope_qknorm_fwd(qv, kv, qo, ko, p, stream)
-            if evs:
-                evs[i][1].record(stream)
-            cat.rope_qknorm_bwd(qv, kv, g, g, dq, dk, p, stream)
-            if evs:
-                evs[i][2].record(stream)
+    # the incoming gradients of q and k: two distinct N(0, 1) tensors (v is not
+    # otherwise used here), so that the gradient launch reads both from memory
+    gq, gk = g, v
+    launch = {"rope_fwd": lambda: cat.rope_qknorm_fwd(qv, kv, qo, ko, p, stream),
+              "rope_bwd": lambda: cat.rope_qknorm_bwd(qv, kv, gq, gk, dq, dk, p, stream)}
+
+    def run(n, which=names):
+        for _ in range(n):
+            for name in which:
+                launch[name]()
 
     run(args.warmup)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     run(args.steps)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    run(args.steps, evs)
-    torch.cuda.synchronize()
-    kern = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-            for i, n in enumerate(names)}
+    # per launch: each kind back to back on its own (events around single
+    # launches of this length would also time the host's enqueue gaps)
+    kern = {}
+    for name in names:
+        t0.record(stream)
+        run(args.steps, [name])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        kern[name] = t0.elapsed_time(t1) / args.steps
     elem = B * H * T * D
     byt = {"rope_fwd": 4.0 * elem * 2, "rope_bwd": 6.0 * elem * 2}
     gbs = (byt["rope_fwd"] + byt["rope_bwd"]) / (ms * 1e-3) / 1e9
     dom = max(names, key=lambda n: kern[n])
     ach = byt[dom] / (kern[dom] * 1e-3) / 1e9
+    if args.copy_calibration_mib > 0:  # a plain device copy of known size (counter scaling)
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    sha = kernel_source_sha("rope")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle (one host thread) over the whole workload: forward and
+        # gradient of q and k
+        import oracle
+        hq, hk, hgq, hgk = (t.cpu() for t in (q, k, gq, gk))
+        c0 = time.perf_counter()
+        oracle.rope_qknorm_fwd(hq, p.pos0, p.base, p.rope, p.qk_norm, p.q_gain, p.eps)
+        oracle.rope_qknorm_fwd(hk, p.pos0, p.base, p.rope, p.qk_norm, p.k_gain, p.eps)
+        oracle.rope_qknorm_bwd(hq, hgq, p.pos0, p.base, p.rope, p.qk_norm, p.q_gain, p.eps)
+        oracle.rope_qknorm_bwd(hk, hgk, p.pos0, p.base, p.rope, p.qk_norm, p.k_gain, p.eps)
+        dt = time.perf_counter() - c0
+        cpu = {"value": round((byt["rope_fwd"] + byt["rope_bwd"]) / dt / 1e9, 4), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": (f"one fp64 forward and gradient over the whole workload ({B * H * T} "
+                          f"q rows and as many k rows); {dt:.3f} s wall; host "
+                          f"{platform.processor() or platform.machine()}"),
+               "seconds": round(dt, 4)}
     out = {
         "metric": "RoPE + QK-norm prologue (forward + gradient): algorithmic bytes per second",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -404,8 +436,10 @@ def rope_bench(args) -> int:
         "kernel_ms": {n: round(v_, 5) for n, v_ in kern.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": byt[dom]},
-        "cpu_baseline": None,
+                     "traffic": read_traffic(dom, f"rope_gpt2s_B{B}_H{H}_T{T}_D{D}", sha),
+                     "algorithmic_bytes_per_launch": byt[dom]},
+        "cpu_baseline": cpu,
+        "kernel_src_sha": sha,
         "l2_flushed": False,
     }
     print(json.dumps(out), flush=True)
