@@ -5,7 +5,8 @@ bit for bit (the kernels are deterministic), with eager work and
 synchronisations between the replays.  The kernels record no memset and
 allocate nothing, so they are capturable.  The cases cover the plain and the
 strided entry points (with a window and dropout, and the two-launch backward at
-D = 128) and both decode paths."""
+D = 128), the entry points with stored dropout keep bits, and both decode
+paths."""
 import sys
 
 import pytest
@@ -21,22 +22,35 @@ def _note(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("B,H,T,D,window,p", [
-    (2, 3, 300, 64, 0, 0.0),      # attn_fwd / attn_bwd (one backward launch)
-    (2, 2, 300, 128, 100, 0.1),   # strided entry points: window, dropout, two backward launches
-    (1, 3, 200, 64, 70, 0.2),     # strided, window and dropout at D = 64
+@pytest.mark.parametrize("B,H,T,D,window,p,keep_bits", [
+    (2, 3, 300, 64, 0, 0.0, False),     # attn_fwd / attn_bwd (one backward launch)
+    (2, 2, 300, 128, 100, 0.1, False),  # strided entry points: window, dropout, two backward launches
+    (1, 3, 200, 64, 70, 0.2, False),    # strided, window and dropout at D = 64
+    (2, 3, 300, 64, 0, 0.1, True),      # dropout with stored keep bits
+    (1, 2, 260, 128, 90, 0.2, True),    # stored keep bits, window, two backward launches
 ])
-def test_attention_step_graph_replays_match_eager(B, H, T, D, window, p):
+def test_attention_step_graph_replays_match_eager(B, H, T, D, window, p, keep_bits):
+    """With stored keep bits the keep buffer starts zeroed for the eager step and
+    is set to all ones (every weight kept) before each replay, so a word of a
+    visible pair that the replayed forward did not rewrite would change the
+    backward's outputs."""
     import causal_head_self_amd as cat
-    _note(f"[graph] attention fwd+bwd B={B} H={H} T={T} D={D} window={window} p={p}")
+    _note(f"[graph] attention fwd+bwd B={B} H={H} T={T} D={D} window={window} p={p} "
+          f"keep_bits={keep_bits}")
     dev = torch.device("cuda")
     q, k, v, dO = (t.to(dev) for t in workloads.attention_inputs(B, H, T, D, "bf16", 501))
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     delta = torch.empty_like(lse)
+    keep = (torch.zeros(cat.dropout_keep_bytes(B, H, T) // 4, dtype=torch.int32, device=dev)
+            if keep_bits else None)
 
     def step():
-        if window == 0 and p == 0.0:
+        if keep_bits:
+            cat.attn_fwd_strided_keep(q, k, v, o, lse, keep, window=window, dropout_p=p, seed=99)
+            cat.attn_bwd_strided_keep(q, k, v, o, lse, dO, dq, dk, dv, delta, keep,
+                                      window=window, dropout_p=p)
+        elif window == 0 and p == 0.0:
             cat.attn_fwd(q, k, v, o, lse)
             cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta)
         else:
@@ -46,7 +60,9 @@ def test_attention_step_graph_replays_match_eager(B, H, T, D, window, p):
 
     step()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (o, lse, dq, dk, dv, delta)]
+    outs = (o, lse, dq, dk, dv, delta)
+    names = ("o", "lse", "dq", "dk", "dv", "delta")
+    ref = [t.clone() for t in outs]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):  # warm the stream before capture
@@ -59,11 +75,12 @@ def test_attention_step_graph_replays_match_eager(B, H, T, D, window, p):
     for rep in range(3):
         for t in (o, lse, dq, dk, dv, delta):
             t.fill_(float("nan"))  # eager work between replays
+        if keep_bits:
+            keep.fill_(-1)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, a, r in zip(("o", "lse", "dq", "dk", "dv", "delta"),
-                              (o, lse, dq, dk, dv, delta), ref):
+        for name, a, r in zip(names, outs, ref):
             assert torch.equal(a, r), f"replay {rep}: {name}"
 
 
