@@ -1,6 +1,7 @@
 """A seeded sweep of random combinations of the training-attention options
 (batch, heads, ragged length, head dim, window, dropout, strided or contiguous
-layout) against the fp64 oracle, element by element.  The cases are drawn
+layout) against the fp64 oracle, element by element; with dropout, the entry
+points with stored keep bits must give the same bits.  The cases are drawn
 from a fixed seed, so every run checks the same list."""
 import math
 import random
@@ -74,3 +75,17 @@ def test_random_combination_matches_oracle(B, H, T, D, window, p, fused, seed):
         err = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
         assert np.all(np.isfinite(got)), name
         assert float(err.max()) <= 2e-2, f"{name}: {float(err.max()):.3e}"
+    if p > 0:  # the stored-keep-bit entry points give the same bits as the drawing ones
+        keep = torch.full((cat.dropout_keep_bytes(B, H, T) // 4,), -1, dtype=torch.int32,
+                          device=dev)
+        o2, dq2, dk2, dv2 = (torch.empty((B, H, T, D), dtype=torch.bfloat16, device=dev)
+                             for _ in range(4))
+        lse2, delta2 = torch.empty_like(lse), torch.empty_like(delta)
+        cat.attn_fwd_strided_keep(qd, kd, vd, o2, lse2, keep, scale, window=window, dropout_p=p,
+                                  seed=seed)
+        cat.attn_bwd_strided_keep(qd, kd, vd, o2, lse2, gd, dq2, dk2, dv2, delta2, keep, scale,
+                                  window=window, dropout_p=p)
+        torch.cuda.synchronize()
+        for name, a, b in (("o", od, o2), ("lse", lse, lse2), ("dq", dqd, dq2), ("dk", dkd, dk2),
+                           ("dv", dvd, dv2), ("delta", delta, delta2)):
+            assert torch.equal(a.contiguous(), b), f"stored keep bits: {name}"
