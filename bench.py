@@ -39,7 +39,9 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "attention": ["causal_head_self_amd/csrc/attn_bf16.hip",
                   "causal_head_self_amd/csrc/attn_bf16_d64.hip",
-                  "causal_head_self_amd/csrc/attn_device.h"],
+                  "causal_head_self_amd/csrc/attn_bwd_plain.hip",
+                  "causal_head_self_amd/csrc/attn_device.h",
+                  "causal_head_self_amd/build.py"],  # per-file compiler flags
     "decode": ["causal_head_self_amd/csrc/attn_decode.hip",
                "causal_head_self_amd/csrc/attn_device.h"],
     "rope": ["causal_head_self_amd/csrc/attn_rope.hip",

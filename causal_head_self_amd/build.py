@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcausal_attn.so")
-SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_bf16_d64.hip", "attn_decode.hip", "attn_f32.hip",
+SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_bf16_d64.hip", "attn_bwd_plain.hip", "attn_decode.hip", "attn_f32.hip",
            "attn_rope.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,7 +31,12 @@ FLAGS = [
 # Kernel-only sources: NaN inputs are outside the contract (results unspecified),
 # so fmax needs no NaN canonicalisation.  Not used for attn_api.hip, whose
 # argument checks must see NaN.
-KERNEL_ONLY_FLAGS = {"attn_bf16_d64.hip": ["-fno-honor-nans"]}
+KERNEL_ONLY_FLAGS = {
+    "attn_bf16_d64.hip": ["-fno-honor-nans"],
+    # the one-launch backward without dropout alone, under LLVM's iterative ILP
+    # machine scheduler (see the head of that file)
+    "attn_bwd_plain.hip": ["-fno-honor-nans", "-mllvm", "--amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def _compile(src: str) -> str:

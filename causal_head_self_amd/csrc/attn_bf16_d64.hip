@@ -1020,8 +1020,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         dq_item<1, kDrop, kKeep>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
 }
 
+#ifndef CATTN_D64_KERNELS_ONLY
+// The one-launch backward without dropout is instantiated in attn_bwd_plain.hip,
+// which is compiled with its own instruction-scheduling strategy.
+extern template __global__ void attn_bwd_d64_kernel<false, false>(BwdParams, int, int);
+#endif
+
 }  // namespace d64
 
+#ifndef CATTN_D64_KERNELS_ONLY
 static d64::View view(const void* p, const Strides& s)
 {
     return d64::View{(bf16*)p, s.sb, s.sh, s.st};
@@ -1122,5 +1129,7 @@ hipError_t launch_bwd_bf16_d64(const AttnArgs& a, hipStream_t st)
     hipLaunchKernelGGL(k, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nb, a.n_cu);
     return hipGetLastError();
 }
+
+#endif  // CATTN_D64_KERNELS_ONLY
 
 }  // namespace cattn
