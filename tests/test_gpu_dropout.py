@@ -5,8 +5,10 @@ with v; inverted dropout in training mode, keep decisions from Philox4x32-10).
 The keep decisions are integer results and are compared exactly: with q = 0
 every visible weight of row i is 1/(i+1), and with v = the identity (D >= T)
 o[i][j] is nonzero exactly when weight (i, j) is kept.  Values: dropout scales
-kept weights by 1/(1-p), so the bar is 2e-2 * max(1, |ref|) per element (the
-bf16 rounding of outputs that grow with 1/(1-p)).
+kept weights by 1/(1-p), and with them the rounding errors of every product
+they enter: the stated 2e-2 holds except where the stated roundings alone (the
+CPU rounding model, with the same keep decisions) miss it, and then only by
+what they cost there (tests/tolerance.py).
 """
 import math
 import sys
@@ -17,6 +19,7 @@ import torch
 
 import oracle
 import workloads
+from tests import rounding_model, tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -43,17 +46,17 @@ def gpu_drop(q, k, v, dO, p, seed, window=0):
     return {n: t.float().cpu().numpy().astype(np.float64) for n, t in out.items()}
 
 
-def check(got, ref, label, dO=None):
+def check(got, ref, label, dO=None, model=None):
     for name in ref:
         a, r = got[name], ref[name]
         if name == "delta":  # defined on the stored bf16 o (as without dropout)
             bound = np.sum(np.abs(dO) * (2.0 ** -8 * np.abs(got["o"]) + 4e-3), axis=-1) + 1e-4
             assert np.all(np.abs(a - r) <= bound), f"{label} delta"
             continue
-        err = np.abs(a - r) / np.maximum(1.0, np.abs(r))
-        _note(f"    {name}: max err {float(err.max()):.2e} (max|ref| {float(np.abs(r).max()):.2f})")
-        assert np.all(np.isfinite(a)), f"{label} {name}: non-finite"
-        assert float(err.max()) <= 2e-2, f"{label} {name}: {float(err.max()):.3e}"
+        _note(f"    {name}: max err {float(np.abs(a - r).max()):.2e} "
+              f"(max|ref| {float(np.abs(r).max()):.2f})")
+        mf = None if model is None else (lambda n=name: model()[n])
+        tolerance.check(a, r, f"{label} {name}", "bf16", mf)
 
 
 @pytest.mark.parametrize("T,D,window", [(64, 64, 0), (40, 128, 0), (64, 64, 20)])
@@ -92,7 +95,7 @@ def test_dropout_matches_oracle(shape, p, window):
     o, lse = oracle.attn_fwd_dropout(q, k, v, s, p, seed, window=window)
     dq, dk, dv, delta = oracle.attn_bwd_dropout(q, k, v, dO, s, p, seed, window=window)
     check(got, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta), f"p{p} T{T} D{D}",
-          dO.double().numpy())
+          dO.double().numpy(), rounding_model.lazy(q, k, v, dO, s, window, p, seed))
 
 
 def test_dropout_seed_determinism():
@@ -125,7 +128,8 @@ def test_qkv_autograd_with_dropout():
     g = x.grad.view(B, T, 3, H, D).permute(2, 0, 3, 1, 4)
     got = dict(o=as_np(y.view(B, T, H, D).permute(0, 2, 1, 3)), dq=as_np(g[0]), dk=as_np(g[1]),
                dv=as_np(g[2]))
-    check(got, dict(o=o, dq=dq, dk=dk, dv=dv), "qkv dropout")
+    check(got, dict(o=o, dq=dq, dk=dk, dv=dv), "qkv dropout", None,
+          rounding_model.lazy(q, k, v, dO, s, 0, p, seed))
 
 
 @pytest.mark.parametrize("shape,p,window", [
@@ -218,7 +222,9 @@ def test_stored_keep_bits_past_2_32_bytes():
                                                  seed, bh0=bh)
         _note(f"  head {bh}: keep words from byte {bh * n_words * T * 4}")
         check(got, dict(o=ro, lse=rl, dq=rq, dk=rk, dv=rv, delta=rd), f"head {bh}",
-              cpu(dO).double().numpy())
+              cpu(dO).double().numpy(),
+              rounding_model.lazy(cpu(q), cpu(k), cpu(v), cpu(dO), oracle.widen_scale(scale), 0, p,
+                                  seed, bh0=bh))
         words = keep[bh * n_words * T:(bh + 1) * n_words * T].cpu().numpy().astype(np.uint32)
         words = words.reshape(n_words, T)
         for _ in range(4000):

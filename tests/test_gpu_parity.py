@@ -1,11 +1,13 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
-Tolerances (max abs error, element by element): 1e-4 for fp32 inputs and 2e-2
-for bf16 inputs with unit-variance values.  The oracle consumes exactly the
-values the GPU receives (bf16 inputs widened to fp64, scale widened from its
-float32 value).  Full-size configurations are checked head by head on sampled
-(batch, head) pairs, in the launch configuration the benchmark times, plus
-properties that hold for every head (exact row 0, determinism).
+Bars (max abs error, element by element; tests/tolerance.py): 1e-4 for fp32
+inputs and 2e-2 for bf16 inputs, as stated.  The five configurations are
+compared on every head, in the launch configuration the benchmark times, at
+exactly those bars.  Elsewhere (ragged shapes, windows, head dim 128) a bf16
+element may miss 2e-2 only by what the stated roundings cost there, as the CPU
+rounding model (tests/rounding_model.py) computes it; each such element is
+reported.  The oracle consumes exactly the values the GPU receives (bf16 inputs
+widened to fp64, scale widened from its float32 value).
 """
 import math
 import sys
@@ -16,22 +18,12 @@ import torch
 
 import oracle
 import workloads
+from tests import rounding_model, tolerance
 from workloads import ATTN_CONFIGS
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-
-
-def scaled_tol(D):
-    """Head dim 128 is outside the configurations the 2e-2 bar is stated for.
-    There the bar is 2e-2 * max(1, |ref|) per element: 2e-2 absolute on
-    unit-scale values and 2 % relative above.  An exact CPU emulation of the
-    bf16 pipeline's roundings (P and dS to bf16, outputs to bf16) shows errors
-    of at most 1.4 % of max(1, |ref|) at D = 64 and 128 alike, and reproduces
-    the one D = 128 element above 2e-2 absolute (|ref| 3.2, error 0.0202) bit
-    for bit, so the rounding model, not the kernel, sets that error."""
-    return D > 64
 
 
 def _note(msg):
@@ -77,21 +69,18 @@ def delta_bound(ref, dO):
     return np.sum(g * (2.0 ** -8 * np.abs(ref["o"]) + 4e-3), axis=-1) + 1e-4
 
 
-def assert_close(got, ref, tol, label, delta_tol=None, scaled=False):
-    for name in ref:
-        if name == "delta" and delta_tol is not None:
-            bad = np.abs(got[name] - ref[name]) > delta_tol
-            assert not np.any(bad), f"{label} delta beyond its derived bound at {np.argwhere(bad)[:5]}"
-            continue
-        err = np.abs(got[name] - ref[name])
-        if scaled:
-            err = err / np.maximum(1.0, np.abs(ref[name]))
-        worst = float(err.max()) if err.size else 0.0
-        idx = np.unravel_index(int(err.argmax()), err.shape) if err.size else ()
-        assert np.all(np.isfinite(got[name])), f"{label} {name}: non-finite output"
-        assert worst <= tol, (f"{label} {name}: max abs err {worst:.3e} at {idx} "
-                              f"(got {got[name][idx]:.6f}, ref {ref[name][idx]:.6f}, "
-                              f"max|ref| {float(np.abs(ref[name]).max()):.3f})")
+def assert_close(got, ref, dtype, label, delta_tol=None, model=None):
+    """Every tensor of ref within its bar; delta within its derived bound.
+    model: zero-argument callable returning the rounding model's dict, or None."""
+    if delta_tol is not None and "delta" in ref:
+        bad = np.abs(got["delta"] - ref["delta"]) > delta_tol
+        assert not np.any(bad), f"{label} delta beyond its derived bound at {np.argwhere(bad)[:5]}"
+    tolerance.check_all(got, ref, label, dtype, model if dtype == "bf16" else None,
+                        skip=("delta",) if delta_tol is not None else ())
+
+
+def model_of(q, k, v, dO, scale, window=0):
+    return rounding_model.lazy(q, k, v, dO, oracle.widen_scale(scale), window)
 
 
 def check_case(B, H, T, D, dtype, seed=workloads.SEED, with_bwd=True):
@@ -101,7 +90,8 @@ def check_case(B, H, T, D, dtype, seed=workloads.SEED, with_bwd=True):
     got = gpu_attention(q, k, v, dO, scale, with_bwd)
     ref = oracle_attention(q, k, v, dO, scale, with_bwd)
     dtol = delta_bound(ref, dO) if dtype == "bf16" and with_bwd else None
-    assert_close(got, ref, TOL[dtype], f"B{B} H{H} T{T} D{D} {dtype}", dtol, scaled_tol(D))
+    assert_close(got, ref, dtype, f"B{B} H{H} T{T} D{D} {dtype}", dtol,
+                 model_of(q, k, v, dO, scale))
     return got, ref
 
 
@@ -164,9 +154,9 @@ def test_split_backward_entry_points(shape, dtype):
     full = oracle_attention(q, k, v, dO, scale)
     dtol = delta_bound(full, dO) if dtype == "bf16" else None
     ref = {n: full[n] for n in got}
-    assert_close(got, ref, TOL[dtype], f"split B{B} H{H} T{T} D{D} {dtype}", dtol, scaled_tol(D))
-    assert_close(fused, ref, TOL[dtype], f"fused B{B} H{H} T{T} D{D} {dtype}", dtol,
-                 scaled_tol(D))
+    model = model_of(q, k, v, dO, scale)
+    assert_close(got, ref, dtype, f"split B{B} H{H} T{T} D{D} {dtype}", dtol, model)
+    assert_close(fused, ref, dtype, f"fused B{B} H{H} T{T} D{D} {dtype}", dtol, model)
     # the two paths compute Delta and dS in different orders; they agree to the
     # bf16 storage rounding of the gradients
     for n in ("dq", "dk", "dv"):
@@ -174,27 +164,21 @@ def test_split_backward_entry_points(shape, dtype):
 
 
 # ---------------------------------------------------------------------------
-# full-size configurations: sampled heads, element by element
+# full-size configurations: every head, element by element
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["gpt2s", "gpt400m", "long", "gpt2s_d128"])
-def test_full_config_sampled_heads(name):
+def test_full_config_every_head(name):
     c = ATTN_CONFIGS[name]
-    _note(f"[parity] config {name} B={c.B} H={c.H} T={c.T} D={c.D} {c.dtype} (sampled heads)")
+    _note(f"[parity] config {name} B={c.B} H={c.H} T={c.T} D={c.D} {c.dtype} (every head)")
     q, k, v, dO = workloads.config_inputs(c)
     got = gpu_attention(q, k, v, dO, c.scale)
     # every head: row 0 sees only key 0, so o[.., 0, :] == v[.., 0, :] bit for bit
     v_np = v.float().numpy().astype(np.float64)
     assert np.array_equal(got["o"][:, :, 0, :], v_np[:, :, 0, :])
-    for name_ in got:
-        assert np.all(np.isfinite(got[name_])), name_
-    heads = [(0, 0), (c.B // 2, c.H // 3), (c.B - 1, c.H - 1)]
-    for b, h in heads:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oracle_attention(q[sl], k[sl], v[sl], dO[sl], c.scale)
-        sub = {key: got[key][sl] for key in ref}
-        assert_close(sub, ref, TOL[c.dtype], f"{name} head (b={b}, h={h})",
-                     delta_bound(ref, dO[sl]), scaled_tol(c.D))
+    ref = oracle_attention(q, k, v, dO, c.scale)
+    # the configurations: the stated bar, with no rounding-model allowance
+    assert_close(got, ref, c.dtype, name, delta_bound(ref, dO), None)
 
 
 def test_tensors_past_2_31_elements():
@@ -233,8 +217,8 @@ def test_tensors_past_2_31_elements():
                for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv),
                             ("delta", delta))}
         ref = oracle_attention(cpu(q), cpu(k), cpu(v), cpu(dO), scale)
-        assert_close(got, ref, TOL["bf16"], f"head {bh} (elements {first}..{last})",
-                     delta_bound(ref, cpu(dO)))
+        assert_close(got, ref, "bf16", f"head {bh} (elements {first}..{last})",
+                     delta_bound(ref, cpu(dO)), model_of(cpu(q), cpu(k), cpu(v), cpu(dO), scale))
     del q, k, v, dO, o, dq, dk, dv
     torch.cuda.empty_cache()
 
@@ -375,8 +359,8 @@ def test_strided_views_match_oracle_and_contiguous_path(shape):
     for name, val in got.items():
         assert np.array_equal(val, ref_gpu[name]), f"{name}: strided differs from contiguous"
     ref = oracle_attention(q, k, v, dO, scale)
-    assert_close(got, ref, TOL["bf16"], f"strided B{B} H{H} T{T}", delta_bound(ref, dO),
-                 scaled_tol(D))
+    assert_close(got, ref, "bf16", f"strided B{B} H{H} T{T}", delta_bound(ref, dO),
+                 model_of(q, k, v, dO, scale))
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -440,8 +424,8 @@ def test_sliding_window_matches_oracle(shape, window):
     scale = 1.0 / math.sqrt(D)
     got = windowed_gpu(q, k, v, dO, scale, window)
     ref = windowed_oracle(q, k, v, dO, scale, window)
-    assert_close(got, ref, TOL["bf16"], f"window {window} B{B} H{H} T{T} D{D}",
-                 delta_bound(ref, dO), scaled_tol(D))
+    assert_close(got, ref, "bf16", f"window {window} B{B} H{H} T{T} D{D}",
+                 delta_bound(ref, dO), model_of(q, k, v, dO, scale, window))
 
 
 @pytest.mark.parametrize("window", [300, 301, 4096])
@@ -456,20 +440,17 @@ def test_window_at_least_T_is_the_causal_path_bitwise(window):
         assert np.array_equal(got[name], causal[name]), f"{name}: window >= T differs"
 
 
-def test_sliding_window_long_sequence_sampled_head():
+def test_sliding_window_long_sequence_every_head():
     # T = 1024 with a quarter-length window: many fully skipped tiles per
-    # query block; one (b, h) pair checked against the oracle
+    # query block
     B, H, T, D, W = 2, 3, 1024, 64, 256
-    _note(f"[parity] window={W} B={B} H={H} T={T} sampled head")
+    _note(f"[parity] window={W} B={B} H={H} T={T} every head")
     q, k, v, dO = workloads.attention_inputs(B, H, T, D, "bf16", 4242)
     scale = 1.0 / math.sqrt(D)
     got = windowed_gpu(q, k, v, dO, scale, W)
-    b, h = 1, 2
-    sl = lambda t: t[b:b + 1, h:h + 1]
-    ref = windowed_oracle(sl(q), sl(k), sl(v), sl(dO), scale, W)
-    got = {name: val[b:b + 1, h:h + 1] for name, val in got.items()}
-    assert_close(got, ref, TOL["bf16"], f"window {W} T{T} head ({b},{h})",
-                 delta_bound(ref, sl(dO)))
+    ref = windowed_oracle(q, k, v, dO, scale, W)
+    assert_close(got, ref, "bf16", f"window {W} T{T}", delta_bound(ref, dO),
+                 model_of(q, k, v, dO, scale, W))
 
 
 def test_qkv_autograd_window_matches_oracle():
@@ -487,18 +468,18 @@ def test_qkv_autograd_window_matches_oracle():
     got_o = as_np(y.view(B, T, H, D).permute(0, 2, 1, 3))
     g = qkv.grad.view(B, T, 3, H, D).permute(2, 0, 3, 1, 4)
     got = {"o": got_o, "dq": as_np(g[0]), "dk": as_np(g[1]), "dv": as_np(g[2])}
-    assert_close(got, {n: ref[n] for n in got}, TOL["bf16"], f"qkv window {W}", None,
-                 scaled_tol(D))
+    assert_close(got, {n: ref[n] for n in got}, "bf16", f"qkv window {W}", None,
+                 model_of(q, k, v, dO, 1.0 / math.sqrt(D), W))
 
 
 @pytest.mark.parametrize("name,window,p", [("long", 1024, 0.0), ("gpt2s", 0, 0.1),
                                            ("gpt2s_d128", 256, 0.0)])
-def test_full_size_window_and_dropout_sampled_heads(name, window, p):
+def test_full_size_window_and_dropout_every_head(name, window, p):
     """The bench launches with a window or dropout, at the full workload size:
-    two sampled (b, h) pairs against the oracle."""
+    every head against the oracle."""
     import causal_head_self_amd as cat
     c = ATTN_CONFIGS[name]
-    _note(f"[parity] {name} B={c.B} H={c.H} T={c.T} D={c.D} window={window} p={p} (sampled)")
+    _note(f"[parity] {name} B={c.B} H={c.H} T={c.T} D={c.D} window={window} p={p} (every head)")
     q, k, v, dO = workloads.config_inputs(c)
     dev = torch.device("cuda")
     qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, dO))
@@ -511,18 +492,14 @@ def test_full_size_window_and_dropout_sampled_heads(name, window, p):
                          dropout_p=p, seed=42)
     torch.cuda.synchronize()
     s = oracle.widen_scale(c.scale)
-    for b, h in ((0, 1), (c.B - 1, c.H - 1)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        qs, ks, vs, gs = q[sl], k[sl], v[sl], dO[sl]
-        if p > 0:  # the draws are indexed by the global (b, h) pair
-            ro, rlse = oracle.attn_fwd_dropout(qs, ks, vs, s, p, 42, window=window, bh0=b * c.H + h)
-            rdq, rdk, rdv, rdl = oracle.attn_bwd_dropout(qs, ks, vs, gs, s, p, 42, window=window,
-                                                         bh0=b * c.H + h)
-        else:
-            ro, rlse = oracle.attn_fwd(qs, ks, vs, s, window=window)
-            rdq, rdk, rdv, rdl = oracle.attn_bwd(qs, ks, vs, gs, s, window=window)
-        ref = dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv, delta=rdl)
-        got = {n: t[sl].float().cpu().numpy().astype(np.float64)
-               for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta).items()}
-        assert_close(got, ref, TOL["bf16"], f"{name} W{window} head ({b},{h})",
-                     delta_bound(ref, gs), scaled_tol(c.D))
+    if p > 0:  # the draws are indexed by the (b, h) pair: b * H + h
+        ro, rlse = oracle.attn_fwd_dropout(q, k, v, s, p, 42, window=window)
+        rdq, rdk, rdv, rdl = oracle.attn_bwd_dropout(q, k, v, dO, s, p, 42, window=window)
+    else:
+        ro, rlse = oracle.attn_fwd(q, k, v, s, window=window)
+        rdq, rdk, rdv, rdl = oracle.attn_bwd(q, k, v, dO, s, window=window)
+    ref = dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv, delta=rdl)
+    got = {n: t.float().cpu().numpy().astype(np.float64)
+           for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta).items()}
+    model = rounding_model.lazy(q, k, v, dO, s, window, p, 42)
+    assert_close(got, ref, "bf16", f"{name} W{window} p{p}", delta_bound(ref, dO), model)

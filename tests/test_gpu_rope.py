@@ -6,8 +6,10 @@ Bar for the prologue's own outputs: |got - ref| <= 2^-8 |ref| + 2e-3, i.e. the
 bf16 rounding of the result (at most 2^-9 relative) with room for the fp32
 angle (position times a frequency rounded to fp32: under 2.5e-4 rad at
 position 4096, which moves a unit-size pair by as much).  End to end, the
-attention outputs keep the 2e-2 bar (applied to max(1, |ref|) for the
-gradients, which the prologue scales by the gain over the row's RMS).
+attention outputs keep the stated 2e-2; the q and k gradients get it times
+max(1, q_gain * k_gain / rms(row)), the scale the prologue's Jacobian and the
+normalised operands put on the attention's gradient errors, plus one bf16 step
+of the value for the extra bf16 store between the two launches.
 """
 import math
 import sys
@@ -18,6 +20,7 @@ import torch
 
 import oracle
 import workloads
+from tests import tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -98,8 +101,18 @@ def test_attention_with_prologue_matches_oracle(D, window):
     dk = oracle.rope_qknorm_bwd(k, dka, gain=1.0)
     got_o = _np(y.view(B, T, H, D).permute(0, 2, 1, 3))
     g = x.grad.view(B, T, 3, H, D).permute(2, 0, 3, 1, 4)
-    for name, a, r in (("o", got_o, o), ("dq", _np(g[0]), dq), ("dk", _np(g[1]), dk),
-                       ("dv", _np(g[2]), dv)):
-        err = np.abs(a - r) / (1.0 if name == "o" else np.maximum(1.0, np.abs(r)))
-        _note(f"    {name}: max err {float(err.max()):.2e} (max|ref| {float(np.abs(r).max()):.2f})")
-        assert np.all(np.isfinite(a)) and float(err.max()) <= 2e-2, name
+    # The prologue's gradient maps the attention's dq (dk) through the norm's
+    # Jacobian, whose scale is gain / rms(row) (the rotation keeps lengths), and
+    # the attention's own dq (dk) errors carry the other side's gain (dq sums
+    # normalised keys, dk normalised queries): the stated 2e-2 times
+    # max(1, q_gain * k_gain / rms(row)), plus one bf16 step of the value for the
+    # extra bf16 store of the attention's gradient between the two launches.
+    gain = 1.2 * 1.0
+    rms = lambda x: np.sqrt(np.mean(x.double().numpy() ** 2, axis=-1, keepdims=True))
+    for name, a, r, f in (("o", got_o, o, 1.0), ("dq", _np(g[0]), dq, gain / rms(q)),
+                          ("dk", _np(g[1]), dk, gain / rms(k)), ("dv", _np(g[2]), dv, 1.0)):
+        b = tolerance.BF16 * np.maximum(1.0, f) + (tolerance.ulp_bf16(r) if name in ("dq", "dk")
+                                                   else 0.0)
+        _note(f"    {name}: max err {float(np.abs(a - r).max()):.2e}, worst err / bar "
+              f"{float((np.abs(a - r) / b).max()):.3f} (max|ref| {float(np.abs(r).max()):.2f})")
+        assert np.all(np.isfinite(a)) and np.all(np.abs(a - r) <= b), name

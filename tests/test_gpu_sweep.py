@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workloads
+from tests import rounding_model, tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -68,13 +69,11 @@ def test_random_combination_matches_oracle(B, H, T, D, window, p, fused, seed):
         ro, rl = oracle.attn_fwd(q, k, v, s, window=window)
         rdq, rdk, rdv, _ = oracle.attn_bwd(q, k, v, dO, s, window=window)
     as_np = lambda t: t.float().cpu().numpy().astype(np.float64)
-    # the stated 2e-2 bar on unit-scale values, 2 % relative above them (head
-    # dim 128 and dropout scale the values up; see the D = 128 reading)
-    for name, got, ref in (("o", as_np(od), ro), ("lse", as_np(lse), rl), ("dq", as_np(dqd), rdq),
-                           ("dk", as_np(dkd), rdk), ("dv", as_np(dvd), rdv)):
-        err = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
-        assert np.all(np.isfinite(got)), name
-        assert float(err.max()) <= 2e-2, f"{name}: {float(err.max()):.3e}"
+    # the stated 2e-2, except where the stated roundings alone (the CPU rounding
+    # model) miss it (tests/tolerance.py)
+    model = rounding_model.lazy(q, k, v, dO, s, window, p, seed)
+    got = dict(o=as_np(od), lse=as_np(lse), dq=as_np(dqd), dk=as_np(dkd), dv=as_np(dvd))
+    tolerance.check_all(got, dict(o=ro, lse=rl, dq=rdq, dk=rdk, dv=rdv), "sweep", "bf16", model)
     if p > 0:  # the stored-keep-bit entry points give the same bits as the drawing ones
         keep = torch.full((cat.dropout_keep_bytes(B, H, T) // 4,), -1, dtype=torch.int32,
                           device=dev)
