@@ -14,6 +14,8 @@ the computation.  PyTorch supplies device memory and streams.
         fused [B, T, 3C] c_attn output, returning [B, T, C] with no layout copies
     attn_decode / decode_attention                          -- one new token per
         sequence against a [B, T_max, H, D] KV cache
+    attn_decode_noalloc                                     -- the same without a
+        workspace (the library's fixed device scratch), for callers that cannot allocate
     rope_qknorm_fwd / rope_qknorm_bwd                       -- RoPE and QK norm on
         query and key rows (also as causal_attention_qkv(..., prologue=Prologue()))
 
@@ -27,12 +29,13 @@ import math
 
 import torch
 
-from ._lib import (ABI_VERSION, ATTN_BF16, ATTN_F32, EXPORTS, LIB_PATH, AttnError, AttnView,
-                   check, load_library, status_str)
+from ._lib import (ABI_VERSION, ATTN_BF16, ATTN_F32, DECODE_SCRATCH_BYTES, EXPORTS, LIB_PATH,
+                   AttnError, AttnView, check, load_library, status_str)
 
 __all__ = [
     "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
-    "attn_bwd_strided", "attn_decode", "decode_workspace_bytes", "decode_attention",
+    "attn_bwd_strided", "attn_decode", "attn_decode_noalloc", "decode_workspace_bytes",
+    "decode_attention", "DECODE_SCRATCH_BYTES",
     "rope_qknorm_fwd", "rope_qknorm_bwd", "Prologue",
     "attn_status_str", "causal_attention", "causal_attention_qkv", "qkv_heads", "AttnError",
     "ATTN_F32", "ATTN_BF16", "load_library", "LIB_PATH", "EXPORTS", "ABI_VERSION",
@@ -366,6 +369,28 @@ def attn_decode(q, k_cache, v_cache, cache_lens, o, lse, workspace, scale: float
         _ptr(cache_lens, "cache_lens"), _ptr(o, "o"), _ptr(lse, "lse"),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), B, H, T_max,
         D, int(window), scale, _dtype_code(q), _stream(stream))
+    check(rc)
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, cache_lens, o, lse, scale: float | None = None,
+                        window: int = 0, stream=None) -> None:
+    """C ABI attn_decode_noalloc: attn_decode without a workspace (the library's
+    fixed device scratch of DECODE_SCRATCH_BYTES holds the split path's
+    partials; calls that overlap in time on one device race on it)."""
+    if k_cache.dim() != 4:
+        raise ValueError(f"k_cache must be [B, T_max, H, D], got {tuple(k_cache.shape)}")
+    B, T_max, H, D = (int(s) for s in k_cache.shape)
+    if tuple(q.shape) != (B, H, D) or tuple(o.shape) != (B, H, D):
+        raise ValueError("q and o must be [B, H, D] for a [B, T_max, H, D] cache")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(lse.shape) != (B, H):
+        raise ValueError("v_cache must match k_cache and lse must be [B, H]")
+    if cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().attn_decode_noalloc(
+        _ptr(q, "q"), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+        _ptr(cache_lens, "cache_lens"), _ptr(o, "o"), _ptr(lse, "lse"), B, H, T_max, D,
+        int(window), scale, _dtype_code(q), _stream(stream))
     check(rc)
 
 

@@ -28,6 +28,7 @@ STATUS = {
     10: "ATTN_ERR_LAYOUT",
     11: "ATTN_ERR_WORKSPACE",
     12: "ATTN_ERR_PARAM",
+    13: "ATTN_ERR_SCRATCH",
 }
 
 ATTN_ROPE = 1
@@ -37,8 +38,11 @@ ATTN_QK_NORM = 2
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
            "attn_bwd_strided", "attn_dropout_keep_bytes", "attn_fwd_strided_keep",
            "attn_bwd_strided_keep", "attn_decode", "attn_decode_workspace_bytes",
-           "attn_rope_qknorm_fwd", "attn_rope_qknorm_bwd", "attn_status_str", "attn_abi_version")
-ABI_VERSION = (1 << 16) | 5
+           "attn_decode_noalloc", "attn_rope_qknorm_fwd", "attn_rope_qknorm_bwd",
+           "attn_status_str", "attn_abi_version")
+ABI_VERSION = (1 << 16) | 6
+# the fixed device scratch of attn_decode_noalloc (CAUSAL_ATTN_DECODE_SCRATCH_BYTES)
+DECODE_SCRATCH_BYTES = 16 << 20
 
 
 class AttnView(ctypes.Structure):
@@ -102,6 +106,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_decode.argtypes = ([_vp] * 7 + [ctypes.c_size_t] + [_int] * 5 +
                                 [ctypes.c_float, _int, _vp])
     lib.attn_decode.restype = _int
+    lib.attn_decode_noalloc.argtypes = [_vp] * 6 + [_int] * 5 + [ctypes.c_float, _int, _vp]
+    lib.attn_decode_noalloc.restype = _int
     _rope_tail = [_int] * 5 + [ctypes.c_float] * 4 + [_int, _int, _vp]
     lib.attn_rope_qknorm_fwd.argtypes = [AttnView] * 4 + _rope_tail
     lib.attn_rope_qknorm_fwd.restype = _int

@@ -243,6 +243,9 @@ const char* attn_status_str(int st)
     case ATTN_ERR_PARAM:
         return "RoPE / QK norm: flags must be 0..3, 0 <= pos0 and pos0 + T <= 2^24, rope_base "
                "finite and > 0, gains finite, eps finite and >= 0; dropout_p must be in [0, 1)";
+    case ATTN_ERR_SCRATCH:
+        return "attn_decode_noalloc: the two-launch path would need more than the library's "
+               "fixed scratch (CAUSAL_ATTN_DECODE_SCRATCH_BYTES); use attn_decode with a workspace";
     default: return "unknown status";
     }
 }
@@ -529,11 +532,14 @@ size_t attn_decode_workspace_bytes(int B, int H, int T_max, int D)
     return (size_t)B * H * cattn::decode_slices(T_max) * (size_t)(D + 4) * sizeof(float);
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_lens,
-                void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int H,
-                int T_max, int D, int window, float scale, int dtype, void* stream)
+// Argument checks of attn_decode (in the documented order); workspace == nullptr
+// with check_workspace false: those of attn_decode_noalloc.
+static int decode_check(const void* q, const void* k_cache, const void* v_cache,
+                        const int* cache_lens, const void* o, const float* lse,
+                        const void* workspace, size_t workspace_bytes, bool check_workspace,
+                        int B, int H, int T_max, int D, int window, float scale, int dtype)
 {
-    if (!q || !k_cache || !v_cache || !cache_lens || !o || !lse || !workspace)
+    if (!q || !k_cache || !v_cache || !cache_lens || !o || !lse || (check_workspace && !workspace))
         return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || T_max < 1 || window < 0) return ATTN_ERR_SHAPE;
     if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
@@ -542,11 +548,12 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     const long long slices = cattn::decode_slices(T_max);
     if ((long long)B * H * slices > 0x7fffffffLL || (long long)B * T_max * H * D > (1LL << 40))
         return ATTN_ERR_OVERFLOW;
-    for (const void* p : {q, k_cache, v_cache, (const void*)o, (const void*)workspace})
+    for (const void* p : {q, k_cache, v_cache, o})
         if ((uintptr_t)p % 16) return ATTN_ERR_ALIGN;
+    if (check_workspace && (uintptr_t)workspace % 16) return ATTN_ERR_ALIGN;
     if ((uintptr_t)lse % 4 || (uintptr_t)cache_lens % 4) return ATTN_ERR_ALIGN;
     const size_t need = attn_decode_workspace_bytes(B, H, T_max, D);
-    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (check_workspace && workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     const size_t bh = (size_t)B * H;
     const size_t cache = (size_t)B * T_max * H * D * 2;
     auto span = [](const void* p, size_t n) {
@@ -555,12 +562,20 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     const Span in[4] = {span(q, bh * D * 2), span(k_cache, cache), span(v_cache, cache),
                         span(cache_lens, (size_t)B * 4)};
     const Span out[3] = {span(o, bh * D * 2), span(lse, bh * 4), span(workspace, need)};
-    for (int i = 0; i < 3; ++i) {
+    const int n_out = check_workspace ? 3 : 2;
+    for (int i = 0; i < n_out; ++i) {
         for (int j = 0; j < 4; ++j)
             if (overlaps(out[i], in[j])) return ATTN_ERR_ALIAS;
-        for (int j = i + 1; j < 3; ++j)
+        for (int j = i + 1; j < n_out; ++j)
             if (overlaps(out[i], out[j])) return ATTN_ERR_ALIAS;
     }
+    return ATTN_OK;
+}
+
+static cattn::DecodeArgs decode_args(const void* q, const void* k_cache, const void* v_cache,
+                                     const int* cache_lens, void* o, float* lse, int B, int H,
+                                     int T_max, int D, int window, float scale)
+{
     cattn::DecodeArgs a{};
     a.q = q;
     a.k_cache = k_cache;
@@ -568,7 +583,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     a.lens = cache_lens;
     a.o = o;
     a.lse = lse;
-    a.part = (float*)workspace;
+    a.part = nullptr;
     a.B = B;
     a.H = H;
     a.T_max = T_max;
@@ -576,7 +591,35 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     a.window = window;
     a.scale = scale;
     a.n_cu = cu_count();
+    return a;
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_lens,
+                void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int H,
+                int T_max, int D, int window, float scale, int dtype, void* stream)
+{
+    const int st = decode_check(q, k_cache, v_cache, cache_lens, o, lse, workspace,
+                                workspace_bytes, true, B, H, T_max, D, window, scale, dtype);
+    if (st != ATTN_OK) return st;
+    cattn::DecodeArgs a =
+        decode_args(q, k_cache, v_cache, cache_lens, o, lse, B, H, T_max, D, window, scale);
+    a.part = (float*)workspace;
     return status(cattn::launch_decode_bf16(a, (hipStream_t)stream));
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int* cache_lens, void* o, float* lse, int B, int H, int T_max,
+                        int D, int window, float scale, int dtype, void* stream)
+{
+    const int st = decode_check(q, k_cache, v_cache, cache_lens, o, lse, nullptr, 0, false, B, H,
+                                T_max, D, window, scale, dtype);
+    if (st != ATTN_OK) return st;
+    const cattn::DecodeArgs a =
+        decode_args(q, k_cache, v_cache, cache_lens, o, lse, B, H, T_max, D, window, scale);
+    if (cattn::decode_two_launches(a) &&
+        attn_decode_workspace_bytes(B, H, T_max, D) > CAUSAL_ATTN_DECODE_SCRATCH_BYTES)
+        return ATTN_ERR_SCRATCH;
+    return status(cattn::launch_decode_bf16_noalloc(a, (hipStream_t)stream));
 }
 
 int attn_rope_qknorm_fwd(attn_view_t q, attn_view_t k, attn_view_t q_out, attn_view_t k_out,

@@ -25,6 +25,9 @@
 //   decode_combine_kernel: one wave per (b, h) merges the slices' partials:
 //     M = max m_s, L = sum 2^(m_s - M) l_s, o = sum 2^(m_s - M) o_s / L,
 //     lse = (M + log2 L) ln 2.
+#include <atomic>
+
+#include "../../include/causal_attn.h"
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -360,18 +363,23 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(
 
 int decode_slices(int T_max) { return (T_max + dec::kPos - 1) / dec::kPos; }
 
+// One launch when every wave has at most one slice, or when the heads alone
+// spread over half the compute units or more.  Otherwise (few heads, long
+// caches) one workgroup per head would leave most compute units idle and each
+// streaming its whole cache; the split path spreads the slices over the
+// machine and pays a second launch for the merge.
+bool decode_two_launches(const DecodeArgs& a)
+{
+    const int nw = a.D == 128 ? 8 : 16;  // waves of a one-launch workgroup
+    return !(decode_slices(a.T_max) <= nw || (long long)a.B * a.H * 2 >= a.n_cu);
+}
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st)
 {
     const int n_slice = decode_slices(a.T_max);
     const float sl2 = a.scale * kLog2e;
-    const int nw = a.D == 128 ? 8 : 16;  // waves of a one-launch workgroup
     const long long heads = (long long)a.B * a.H;
-    // One launch when every wave has at most one slice, or when the heads alone
-    // spread over half the compute units or more.  Otherwise (few heads, long
-    // caches) one workgroup per head would leave most compute units idle and
-    // each streaming its whole cache; the split path spreads the slices over
-    // the machine and pays a second launch for the merge.
-    if (n_slice <= nw || heads * 2 >= a.n_cu) {
+    if (!decode_two_launches(a)) {
         const dim3 grid((unsigned)heads);
         if (a.D == 128)
             hipLaunchKernelGGL((dec::decode_fused_kernel<2, 8>), grid, dim3(64 * min(8, n_slice)), 0, st,
@@ -402,6 +410,46 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st)
         hipLaunchKernelGGL(dec::decode_combine_kernel<1>, grid_c, dim3(64), 0, st, a.part,
                            (bf16*)a.o, a.lse, n_slice);
     return hipGetLastError();
+}
+
+// The partials of attn_decode_noalloc, for callers that cannot allocate:
+// [B][H][slices][D + 4] fp32 of the call, at most
+// CAUSAL_ATTN_DECODE_SCRATCH_BYTES.  The name is a host-side stand-in for the
+// array; kernels get the device address that hipGetSymbolAddress returns for
+// the current device (each device holds its own copy).
+static __device__ __align__(256) float scratch[CAUSAL_ATTN_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept; concurrent first calls store the same
+// value.
+static hipError_t scratch_address(float** out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<float*> addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    float* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* v = nullptr;
+        e = hipGetSymbolAddress(&v, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (v == nullptr) return hipErrorInvalidSymbol;
+        p = (float*)v;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+hipError_t launch_decode_bf16_noalloc(DecodeArgs a, hipStream_t st)
+{
+    float* p = nullptr;
+    const hipError_t e = scratch_address(&p);
+    if (e != hipSuccess) return e;
+    a.part = p;
+    return launch_decode_bf16(a, st);
 }
 
 }  // namespace cattn

@@ -56,7 +56,13 @@ struct DecodeArgs {
 };
 
 int decode_slices(int T_max);
+// true when launch_decode_bf16 takes the two-launch path (which needs a.part)
+bool decode_two_launches(const DecodeArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
+// launch_decode_bf16 with a.part pointing at the library's fixed scratch
+// (CAUSAL_ATTN_DECODE_SCRATCH_BYTES per device); the caller has checked that
+// the two-launch path's partials fit in it
+hipError_t launch_decode_bf16_noalloc(DecodeArgs a, hipStream_t st);
 
 // RoPE / QK norm on query and key rows (forward, or gradient when grad is set).
 struct RopeFreqs {

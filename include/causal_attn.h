@@ -33,8 +33,13 @@
  *     on it and the call returns without synchronising: buffers must stay
  *     alive until the stream has run the work.
  *   - Ownership: the caller allocates and frees every buffer.  The library
- *     allocates no memory and keeps no mutable global state; calls on
- *     different streams with disjoint buffers may run concurrently.
+ *     allocates no memory.  Its only mutable global state is a per-device
+ *     cache of the device's compute-unit count (which picks the work
+ *     placement), filled on first use with atomic stores of the same value
+ *     by any racing threads, and the per-device address of the fixed scratch
+ *     of attn_decode_noalloc (below).  Calls on different streams with
+ *     disjoint buffers may run concurrently, except attn_decode_noalloc calls
+ *     on one device, which share that device's scratch.
  *   - Outputs are fully overwritten, never accumulated into.  No output may
  *     overlap an input or another output.
  *   - Errors: every argument check runs before any HIP call; on a non-zero
@@ -69,7 +74,8 @@ typedef enum {
     ATTN_ERR_HIP = 9,           /* a kernel launch failed                   */
     ATTN_ERR_LAYOUT = 10,       /* strided views: unsupported dtype/D or strides */
     ATTN_ERR_WORKSPACE = 11,    /* decode: workspace smaller than required  */
-    ATTN_ERR_PARAM = 12         /* RoPE / QK norm parameters, or dropout_p    */
+    ATTN_ERR_PARAM = 12,        /* RoPE / QK norm parameters, or dropout_p    */
+    ATTN_ERR_SCRATCH = 13       /* attn_decode_noalloc: beyond its fixed scratch */
 } attn_status_t;
 
 /* Forward.  Reads q, k, v; writes o ([B][H][T][D], dtype) and lse
@@ -245,6 +251,31 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
                 void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int H,
                 int T_max, int D, int window, float scale, int dtype, void* stream);
 
+/* attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same operation, arguments (less the workspace),
+ * layouts, checks and kernels as attn_decode; the per-slice partials of the
+ * two-launch path go to a scratch array of CAUSAL_ATTN_DECODE_SCRATCH_BYTES
+ * that the library holds in device memory.  Each GPU the library runs on
+ * holds its own copy of that array until the process ends; its address is
+ * looked up (hipGetSymbolAddress) on the first call on each device.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - The argument checks of attn_decode run first (without the workspace
+ *     ones), then the device's compute-unit count is queried, which picks the
+ *     path; a call whose two-launch path would need more scratch than the
+ *     maximum (attn_decode_workspace_bytes(B, H, T_max, D) bytes) returns
+ *     ATTN_ERR_SCRATCH with nothing enqueued.  The one-launch path uses no
+ *     scratch.
+ *   - Every call on one device shares that device's scratch, which keeps the
+ *     last call's partials.  Calls that overlap in time on one device (other
+ *     streams, other host threads) race on it: the caller serialises them.
+ *     Nothing in it needs clearing; each call writes every slot it reads.
+ *   - A failed address lookup returns ATTN_ERR_HIP. */
+#define CAUSAL_ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int* cache_lens, void* o, float* lse, int B, int H, int T_max,
+                        int D, int window, float scale, int dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * RoPE and QK norm on the query and key rows.  nanochat, section 9, lists
  * RoPE position encoding and QK norm (x1.2) among its attention's parts; the
@@ -281,7 +312,7 @@ const char* attn_status_str(int status);
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 5)
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 6)
 
 #ifdef __cplusplus
 }
