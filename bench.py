@@ -11,8 +11,14 @@ fp32 accumulation; q, k, v, dO iid N(0, 1), seeds 42+idx).  Metric: causal
 fwd+bwd TFLOP/s with work = 7 * B * H * T^2 * D (forward 2 GEMMs and backward
 5 GEMMs over the causal half), also as a fraction of the bf16 dense MFMA peak.
 
-Prints ONE JSON line.  Extra keys: pct_of_peak, fwd_tflops, per-kernel times,
-the roofline of the dominant kernel and the CPU-oracle baseline.
+Prints ONE JSON line.  Extra keys: pct_of_peak, fwd_tflops, per-kernel times
+(each kernel timed on its own, launches back to back), the roofline of the
+dominant kernel, the CPU-oracle baseline (every host core this process may
+use, forward alone and forward + backward) and, for the default workload,
+"configs": every configuration of the contract timed in the same run (the tiny
+fp32 one, GPT-2 small, the ~400M shape, the long context and the whole
+pre-norm sublayer), forward and forward + backward, with the oracle's seconds
+beside each.
 """
 from __future__ import annotations
 
@@ -101,45 +107,77 @@ def read_traffic(kernel: str, workload: str, sha: str):
         return None
 
 
-def cpu_baseline(cfg, inputs, threads: int, window: int = 0):
-    """The fp64 oracle, as it stands, on the host cores: one fwd+bwd pass
-    over the sample (all heads of the workload), timed with a wall clock."""
+def host_info() -> dict:
+    """The host the oracle runs on: CPU model, the cores this process may use,
+    the machine's logical CPUs and OMP_NUM_THREADS as set."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "affinity_cores": affinity, "os_cpu_count": os.cpu_count(),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def oracle_attention_seconds(cfg, inputs, threads: int, window: int = 0):
+    """The fp64 oracle, as it stands: (forward seconds, backward seconds) over
+    the given inputs, wall clock."""
     import oracle
     q, k, v, dO = inputs
     s = oracle.widen_scale(cfg.scale)
     t0 = time.perf_counter()
     oracle.attn_fwd(q, k, v, s, window=window, nthreads=threads)
+    t1 = time.perf_counter()
     oracle.attn_bwd(q, k, v, dO, s, window=window, nthreads=threads)
-    dt = time.perf_counter() - t0
-    work = 7.0 * cfg.B * cfg.H * cfg.D * 2.0 * visible_pairs(cfg.T, window)
+    t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
+
+
+def cpu_baseline(cfg, inputs, window: int = 0):
+    """The fp64 oracle, as it stands, on every host core this process may use:
+    the forward alone and then the backward, over all heads of the workload."""
+    info = host_info()
+    threads = info["affinity_cores"]
+    tf, tb = oracle_attention_seconds(cfg, inputs, threads, window)
+    work_f = 2.0 * cfg.B * cfg.H * cfg.D * 2.0 * visible_pairs(cfg.T, window)
+    work = 3.5 * work_f
     return {
-        "value": round(work / dt / 1e12, 6),
+        "value": round(work / (tf + tb) / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"one fp64 fwd+bwd pass over all {cfg.B * cfg.H} heads of the same workload "
-                   f"(B={cfg.B}, H={cfg.H}, T={cfg.T}, D={cfg.D}); {dt:.2f} s wall; "
-                   f"host {platform.processor() or platform.machine()}"),
-        "seconds": round(dt, 3),
+        "sample": (f"one fp64 forward then backward pass over all {cfg.B * cfg.H} heads of the "
+                   f"same workload (B={cfg.B}, H={cfg.H}, T={cfg.T}, D={cfg.D}); "
+                   f"{tf:.2f} s + {tb:.2f} s wall on {threads} threads"),
+        "seconds": round(tf + tb, 3),
+        "fwd_seconds": round(tf, 3),
+        "fwd_value": round(work_f / tf / 1e12, 6),
+        "host": info,
     }
 
 
-def sublayer_bench(args) -> int:
+def sublayer_measure(args, with_oracle: bool = True) -> dict:
     """The pre-norm attention sublayer around the GPT-2-small shape: LayerNorm,
-    c_attn, split to heads, causal attention (the HIP kernels), merge, c_proj,
-    residual; forward and backward through torch autograd.  Work per step:
-    the c_attn and c_proj GEMMs (2*N*C*3C + 2*N*C*C forward, 3x that forward
-    plus backward) plus the attention's 7*B*H*T^2*D.  The attention share is
-    the time of attn_fwd + attn_bwd alone at the same shape over the step time."""
+    c_attn, causal attention on strided views of the c_attn output (the HIP
+    kernels), c_proj, residual; forward and backward through torch autograd.
+    Work per step: the c_attn and c_proj GEMMs (2*N*C*3C + 2*N*C*C forward, 3x
+    that forward plus backward) plus the attention's 7*B*H*T^2*D (2*B*H*T^2*D
+    forward).  The attention share is the time of attn_fwd + attn_bwd alone at
+    the same shape over the step time.  The oracle baseline is one of the eight
+    sequences (fp64 sublayer forward and backward), scaled to the whole batch."""
     import torch
     import causal_head_self_amd as cat
     from causal_head_self_amd.sublayer import attention_sublayer
     import workloads
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        return 1
-    cat.load_library()
     cfg = workloads.SUBLAYER_CONFIG
     inp = workloads.sublayer_inputs(cfg)
     names = ["x", "g", "bl", "Wa", "ba", "Wp", "bp"]
@@ -147,61 +185,102 @@ def sublayer_bench(args) -> int:
     dy = inp["dy"].cuda()
     stream = torch.cuda.current_stream()
 
+    def forward():
+        return attention_sublayer(dev["x"], dev["g"], dev["bl"], dev["Wa"], dev["ba"], dev["Wp"],
+                                  dev["bp"], cfg.H)
+
     def step():
         for n in names:
             dev[n].grad = None
-        y = attention_sublayer(dev["x"], dev["g"], dev["bl"], dev["Wa"], dev["ba"], dev["Wp"],
-                               dev["bp"], cfg.H)
-        y.backward(dy)
+        forward().backward(dy)
+
+    def fwd_only():
+        with torch.no_grad():
+            forward()
+
+    def timed(body, n):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(n):
+            body()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = timed(step, args.steps)
+    fwd_ms = timed(fwd_only, args.steps)
 
-    # attention alone at the same shape
+    # attention alone at the same shape (the gpt2s inputs)
     B, T, C, H = cfg.B, cfg.T, cfg.C, cfg.H
     D = C // H
-    q = torch.randn(B, H, T, D, device="cuda", dtype=torch.bfloat16)
-    k, v, dO = torch.randn_like(q), torch.randn_like(q), torch.randn_like(q)
-    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
-    lse = torch.empty(B, H, T, device="cuda")
-    delta = torch.empty_like(lse)
-    sc = 1.0 / math.sqrt(D)
-    for _ in range(args.warmup):
-        cat.attn_fwd(q, k, v, o, lse, sc, stream)
-        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, sc, stream)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(args.steps):
-        cat.attn_fwd(q, k, v, o, lse, sc, stream)
-        cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, sc, stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    attn_ms = t0.elapsed_time(t1) / args.steps
-
+    a = measure_attention(workloads.ATTN_CONFIGS["gpt2s"],
+                          workloads.config_inputs(workloads.ATTN_CONFIGS["gpt2s"]),
+                          args.steps, args.warmup)
+    attn_ms = a["step_ms"]
     N = B * T
     gemm_fwd = 2.0 * N * C * 3 * C + 2.0 * N * C * C
     attn = 7.0 * B * H * T * T * D
     work = 3.0 * gemm_fwd + attn
-    value = work / (ms * 1e-3) / 1e12
+    work_f = gemm_fwd + 2.0 * B * H * T * T * D
+    out = {
+        "value": round(work / (ms * 1e-3) / 1e12, 3), "ms_per_step": round(ms, 5),
+        "fwd_tflops": round(work_f / (fwd_ms * 1e-3) / 1e12, 3), "fwd_ms": round(fwd_ms, 5),
+        "attention_ms": round(attn_ms, 5), "attention_share": round(attn_ms / ms, 4),
+        "attention_tflops": round(a["tflops"], 3),
+        "shape": {"B": B, "T": T, "C": C, "H": H, "dtype": cfg.dtype},
+    }
+    if with_oracle:
+        import oracle
+        one = workloads.sublayer_inputs(cfg, B=1)
+        args_ = [one[n] for n in names]
+        threads = host_info()["affinity_cores"]
+        c0 = time.perf_counter()
+        oracle.sublayer_fwd(*args_, n_head=H, nthreads=threads)
+        c1 = time.perf_counter()
+        oracle.sublayer_bwd(*args_, dy=one["dy"], n_head=H, nthreads=threads)
+        c2 = time.perf_counter()
+        out["oracle"] = {"fwd_seconds": round(c1 - c0, 4), "fwd_bwd_seconds": round(c2 - c0, 4),
+                         "fwd_bwd_tflops": round(work / B / (c2 - c0) / 1e12, 6),
+                         "threads": threads,
+                         "sample": "one of the 8 sequences (B=1), TFLOP/s scaled per sequence"}
+    return out
+
+
+def sublayer_bench(args) -> int:
+    import torch
+    import causal_head_self_amd as cat
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    cat.load_library()
+    cfg = workloads.SUBLAYER_CONFIG
+    m = sublayer_measure(args, with_oracle=not args.no_cpu_baseline)
+    cpu = None
+    if "oracle" in m:
+        o = m.pop("oracle")
+        cpu = {"value": o["fwd_bwd_tflops"], "unit": "TFLOP/s", "cores": o["threads"],
+               "kind": "oracle", "sample": (f"fp64 sublayer forward and backward of one of the 8 "
+                                            f"sequences: {o['fwd_bwd_seconds']} s wall"),
+               "host": host_info()}
     out = {
         "metric": "causal attention sublayer fwd+bwd TFLOP/s (LN, c_attn, attention, c_proj, residual)",
-        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "value": m["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": m["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": (f"pre-norm attention sublayer, B={B} T={T} C={C} H={H} {cfg.dtype}; "
-                                "x, dy N(0,1), GPT-2 init weights, seeds 42+idx"),
-                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "attention_ms": round(attn_ms, 5),
-        "attention_share": round(attn_ms / ms, 4),
-        "attention_tflops": round(attn / (attn_ms * 1e-3) / 1e12, 3),
+        "config": {"workload": (f"pre-norm attention sublayer, B={cfg.B} T={cfg.T} C={cfg.C} "
+                                f"H={cfg.H} {cfg.dtype}; x, dy N(0,1), GPT-2 init weights, "
+                                "seeds 42+idx"),
+                   "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
+        "fwd_tflops": m["fwd_tflops"], "fwd_ms": m["fwd_ms"],
+        "attention_ms": m["attention_ms"], "attention_share": m["attention_share"],
+        "attention_tflops": m["attention_tflops"],
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -299,10 +378,8 @@ def decode_bench(args) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        try:
-            threads = min(16, len(os.sched_getaffinity(0)))
-        except AttributeError:
-            threads = min(16, os.cpu_count() or 1)
+        info = host_info()
+        threads = info["affinity_cores"]
         c0 = time.perf_counter()
         oracle.attn_decode(host[0], host[1], host[2], lens, oracle.widen_scale(cfg.scale),
                            nthreads=threads)
@@ -310,9 +387,8 @@ def decode_bench(args) -> int:
         cpu = {"value": round(alg_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": (f"one fp64 decode step over the whole workload ({B * H} heads, "
-                          f"{sum(lens)} cached positions); {dt:.3f} s wall; host "
-                          f"{platform.processor() or platform.machine()}"),
-               "seconds": round(dt, 4)}
+                          f"{sum(lens)} cached positions); {dt:.3f} s wall on {threads} threads"),
+               "seconds": round(dt, 4), "host": info}
     out = {
         "metric": "decode attention against a KV cache: algorithmic bytes per second",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -423,9 +499,8 @@ def rope_bench(args) -> int:
         cpu = {"value": round((byt["rope_fwd"] + byt["rope_bwd"]) / dt / 1e9, 4), "unit": "GB/s",
                "cores": 1, "kind": "oracle",
                "sample": (f"one fp64 forward and gradient over the whole workload ({B * H * T} "
-                          f"q rows and as many k rows); {dt:.3f} s wall; host "
-                          f"{platform.processor() or platform.machine()}"),
-               "seconds": round(dt, 4)}
+                          f"q rows and as many k rows); {dt:.3f} s wall on one thread"),
+               "seconds": round(dt, 4), "host": host_info()}
     out = {
         "metric": "RoPE + QK-norm prologue (forward + gradient): algorithmic bytes per second",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -464,6 +539,8 @@ def main() -> int:
                     help="with --dropout: the forward stores its keep bits and the backward "
                          "loads them (attn_*_strided_keep) instead of drawing them again")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-all-configs", action="store_true",
+                    help="default workload: skip timing the other configurations in the same run")
     ap.add_argument("--graph", action="store_true",
                     help="decode configs: also time the steps replayed from a captured HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -493,8 +570,85 @@ def main() -> int:
     cat.load_library()  # raises if the HIP library is missing
     torch.manual_seed(42)
     cfg = workloads.ATTN_CONFIGS[args.config]
-    dev = torch.device("cuda:0")
+    W, P = args.window, args.dropout
+    if W < 0 or not 0.0 <= P < 1.0 or ((W or P) and (cfg.dtype != "bf16" or cfg.D not in (64, 128))):
+        print("bench.py: --window needs W >= 0, --dropout 0 <= p < 1, and either a bf16 "
+              "workload with D 64 or 128", file=sys.stderr)
+        return 2
     host_inputs = workloads.config_inputs(cfg)
+    m = measure_attention(cfg, host_inputs, args.steps, args.warmup, W, P,
+                          args.keep_bits and P > 0, args.copy_calibration_mib)
+    B, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    work = kernel_work(cfg, W)
+    kern_ms = m["kernel_ms"]
+    dominant = max(kern_ms, key=lambda n: kern_ms[n])
+    achieved = work[dominant]["flops"] / (kern_ms[dominant] * 1e-3) / 1e12
+    sha = kernel_source_sha()
+    workload_name = (f"{cfg.name}_B{B}_H{H}_T{T}_D{D}_{cfg.dtype}" + (f"_W{W}" if W else "")
+                     + (f"_drop{P:g}" if P else ""))
+    roofline = {
+        "bound": "mfma",
+        "kernel": dominant,
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": read_traffic(dominant, workload_name, sha),
+        "algorithmic_flops_per_launch": work[dominant]["flops"],
+    }
+    cpu = None
+    if not args.no_cpu_baseline and not P:
+        cpu = cpu_baseline(cfg, host_inputs, W)
+    out = {
+        "metric": METRIC,
+        "value": round(m["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"causal MHA fwd+bwd, {cfg.name}: B={B} H={H} T={T} D={D} {cfg.dtype} "
+                         "storage / fp32 accumulate, q,k,v,dO iid N(0,1) seeds 42+idx"
+                         + (f", sliding window W={W}" if W else "")
+                         + (f", attention dropout p={P:g} (Philox seed 42)" if P else "")
+                         + (", keep bits stored by the forward" if m["keep_bits"] else "")),
+            "B": B, "H": H, "T": T, "D": D, "window": W, "dropout": P,
+            "keep_bits": m["keep_bits"], "global_batch": B,
+            "seq_len": T,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * m["tflops"] / peak, 2),
+        "fwd_tflops": round(m["fwd_tflops"], 3),
+        "fwd_pct_of_peak": round(100.0 * m["fwd_tflops"] / peak, 2),
+        # each kernel timed on its own, K launches back to back
+        "kernel_ms": {n: round(v_, 5) for n, v_ in kern_ms.items()},
+        "kernel_src_sha": sha,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "l2_flushed": False,
+    }
+    if args.config == "gpt2s" and not (W or P) and not args.no_all_configs:
+        out["configs"] = all_configs(args, cat, workloads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def measure_attention(cfg, host_inputs, steps, warmup, W=0, P=0.0, keep_bits=False,
+                      copy_calibration_mib=0):
+    """One workload on the GPU.  step_ms: K whole steps (forward + backward)
+    between two events on the launch stream, nothing else in the region.
+    kernel_ms: each call timed on its own, K launches back to back (the
+    forward's outputs from one call feed every backward)."""
+    import torch
+    import causal_head_self_amd as cat
+    dev = torch.device("cuda:0")
     q, k, v, dO = (t.to(dev) for t in host_inputs)
     B, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
     o = torch.empty_like(q)
@@ -503,15 +657,9 @@ def main() -> int:
     delta = torch.empty_like(lse)
     scale = cfg.scale
     stream = torch.cuda.current_stream()
-
-    W, P = args.window, args.dropout
-    if W < 0 or not 0.0 <= P < 1.0 or ((W or P) and (cfg.dtype != "bf16" or D not in (64, 128))):
-        print("bench.py: --window needs W >= 0, --dropout 0 <= p < 1, and either a bf16 "
-              "workload with D 64 or 128", file=sys.stderr)
-        return 2
     strided = bool(W or P)
     keep = None
-    if args.keep_bits and P > 0:
+    if keep_bits:
         keep = torch.empty((cat.dropout_keep_bytes(B, H, T) // 4,), dtype=torch.int32, device=dev)
 
     def fwd():
@@ -533,122 +681,64 @@ def main() -> int:
         else:
             cat.attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stream)
 
-    def step():
+    def timed(body, n):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(n):
+            body()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    for _ in range(warmup):
         fwd()
         bwd()
-
-    for _ in range(args.warmup):
-        step()
     torch.cuda.synchronize()
-
-    # headline: K whole steps between two events, nothing else in the region
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-
-    # per-kernel: the same K steps with an event between consecutive calls
-    # (attn_fwd and attn_bwd are one kernel launch each at head dim 64; at 128
-    # attn_bwd is two, dQ then dK/dV, timed together as "bwd")
-    names = ["fwd", "bwd"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e in evs:
-        e[0].record(stream)
-        fwd()
-        e[1].record(stream)
-        bwd()
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-               for i, n in enumerate(names)}
-    per_iter = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
-    step_iter = sorted(e[0].elapsed_time(e[2]) for e in evs)
-
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
+    step_ms = timed(lambda: (fwd(), bwd()), steps)
+    kern = {"fwd": timed(fwd, steps), "bwd": timed(bwd, steps)}
+    if copy_calibration_mib > 0:  # a plain device copy of known size (counter scaling)
+        n = copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-
     work = kernel_work(cfg, W)
     flops_f = work["fwd"]["flops"]
     flops_fb = flops_f + work["bwd"]["flops"]
-    value = flops_fb / (ms_per_step * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    return {"step_ms": step_ms, "kernel_ms": kern, "tflops": flops_fb / (step_ms * 1e-3) / 1e12,
+            "fwd_tflops": flops_f / (kern["fwd"] * 1e-3) / 1e12, "keep_bits": keep is not None}
 
-    dominant = max(names, key=lambda n: kern_ms[n])
-    achieved = work[dominant]["flops"] / (kern_ms[dominant] * 1e-3) / 1e12
-    sha = kernel_source_sha()
-    workload_name = (f"{cfg.name}_B{B}_H{H}_T{T}_D{D}_{cfg.dtype}" + (f"_W{W}" if W else "")
-                     + (f"_drop{P:g}" if P else ""))
-    roofline = {
-        "bound": "mfma",
-        "kernel": dominant,
-        "achieved": round(achieved, 2),
-        "peak": peak,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / peak, 4),
-        "traffic": read_traffic(dominant, workload_name, sha),
-        "algorithmic_flops_per_launch": work[dominant]["flops"],
-    }
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        try:
-            threads = min(16, len(os.sched_getaffinity(0)))
-        except AttributeError:
-            threads = min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(cfg, host_inputs, threads, W) if not P else None
-
-    fwd_tflops = flops_f / (kern_ms["fwd"] * 1e-3) / 1e12
-    out = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic",
-        "config": {
-            "workload": (f"causal MHA fwd+bwd, {cfg.name}: B={B} H={H} T={T} D={D} {cfg.dtype} "
-                         "storage / fp32 accumulate, q,k,v,dO iid N(0,1) seeds 42+idx"
-                         + (f", sliding window W={W}" if W else "")
-                         + (f", attention dropout p={P:g} (Philox seed 42)" if P else "")
-                         + (", keep bits stored by the forward" if keep is not None else "")),
-            "B": B, "H": H, "T": T, "D": D, "window": W, "dropout": P,
-            "keep_bits": keep is not None, "global_batch": B,
-            "seq_len": T,
-            "parallelism": "single GPU",
-        },
-        "pct_of_peak": round(100.0 * value / peak, 2),
-        "fwd_tflops": round(fwd_tflops, 3),
-        "fwd_pct_of_peak": round(100.0 * fwd_tflops / peak, 2),
-        "kernel_ms": {n: round(v_, 5) for n, v_ in kern_ms.items()},
-        # per-iteration spread of the per-kernel pass (events between the calls)
-        "kernel_ms_median": {n: round(v_[len(v_) // 2], 5) for n, v_ in per_iter.items()},
-        "kernel_ms_min": {n: round(v_[0], 5) for n, v_ in per_iter.items()},
-        "step_ms_median": round(step_iter[len(step_iter) // 2], 5),
-        "step_ms_min": round(step_iter[0], 5),
-        "kernel_src_sha": sha,
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "l2_flushed": False,
-    }
-    print(json.dumps(out), flush=True)
-    return 0
+def all_configs(args, cat, workloads) -> dict:
+    """Every configuration of the contract in the same run: GPU forward and
+    forward + backward TFLOP/s (K steps each), and the fp64 oracle's seconds
+    beside them (all heads of each attention workload; one of the sublayer's
+    eight sequences)."""
+    threads = host_info()["affinity_cores"]
+    res = {}
+    for name in ("tiny", "gpt2s", "gpt400m", "long"):
+        c = workloads.ATTN_CONFIGS[name]
+        inputs = workloads.config_inputs(c)
+        m = measure_attention(c, inputs, args.steps, args.warmup)
+        peak = PEAK_BF16_TFLOPS if c.dtype == "bf16" else PEAK_F32_TFLOPS
+        entry = {
+            "shape": {"B": c.B, "H": c.H, "T": c.T, "D": c.D, "dtype": c.dtype},
+            "fwd_bwd_tflops": round(m["tflops"], 3), "fwd_tflops": round(m["fwd_tflops"], 3),
+            "pct_of_peak": round(100.0 * m["tflops"] / peak, 2), "peak_tflops": peak,
+            "step_ms": round(m["step_ms"], 5), "kernel_ms": {n: round(x, 5) for n, x in
+                                                            m["kernel_ms"].items()},
+        }
+        if not args.no_cpu_baseline:
+            tf, tb = oracle_attention_seconds(c, inputs, threads)
+            wf = 2.0 * c.B * c.H * c.D * 2.0 * visible_pairs(c.T)
+            entry["oracle"] = {"fwd_seconds": round(tf, 4), "fwd_bwd_seconds": round(tf + tb, 4),
+                               "fwd_bwd_tflops": round(3.5 * wf / (tf + tb) / 1e12, 6),
+                               "threads": threads, "sample": "all heads"}
+        res[name] = entry
+    res["sublayer"] = sublayer_measure(args, with_oracle=not args.no_cpu_baseline)
+    return res
 
 
 if __name__ == "__main__":
