@@ -484,6 +484,44 @@ def rope_bench(args) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
     sha = kernel_source_sha("rope")
+
+    # The whole attention step with the prologue, both ways: fused into the
+    # attention kernels (the key pass, the forward turning the queries in
+    # registers, the backward applying the prologue's gradient in registers),
+    # and as separate passes around the strided attention.
+    y = torch.empty((B, T, H * D), dtype=torch.bfloat16, device=dev)
+    ov = y.view(B, T, H, D).permute(0, 2, 1, 3)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dqkv2 = torch.empty_like(qkv)
+    dq2, dk2, dv2 = cat.qkv_heads(dqkv2, H)
+    vv = cat.qkv_heads(qkv, H)[2]
+    qr, kr, dqa, dka = (torch.empty_like(q) for _ in range(4))
+    gO = g  # the incoming gradient of the attention output, as [B, H, T, D]
+
+    def fused():
+        cat.attn_fwd_strided_rope(qv, kv, vv, ov, lse, qr, kr, p, stream=stream)
+        cat.attn_bwd_strided_rope(qv, kv, qr, kr, vv, ov, lse, gO, dq2, dk2, dv2, delta, p,
+                                  stream=stream)
+
+    def two_pass():
+        cat.rope_qknorm_fwd(qv, kv, qr, kr, p, stream)
+        cat.attn_fwd_strided(qr, kr, vv, ov, lse, stream=stream)
+        cat.attn_bwd_strided(qr, kr, vv, ov, lse, gO, dqa, dka, dv2, delta, stream=stream)
+        cat.rope_qknorm_bwd(qv, kv, dqa, dka, dq2, dk2, p, stream)
+
+    e2e = {}
+    for name, body in (("fused", fused), ("two_pass", two_pass)):
+        for _ in range(args.warmup):
+            body()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            body()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        e2e[name] = t0.elapsed_time(t1) / args.steps
+    attn_flops = 7.0 * B * H * T * T * D
     cpu = None
     if not args.no_cpu_baseline:
         # the oracle (one host thread) over the whole workload: forward and
@@ -511,6 +549,12 @@ def rope_bench(args) -> int:
                                 f"H={H} D={D}"),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "kernel_ms": {n: round(v_, 5) for n, v_ in kern.items()},
+        "attention_step_ms": {"fused": round(e2e["fused"], 5), "two_pass": round(e2e["two_pass"], 5),
+                              "note": ("causal attention forward + backward with RoPE + QK norm "
+                                       "on the gpt2s shape: the prologue fused into the kernels, "
+                                       "or as separate passes")},
+        "attention_step_tflops": {n: round(attn_flops / (v_ * 1e-3) / 1e12, 3)
+                                  for n, v_ in e2e.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                      "traffic": read_traffic(dom, f"rope_gpt2s_B{B}_H{H}_T{T}_D{D}", sha),

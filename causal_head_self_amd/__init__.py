@@ -18,6 +18,8 @@ the computation.  PyTorch supplies device memory and streams.
         workspace (the library's fixed device scratch), for callers that cannot allocate
     rope_qknorm_fwd / rope_qknorm_bwd                       -- RoPE and QK norm on
         query and key rows (also as causal_attention_qkv(..., prologue=Prologue()))
+    attn_fwd_strided_rope / attn_bwd_strided_rope           -- attention with that
+        prologue fused into its kernels (what causal_attention_qkv uses without dropout)
 
 Tensors are contiguous [B, H, T, D] (D in {32, 64}; 128 in bf16) of float32 or bfloat16 on
 the current GPU; lse and delta are float32 [B, H, T].
@@ -36,7 +38,8 @@ __all__ = [
     "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_strided",
     "attn_bwd_strided", "attn_decode", "attn_decode_noalloc", "decode_workspace_bytes",
     "decode_attention", "DECODE_SCRATCH_BYTES",
-    "rope_qknorm_fwd", "rope_qknorm_bwd", "Prologue",
+    "rope_qknorm_fwd", "rope_qknorm_bwd", "Prologue", "attn_fwd_strided_rope",
+    "attn_bwd_strided_rope",
     "attn_status_str", "causal_attention", "causal_attention_qkv", "qkv_heads", "AttnError",
     "ATTN_F32", "ATTN_BF16", "load_library", "LIB_PATH", "EXPORTS", "ABI_VERSION",
 ]
@@ -159,6 +162,37 @@ def attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, scale: float | None
     check(rc)
 
 
+def attn_fwd_strided_rope(q, k, v, o, lse, q_rot, k_rot, prologue: "Prologue" = None,
+                          scale: float | None = None, stream=None, window: int = 0) -> None:
+    """C ABI attn_fwd_strided_rope: the prologue (RoPE / QK norm) fused into the
+    attention forward.  q, k are the rows before the prologue; q_rot, k_rot
+    receive them after it (the backward needs both)."""
+    p = prologue or Prologue()
+    B, H, T, D = _shape(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().attn_fwd_strided_rope(
+        _view(q, "q"), _view(k, "k"), _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"),
+        _view(q_rot, "q_rot"), _view(k_rot, "k_rot"), B, H, T, D, int(window), scale,
+        *p.args(), _dtype_code(q), _stream(stream))
+    check(rc)
+
+
+def attn_bwd_strided_rope(q, k, q_rot, k_rot, v, o, lse, dO, dq, dk, dv, delta,
+                          prologue: "Prologue" = None, scale: float | None = None, stream=None,
+                          window: int = 0) -> None:
+    """C ABI attn_bwd_strided_rope: dq and dk with respect to the rows before the
+    prologue (q, k), from the forward's q_rot, k_rot, o and lse."""
+    p = prologue or Prologue()
+    B, H, T, D = _shape(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().attn_bwd_strided_rope(
+        _view(q, "q"), _view(k, "k"), _view(q_rot, "q_rot"), _view(k_rot, "k_rot"),
+        _view(v, "v"), _view(o, "o"), _ptr(lse, "lse"), _view(dO, "dO"), _view(dq, "dq"),
+        _view(dk, "dk"), _view(dv, "dv"), _ptr(delta, "delta"), B, H, T, D, int(window), scale,
+        *p.args(), _dtype_code(q), _stream(stream))
+    check(rc)
+
+
 def dropout_keep_bytes(B: int, H: int, T: int) -> int:
     """C ABI attn_dropout_keep_bytes: size of the stored keep bits of one call."""
     return int(load_library().attn_dropout_keep_bytes(int(B), int(H), int(T)))
@@ -221,14 +255,18 @@ class _CausalAttentionQKV(torch.autograd.Function):
         y = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
         o = y.view(B, T, n_head, C // n_head).permute(0, 2, 1, 3)  # [B, H, T, D] view of y
         lse = torch.empty((B, n_head, T), dtype=torch.float32, device=qkv.device)
+        fused = prologue is not None and dropout_p == 0.0
         if prologue is not None:  # rotated / normalised q and k, contiguous [B, H, T, D]
             qa = torch.empty(q.shape, dtype=q.dtype, device=q.device)
             ka = torch.empty_like(qa)
-            rope_qknorm_fwd(q, k, qa, ka, prologue)
+            if not fused:
+                rope_qknorm_fwd(q, k, qa, ka, prologue)
         else:
             qa, ka = q, k
         keep = None
-        if dropout_p > 0.0 and keep_bits:  # the forward's keep decisions, for the backward
+        if fused:  # the prologue inside the attention kernels
+            attn_fwd_strided_rope(q, k, v, o, lse, qa, ka, prologue, window=window)
+        elif dropout_p > 0.0 and keep_bits:  # the forward's keep decisions, for the backward
             keep = torch.empty((dropout_keep_bytes(B, n_head, T) // 4,), dtype=torch.int32,
                                device=qkv.device)
             attn_fwd_strided_keep(qa, ka, v, o, lse, keep, window=window, dropout_p=dropout_p,
@@ -271,6 +309,10 @@ class _CausalAttentionQKV(torch.autograd.Function):
 
         if ctx.prologue is None:
             bwd(q, k, dq, dk)
+        elif ctx.dropout[0] == 0.0:  # the prologue's gradient inside the attention kernels
+            qa, ka = ctx.saved_tensors[3:5]
+            attn_bwd_strided_rope(q, k, qa, ka, v, o, lse, dO, dq, dk, dv, delta, ctx.prologue,
+                                  window=ctx.window)
         else:
             qa, ka = ctx.saved_tensors[3:5]
             dqa, dka = torch.empty_like(qa), torch.empty_like(ka)
@@ -286,8 +328,9 @@ def causal_attention_qkv(qkv: torch.Tensor, n_head: int, window: int = 0,
     chunks of C, each [B, T, H, D]) -> y [B, T, C] (heads merged), read and
     written in place through strided views (bf16, head dim 64 or 128).  window W > 0
     restricts query i to keys i-W < j <= i (sliding window).  prologue applies
-    RoPE and/or QK norm to q and k first (one extra read and write of q and k
-    each way).  dropout_p > 0 drops attention weights (training mode); the
+    RoPE and/or QK norm to q and k first: without dropout inside the attention
+    kernels (attn_fwd_strided_rope / attn_bwd_strided_rope), with dropout as
+    separate passes (one extra read and write of q and k each way).  dropout_p > 0 drops attention weights (training mode); the
     Philox seed is drawn from torch's default generator unless given, and the
     backward reuses it.  With keep_bits (the default) the forward stores its
     keep decisions (dropout_keep_bytes(B, H, T) bytes, held for the backward)

@@ -39,8 +39,9 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_str
            "attn_bwd_strided", "attn_dropout_keep_bytes", "attn_fwd_strided_keep",
            "attn_bwd_strided_keep", "attn_decode", "attn_decode_workspace_bytes",
            "attn_decode_noalloc", "attn_rope_qknorm_fwd", "attn_rope_qknorm_bwd",
-           "attn_status_str", "attn_abi_version")
-ABI_VERSION = (1 << 16) | 6
+           "attn_fwd_strided_rope", "attn_bwd_strided_rope", "attn_status_str",
+           "attn_abi_version")
+ABI_VERSION = (1 << 16) | 7
 # the fixed device scratch of attn_decode_noalloc (CAUSAL_ATTN_DECODE_SCRATCH_BYTES)
 DECODE_SCRATCH_BYTES = 16 << 20
 
@@ -113,6 +114,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_rope_qknorm_fwd.restype = _int
     lib.attn_rope_qknorm_bwd.argtypes = [AttnView] * 6 + _rope_tail
     lib.attn_rope_qknorm_bwd.restype = _int
+    lib.attn_fwd_strided_rope.argtypes = ([AttnView] * 4 + [_vp] + [AttnView] * 2 +
+                                          [_int] * 5 + [ctypes.c_float] + [_int] +
+                                          [ctypes.c_float] * 4 + [_int, _int, _vp])
+    lib.attn_fwd_strided_rope.restype = _int
+    lib.attn_bwd_strided_rope.argtypes = ([AttnView] * 6 + [_vp] + [AttnView] * 4 + [_vp] +
+                                          [_int] * 5 + [ctypes.c_float] + [_int] +
+                                          [ctypes.c_float] * 4 + [_int, _int, _vp])
+    lib.attn_bwd_strided_rope.restype = _int
     lib.attn_status_str.argtypes = [_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []

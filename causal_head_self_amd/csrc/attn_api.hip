@@ -128,6 +128,33 @@ bool views_disjoint(const attn_view_t& a, const attn_view_t& b, int B, int H, in
     return r >= w && st - r >= w;
 }
 
+// True when the (b, h, t, d) elements of a view address distinct memory: taken
+// in order of increasing stride (the D columns have stride 1; dimensions of
+// size 1 do not count), every stride must exceed the span of the dimensions
+// before it.  An output that fails this would have several lanes write one
+// element.
+bool view_is_injective(const attn_view_t& v, int B, int H, int T, int D)
+{
+    long long st[3] = {v.stride_t, v.stride_h, v.stride_b};
+    long long sz[3] = {T, H, B};
+    for (int i = 0; i < 3; ++i)  // sort by stride (three elements)
+        for (int j = i + 1; j < 3; ++j)
+            if (st[j] < st[i]) {
+                const long long a = st[i], b = sz[i];
+                st[i] = st[j];
+                sz[i] = sz[j];
+                st[j] = a;
+                sz[j] = b;
+            }
+    long long span = D;  // elements spanned by the dimensions taken so far
+    for (int i = 0; i < 3; ++i) {
+        if (sz[i] <= 1) continue;
+        if (st[i] < span) return false;
+        span = st[i] * (sz[i] - 1) + span;
+    }
+    return true;
+}
+
 int validate_views(const VSpan* vs, int n, const float* const* rows, int nrows, int B, int H,
                    int T, int D, float scale, int dtype)
 {
@@ -154,10 +181,11 @@ int validate_views(const VSpan* vs, int n, const float* const* rows, int nrows, 
         if ((uintptr_t)vs[i].v->data % 16) return ATTN_ERR_ALIGN;
     for (int i = 0; i < nrows; ++i)
         if ((uintptr_t)rows[i] % 4) return ATTN_ERR_ALIGN;
-    // aliasing: outputs against everything (views and row tensors)
+    // aliasing: outputs against themselves and against everything (views and row tensors)
     const size_t row_bytes = (size_t)BH * T * sizeof(float);
     for (int i = 0; i < n; ++i) {
         if (!vs[i].output) continue;
+        if (!view_is_injective(*vs[i].v, B, H, T, D)) return ATTN_ERR_ALIAS;
         for (int j = 0; j < n; ++j)
             if (j != i && !(vs[j].output && j < i) &&
                 !views_disjoint(*vs[i].v, *vs[j].v, B, H, T, D, 2))
@@ -524,6 +552,109 @@ int attn_bwd_strided_keep(attn_view_t q, attn_view_t k, attn_view_t v, attn_view
     if (ks != ATTN_OK) return ks;
     return bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, D, window, dropout_p, 0,
                        scale, dtype, keep, stream);
+}
+
+// The prologue parameters of the fused entry points, as for attn_rope_qknorm_*.
+static void set_rope(cattn::AttnArgs& a, int pos0, float base, float q_gain, float k_gain,
+                     float eps, int flags)
+{
+    const cattn::RopeArgs r = rope_args(a.B, a.H, a.T, a.D, pos0, base, q_gain, k_gain, eps, flags,
+                                        false);
+    a.rope = true;
+    a.pos0 = pos0;
+    a.rope_flags = flags;
+    a.q_gain = q_gain;
+    a.k_gain = k_gain;
+    a.rope_eps = eps;
+    a.freqs = r.freqs;
+}
+
+int attn_fwd_strided_rope(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                          attn_view_t q_rot, attn_view_t k_rot, int B, int H, int T, int D,
+                          int window, float scale, int pos0, float rope_base, float q_gain,
+                          float k_gain, float eps, int flags, int dtype, void* stream)
+{
+    const VSpan vs[6] = {{&q, false}, {&k, false}, {&v, false},
+                         {&o, true},  {&q_rot, true}, {&k_rot, true}};
+    const float* rows[1] = {lse};
+    int st = validate_views(vs, 6, rows, 1, B, H, T, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    if (window < 0) return ATTN_ERR_SHAPE;
+    if (!rope_params_ok(T, pos0, rope_base, q_gain, k_gain, eps, flags)) return ATTN_ERR_PARAM;
+    const uintptr_t rlo = (uintptr_t)lse, rhi = rlo + (size_t)B * H * T * sizeof(float);
+    for (int i = 0; i < 3; ++i) {  // lse (an output) apart from the inputs
+        const uintptr_t lo = (uintptr_t)vs[i].v->data;
+        const uintptr_t hi = lo + (uintptr_t)view_extent(*vs[i].v, B, H, T, D) * 2;
+        if (lo < rhi && rlo < hi) return ATTN_ERR_ALIAS;
+    }
+    cattn::AttnArgs a = make_args(B, H, T, D, scale);
+    a.q = q.data;
+    a.k = k.data;
+    a.v = v.data;
+    a.o = o.data;
+    a.o_out = o.data;
+    a.lse = lse;
+    a.sq = strides_of(q);
+    a.sk = strides_of(k);
+    a.sv = strides_of(v);
+    a.so = strides_of(o);
+    a.q_rot = q_rot.data;
+    a.k_rot = k_rot.data;
+    a.sqr = strides_of(q_rot);
+    a.skr = strides_of(k_rot);
+    a.window = window;
+    set_rope(a, pos0, rope_base, q_gain, k_gain, eps, flags);
+    return status(cattn::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+int attn_bwd_strided_rope(attn_view_t q, attn_view_t k, attn_view_t q_rot, attn_view_t k_rot,
+                          attn_view_t v, attn_view_t o, const float* lse, attn_view_t dO,
+                          attn_view_t dq, attn_view_t dk, attn_view_t dv, float* delta, int B,
+                          int H, int T, int D, int window, float scale, int pos0, float rope_base,
+                          float q_gain, float k_gain, float eps, int flags, int dtype, void* stream)
+{
+    const VSpan vs[10] = {{&q, false},  {&k, false},  {&q_rot, false}, {&k_rot, false},
+                          {&v, false},  {&o, false},  {&dO, false},    {&dq, true},
+                          {&dk, true},  {&dv, true}};
+    const float* rows[2] = {lse, delta};
+    int st = validate_views(vs, 10, rows, 2, B, H, T, D, scale, dtype);
+    if (st != ATTN_OK) return st;
+    if (window < 0) return ATTN_ERR_SHAPE;
+    if (!rope_params_ok(T, pos0, rope_base, q_gain, k_gain, eps, flags)) return ATTN_ERR_PARAM;
+    const size_t rb = (size_t)B * H * T * sizeof(float);
+    const uintptr_t dlo = (uintptr_t)delta, dhi = dlo + rb;  // delta (an output) apart from inputs
+    if (dlo < (uintptr_t)lse + rb && (uintptr_t)lse < dhi) return ATTN_ERR_ALIAS;
+    for (int i = 0; i < 7; ++i) {
+        const uintptr_t lo = (uintptr_t)vs[i].v->data;
+        const uintptr_t hi = lo + (uintptr_t)view_extent(*vs[i].v, B, H, T, D) * 2;
+        if (lo < dhi && dlo < hi) return ATTN_ERR_ALIAS;
+    }
+    cattn::AttnArgs a = make_args(B, H, T, D, scale);
+    a.q = q_rot.data;  // the attention runs on the rows after the prologue
+    a.k = k_rot.data;
+    a.v = v.data;
+    a.o = o.data;
+    a.dO = dO.data;
+    a.lse = const_cast<float*>(lse);
+    a.delta = delta;
+    a.dq = dq.data;
+    a.dk = dk.data;
+    a.dv = dv.data;
+    a.sq = strides_of(q_rot);
+    a.sk = strides_of(k_rot);
+    a.sv = strides_of(v);
+    a.so = strides_of(o);
+    a.sdo = strides_of(dO);
+    a.sdq = strides_of(dq);
+    a.sdk = strides_of(dk);
+    a.sdv = strides_of(dv);
+    a.xq = q.data;
+    a.xk = k.data;
+    a.sxq = strides_of(q);
+    a.sxk = strides_of(k);
+    a.window = window;
+    set_rope(a, pos0, rope_base, q_gain, k_gain, eps, flags);
+    return status(cattn::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int T_max, int D)

@@ -26,6 +26,8 @@
 //    than 2^8 in the exponent (lazy rescale), so most tiles skip rescaling
 //    the accumulators; the row sum is taken on the bf16 P that feeds the PV
 //    product, two at a time with v_dot2_f32_bf16.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -351,6 +353,176 @@ __device__ __forceinline__ bf16* head_of(const View& v, int bh, int H)
     return v.p + (long long)b * v.sb + (long long)h * v.sh;
 }
 
+// RoPE / QK-norm prologue fused into the kernels (nanochat, section 9 lists
+// RoPE and QK norm among its attention's parts; standard forms, as in
+// attn_rope.hip): the row at position p = pos0 + t becomes
+//   y = gain * R(x) / sqrt(mean(x^2) + eps)   (R alone without the norm),
+// R turning column pair (i, i + D/2) by p * base^(-2i/D).  The forward
+// applies it to its register-resident query rows (and writes them out for the
+// backward); the backward items apply the transposed Jacobian of the prologue
+// to their dQ (dK) rows before storing them:
+//   dx = R^T(gain/rms g - gain/rms^3 mean(g z) z),  z = R(x).
+struct RopeP {
+    View xq, xk;  // rows before the prologue (backward: where the gradient is taken)
+    View yq;      // forward: the queries after the prologue, written for the backward
+    int pos0, flags;  // flags: bit 0 RoPE, bit 1 QK norm
+    float q_gain, k_gain, eps;
+    RopeFreqs fr;  // revolutions per position of pair i, base^(-2i/D) / (2 pi)
+    double step4, step8;  // base^(-8/D), base^(-16/D): pair i + 4 (+ 8) over pair i
+};
+struct NoRope {};
+template <bool kRope>
+using RopeArg = typename std::conditional<kRope, RopeP, NoRope>::type;
+
+// Index 0, opaque to the compiler: table reads indexed from it are issued where
+// the table is used, not hoisted to the kernel's start and held in scalar
+// registers through the main loop.
+__device__ __forceinline__ int here0()
+{
+    int z = 0;
+    asm volatile("" : "+s"(z));
+    return z;
+}
+
+// Position times this lane's frequency multiplier: a lane of the upper half
+// (hi = 1) turns pair i + di where the lower half turns pair i, and
+// base^(-2(i + di)/D) = base^(-2i/D) * step with step = base^(-2di/D), so one
+// wave-uniform table entry serves both halves.
+__device__ __forceinline__ double lane_pos(int p, int hi, double step)
+{
+    return (double)p * (hi ? step : 1.0);
+}
+
+// Cosine and sine of the angle pm * f revolutions (one fp64 multiply, the
+// fraction to the hardware sine and cosine).
+__device__ __forceinline__ void rope_angle(const RopeP& rp, double pm, double f, float& c, float& s)
+{
+    c = 1.f;
+    s = 0.f;
+    if (rp.flags & 1) {
+        const double r = pm * f;
+        const float turn = (float)(r - floor(r));
+        s = __builtin_amdgcn_sinf(turn);
+        c = __builtin_amdgcn_cosf(turn);
+    }
+}
+
+// Forward prologue of one query row held as MFMA operands: x[ks] holds columns
+// 16 ks + 8 hi .. + 7 (the other 32 of each 64 in lane l ^ 32), so pair
+// (i, i + D/2) sits in x[ks] and x[ks + 2 NP] of the same lane.
+template <int NP>
+__device__ __forceinline__ void rope_rows(bf16x8 (&x)[4 * NP], const RopeP& rp, int p, int hi)
+{
+    constexpr int D = HD * NP, HALF = 2 * NP;
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4 * NP; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf((float)x[ks][e], (float)x[ks][e], ss);
+    const bool norm = rp.flags & 2;
+    const float f = norm ? rp.q_gain / sqrtf(halves_sum(ss) / (float)D + rp.eps) : 1.f;
+    const int i0 = here0();
+    const double pm = lane_pos(p, hi, rp.step8);
+#pragma unroll
+    for (int ks = 0; ks < HALF; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float c, s;
+            rope_angle(rp, pm, rp.fr.f[i0 + 16 * ks + e], c, s);
+            const float u = (float)x[ks][e], w = (float)x[ks + HALF][e];
+            x[ks][e] = (bf16)(f * (u * c - w * s));
+            x[ks + HALF][e] = (bf16)(f * (u * s + w * c));
+        }
+}
+
+// Backward epilogue of one row: acc[dt][4g + e] times mult is the gradient with
+// respect to the prologue's output at column 32 dt + 8 g + 4 hi + e (pair
+// (i, i + D/2) in acc[dt] and acc[dt + NP] of the same lane); xr points at the
+// row before the prologue, readable in every lane (for a row past T, valid
+// false, it points at a row of the sequence and the lane's results are
+// dropped; lanes l and l ^ 32 hold the same row).  Stores the gradient with
+// respect to that row, in bf16, where valid.  The row's sum of squares and m = sum(g z) over the whole
+// row are needed before any output, so the row is swept twice.  At head dim 64
+// the row and its angles are kept in registers between the sweeps (the loads
+// issued first, the angles computed while they are in flight); at 128 that
+// would spill, so the second sweep loads and computes them again.
+template <int NP>
+__device__ __forceinline__ void rope_grad_store(const f32x16 (&acc)[2 * NP], float mult,
+                                                const bf16* xr, bool valid, bf16* out,
+                                                const RopeP& rp, float gain, int p, int hi)
+{
+    constexpr int D = HD * NP;
+    constexpr bool kKeep = NP == 1;
+    bf16x4 u[NP][4], w[NP][4];
+    float c[NP][4][4], s[NP][4][4];
+    auto load = [&](int dt, int g) {
+        u[dt][g] = *(const bf16x4*)(xr + 32 * dt + 8 * g + 4 * hi);
+        w[dt][g] = *(const bf16x4*)(xr + 32 * (dt + NP) + 8 * g + 4 * hi);
+    };
+    const int i0 = here0();
+    const double pm = lane_pos(p, hi, rp.step4);
+    auto angles = [&](int dt, int g) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            rope_angle(rp, pm, rp.fr.f[i0 + 32 * dt + 8 * g + e], c[dt][g][e], s[dt][g][e]);
+    };
+    // z = R(x) at (dt, g, e)
+    auto rot = [&](int dt, int g, int e, float& zl, float& zh) {
+        const float a = (float)u[dt][g][e], b = (float)w[dt][g][e];
+        zl = a * c[dt][g][e] - b * s[dt][g][e];
+        zh = a * s[dt][g][e] + b * c[dt][g][e];
+    };
+#pragma unroll
+    for (int dt = 0; dt < NP; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) load(dt, g);
+    float ss = 0.f, m = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NP; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            angles(dt, g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = (float)u[dt][g][e], b = (float)w[dt][g][e];
+                float zl, zh;
+                rot(dt, g, e, zl, zh);
+                ss = fmaf(a, a, fmaf(b, b, ss));
+                m = fmaf(mult * acc[dt][4 * g + e], zl, fmaf(mult * acc[dt + NP][4 * g + e], zh, m));
+            }
+        }
+    float a1 = 1.f, a3 = 0.f;
+    if (rp.flags & 2) {
+        const float inv = 1.0f / sqrtf(halves_sum(ss) / (float)D + rp.eps);
+        a1 = gain * inv;
+        a3 = gain * inv * inv * inv * (halves_sum(m) / (float)D);
+    }
+    if (!valid) return;
+    // dx = R^T(a1 g - a3 z)
+#pragma unroll
+    for (int dt = 0; dt < NP; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            if constexpr (!kKeep) {
+                load(dt, g);
+                angles(dt, g);
+            }
+            float lo[4], hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float zl, zh;
+                rot(dt, g, e, zl, zh);
+                const float cc = c[dt][g][e], sn = s[dt][g][e];
+                const float dl = a1 * (mult * acc[dt][4 * g + e]) - a3 * zl;
+                const float dh = a1 * (mult * acc[dt + NP][4 * g + e]) - a3 * zh;
+                lo[e] = dl * cc + dh * sn;
+                hv[e] = -dl * sn + dh * cc;
+            }
+            store_bf16x4(out + 32 * dt + 8 * g + 4 * hi, lo[0], lo[1], lo[2], lo[3]);
+            store_bf16x4(out + 32 * (dt + NP) + 8 * g + 4 * hi, hv[0], hv[1], hv[2], hv[3]);
+        }
+}
+
 // ---------------------------------------------------------------------------
 // forward: 128 queries per workgroup (32 per wave), 64-key K and V tiles,
 // double-buffered through LDS (the copy of tile j+1 is in flight while tile j
@@ -359,10 +531,10 @@ __device__ __forceinline__ bf16* head_of(const View& v, int bh, int H)
 // three waves that share a SIMD overlap each other's LDS latency.  Every wave
 // needs tiles 0..last_w; only the last one crosses its diagonal and is masked.
 // ---------------------------------------------------------------------------
-template <int NP, bool kDrop, bool kKeep = false>
+template <int NP, bool kDrop, bool kKeep = false, bool kRope = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_fwd_d64_kernel(
     View Q, View K, View V, View O, float* __restrict__ LSE, int BH, int H, int T, int W,
-    int n_qtiles, float scale, float scale_log2, int n_cu, Dropout dr)
+    int n_qtiles, float scale, float scale_log2, int n_cu, Dropout dr, RopeArg<kRope> rp)
 {
     // Separate arrays per buffer (not one indexed array): with the buffer of every
     // access known at compile time, the compiler can tell that an LDS read does not
@@ -401,6 +573,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int ks = 0; ks < 4 * NP; ++ks)
         qreg[ks] = (qrow < T) ? *(const bf16x8*)(qh + (size_t)qrow * Q.st + 16 * ks + 8 * hi)
                               : zero_bf16x8();
+    if constexpr (kRope) {  // the query rows after the prologue, also kept for the backward
+        rope_rows<NP>(qreg, rp, rp.pos0 + qrow, hi);
+        if (qrow < T) {
+            bf16* yr = head_of(rp.yq, bh, H) + (size_t)qrow * rp.yq.st + 8 * hi;
+#pragma unroll
+            for (int ks = 0; ks < 4 * NP; ++ks) *(bf16x8*)(yr + 16 * ks) = qreg[ks];
+        }
+    }
     f32x16 oacc[2 * NP];
 #pragma unroll
     for (int dt = 0; dt < 2 * NP; ++dt) oacc[dt] = f32x16{};
@@ -549,9 +729,10 @@ struct BwdParams {
 // Delta_i = sum_d dO_id O_id is formed from the rows the wave holds as MFMA
 // operands and written out.
 // ---------------------------------------------------------------------------
-template <int NP, bool kDrop, bool kKeep = false>
+template <int NP, bool kDrop, bool kKeep = false, bool kRope = false>
 __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char* sK0, char* sK1,
-                                        char* sV0, char* sV1)
+                                        char* sV0, char* sV1,
+                                        const RopeArg<kRope>& rp = RopeArg<kRope>{})
 {
     const int BH = a.BH, T = a.T;
     const float scale = a.scale, scale_log2 = a.scale_log2;
@@ -686,7 +867,12 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
         if (j + 1 < n_kv) step(j + 1, sK1, sV1, sK0, sV0);
     }
 
-    if (valid) {
+    if constexpr (kRope) {  // through the prologue's transposed Jacobian (every lane takes part)
+        const bf16* xr = head_of(rp.xq, bh, a.H) + (size_t)(valid ? qrow : 0) * rp.xq.st;
+        rope_grad_store<NP>(dqacc, scale, xr, valid,
+                            head_of(a.dQ, bh, a.H) + (size_t)qrow * a.dQ.st, rp, rp.q_gain,
+                            rp.pos0 + qrow, hi);
+    } else if (valid) {
         bf16* row = head_of(a.dQ, bh, a.H) + (size_t)qrow * a.dQ.st;
 #pragma unroll
         for (int dt = 0; dt < 2 * NP; ++dt)
@@ -714,11 +900,13 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
 // leaves -Delta in the row buffer, which the next step's barrier publishes.
 // Otherwise Delta is read from memory (written by a dQ pass).
 // ---------------------------------------------------------------------------
-template <int NP, bool kDeltaFromO, bool kDrop, bool kKeep = false>
+template <int NP, bool kDeltaFromO, bool kDrop, bool kKeep = false, bool kRope = false>
 __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, char* sQ0, char* sQ1,
                                           char* sG0, char* sG1, char* sO0, char* sO1,
-                                          float (*sR0)[kTile], float (*sR1)[kTile])
+                                          float (*sR0)[kTile], float (*sR1)[kTile],
+                                          const RopeArg<kRope>& rp = RopeArg<kRope>{})
 {
+    static_assert(!(kRope && kDrop), "the fused prologue has no dropout variant");
     const int T = a.T;
     const float scale = a.scale, scale_log2 = a.scale_log2;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -943,6 +1131,24 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         if (i - 1 >= i0) step(i - 1, sQ1, sG1, sR1, sQ0, sG0, sO0, sR0);
     }
 
+    if constexpr (kRope) {
+        // dV first (its accumulators are then free), then dK through the prologue's
+        // transposed Jacobian (every lane takes part)
+        if (valid) {
+            bf16* vrow = head_of(a.dV, bh, a.H) + (size_t)key * a.dV.st;
+#pragma unroll
+            for (int dt = 0; dt < 2 * NP; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    store_bf16x4(vrow + 32 * dt + 8 * g + 4 * hi, dvacc[dt][4 * g],
+                                 dvacc[dt][4 * g + 1], dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]);
+        }
+        const bf16* xr = head_of(rp.xk, bh, a.H) + (size_t)(valid ? key : 0) * rp.xk.st;
+        rope_grad_store<NP>(dkacc, scale, xr, valid,
+                            head_of(a.dK, bh, a.H) + (size_t)key * a.dK.st, rp, rp.k_gain,
+                            rp.pos0 + key, hi);
+        return;
+    }
     if (valid) {
         bf16* krow = head_of(a.dK, bh, a.H) + (size_t)key * a.dK.st;
         bf16* vrow = head_of(a.dV, bh, a.H) + (size_t)key * a.dV.st;
@@ -961,9 +1167,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
 }
 
 // dQ alone (also writes Delta).
-template <int NP, bool kDrop, bool kKeep = false>
+template <int NP, bool kDrop, bool kKeep = false, bool kRope = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dq_d64_kernel(
-    BwdParams a, int n_qtiles, int n_cu)
+    BwdParams a, int n_qtiles, int n_cu, RopeArg<kRope> rp)
 {
     // one array per buffer, so that reads are provably apart from in-flight copies
     __shared__ __attribute__((aligned(1024))) char sK0[NP * kTileBytes];
@@ -971,13 +1177,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char sV0[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV1[NP * kTileBytes];
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    dq_item<NP, kDrop, kKeep>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1);
+    dq_item<NP, kDrop, kKeep, kRope>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1,
+                                     rp);
 }
 
 // dK, dV alone, from a Delta in memory.
-template <int NP, bool kDrop, bool kKeep = false>
+template <int NP, bool kDrop, bool kKeep = false, bool kRope = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dkdv_d64_kernel(
-    BwdParams a, int n_cu)
+    BwdParams a, int n_cu, RopeArg<kRope> rp)
 {
     __shared__ __attribute__((aligned(1024))) char sQ0[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sQ1[NP * kTileBytes];
@@ -986,8 +1193,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
     __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
-    dkdv_item<NP, false, kDrop, kKeep>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1, nullptr, nullptr,
-                                sR0, sR1);
+    dkdv_item<NP, false, kDrop, kKeep, kRope>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1,
+                                              nullptr, nullptr, sR0, sR1, rp);
 }
 
 // ---------------------------------------------------------------------------
@@ -999,9 +1206,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 // count (a dK/dV tile costs more): level v holds the dK/dV items of key block v
 // and the dQ items of query block n - 1 - v, BH of each.
 // ---------------------------------------------------------------------------
-template <bool kDrop, bool kKeep = false>
+template <bool kDrop, bool kKeep = false, bool kRope = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_d64_kernel(
-    BwdParams a, int n_blocks, int n_cu)
+    BwdParams a, int n_blocks, int n_cu, RopeArg<kRope> rp)
 {
     __shared__ __attribute__((aligned(1024))) char s0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char s1[kTileBytes];
@@ -1015,15 +1222,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int BH = a.BH;
     const int level = item / (2 * BH), r = item - level * 2 * BH;
     if (r < BH)
-        dkdv_item<1, true, kDrop, kKeep>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1);
+        dkdv_item<1, true, kDrop, kKeep, kRope>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1, rp);
     else
-        dq_item<1, kDrop, kKeep>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3);
+        dq_item<1, kDrop, kKeep, kRope>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3, rp);
 }
 
 #ifndef CATTN_D64_KERNELS_ONLY
 // The one-launch backward without dropout is instantiated in attn_bwd_plain.hip,
 // which is compiled with its own instruction-scheduling strategy.
-extern template __global__ void attn_bwd_d64_kernel<false, false>(BwdParams, int, int);
+extern template __global__ void attn_bwd_d64_kernel<false, false, false>(BwdParams, int, int, NoRope);
 #endif
 
 }  // namespace d64
@@ -1048,8 +1255,63 @@ static d64::Dropout dropout_of(const AttnArgs& a)
     return d;
 }
 
+static d64::RopeP rope_p(const AttnArgs& a)
+{
+    d64::RopeP r;
+    r.xq = view(a.xq, a.sxq);
+    r.xk = view(a.xk, a.sxk);
+    r.yq = view(a.q_rot, a.sqr);
+    r.pos0 = a.pos0;
+    r.flags = a.rope_flags;
+    r.q_gain = a.q_gain;
+    r.k_gain = a.k_gain;
+    r.eps = a.rope_eps;
+    r.fr = a.freqs;
+    r.step4 = a.freqs.f[4] / a.freqs.f[0];
+    r.step8 = a.freqs.f[8] / a.freqs.f[0];
+    return r;
+}
+
+// Forward with the RoPE / QK-norm prologue: the keys through the prologue pass
+// (k -> k_rot), then the forward on the raw queries (turned in registers and
+// written to q_rot) and k_rot.
+static hipError_t launch_fwd_rope_bf16_d64(const AttnArgs& a, hipStream_t st)
+{
+    RopeArgs r{};
+    r.k = a.k;
+    r.sk = a.sk;
+    r.k_out = a.k_rot;
+    r.sko = a.skr;
+    r.dk_in = a.k;
+    r.sdk = a.sk;
+    r.B = a.B;
+    r.H = a.H;
+    r.T = a.T;
+    r.D = a.D;
+    r.pos0 = a.pos0;
+    r.flags = a.rope_flags;
+    r.q_gain = a.q_gain;
+    r.k_gain = a.k_gain;
+    r.eps = a.rope_eps;
+    r.freqs = a.freqs;
+    r.grad = false;
+    r.k_only = true;
+    const hipError_t e = launch_rope_qknorm(r, st);
+    if (e != hipSuccess) return e;
+    const int BH = a.B * a.H;
+    const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
+    auto k = a.D == 128 ? d64::attn_fwd_d64_kernel<2, false, false, true>
+                        : d64::attn_fwd_d64_kernel<1, false, false, true>;
+    hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
+                       view(a.q, a.sq), view(a.k_rot, a.skr), view(a.v, a.sv), view(a.o_out, a.so),
+                       a.lse, BH, a.H, a.T, window_of(a), nqt, a.scale, a.scale * kLog2e, a.n_cu,
+                       dropout_of(a), rope_p(a));
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
+    if (a.rope) return launch_fwd_rope_bf16_d64(a, st);
     const int BH = a.B * a.H;
     const int nqt = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
     const bool drop = a.dropout_p16 > 0;
@@ -1061,7 +1323,7 @@ hipError_t launch_fwd_bf16_d64(const AttnArgs& a, hipStream_t st)
     hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st,
                        view(a.q, a.sq), view(a.k, a.sk), view(a.v, a.sv), view(a.o_out, a.so),
                        a.lse, BH, a.H, a.T, window_of(a), nqt, a.scale, a.scale * kLog2e, a.n_cu,
-                       dropout_of(a));
+                       dropout_of(a), d64::NoRope{});
     return hipGetLastError();
 }
 
@@ -1098,7 +1360,15 @@ hipError_t launch_dq_bf16_d64(const AttnArgs& a, hipStream_t st)
                                 : drop ? d64::attn_bwd_dq_d64_kernel<2, true> : d64::attn_bwd_dq_d64_kernel<2, false>)
                         : (keep ? d64::attn_bwd_dq_d64_kernel<1, true, true>
                                 : drop ? d64::attn_bwd_dq_d64_kernel<1, true> : d64::attn_bwd_dq_d64_kernel<1, false>);
-    hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nqt, a.n_cu);
+    if (a.rope) {
+        auto kr = a.D == 128 ? d64::attn_bwd_dq_d64_kernel<2, false, false, true>
+                             : d64::attn_bwd_dq_d64_kernel<1, false, false, true>;
+        hipLaunchKernelGGL(kr, dim3(nqt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nqt, a.n_cu,
+                           rope_p(a));
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k, dim3(nqt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nqt, a.n_cu,
+                       d64::NoRope{});
     return hipGetLastError();
 }
 
@@ -1112,7 +1382,15 @@ hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st)
                                 : drop ? d64::attn_bwd_dkdv_d64_kernel<2, true> : d64::attn_bwd_dkdv_d64_kernel<2, false>)
                         : (keep ? d64::attn_bwd_dkdv_d64_kernel<1, true, true>
                                 : drop ? d64::attn_bwd_dkdv_d64_kernel<1, true> : d64::attn_bwd_dkdv_d64_kernel<1, false>);
-    hipLaunchKernelGGL(k, dim3(nkt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), a.n_cu);
+    if (a.rope) {
+        auto kr = a.D == 128 ? d64::attn_bwd_dkdv_d64_kernel<2, false, false, true>
+                             : d64::attn_bwd_dkdv_d64_kernel<1, false, false, true>;
+        hipLaunchKernelGGL(kr, dim3(nkt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), a.n_cu,
+                           rope_p(a));
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k, dim3(nkt * BH), dim3(d64::kThreads), 0, st, bwd_params(a), a.n_cu,
+                       d64::NoRope{});
     return hipGetLastError();
 }
 
@@ -1124,9 +1402,15 @@ hipError_t launch_bwd_bf16_d64(const AttnArgs& a, hipStream_t st)
     }
     const int BH = a.B * a.H;
     const int nb = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
+    if (a.rope) {
+        hipLaunchKernelGGL((d64::attn_bwd_d64_kernel<false, false, true>), dim3(2 * nb * BH),
+                           dim3(d64::kThreads), 0, st, bwd_params(a), nb, a.n_cu, rope_p(a));
+        return hipGetLastError();
+    }
     auto k = a.dropout_p16 > 0 ? (a.keep ? d64::attn_bwd_d64_kernel<true, true> : d64::attn_bwd_d64_kernel<true>)
                                : d64::attn_bwd_d64_kernel<false>;
-    hipLaunchKernelGGL(k, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nb, a.n_cu);
+    hipLaunchKernelGGL(k, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nb, a.n_cu,
+                       d64::NoRope{});
     return hipGetLastError();
 }
 

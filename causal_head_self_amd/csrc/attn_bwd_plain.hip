@@ -1,5 +1,5 @@
 // attn_bwd_plain.hip -- the one-launch backward at head dim 64 without dropout
-// (attn_bwd_d64_kernel<false, false> of attn_bf16_d64.hip), instantiated in a
+// (attn_bwd_d64_kernel<false, false, false> of attn_bf16_d64.hip), instantiated in a
 // translation unit of its own so that the build can compile it with another
 // instruction-scheduling strategy than the other kernels: LLVM's iterative ILP
 // scheduler, which interleaves this kernel's MFMA and VALU work more closely
@@ -11,6 +11,6 @@
 
 namespace cattn {
 namespace d64 {
-template __global__ void attn_bwd_d64_kernel<false, false>(BwdParams, int, int);
+template __global__ void attn_bwd_d64_kernel<false, false, false>(BwdParams, int, int, NoRope);
 }  // namespace d64
 }  // namespace cattn

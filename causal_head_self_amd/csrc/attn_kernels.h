@@ -6,6 +6,10 @@
 
 namespace cattn {
 
+struct RopeFreqs {
+    double f[64];  // base^(-2i/D) / (2 pi), i < D/2: revolutions per position
+};
+
 // Element strides of a [B][H][T][D] tensor whose D elements are contiguous.
 struct Strides {
     long long sb, sh;  // between batches, between heads
@@ -38,6 +42,20 @@ struct AttnArgs {
     unsigned int* keep;
     // strides of q, k, v, o, dO, dq, dk, dv (contiguous unless a strided entry point set them)
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+    // RoPE / QK-norm prologue fused into the kernels (bf16, D = 64 / 128, no dropout).
+    // Forward: q, k are the rows before the prologue; k_rot gets the keys after it (a
+    // separate pass) and q_rot the queries (written by the forward).  Backward: q, k are
+    // the rows after the prologue, xq, xk the rows before; dq, dk are taken with respect
+    // to xq, xk.
+    bool rope;
+    const void* xq;
+    const void* xk;
+    void* q_rot;
+    void* k_rot;
+    Strides sxq, sxk, sqr, skr;
+    int pos0, rope_flags;
+    float q_gain, k_gain, rope_eps;
+    RopeFreqs freqs;
 };
 
 // Decode (one query per sequence against a [B][T_max][H][D] KV cache).
@@ -65,9 +83,6 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16_noalloc(DecodeArgs a, hipStream_t st);
 
 // RoPE / QK norm on query and key rows (forward, or gradient when grad is set).
-struct RopeFreqs {
-    double f[64];  // base^(-2i/D) / (2 pi), i < D/2: revolutions per position
-};
 
 struct RopeArgs {
     const void* q;       // [B][H][T][D] views (strides sq, sk)
@@ -83,6 +98,7 @@ struct RopeArgs {
     int flags;           // bit 0: RoPE, bit 1: QK norm
     float q_gain, k_gain, eps;
     bool grad;
+    bool k_only;  // forward on the keys alone (k -> k_out); q, q_out unused
 };
 
 hipError_t launch_rope_qknorm(const RopeArgs& a, hipStream_t st);

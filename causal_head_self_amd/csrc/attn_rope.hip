@@ -176,8 +176,14 @@ hipError_t launch_rope_qknorm(const RopeArgs& a, hipStream_t st)
     p.g[1] = rview(a.dk_in, a.sdk);
     p.gain[0] = a.q_gain;
     p.gain[1] = a.k_gain;
+    if (a.k_only) {  // the keys in slot 0, one launch row of workgroups
+        p.x[0] = p.x[1];
+        p.y[0] = p.y[1];
+        p.g[0] = p.g[1];
+        p.gain[0] = p.gain[1];
+    }
     const long long rows = (long long)a.B * a.H * a.T;
-    const dim3 grid((unsigned)((rows + rope::kRowsPerWG - 1) / rope::kRowsPerWG), 2);
+    const dim3 grid((unsigned)((rows + rope::kRowsPerWG - 1) / rope::kRowsPerWG), a.k_only ? 1 : 2);
     const dim3 block(rope::kThreads);
     if (a.D == 128) {
         if (a.grad)

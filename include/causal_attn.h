@@ -132,7 +132,9 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
  * multiples of 8, stride_t >= D, and T * stride_t * 2 bytes below 2^32
  * (ATTN_ERR_LAYOUT otherwise).  lse and delta stay contiguous fp32 [B][H][T].
  * Aliasing: inputs may share memory with each other.  An output must not share
- * an element with an input or another output.  The check (ATTN_ERR_ALIAS) is
+ * an element with an input or another output, nor address one element twice
+ * (taken in order of increasing stride, each stride of a dimension of size > 1
+ * must reach past the elements the smaller ones span).  The check (ATTN_ERR_ALIAS) is
  * conservative: two views whose address ranges intersect are accepted only if
  * they have equal strides, stride_b is a multiple of stride_t, and their
  * per-token footprints of (H-1)*stride_h + D elements do not meet modulo
@@ -191,9 +193,12 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
  *   keep:       uint32 words, [B*H][ceil(T/32)][T]: bit t of word (b*H + h, w, i)
  *               is the keep decision of query i and key 32 w + t (1 = kept).  The
  *               forward writes the words of the (query, 32-key block) pairs it
- *               visits; the rest of the buffer is neither written nor read.  The
- *               caller owns it; 4-byte aligned; it must not overlap any other
- *               buffer of the call (ATTN_ERR_ALIAS).
+ *               visits and never writes the rest.  With a window the backward
+ *               may read words the forward did not write, but only for pairs
+ *               outside the window, whose weight is zero whatever the bit says,
+ *               so the results do not depend on them.  The caller owns the
+ *               buffer; 4-byte aligned; it must not overlap any other buffer of
+ *               the call (ATTN_ERR_ALIAS).
  *   keep_bytes: its size, at least attn_dropout_keep_bytes(B, H, T)
  *               (ATTN_ERR_WORKSPACE otherwise; 0 for a non-positive size).
  *
@@ -306,13 +311,43 @@ int attn_rope_qknorm_bwd(attn_view_t q, attn_view_t k, attn_view_t dq_out, attn_
                          float rope_base, float q_gain, float k_gain, float eps, int flags,
                          int dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Attention with the RoPE / QK-norm prologue above fused into its kernels
+ * (nanochat, section 9: RoPE and QK norm on the queries and keys of its
+ * attention).  The result is that of attn_rope_qknorm_fwd followed by
+ * attn_fwd_strided on its outputs, and for the backward attn_bwd_strided
+ * followed by attn_rope_qknorm_bwd, with fewer passes over memory:
+ *   fwd: the keys go through the prologue pass (k -> k_rot); the forward
+ *        kernel reads the raw queries, applies the prologue to them in
+ *        registers and writes them to q_rot.  q_rot and k_rot are outputs
+ *        that the backward needs.
+ *   bwd: the kernels run on q_rot and k_rot and apply the prologue's
+ *        transposed Jacobian to each dQ and dK row in registers, so dq and dk
+ *        come out with respect to the raw q and k (no intermediate gradient
+ *        of q_rot or k_rot is stored).
+ * Views, window and scale as for the strided entry points (bf16, D = 64 or
+ * 128); prologue parameters as for attn_rope_qknorm_fwd (ATTN_ERR_PARAM).
+ * No dropout.  Outputs (o, lse, q_rot, k_rot; dq, dk, dv, delta) must not
+ * overlap any input or each other (ATTN_ERR_ALIAS).  Errors as for the
+ * strided calls, checked before any HIP call; two launches each way (the key
+ * pass and the forward; the backward launches as attn_bwd_strided). */
+int attn_fwd_strided_rope(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o, float* lse,
+                          attn_view_t q_rot, attn_view_t k_rot, int B, int H, int T, int D,
+                          int window, float scale, int pos0, float rope_base, float q_gain,
+                          float k_gain, float eps, int flags, int dtype, void* stream);
+int attn_bwd_strided_rope(attn_view_t q, attn_view_t k, attn_view_t q_rot, attn_view_t k_rot,
+                          attn_view_t v, attn_view_t o, const float* lse, attn_view_t dO,
+                          attn_view_t dq, attn_view_t dk, attn_view_t dv, float* delta, int B,
+                          int H, int T, int D, int window, float scale, int pos0, float rope_base,
+                          float q_gain, float k_gain, float eps, int flags, int dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_str(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 6)
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 7)
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "causal_attn.h")
 
 # Fake, distinct, 16-byte-aligned addresses far apart (never dereferenced).
-P = [0x10000000 * (i + 1) for i in range(12)]
+P = [0x10000000 * (i + 1) for i in range(14)]
+
+# Every call below hands fake device pointers to the library and expects a
+# status from its argument checks.  If one of those checks regressed, a call
+# would reach a kernel launch at those addresses; on a host without a GPU that
+# launch can only fail, so the module runs only where no GPU is visible.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="fake device pointers: run where no GPU is visible")
 
 
 def _declared_functions():
@@ -42,11 +49,11 @@ def test_abi_version_and_status_strings():
     lib = cat.load_library()
     assert lib.attn_abi_version() == _lib.ABI_VERSION
     seen = set()
-    for code in range(0, 13):
+    for code in range(0, 14):
         s = cat.attn_status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 13
+    assert len(seen) == 14
     assert cat.attn_status_str(1234) == "unknown status"
     assert cat.attn_status_str(-1) == "unknown status"
 
@@ -456,3 +463,76 @@ def test_rope_qknorm_validation(fwd):
     views = [_v(P[j]) for j in range(n)]
     views[n - 1] = _v(P[n - 2])                   # the two outputs on each other
     assert _rope(fwd, views=views) == 8
+
+
+# ---------------------------------------------------------------------------
+# outputs that address one element twice
+# ---------------------------------------------------------------------------
+
+def test_self_overlapping_output_views_are_rejected():
+    B, H, T, D = B_, H_, T_, D_
+    # stride_h = 0 with H > 1: every head writes the same rows
+    bad = cat.AttnView(P[3], H * T * D, 0, D)
+    assert _fwd_s(views=[_v(P[0]), _v(P[1]), _v(P[2]), bad]) == 8
+    # 0 < stride_h < D: neighbouring heads overlap
+    bad = cat.AttnView(P[3], H * T * D, 8, T * D)
+    assert _fwd_s(views=[_v(P[0]), _v(P[1]), _v(P[2]), bad]) == 8
+    # stride_b below one batch's footprint
+    bad = cat.AttnView(P[3], T * D, T * D, D)
+    assert _fwd_s(views=[_v(P[0]), _v(P[1]), _v(P[2]), bad]) == 8
+    # the same for gradients of the backward (dq of the [B, T, 3C] layout is fine,
+    # a dk view with stride_t < H * D across heads is not)
+    C = H * D
+    v = [_v(P[0]), _v(P[1]), _v(P[2]), _v(P[3]), _v(P[5]), _v(P[6]), _v(P[7]), _v(P[8])]
+    v[6] = cat.AttnView(P[7], T * C, D, D)
+    assert _bwd_s(views=v) == 8
+
+
+# ---------------------------------------------------------------------------
+# attention with the fused RoPE / QK-norm prologue: invalid arguments only
+# ---------------------------------------------------------------------------
+
+def _frope(views=None, lse=P[12], B=B_, H=H_, T=T_, D=D_, window=0, scale=0.125, pos0=0,
+           base=10000.0, qg=1.2, kg=1.0, eps=1e-6, flags=3, dtype=1):
+    v = views or [_v(P[j]) for j in (0, 1, 2, 3, 4, 5)]
+    return cat.load_library().attn_fwd_strided_rope(v[0], v[1], v[2], v[3], lse, v[4], v[5], B, H,
+                                                    T, D, window, scale, pos0, base, qg, kg, eps,
+                                                    flags, dtype, None)
+
+
+def _brope(views=None, lse=P[12], delta=P[13], B=B_, H=H_, T=T_, D=D_, window=0, scale=0.125,
+           pos0=0, base=10000.0, qg=1.2, kg=1.0, eps=1e-6, flags=3, dtype=1):
+    v = views or [_v(P[j]) for j in range(10)]
+    return cat.load_library().attn_bwd_strided_rope(v[0], v[1], v[2], v[3], v[4], v[5], lse, v[6],
+                                                    v[7], v[8], v[9], delta, B, H, T, D, window,
+                                                    scale, pos0, base, qg, kg, eps, flags, dtype,
+                                                    None)
+
+
+@pytest.mark.parametrize("fwd", [True, False])
+def test_fused_prologue_validation(fwd):
+    call, n = (_frope, 6) if fwd else (_brope, 10)
+    for i in range(n):  # a NULL view
+        views = [_v(P[j]) for j in range(n)]
+        views[i] = _v(None)
+        assert call(views=views) == 1, i
+    assert call(lse=0) == 1
+    if not fwd:
+        assert call(delta=0) == 1
+    assert call(T=0) == 2 and call(window=-1) == 2
+    assert call(dtype=0) == 10 and call(D=32) == 10 and call(D=48) == 3
+    assert call(scale=0.0) == 7
+    for kw in (dict(flags=4), dict(pos0=-1), dict(pos0=2 ** 24), dict(base=0.0),
+               dict(qg=float("nan")), dict(eps=-1.0)):
+        assert call(**kw) == 12, kw
+    views = [_v(P[j]) for j in range(n)]
+    views[n - 1] = _v(P[0])                       # an output on an input
+    assert call(views=views) == 8
+    views = [_v(P[j]) for j in range(n)]
+    views[n - 1] = _v(P[n - 2])                   # two outputs on each other
+    assert call(views=views) == 8
+    if fwd:
+        assert call(lse=P[1] + 64) == 8           # lse (an output) inside an input view
+    else:
+        assert call(delta=P[1] + 64) == 8         # delta (an output) inside an input view
+        assert call(delta=P[12]) == 8             # delta on lse
