@@ -729,7 +729,9 @@ struct BwdParams {
 // Delta_i = sum_d dO_id O_id is formed from the rows the wave holds as MFMA
 // operands and written out.
 // ---------------------------------------------------------------------------
-template <int NP, bool kDrop, bool kKeep = false, bool kRope = false>
+// kDeltaIn: Delta is read from memory (written by an earlier launch) instead of
+// formed here from the item's O and dO rows and stored.
+template <int NP, bool kDrop, bool kKeep = false, bool kRope = false, bool kDeltaIn = false>
 __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char* sK0, char* sK1,
                                         char* sV0, char* sV1,
                                         const RopeArg<kRope>& rp = RopeArg<kRope>{})
@@ -767,12 +769,19 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     for (int ks = 0; ks < 4 * NP; ++ks) {
         qreg[ks] = valid ? *(const bf16x8*)(qr + 16 * ks) : zero_bf16x8();
         greg[ks] = valid ? *(const bf16x8*)(gr + 16 * ks) : zero_bf16x8();
-        const bf16x8 orow = valid ? *(const bf16x8*)(orr + 16 * ks) : zero_bf16x8();
+        if constexpr (!kDeltaIn) {
+            const bf16x8 orow = valid ? *(const bf16x8*)(orr + 16 * ks) : zero_bf16x8();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dsum = fmaf((float)greg[ks][e], (float)orow[e], dsum);
+            for (int e = 0; e < 8; ++e) dsum = fmaf((float)greg[ks][e], (float)orow[e], dsum);
+        }
     }
-    const float dlt = halves_sum(dsum);  // this lane's 32 columns + the other half's 32
-    if (valid && hi == 0) a.Delta[(size_t)bh * T + qrow] = dlt;
+    float dlt;
+    if constexpr (kDeltaIn) {
+        dlt = valid ? a.Delta[(size_t)bh * T + qrow] : 0.f;
+    } else {
+        dlt = halves_sum(dsum);  // this lane's 32 columns + the other half's 32
+        if (valid && hi == 0) a.Delta[(size_t)bh * T + qrow] = dlt;
+    }
     // rows >= T: -lse = -inf makes P (and dS) exactly 0
     const float nlse2 = valid ? -a.LSE[(size_t)bh * T + qrow] * kLog2e : -INFINITY;
     // dP^T accumulators start from this block (-Delta of the lane's query in every
@@ -1227,6 +1236,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         dq_item<1, kDrop, kKeep, kRope>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3, rp);
 }
 
+// ---------------------------------------------------------------------------
+// Delta = rowsum(dO o O) of every row, as a dQ item forms it (same lanes, same
+// order of the sums): 128 rows per workgroup, 32 per wave.  HBM-bound: reads
+// 2 D bf16 per row, writes 4 bytes.
+// ---------------------------------------------------------------------------
+template <int NP>
+__global__ __launch_bounds__(kThreads) void attn_delta_d64_kernel(BwdParams a, int n_blocks)
+{
+    const int T = a.T;
+    const int bh = blockIdx.x / n_blocks, blk = blockIdx.x - bh * n_blocks;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 31, hi = lane >> 5;
+    const int qrow = blk * kRowsPerWG + wave * 32 + li;
+    const bool valid = qrow < T;
+    const bf16* gr = head_of(a.dO, bh, a.H) + (size_t)(valid ? qrow : 0) * a.dO.st + 8 * hi;
+    const bf16* orr = head_of(a.O, bh, a.H) + (size_t)(valid ? qrow : 0) * a.O.st + 8 * hi;
+    bf16x8 g[4 * NP], o[4 * NP];
+#pragma unroll
+    for (int ks = 0; ks < 4 * NP; ++ks) {
+        g[ks] = *(const bf16x8*)(gr + 16 * ks);
+        o[ks] = *(const bf16x8*)(orr + 16 * ks);
+    }
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4 * NP; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsum = fmaf((float)g[ks][e], (float)o[ks][e], dsum);
+    const float dlt = halves_sum(dsum);
+    if (valid && hi == 0) a.Delta[(size_t)bh * T + qrow] = dlt;
+}
+
+// ---------------------------------------------------------------------------
+// Backward in one launch after the Delta pass (used at head dim 128): dK/dV
+// items and dQ items as in the head-dim-64 kernel, both reading Delta from
+// memory, so a dK/dV item needs no O tiles and the two kinds share 4 tile
+// buffers (65 KB of LDS at NP = 2: two workgroups per CU, 2 waves per SIMD).
+// Same item order: level v holds the dK/dV items of key block v and the dQ
+// items of query block n - 1 - v.  Against a dQ launch followed by a dK/dV
+// launch (384 workgroups each at B8 H6 T1024, for 512 slots, each launch
+// waiting on its heaviest items) the step at that shape drops from 117 to
+// 95 us.  At head dim 64 the kernel that forms Delta in its dK/dV items is as
+// fast or faster (88 against 91 us), so it stays.
+// ---------------------------------------------------------------------------
+template <int NP, bool kDrop, bool kKeep = false, bool kRope = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<NP>, kWavesPerEU<NP>))) void attn_bwd_dpre_kernel(
+    BwdParams a, int n_blocks, int n_cu, RopeArg<kRope> rp)
+{
+    __shared__ __attribute__((aligned(1024))) char s0[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s1[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s2[NP * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s3[NP * kTileBytes];
+    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];
+    __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    const int item = item_of(blockIdx.x, gridDim.x, n_cu);
+    const int BH = a.BH;
+    const int level = item / (2 * BH), r = item - level * 2 * BH;
+    if (r < BH)
+        dkdv_item<NP, false, kDrop, kKeep, kRope>(a, r, level, s0, s1, s2, s3, nullptr, nullptr, sR0,
+                                                  sR1, rp);
+    else
+        dq_item<NP, kDrop, kKeep, kRope, true>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3, rp);
+}
+
 #ifndef CATTN_D64_KERNELS_ONLY
 // The one-launch backward without dropout is instantiated in attn_bwd_plain.hip,
 // which is compiled with its own instruction-scheduling strategy.
@@ -1396,12 +1468,23 @@ hipError_t launch_dkdv_bf16_d64(const AttnArgs& a, hipStream_t st)
 
 hipError_t launch_bwd_bf16_d64(const AttnArgs& a, hipStream_t st)
 {
-    if (a.D == 128) {  // two launches: the LDS of a fused item would leave one per CU
-        const hipError_t e = launch_dq_bf16_d64(a, st);
-        return e == hipSuccess ? launch_dkdv_bf16_d64(a, st) : e;
-    }
     const int BH = a.B * a.H;
     const int nb = (a.T + d64::kRowsPerWG - 1) / d64::kRowsPerWG;
+    if (a.D == 128) {  // the Delta pass, then dK/dV and dQ items in one launch
+        hipLaunchKernelGGL(d64::attn_delta_d64_kernel<2>, dim3(nb * BH), dim3(d64::kThreads), 0, st,
+                           bwd_params(a), nb);
+        if (a.rope) {
+            hipLaunchKernelGGL((d64::attn_bwd_dpre_kernel<2, false, false, true>), dim3(2 * nb * BH),
+                               dim3(d64::kThreads), 0, st, bwd_params(a), nb, a.n_cu, rope_p(a));
+            return hipGetLastError();
+        }
+        auto k = a.dropout_p16 > 0 ? (a.keep ? d64::attn_bwd_dpre_kernel<2, true, true>
+                                             : d64::attn_bwd_dpre_kernel<2, true>)
+                                   : d64::attn_bwd_dpre_kernel<2, false>;
+        hipLaunchKernelGGL(k, dim3(2 * nb * BH), dim3(d64::kThreads), 0, st, bwd_params(a), nb,
+                           a.n_cu, d64::NoRope{});
+        return hipGetLastError();
+    }
     if (a.rope) {
         hipLaunchKernelGGL((d64::attn_bwd_d64_kernel<false, false, true>), dim3(2 * nb * BH),
                            dim3(d64::kThreads), 0, st, bwd_params(a), nb, a.n_cu, rope_p(a));

@@ -2,9 +2,10 @@
 // Delta, dQ, dK/dV), same operation as attn_bf16.hip (CS336 from-scratch
 // tutorial, lmnt.cn, section 5.1 CausalSelfAttention.forward, diagonal kept).
 //
-// fp32 has no full-rate matrix path that keeps fp32 products exact, and the
-// fp32 workloads here are small (the pages' tiny CPU config: T = 64, D = 32),
-// so these kernels use exact fp32 FMA on the vector ALUs: one lane per query
+// gfx950 does have fp32 MFMA, but its dense fp32 rate (157 TFLOP/s) is that of
+// the vector ALUs' packed FMA, so it would buy no throughput, and the fp32
+// workloads here are small (the pages' tiny CPU config: T = 64, D = 32).  These
+// kernels use plain fp32 FMA on the vector ALUs: one lane per query
 // (forward, dQ) or per key (dK/dV), with 64-row K/V (or Q/dO) tiles shared
 // through LDS.  Launch latency, not arithmetic, bounds them at that size.
 #include "attn_device.h"

@@ -89,9 +89,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * ([B][H][T][D], dtype).  delta is caller-owned fp32 [B][H][T] workspace; on
  * return it holds Delta[i] = sum_d dO[i][d] * o[i][d], the softmax-backward
  * row term.  For bf16 at D = 64 this is one kernel launch on `stream` whose
- * dK/dV work forms Delta itself from o and dO; otherwise it enqueues the two
- * stages below (dQ with Delta, then dK/dV).  Either way the results equal
- * those of the two stages up to the fp32 summation order. */
+ * dK/dV work forms Delta itself from o and dO; for bf16 at D = 128, a launch
+ * that writes Delta and then one launch of dQ and dK/dV work that reads it;
+ * otherwise it enqueues the two stages below (dQ with Delta, then dK/dV).
+ * Either way the results equal those of the two stages up to the fp32
+ * summation order. */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv,
              float* delta, int B, int H, int T, int D, float scale, int dtype,
