@@ -87,6 +87,26 @@ def kernel_work(cfg, window: int = 0):
     }
 
 
+MIN_WARMUP_SECONDS = 0.25
+
+
+def warm_up(body, n: int) -> None:
+    """n untimed calls of body, then more in groups of 10 until at least
+    MIN_WARMUP_SECONDS of wall time has passed.  The GPU's clock follows its
+    load: right after host-side work (the oracle timings) a warm-up of a few
+    milliseconds has left a whole timed region several times slower than the
+    same steps a moment later."""
+    import torch
+    t_end = time.perf_counter() + MIN_WARMUP_SECONDS
+    for _ in range(n):
+        body()
+    torch.cuda.synchronize()
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            body()
+        torch.cuda.synchronize()
+
+
 def read_traffic(kernel: str, workload: str, sha: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, if it was taken on the current kernel source."""
@@ -208,9 +228,7 @@ def sublayer_measure(args, with_oracle: bool = True) -> dict:
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / n
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     ms = timed(step, args.steps)
     fwd_ms = timed(fwd_only, args.steps)
 
@@ -319,9 +337,7 @@ def decode_bench(args) -> int:
     def step(s=stream):
         cat.attn_decode(q, kc, vc, ln, o, lse, ws, cfg.scale, 0, s)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(args.steps):
@@ -454,8 +470,7 @@ def rope_bench(args) -> int:
             for name in which:
                 launch[name]()
 
-    run(args.warmup)
-    torch.cuda.synchronize()
+    warm_up(lambda: run(1), args.warmup)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     run(args.steps)
@@ -512,9 +527,7 @@ def rope_bench(args) -> int:
 
     e2e = {}
     for name, body in (("fused", fused), ("two_pass", two_pass)):
-        for _ in range(args.warmup):
-            body()
-        torch.cuda.synchronize()
+        warm_up(body, args.warmup)
         t0.record(stream)
         for _ in range(args.steps):
             body()
@@ -735,10 +748,7 @@ def measure_attention(cfg, host_inputs, steps, warmup, W=0, P=0.0, keep_bits=Fal
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / n
 
-    for _ in range(warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
+    warm_up(lambda: (fwd(), bwd()), warmup)
     step_ms = timed(lambda: (fwd(), bwd()), steps)
     kern = {"fwd": timed(fwd, steps), "bwd": timed(bwd, steps)}
     if copy_calibration_mib > 0:  # a plain device copy of known size (counter scaling)
