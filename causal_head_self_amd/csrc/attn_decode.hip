@@ -22,7 +22,7 @@
 //     (DPP), the slice's softmax runs in base 2 on fp32, and the slice's
 //     partial (running max m, normaliser l, unnormalised o) goes to the
 //     workspace.
-//   decode_combine_kernel: one wave per (b, h) merges the slices' partials:
+//   decode_combine_kernel: four waves per (b, h) merge the slices' partials:
 //     M = max m_s, L = sum 2^(m_s - M) l_s, o = sum 2^(m_s - M) o_s / L,
 //     lse = (M + log2 L) ln 2.
 #include <atomic>
@@ -157,35 +157,45 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(
 }
 
 // Merge of the slices of one (b, h) into o (bf16) and lse (natural log).
-// Slices are taken 64 at a time, one per lane: their m and l load in one
-// round, the weights 2^(m_s - M) are formed in the lanes, and each weight is
-// broadcast (readlane) to the sum over the slices' o rows, whose loads are
-// independent of one another.
+// kCW waves per (b, h): wave w merges a contiguous share of the slices, then
+// wave 0 adds the waves' sums in LDS.  Within a wave, slices are taken 64 at
+// a time, one per lane: their m and l load in one round, the weights
+// 2^(m_s - M) are formed in the lanes, and each weight is broadcast
+// (readlane) to the sum over the slices' o rows, whose loads are independent
+// of one another.  Every wave forms the global M itself.
+constexpr int kCW = 4;
+
 template <int NL>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part,
-                                                            bf16* __restrict__ o,
-                                                            float* __restrict__ lse, int n_slice)
+__global__ __launch_bounds__(64 * kCW) void decode_combine_kernel(const float* __restrict__ part,
+                                                                  bf16* __restrict__ o,
+                                                                  float* __restrict__ lse,
+                                                                  int n_slice)
 {
     constexpr int D = 64 * NL;
     constexpr int P = D + 4;
-    const int bh = blockIdx.x, lane = threadIdx.x;
+    __shared__ float s_acc[kCW][D];
+    __shared__ float s_L[kCW];
+    const int bh = blockIdx.x, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float* pb = part + (size_t)bh * n_slice * P;
     float M = -INFINITY;
     for (int s = lane; s < n_slice; s += 64) M = fmaxf(M, pb[(size_t)s * P + D]);
 #pragma unroll
     for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
+    const int per = (n_slice + kCW - 1) / kCW;
+    const int sb = wave * per, se = min(n_slice, sb + per);
     float L = 0.f;
     float acc[NL];
 #pragma unroll
     for (int n = 0; n < NL; ++n) acc[n] = 0.f;
     if (M != -INFINITY) {
-        for (int s0 = 0; s0 < n_slice; s0 += 64) {
+        for (int s0 = sb; s0 < se; s0 += 64) {
             const int s = s0 + lane;
             const float* ps = pb + (size_t)s * P;
-            // 0 for a lane past the last slice and for an empty slice (m = -inf)
-            const float w = s < n_slice ? fast_exp2(ps[D] - M) : 0.f;
-            L = s < n_slice ? fmaf(w, ps[D + 1], L) : L;
-            const int cnt = min(64, n_slice - s0);
+            // 0 for a lane past the wave's last slice and for an empty slice (m = -inf)
+            const float w = s < se ? fast_exp2(ps[D] - M) : 0.f;
+            L = s < se ? fmaf(w, ps[D + 1], L) : L;
+            const int cnt = min(64, se - s0);
             const float* row = pb + (size_t)s0 * P + lane;
             // blocks of 8 slices, loads first (readlane is convergent, so the
             // compiler does not unroll a loop with a remainder around it)
@@ -212,10 +222,23 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 #pragma unroll
         for (int k = 1; k < 64; k <<= 1) L += __shfl_xor(L, k, 64);
     }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
-    for (int n = 0; n < NL; ++n) o[(size_t)bh * D + lane + 64 * n] = (bf16)(acc[n] * inv);
-    if (lane == 0) lse[bh] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
+    for (int n = 0; n < NL; ++n) s_acc[wave][lane + 64 * n] = acc[n];
+    if (lane == 0) s_L[wave] = L;
+    __syncthreads();
+    if (wave != 0) return;
+    float Lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCW; ++w) Lt += s_L[w];
+    const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
+#pragma unroll
+    for (int n = 0; n < NL; ++n) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < kCW; ++w) a += s_acc[w][lane + 64 * n];
+        o[(size_t)bh * D + lane + 64 * n] = (bf16)(a * inv);
+    }
+    if (lane == 0) lse[bh] = M == -INFINITY ? -INFINITY : (M + log2f(Lt)) * kLn2;
 }
 
 // Whole decode of one (b, h) in one workgroup of NW waves: wave w takes the
@@ -404,10 +427,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.D == 128)
-        hipLaunchKernelGGL(dec::decode_combine_kernel<2>, grid_c, dim3(64), 0, st, a.part,
+        hipLaunchKernelGGL(dec::decode_combine_kernel<2>, grid_c, dim3(64 * dec::kCW), 0, st, a.part,
                            (bf16*)a.o, a.lse, n_slice);
     else
-        hipLaunchKernelGGL(dec::decode_combine_kernel<1>, grid_c, dim3(64), 0, st, a.part,
+        hipLaunchKernelGGL(dec::decode_combine_kernel<1>, grid_c, dim3(64 * dec::kCW), 0, st, a.part,
                            (bf16*)a.o, a.lse, n_slice);
     return hipGetLastError();
 }
