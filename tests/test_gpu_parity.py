@@ -115,8 +115,11 @@ def test_bf16_shapes_and_ragged_tails(shape):
     check_case(*shape, "bf16", seed=100 + sum(shape))
 
 
+# Four waves share each 64-row block, 16 rows of every tile each: lengths that
+# leave some waves without a visible row (T = 1, 17, 48) or with a ragged share.
 @pytest.mark.parametrize("shape", [
     (1, 1, 1, 32), (1, 2, 100, 64), (2, 1, 130, 32), (1, 1, 300, 32),
+    (1, 1, 17, 32), (2, 2, 48, 64), (1, 1, 65, 64), (1, 3, 200, 64),
 ])
 def test_fp32_shapes_and_ragged_tails(shape):
     check_case(*shape, "f32", seed=200 + sum(shape))
