@@ -127,7 +127,7 @@ def test_fp32_shapes_and_ragged_tails(shape):
 
 @pytest.mark.parametrize("shape,dtype", [
     ((1, 1, 65, 64), "bf16"), ((2, 3, 300, 64), "bf16"), ((1, 2, 257, 32), "bf16"),
-    ((1, 2, 100, 64), "f32"), ((2, 2, 200, 128), "bf16"),
+    ((1, 2, 100, 64), "f32"), ((2, 2, 200, 128), "bf16"), ((1, 3, 333, 128), "bf16"),
 ])
 def test_split_backward_entry_points(shape, dtype):
     """attn_bwd_dq (which also writes Delta) followed by attn_bwd_dkdv (which
@@ -160,6 +160,12 @@ def test_split_backward_entry_points(shape, dtype):
     model = model_of(q, k, v, dO, scale)
     assert_close(got, ref, dtype, f"split B{B} H{H} T{T} D{D} {dtype}", dtol, model)
     assert_close(fused, ref, dtype, f"fused B{B} H{H} T{T} D{D} {dtype}", dtol, model)
+    if dtype == "bf16" and D == 128:
+        # at head dim 128 attn_bwd is a Delta pass (summed in the dQ items' order)
+        # and one launch of the same dQ and dK/dV items: bit for bit the two stages
+        for n in ("dq", "dk", "dv", "delta"):
+            assert np.array_equal(got[n], fused[n]), n
+        return
     # the two paths compute Delta and dS in different orders; they agree to the
     # bf16 storage rounding of the gradients
     for n in ("dq", "dk", "dv"):
