@@ -4,6 +4,11 @@
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection switched off (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+
+A second library, libcausal_attn_lds_poison.so, is the same sources compiled
+with -DCATTN_LDS_POISON: each kernel fills its LDS arrays with NaN words
+before first use, so a read of LDS the kernel never wrote changes its results
+(tests/test_gpu_lds_poison.py compares the two libraries bit for bit).
 """
 from __future__ import annotations
 
@@ -17,6 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcausal_attn.so")
+LIB_POISON = os.path.join(PKG, "libcausal_attn_lds_poison.so")
+POISON_FLAGS = ["-DCATTN_LDS_POISON"]
 SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_bf16_d64.hip", "attn_bwd_plain.hip", "attn_decode.hip", "attn_f32.hip",
            "attn_rope.hip"]
 ARCH = "gfx950"
@@ -39,27 +46,41 @@ KERNEL_ONLY_FLAGS = {
 }
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *KERNEL_ONLY_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, poison = job
+    tag = "_lds_poison" if poison else ""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [HIPCC, *FLAGS, *KERNEL_ONLY_FLAGS.get(src, []), *(POISON_FLAGS if poison else []),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, lds_poison: bool = True) -> str:
+    """Compile and link libcausal_attn.so (and, unless lds_poison is False,
+    the LDS-poisoning debug library beside it).  Returns the release path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(src, False) for src in SOURCES]
+    if lds_poison:
+        jobs += [(src, True) for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    if lds_poison:
+        _link(objs[len(SOURCES):], LIB_POISON)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB}" + (f" and {LIB_POISON}" if lds_poison else ""))
     return LIB
 
 

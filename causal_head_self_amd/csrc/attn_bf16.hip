@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     constexpr int VST = kTileN + 8;    // padded LDS row stride (V^T)
     __shared__ __attribute__((aligned(16))) bf16 sK[kTileN * KST];
     __shared__ __attribute__((aligned(16))) bf16 sVt[HD * VST];
+    lds_poison(sK, sVt);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, hi = lane >> 5;
@@ -197,6 +198,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_bf16_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sK[kTileN * KST];
     __shared__ __attribute__((aligned(16))) bf16 sV[kTileN * KST];
     __shared__ __attribute__((aligned(16))) bf16 sKt[HD * TST];
+    lds_poison(sK, sV, sKt);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, hi = lane >> 5;
@@ -302,6 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv_bf16_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sGt[HD * TST];
     __shared__ __attribute__((aligned(16))) float sL[kTileM];
     __shared__ __attribute__((aligned(16))) float sD[kTileM];
+    lds_poison(sQ, sG, sQt, sGt, sL, sD);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, hi = lane >> 5;

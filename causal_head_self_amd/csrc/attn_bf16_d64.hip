@@ -543,6 +543,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char sK1[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV0[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV1[NP * kTileBytes];
+    lds_poison(sK0, sK1, sV0, sV1);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1185,6 +1186,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char sK1[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV0[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV1[NP * kTileBytes];
+    lds_poison(sK0, sK1, sV0, sV1);
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     dq_item<NP, kDrop, kKeep, kRope>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1,
                                      rp);
@@ -1201,6 +1203,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char sG1[NP * kTileBytes];
     __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
     __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    lds_poison(sQ0, sQ1, sG0, sG1, sR0, sR1);
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     dkdv_item<NP, false, kDrop, kKeep, kRope>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1,
                                               nullptr, nullptr, sR0, sR1, rp);
@@ -1227,6 +1230,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     __shared__ __attribute__((aligned(1024))) char s5[kTileBytes];
     __shared__ __attribute__((aligned(16))) float sR0[2][kTile];
     __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    lds_poison(s0, s1, s2, s3, s4, s5, sR0, sR1);
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     const int BH = a.BH;
     const int level = item / (2 * BH), r = item - level * 2 * BH;
@@ -1289,6 +1293,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char s3[NP * kTileBytes];
     __shared__ __attribute__((aligned(16))) float sR0[2][kTile];
     __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    lds_poison(s0, s1, s2, s3, sR0, sR1);
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     const int BH = a.BH;
     const int level = item / (2 * BH), r = item - level * 2 * BH;

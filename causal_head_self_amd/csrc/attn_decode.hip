@@ -175,6 +175,7 @@ __global__ __launch_bounds__(64 * kCW) void decode_combine_kernel(const float* _
     constexpr int P = D + 4;
     __shared__ float s_acc[kCW][D];
     __shared__ float s_L[kCW];
+    lds_poison(s_acc, s_L);
     const int bh = blockIdx.x, lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float* pb = part + (size_t)bh * n_slice * P;
@@ -256,6 +257,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fused_kernel(
     constexpr int D = 64 * NL;
     __shared__ float s_o[NW][D];
     __shared__ float s_m[NW], s_l[NW];
+    lds_poison(s_o, s_m, s_l);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
     const int g = lane >> 3, sub = lane & 7;

@@ -31,6 +31,30 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// LDS poisoning, for debug builds compiled with -DCATTN_LDS_POISON: every LDS
+// array of a kernel is filled with all-ones words (a NaN as fp32 and as each
+// bf16 half) before the kernel touches LDS, so that a read of LDS the kernel
+// has not written shows up as NaN or as a changed result instead of reusing
+// whatever an earlier workgroup left there.  Release builds compile it away.
+template <typename T>
+__device__ __forceinline__ void lds_poison_one(T& a)
+{
+    static_assert(sizeof(T) % 4 == 0, "LDS arrays are whole 32-bit words");
+    uint32_t* w = (uint32_t*)&a;
+    for (int i = threadIdx.x; i < (int)(sizeof(T) / 4); i += blockDim.x) w[i] = 0xFFFFFFFFu;
+}
+
+template <typename... Ts>
+__device__ __forceinline__ void lds_poison(Ts&... a)
+{
+#ifdef CATTN_LDS_POISON
+    (lds_poison_one(a), ...);
+    __syncthreads();
+#else
+    ((void)a, ...);
+#endif
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_fwd_f32_kernel(
     __shared__ __attribute__((aligned(16))) float sV[kRows][HD];
     __shared__ float sO[kWaves - 1][kRows][HD];  // waves 1.. hand their state to wave 0
     __shared__ float sM[kWaves - 1][kRows], sL[kWaves - 1][kRows];
+    lds_poison(sK, sV, sO, sM, sL);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x % BH;
     const int qt = n_qtiles - 1 - blockIdx.x / BH;
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_bwd_dq_f32_kernel(
     __shared__ __attribute__((aligned(16))) float sK[kRows][HD];
     __shared__ __attribute__((aligned(16))) float sV[kRows][HD];
     __shared__ PartF32<HD> part;
+    lds_poison(sK, sV, part);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x % BH;
     const int qt = n_qtiles - 1 - blockIdx.x / BH;
@@ -236,6 +238,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_bwd_dkdv_f32_kernel(
     __shared__ __attribute__((aligned(16))) float sG[kRows][HD];
     __shared__ float sL[kRows], sD[kRows];
     __shared__ PartF32<HD> part;
+    lds_poison(sQ, sG, sL, sD, part);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x % BH;
     const int kt = blockIdx.x / BH;

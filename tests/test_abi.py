@@ -45,6 +45,16 @@ def test_library_exports_every_declared_symbol():
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
+def test_lds_poison_library_loads_with_the_same_abi():
+    """The LDS-poisoning debug build (same sources, -DCATTN_LDS_POISON) is a
+    drop-in copy of the release library: same exports, same ABI version."""
+    from causal_head_self_amd import build as hip_build
+    lib = _lib.load_library(hip_build.LIB_POISON)
+    for name in _declared_functions():
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value, name
+    assert lib.attn_abi_version() == _lib.ABI_VERSION
+
+
 def test_abi_version_and_status_strings():
     lib = cat.load_library()
     assert lib.attn_abi_version() == _lib.ABI_VERSION
