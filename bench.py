@@ -188,11 +188,15 @@ def sublayer_measure(args, with_oracle: bool = True) -> dict:
     """The pre-norm attention sublayer around the GPT-2-small shape: LayerNorm,
     c_attn, causal attention on strided views of the c_attn output (the HIP
     kernels), c_proj, residual; forward and backward through torch autograd.
-    Work per step: the c_attn and c_proj GEMMs (2*N*C*3C + 2*N*C*C forward, 3x
-    that forward plus backward) plus the attention's 7*B*H*T^2*D (2*B*H*T^2*D
-    forward).  The attention share is the time of attn_fwd + attn_bwd alone at
-    the same shape over the step time.  The oracle baseline is one of the eight
-    sequences (fp64 sublayer forward and backward), scaled to the whole batch."""
+    The step is timed twice: eagerly (every launch enqueued from Python and the
+    autograd engine) and as one HIP-graph replay of the captured forward +
+    backward (the same kernels, without the host's launch gaps between them);
+    the graph replay is the reported value.  Work per step: the c_attn and
+    c_proj GEMMs (2*N*C*3C + 2*N*C*C forward, 3x that forward plus backward)
+    plus the attention's 7*B*H*T^2*D (2*B*H*T^2*D forward).  The attention
+    share is the time of attn_fwd + attn_bwd alone at the same shape over the
+    step time.  The oracle baseline is one of the eight sequences (fp64
+    sublayer forward and backward), scaled to the whole batch."""
     import torch
     import causal_head_self_amd as cat
     from causal_head_self_amd.sublayer import attention_sublayer
@@ -229,8 +233,36 @@ def sublayer_measure(args, with_oracle: bool = True) -> dict:
         return t0.elapsed_time(t1) / n
 
     warm_up(step, args.warmup)
-    ms = timed(step, args.steps)
+    eager_ms = timed(step, args.steps)
     fwd_ms = timed(fwd_only, args.steps)
+
+    # The same step captured in a HIP graph (torch.cuda.CUDAGraph records the
+    # launches the C ABI and the torch ops enqueue on the capturing stream).
+    # Fresh leaves, warmed up on a side stream as capture requires, so that
+    # their gradient-accumulation nodes belong to the capturing stream.
+    gdev = {n: inp[n].cuda().requires_grad_(True) for n in names}
+
+    def gstep():
+        for n in names:
+            gdev[n].grad = None
+        attention_sublayer(gdev["x"], gdev["g"], gdev["bl"], gdev["Wa"], gdev["ba"],
+                           gdev["Wp"], gdev["bp"], cfg.H).backward(dy)
+
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            gstep()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    for n in names:
+        gdev[n].grad = None
+    with torch.cuda.graph(graph):
+        attention_sublayer(gdev["x"], gdev["g"], gdev["bl"], gdev["Wa"], gdev["ba"], gdev["Wp"],
+                           gdev["bp"], cfg.H).backward(dy)
+    warm_up(graph.replay, args.warmup)
+    ms = timed(graph.replay, args.steps)
 
     # attention alone at the same shape (the gpt2s inputs)
     B, T, C, H = cfg.B, cfg.T, cfg.C, cfg.H
@@ -246,6 +278,9 @@ def sublayer_measure(args, with_oracle: bool = True) -> dict:
     work_f = gemm_fwd + 2.0 * B * H * T * T * D
     out = {
         "value": round(work / (ms * 1e-3) / 1e12, 3), "ms_per_step": round(ms, 5),
+        "step": "one HIP-graph replay of the captured forward + backward",
+        "eager_value": round(work / (eager_ms * 1e-3) / 1e12, 3),
+        "eager_ms_per_step": round(eager_ms, 5),
         "fwd_tflops": round(work_f / (fwd_ms * 1e-3) / 1e12, 3), "fwd_ms": round(fwd_ms, 5),
         "attention_ms": round(attn_ms, 5), "attention_share": round(attn_ms / ms, 4),
         "attention_tflops": round(a["tflops"], 3),
@@ -295,6 +330,8 @@ def sublayer_bench(args) -> int:
                                 f"H={cfg.H} {cfg.dtype}; x, dy N(0,1), GPT-2 init weights, "
                                 "seeds 42+idx"),
                    "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
+        "step": m["step"], "eager_value": m["eager_value"],
+        "eager_ms_per_step": m["eager_ms_per_step"],
         "fwd_tflops": m["fwd_tflops"], "fwd_ms": m["fwd_ms"],
         "attention_ms": m["attention_ms"], "attention_share": m["attention_share"],
         "attention_tflops": m["attention_tflops"],

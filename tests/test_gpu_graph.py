@@ -125,3 +125,61 @@ def test_decode_graph_replays_match_eager(B, H, T_max, D, lens, step):
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+
+
+def test_sublayer_training_step_graph_replays_match_eager():
+    """The pre-norm sublayer's forward + backward (LayerNorm, the c_attn and
+    c_proj GEMMs, the attention kernels on strided views, the residual, every
+    parameter gradient) captured as one graph, as the benchmark times it.  Each
+    replay must give the eager step's gradients bit for bit; the gradient
+    buffers are filled with NaN and eager GEMM work runs between replays."""
+    from causal_head_self_amd.sublayer import attention_sublayer
+    _note("[graph] sublayer fwd+bwd B=2 T=256 C=768 H=12")
+    cfg = workloads.SUBLAYER_CONFIG
+    inp = workloads.sublayer_inputs(cfg, B=2)
+    names = ["x", "g", "bl", "Wa", "ba", "Wp", "bp"]
+    T = 256
+    inp = {n: (t[:, :T].contiguous() if n in ("x", "dy") else t) for n, t in inp.items()}
+    dy = inp["dy"].cuda()
+
+    def leaves():
+        return {n: inp[n].cuda().requires_grad_(True) for n in names}
+
+    def run(d):
+        for n in names:
+            d[n].grad = None
+        attention_sublayer(d["x"], d["g"], d["bl"], d["Wa"], d["ba"], d["Wp"], d["bp"],
+                           cfg.H).backward(dy)
+
+    eager = leaves()
+    run(eager)
+    torch.cuda.synchronize()
+    ref = {n: eager[n].grad.clone() for n in names}
+
+    d = leaves()
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            run(d)
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    for n in names:
+        d[n].grad = None
+    with torch.cuda.graph(graph):
+        attention_sublayer(d["x"], d["g"], d["bl"], d["Wa"], d["ba"], d["Wp"], d["bp"],
+                           cfg.H).backward(dy)
+    torch.cuda.synchronize()
+    grads = {n: d[n].grad for n in names}
+    junk = torch.randn(1024, 1024, device="cuda")
+    for rep in range(4):
+        for n in names:
+            grads[n].fill_(float("nan"))
+        junk = junk @ junk.T * 1e-3
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(grads[n], ref[n]), f"replay {rep}: grad of {n}"
