@@ -74,6 +74,12 @@ def _bind(path: str):
                                             [ctypes.c_double, _i64, _i64, ctypes.c_uint64, _i64,
                                              _i64])
     lib.oracle_attn_bwd_dropout.restype = None
+    lib.oracle_layernorm_fwd.argtypes = [_dp] * 4 + [_i64] * 2 + [ctypes.c_double, _i64]
+    lib.oracle_layernorm_fwd.restype = ctypes.c_int
+    lib.oracle_layernorm_bwd.argtypes = [_dp] * 8 + [_i64] * 2 + [ctypes.c_double, _i64]
+    lib.oracle_layernorm_bwd.restype = ctypes.c_int
+    lib.oracle_colsum.argtypes = [_dp, _dp, _i64, _i64]
+    lib.oracle_colsum.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -280,4 +286,42 @@ def sublayer_bwd(x, g, bl, Wa, ba, Wp, bp, dy, n_head: int, eps: float = 1e-5,
         _p(out["dWp"]), _p(out["dbp"]), B, T, C, int(n_head), float(eps), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_sublayer_bwd failed ({rc})")
+    return out
+
+
+def layernorm_fwd(x, g, bl, eps: float = 1e-5, nthreads: int = 0, lib: str | None = None):
+    """LayerNorm over the last dimension of x [N, C] (biased variance, eps under
+    the square root), times g [C] plus bl [C]."""
+    x, g, bl = map(_f64, (x, g, bl))
+    N, C = x.shape
+    y = np.empty_like(x)
+    rc = _load(lib).oracle_layernorm_fwd(_p(x), _p(g), _p(bl), _p(y), N, C, float(eps),
+                                         int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_layernorm_fwd failed ({rc})")
+    return y
+
+
+def layernorm_bwd(x, g, bl, du, dres=None, eps: float = 1e-5, nthreads: int = 0,
+                  lib: str | None = None):
+    """Gradients of sum(du * layernorm_fwd(x)) + sum(dres * x): (dx, dg, dbl)."""
+    x, g, bl, du = map(_f64, (x, g, bl, du))
+    N, C = x.shape
+    dr = None if dres is None else _f64(dres)
+    dx = np.empty_like(x)
+    dg, dbl = np.empty_like(g), np.empty_like(bl)
+    rc = _load(lib).oracle_layernorm_bwd(_p(x), _p(g), _p(bl), _p(du),
+                                         None if dr is None else _p(dr), _p(dx), _p(dg),
+                                         _p(dbl), N, C, float(eps), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_layernorm_bwd failed ({rc})")
+    return dx, dg, dbl
+
+
+def colsum(x, lib: str | None = None):
+    """Column sums of x [N, M]: the gradient of a bias added to every row."""
+    x = _f64(x)
+    N, M = x.shape
+    out = np.empty(M, dtype=np.float64)
+    _load(lib).oracle_colsum(_p(x), _p(out), N, M)
     return out

@@ -502,6 +502,41 @@ static void layer_norm_fwd(const double* x, const double* g, const double* bl,
     }
 }
 
+/* Gradient through u = xhat g + bl, xhat = (x - mean) rstd (class LayerNorm,
+ * chain rule): dg = sum_n du xhat, dbl = sum_n du, and per row, with
+ * dxh = du g, dx = rstd (dxh - mean_c(dxh) - xhat mean_c(dxh xhat)), plus the
+ * residual term dres (NULL: none).  xhat, rstd from layer_norm_fwd. */
+static void layer_norm_bwd(const double* du, const double* g, const double* xhat,
+                           const double* rstd, const double* dres, double* dx, double* dg,
+                           double* dbl, int64_t N, int64_t C)
+{
+    for (int64_t c = 0; c < C; ++c) {
+        double ag = 0.0, ab = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            ag += du[n * C + c] * xhat[n * C + c];
+            ab += du[n * C + c];
+        }
+        dg[c] = ag;
+        dbl[c] = ab;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double m1 = 0.0, m2 = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            double dxh = du[n * C + c] * g[c];
+            m1 += dxh;
+            m2 += dxh * xhat[n * C + c];
+        }
+        m1 /= (double)C;
+        m2 /= (double)C;
+        for (int64_t c = 0; c < C; ++c) {
+            double dxh = du[n * C + c] * g[c];
+            dx[n * C + c] = rstd[n] * (dxh - m1 - xhat[n * C + c] * m2) +
+                            (dres ? dres[n * C + c] : 0.0);
+        }
+    }
+}
+
 /* out[N][M] = a[N][Kd] * w[Kd][M] + bias[M] */
 static void linear_fwd(const double* a, const double* w, const double* bias,
                        double* out, int64_t N, int64_t Kd, int64_t M)
@@ -686,35 +721,57 @@ int oracle_sublayer_bwd(const double* x, const double* g, const double* bl,
                 du[n * C + c] = acc;
             }
 
-        /* u = xhat g + bl,  xhat = (x - mean) rstd */
-        for (int64_t c = 0; c < C; ++c) {
-            double ag = 0.0, ab = 0.0;
-            for (int64_t n = 0; n < N; ++n) {
-                ag += du[n * C + c] * S.xhat[n * C + c];
-                ab += du[n * C + c];
-            }
-            dg[c] = ag;
-            dbl[c] = ab;
-        }
-#pragma omp parallel for schedule(static)
-        for (int64_t n = 0; n < N; ++n) {
-            double m1 = 0.0, m2 = 0.0;
-            for (int64_t c = 0; c < C; ++c) {
-                double dxh = du[n * C + c] * g[c];
-                m1 += dxh;
-                m2 += dxh * S.xhat[n * C + c];
-            }
-            m1 /= (double)C;
-            m2 /= (double)C;
-            for (int64_t c = 0; c < C; ++c) {
-                double dxh = du[n * C + c] * g[c];
-                dx[n * C + c] = S.rstd[n] * (dxh - m1 - S.xhat[n * C + c] * m2) +
-                                dy[n * C + c]; /* residual path */
-            }
-        }
+        /* u = LN(x); the residual path adds dy to dx */
+        layer_norm_bwd(du, g, S.xhat, S.rstd, dy, dx, dg, dbl, N, C);
     }
     cache_free(&S);
     free(y); free(da); free(dO); free(dqh); free(dkh); free(dvh); free(dl);
     free(dqkv); free(du);
     return ok ? 0 : 2;
+}
+
+/* ------------------------------------------------------------------------ */
+/* LayerNorm alone (class LayerNorm of the CS336 tutorial, section 3.4: biased */
+/* variance, eps under the square root, gain and bias), its gradient with an  */
+/* optional residual term, and the column sums that are a bias's gradient.    */
+/* x, y, du, dres, dx: [N][C]; g, bl, dg, dbl: [C].                           */
+/* ------------------------------------------------------------------------ */
+
+int oracle_layernorm_fwd(const double* x, const double* g, const double* bl, double* y,
+                         int64_t N, int64_t C, double eps, int64_t nthreads)
+{
+    set_threads(nthreads);
+    double* xhat = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* rstd = (double*)malloc((size_t)N * sizeof(double));
+    int ok = xhat && rstd;
+    if (ok) layer_norm_fwd(x, g, bl, y, xhat, rstd, N, C, eps);
+    free(xhat); free(rstd);
+    return ok ? 0 : 2;
+}
+
+int oracle_layernorm_bwd(const double* x, const double* g, const double* bl, const double* du,
+                         const double* dres, double* dx, double* dg, double* dbl, int64_t N,
+                         int64_t C, double eps, int64_t nthreads)
+{
+    set_threads(nthreads);
+    double* u = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* xhat = (double*)malloc((size_t)(N * C) * sizeof(double));
+    double* rstd = (double*)malloc((size_t)N * sizeof(double));
+    int ok = u && xhat && rstd;
+    if (ok) {
+        layer_norm_fwd(x, g, bl, u, xhat, rstd, N, C, eps);
+        layer_norm_bwd(du, g, xhat, rstd, dres, dx, dg, dbl, N, C);
+    }
+    free(u); free(xhat); free(rstd);
+    return ok ? 0 : 2;
+}
+
+/* out[j] = sum_n x[n][j]: the gradient of a bias added to every row. */
+void oracle_colsum(const double* x, double* out, int64_t N, int64_t M)
+{
+    for (int64_t j = 0; j < M; ++j) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) acc += x[n * M + j];
+        out[j] = acc;
+    }
 }

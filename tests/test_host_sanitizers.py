@@ -78,6 +78,11 @@ ORACLE_SCRIPT = textwrap.dedent("""
                  rng.standard_normal((C, C)) * 0.1, rng.standard_normal(C))
             oracle.sublayer_fwd(x, *w, n_head=nh)
             oracle.sublayer_bwd(x, *w, dy, n_head=nh)
+            x2 = x.reshape(B * T, C)
+            oracle.layernorm_fwd(x2, w[0], w[1])
+            oracle.layernorm_bwd(x2, w[0], w[1], dy.reshape(B * T, C), x2)
+            oracle.layernorm_bwd(x2, w[0], w[1], dy.reshape(B * T, C))
+            oracle.colsum(x2)
         print("sanitized oracle: ok")
     """)
 

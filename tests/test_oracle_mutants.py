@@ -49,12 +49,14 @@ MUTANTS = {
                                     "var /= (double)(C - 1);"),
     "layernorm_eps_outside_sqrt": ("double r = 1.0 / sqrt(var + eps);",
                                    "double r = 1.0 / (sqrt(var) + eps);"),
-    "layernorm_bwd_drops_mean_term": ("dx[n * C + c] = S.rstd[n] * (dxh - m1 - S.xhat[n * C + c] * m2) +",
-                                      "dx[n * C + c] = S.rstd[n] * (dxh - S.xhat[n * C + c] * m2) +"),
+    "layernorm_bwd_drops_mean_term": ("dx[n * C + c] = rstd[n] * (dxh - m1 - xhat[n * C + c] * m2) +",
+                                      "dx[n * C + c] = rstd[n] * (dxh - xhat[n * C + c] * m2) +"),
     "heads_interleaved": ("qkv[(b * T + t) * 3 * C + third * C + h * D + d];",
                           "qkv[(b * T + t) * 3 * C + h * 3 * D + third * D + d];"),
-    "residual_dropped_in_bwd": ("                                dy[n * C + c]; /* residual path */",
-                                "                                0.0;"),
+    "colsum_skips_the_last_row": ("for (int64_t n = 0; n < N; ++n) acc += x[n * M + j];",
+                                  "for (int64_t n = 0; n + 1 < N; ++n) acc += x[n * M + j];"),
+    "residual_dropped_in_bwd": ("layer_norm_bwd(du, g, S.xhat, S.rstd, dy, dx, dg, dbl, N, C);",
+                                "layer_norm_bwd(du, g, S.xhat, S.rstd, NULL, dx, dg, dbl, N, C);"),
     "decode_cache_in_bhtd_order": ("const double* Kj = kc + ((b * Tmax + j) * H + h) * D;",
                                    "const double* Kj = kc + ((b * H + h) * Tmax + j) * D;"),
     "decode_token_one_position_early": ("const int64_t last = len - 1;  /* the new token's position */",
@@ -100,6 +102,9 @@ BATTERY = [
     pins.test_sublayer_against_torch_library_ops,
     pins.test_sublayer_finite_differences,
     pins.test_layernorm_output_is_standardised,
+    pins.test_layernorm_alone_is_standardised_affine_and_shift_invariant,
+    pins.test_layernorm_backward_finite_differences_and_residual,
+    pins.test_colsum_of_a_matrix_with_known_column_sums,
     lambda: pins.test_window_against_torch_sdpa_band_mask(3),
     lambda: pins.test_decode_against_torch_sdpa_single_query(3),
     pins.test_decode_closed_forms,

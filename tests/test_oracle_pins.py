@@ -389,6 +389,68 @@ def test_layernorm_output_is_standardised():
     np.testing.assert_allclose(np.mean(ln0 ** 2), var / (var + 1e-5), rtol=1e-13)
 
 
+def test_layernorm_alone_is_standardised_affine_and_shift_invariant():
+    """The standalone LayerNorm (class LayerNorm, CS336 section 3.4): with g = 1,
+    b = 0 every row has mean 0 and mean square var/(var + eps); the gain and
+    bias act elementwise afterwards; a constant added to a row changes
+    nothing; scaling a row by s with eps scaled by s^2 changes nothing."""
+    r = np.random.default_rng(401)
+    N, C = 6, 24
+    x = 3.0 + 2.0 * r.standard_normal((N, C))
+    g, b = r.standard_normal(C), r.standard_normal(C)
+    y0 = oracle.layernorm_fwd(x, np.ones(C), np.zeros(C))
+    var = x.var(axis=1)
+    assert np.all(np.abs(y0.mean(axis=1)) < 1e-14)
+    np.testing.assert_allclose((y0 ** 2).mean(axis=1), var / (var + 1e-5), rtol=1e-13)
+    np.testing.assert_allclose(oracle.layernorm_fwd(x, g, b), y0 * g + b, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(oracle.layernorm_fwd(x + r.standard_normal((N, 1)), g, b),
+                               oracle.layernorm_fwd(x, g, b), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.layernorm_fwd(7.0 * x, g, b, eps=49e-5),
+                               oracle.layernorm_fwd(x, g, b), rtol=0, atol=1e-12)
+
+
+def test_layernorm_backward_finite_differences_and_residual():
+    """dx, dg, dbl of sum(du * LN(x)) + sum(dres * x) by central differences;
+    without du the gradient is dres itself; and each row's LN part of dx sums
+    to zero (LN is invariant to adding a constant to a row)."""
+    r = np.random.default_rng(409)
+    N, C = 4, 10
+    x = r.standard_normal((N, C)) * 1.5 + 0.5
+    g, b = r.standard_normal(C), r.standard_normal(C)
+    du, dres = r.standard_normal((N, C)), r.standard_normal((N, C))
+    dx, dg, db = oracle.layernorm_bwd(x, g, b, du, dres)
+    h = 1e-6
+
+    def loss(x_, g_, b_):
+        return float(np.sum(du * oracle.layernorm_fwd(x_, g_, b_)) + np.sum(dres * x_))
+
+    for arr, grad in ((x, dx), (g, dg), (b, db)):
+        for flat in range(arr.size):
+            i = np.unravel_index(flat, arr.shape)
+            x0 = arr[i]
+            arr[i] = x0 + h
+            lp = loss(x, g, b)
+            arr[i] = x0 - h
+            lm = loss(x, g, b)
+            arr[i] = x0
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[i]) <= 1e-6 * max(1.0, abs(grad[i])), (i, grad[i], fd)
+    dx0, dg0, db0 = oracle.layernorm_bwd(x, g, b, np.zeros((N, C)), dres)
+    assert np.array_equal(dx0, dres) and not dg0.any() and not db0.any()
+    dxl, _, _ = oracle.layernorm_bwd(x, g, b, du)
+    np.testing.assert_allclose(dxl, dx - dres, rtol=0, atol=1e-13)
+    assert np.all(np.abs(dxl.sum(axis=1)) < 1e-12)
+
+
+def test_colsum_of_a_matrix_with_known_column_sums():
+    """Integer entries (exact in fp64): the column sums of the matrix whose row
+    n, column j holds (n + 1) * (j - 2) are (j - 2) * N (N + 1) / 2."""
+    N, M = 37, 9
+    x = np.fromfunction(lambda n, j: (n + 1) * (j - 2), (N, M))
+    assert np.array_equal(oracle.colsum(x), (np.arange(M) - 2) * N * (N + 1) / 2)
+    assert np.array_equal(oracle.colsum(np.ones((1, 5))), np.ones(5))
+
+
 # --------------------------------------------------------------------------
 # sliding window (query i sees keys i-W < j <= i): nanochat section 9 lists
 # sliding-window attention; the band is the causal mask with the W most
