@@ -20,6 +20,8 @@ the computation.  PyTorch supplies device memory and streams.
         query and key rows (also as causal_attention_qkv(..., prologue=Prologue()))
     attn_fwd_strided_rope / attn_bwd_strided_rope           -- attention with that
         prologue fused into its kernels (what causal_attention_qkv uses without dropout)
+    layernorm_fwd / layernorm_bwd / colsum                  -- the row passes of the
+        pre-norm sublayer (LayerNorm, its gradient with the residual term, bias gradients)
 
 Tensors are contiguous [B, H, T, D] (D in {32, 64}; 128 in bf16) of float32 or bfloat16 on
 the current GPU; lse and delta are float32 [B, H, T].
@@ -39,7 +41,8 @@ __all__ = [
     "attn_bwd_strided", "attn_decode", "attn_decode_noalloc", "decode_workspace_bytes",
     "decode_attention", "DECODE_SCRATCH_BYTES",
     "rope_qknorm_fwd", "rope_qknorm_bwd", "Prologue", "attn_fwd_strided_rope",
-    "attn_bwd_strided_rope",
+    "attn_bwd_strided_rope", "layernorm_fwd", "layernorm_bwd", "layernorm_workspace_bytes",
+    "colsum", "colsum_workspace_bytes",
     "attn_status_str", "causal_attention", "causal_attention_qkv", "qkv_heads", "AttnError",
     "ATTN_F32", "ATTN_BF16", "load_library", "LIB_PATH", "EXPORTS", "ABI_VERSION",
 ]
@@ -487,3 +490,71 @@ def causal_attention(q, k, v, scale: float | None = None):
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     return _CausalAttention.apply(q, k, v, scale)
+
+
+def _rows(t: torch.Tensor, name: str, C: int | None = None, stride: int | None = None):
+    """(N, C, row stride) of a 2-D bf16 GPU tensor whose rows are contiguous."""
+    if not t.is_cuda or t.dim() != 2 or t.dtype != torch.bfloat16 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D bfloat16 GPU tensor with contiguous rows")
+    if C is not None and t.shape[1] != C:
+        raise ValueError(f"{name} must have {C} columns")
+    if stride is not None and t.stride(0) != stride:
+        raise ValueError(f"{name} must have the row stride of x ({stride})")
+    return int(t.shape[0]), int(t.shape[1]), int(t.stride(0))
+
+
+def _vec(t: torch.Tensor, name: str, C: int):
+    if not t.is_cuda or t.dtype != torch.bfloat16 or tuple(t.shape) != (C,) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 [{C}] GPU tensor")
+    return t.data_ptr()
+
+
+def layernorm_workspace_bytes(N: int, C: int) -> int:
+    """C ABI attn_layernorm_workspace_bytes."""
+    return int(load_library().attn_layernorm_workspace_bytes(int(N), int(C)))
+
+
+def colsum_workspace_bytes(N: int, M: int) -> int:
+    """C ABI attn_colsum_workspace_bytes."""
+    return int(load_library().attn_colsum_workspace_bytes(int(N), int(M)))
+
+
+def layernorm_fwd(x, g, b, y, eps: float = 1e-5, stream=None) -> None:
+    """C ABI attn_layernorm_fwd: y = LayerNorm(x) * g + b over the rows of x
+    [N, C] (bf16; y has x's shape and row stride)."""
+    N, C, st = _rows(x, "x")
+    _rows(y, "y", C, st)
+    if y.shape[0] != N:
+        raise ValueError("y must have the rows of x")
+    rc = load_library().attn_layernorm_fwd(x.data_ptr(), _vec(g, "g", C), _vec(b, "b", C),
+                                           y.data_ptr(), N, C, st, float(eps), ATTN_BF16,
+                                           _stream(stream))
+    check(rc)
+
+
+def layernorm_bwd(x, g, dy, dx, dg, db, workspace, dres=None, eps: float = 1e-5,
+                  stream=None) -> None:
+    """C ABI attn_layernorm_bwd: dx (+ dres, the residual branch's gradient),
+    dg, db of LayerNorm from x and dy = d(loss)/d(output); workspace a byte
+    tensor of at least layernorm_workspace_bytes(N, C)."""
+    N, C, st = _rows(x, "x")
+    for t, n in ((dy, "dy"), (dx, "dx")) + (((dres, "dres"),) if dres is not None else ()):
+        _rows(t, n, C, st)
+        if t.shape[0] != N:
+            raise ValueError(f"{n} must have the rows of x")
+    rc = load_library().attn_layernorm_bwd(
+        x.data_ptr(), _vec(g, "g", C), dy.data_ptr(), None if dres is None else dres.data_ptr(),
+        dx.data_ptr(), _vec(dg, "dg", C), _vec(db, "db", C), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), N, C, st, float(eps), ATTN_BF16,
+        _stream(stream))
+    check(rc)
+
+
+def colsum(x, out, workspace, stream=None) -> None:
+    """C ABI attn_colsum: out[j] = sum over the rows of x [N, M] (bf16) of x[:, j];
+    workspace a byte tensor of at least colsum_workspace_bytes(N, M)."""
+    N, M, st = _rows(x, "x")
+    rc = load_library().attn_colsum(x.data_ptr(), _vec(out, "out", M), _ptr(workspace, "workspace"),
+                                    workspace.numel() * workspace.element_size(), N, M, st,
+                                    ATTN_BF16, _stream(stream))
+    check(rc)

@@ -39,9 +39,10 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_str
            "attn_bwd_strided", "attn_dropout_keep_bytes", "attn_fwd_strided_keep",
            "attn_bwd_strided_keep", "attn_decode", "attn_decode_workspace_bytes",
            "attn_decode_noalloc", "attn_rope_qknorm_fwd", "attn_rope_qknorm_bwd",
-           "attn_fwd_strided_rope", "attn_bwd_strided_rope", "attn_status_str",
-           "attn_abi_version")
-ABI_VERSION = (1 << 16) | 7
+           "attn_fwd_strided_rope", "attn_bwd_strided_rope", "attn_layernorm_workspace_bytes",
+           "attn_layernorm_fwd", "attn_layernorm_bwd", "attn_colsum_workspace_bytes",
+           "attn_colsum", "attn_status_str", "attn_abi_version")
+ABI_VERSION = (1 << 16) | 8
 # the fixed device scratch of attn_decode_noalloc (CAUSAL_ATTN_DECODE_SCRATCH_BYTES)
 DECODE_SCRATCH_BYTES = 16 << 20
 
@@ -122,6 +123,18 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                           [_int] * 5 + [ctypes.c_float] + [_int] +
                                           [ctypes.c_float] * 4 + [_int, _int, _vp])
     lib.attn_bwd_strided_rope.restype = _int
+    _ll, _sz = ctypes.c_longlong, ctypes.c_size_t
+    lib.attn_layernorm_workspace_bytes.argtypes = [_int, _int]
+    lib.attn_layernorm_workspace_bytes.restype = _sz
+    lib.attn_layernorm_fwd.argtypes = [_vp] * 4 + [_int, _int, _ll, ctypes.c_float, _int, _vp]
+    lib.attn_layernorm_fwd.restype = _int
+    lib.attn_layernorm_bwd.argtypes = ([_vp] * 8 + [_sz, _int, _int, _ll, ctypes.c_float, _int,
+                                                    _vp])
+    lib.attn_layernorm_bwd.restype = _int
+    lib.attn_colsum_workspace_bytes.argtypes = [_int, _int]
+    lib.attn_colsum_workspace_bytes.restype = _sz
+    lib.attn_colsum.argtypes = [_vp] * 3 + [_sz, _int, _int, _ll, _int, _vp]
+    lib.attn_colsum.restype = _int
     lib.attn_status_str.argtypes = [_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libcausal_attn.so")
 LIB_POISON = os.path.join(PKG, "libcausal_attn_lds_poison.so")
 POISON_FLAGS = ["-DCATTN_LDS_POISON"]
 SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_bf16_d64.hip", "attn_bwd_plain.hip", "attn_decode.hip", "attn_f32.hip",
-           "attn_rope.hip"]
+           "attn_norm.hip", "attn_rope.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

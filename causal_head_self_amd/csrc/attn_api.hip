@@ -256,7 +256,9 @@ const char* attn_status_str(int st)
     switch (st) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
-    case ATTN_ERR_SHAPE: return "B, H and T must be >= 1";
+    case ATTN_ERR_SHAPE:
+        return "B, H and T must be >= 1 (LayerNorm / column sums: N >= 1, 8 <= C <= 4096 and "
+               "M >= 8, multiples of 8)";
     case ATTN_ERR_UNSUPPORTED_D: return "head dim D must be 32 or 64 (or 128 with bf16)";
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_F32 or ATTN_BF16";
     case ATTN_ERR_ALIGN: return "tensors must be 16-byte aligned (lse/delta 4-byte)";
@@ -266,11 +268,15 @@ const char* attn_status_str(int st)
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
     case ATTN_ERR_LAYOUT:
         return "strided views need bf16, D = 64 or 128, strides that are non-negative multiples of 8 "
-               "with stride_t >= D, and T * stride_t * 2 < 2^32";
-    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes()";
+               "with stride_t >= D, and T * stride_t * 2 < 2^32 (row passes: stride >= C, a "
+               "multiple of 8)";
+    case ATTN_ERR_WORKSPACE:
+        return "workspace smaller than the entry point's *_workspace_bytes() (attn_decode, "
+               "attn_layernorm_bwd, attn_colsum)";
     case ATTN_ERR_PARAM:
         return "RoPE / QK norm: flags must be 0..3, 0 <= pos0 and pos0 + T <= 2^24, rope_base "
-               "finite and > 0, gains finite, eps finite and >= 0; dropout_p must be in [0, 1)";
+               "finite and > 0, gains finite, eps finite and >= 0; dropout_p must be in [0, 1); "
+               "LayerNorm eps finite and >= 0";
     case ATTN_ERR_SCRATCH:
         return "attn_decode_noalloc: the two-launch path would need more than the library's "
                "fixed scratch (CAUSAL_ATTN_DECODE_SCRATCH_BYTES); use attn_decode with a workspace";
@@ -801,6 +807,136 @@ int attn_rope_qknorm_bwd(attn_view_t q, attn_view_t k, attn_view_t dq_out, attn_
     a.sdq = strides_of(dq_out);
     a.sdk = strides_of(dk_out);
     return status(cattn::launch_rope_qknorm(a, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---- row passes of the sublayer (LayerNorm, column sums) ----------------------
+
+namespace {
+
+// Bytes of N rows of C bf16 elements `stride` apart.
+size_t rows_bytes(int N, int C, long long stride) { return ((size_t)(N - 1) * stride + C) * 2; }
+
+int rows_check(int N, int C, long long stride, int dtype, int c_max)
+{
+    if (N < 1 || C < 8 || C % 8 || C > c_max) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (stride < C || stride % 8) return ATTN_ERR_LAYOUT;
+    if ((long long)(N - 1) * stride > (1LL << 40)) return ATTN_ERR_OVERFLOW;
+    return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (uintptr_t)p % 16 == 0; }
+
+Span span_of(const void* p, size_t bytes)
+{
+    return Span{(uintptr_t)p, (uintptr_t)p + bytes};
+}
+
+// Outputs (first n_out) must not overlap any span after them or each other.
+bool spans_alias(const Span* s, int n_out, int n)
+{
+    for (int i = 0; i < n_out; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if (overlaps(s[i], s[j])) return true;
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_layernorm_workspace_bytes(int N, int C)
+{
+    if (N < 1 || C < 1) return 0;
+    return (size_t)cattn::layernorm_bwd_workgroups(N) * 2 * C * sizeof(float);
+}
+
+size_t attn_colsum_workspace_bytes(int N, int M)
+{
+    if (N < 1 || M < 1) return 0;
+    return (size_t)cattn::colsum_row_blocks(N) * M * sizeof(float);
+}
+
+int attn_layernorm_fwd(const void* x, const void* g, const void* b, void* y, int N, int C,
+                       long long stride, float eps, int dtype, void* stream)
+{
+    if (!x || !g || !b || !y) return ATTN_ERR_NULL;
+    int st = rows_check(N, C, stride, dtype, 4096);
+    if (st != ATTN_OK) return st;
+    if (!isfinite(eps) || eps < 0.0f) return ATTN_ERR_PARAM;
+    if (!aligned16(x) || !aligned16(g) || !aligned16(b) || !aligned16(y)) return ATTN_ERR_ALIGN;
+    const size_t rb = rows_bytes(N, C, stride);
+    const Span sp[4] = {span_of(y, rb), span_of(x, rb), span_of(g, 2 * (size_t)C),
+                        span_of(b, 2 * (size_t)C)};
+    if (spans_alias(sp, 1, 4)) return ATTN_ERR_ALIAS;
+    cattn::NormArgs a{};
+    a.x = x;
+    a.g = g;
+    a.b = b;
+    a.y = y;
+    a.N = N;
+    a.C = C;
+    a.stride = stride;
+    a.eps = eps;
+    return status(cattn::launch_layernorm_fwd(a, (hipStream_t)stream));
+}
+
+int attn_layernorm_bwd(const void* x, const void* g, const void* dy, const void* dres, void* dx,
+                       void* dg, void* db, void* workspace, size_t workspace_bytes, int N, int C,
+                       long long stride, float eps, int dtype, void* stream)
+{
+    if (!x || !g || !dy || !dx || !dg || !db || !workspace) return ATTN_ERR_NULL;
+    int st = rows_check(N, C, stride, dtype, 4096);
+    if (st != ATTN_OK) return st;
+    if (!isfinite(eps) || eps < 0.0f) return ATTN_ERR_PARAM;
+    if (!aligned16(x) || !aligned16(g) || !aligned16(dy) || (dres && !aligned16(dres)) ||
+        !aligned16(dx) || !aligned16(dg) || !aligned16(db) || !aligned16(workspace))
+        return ATTN_ERR_ALIGN;
+    const size_t need = attn_layernorm_workspace_bytes(N, C);
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t rb = rows_bytes(N, C, stride), cb = 2 * (size_t)C;
+    const Span sp[8] = {span_of(dx, rb), span_of(dg, cb), span_of(db, cb), span_of(workspace, need),
+                        span_of(x, rb), span_of(g, cb), span_of(dy, rb),
+                        span_of(dres ? dres : x, rb)};
+    if (spans_alias(sp, 4, 8)) return ATTN_ERR_ALIAS;
+    cattn::NormArgs a{};
+    a.x = x;
+    a.g = g;
+    a.dy = dy;
+    a.dres = dres;
+    a.dx = dx;
+    a.dg = dg;
+    a.db = db;
+    a.workspace = workspace;
+    a.N = N;
+    a.C = C;
+    a.stride = stride;
+    a.eps = eps;
+    return status(cattn::launch_layernorm_bwd(a, (hipStream_t)stream));
+}
+
+int attn_colsum(const void* x, void* out, void* workspace, size_t workspace_bytes, int N, int M,
+                long long stride, int dtype, void* stream)
+{
+    if (!x || !out || !workspace) return ATTN_ERR_NULL;
+    int st = rows_check(N, M, stride, dtype, 1 << 24);
+    if (st != ATTN_OK) return st;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
+    const size_t need = attn_colsum_workspace_bytes(N, M);
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const Span sp[3] = {span_of(out, 2 * (size_t)M), span_of(workspace, need),
+                        span_of(x, rows_bytes(N, M, stride))};
+    if (spans_alias(sp, 2, 3)) return ATTN_ERR_ALIAS;
+    cattn::NormArgs a{};
+    a.x = x;
+    a.y = out;
+    a.workspace = workspace;
+    a.N = N;
+    a.C = M;
+    a.stride = stride;
+    return status(cattn::launch_colsum(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -103,6 +103,30 @@ struct RopeArgs {
 
 hipError_t launch_rope_qknorm(const RopeArgs& a, hipStream_t st);
 
+// LayerNorm and column sums over bf16 rows (the sublayer around the attention).
+struct NormArgs {
+    const void* x;     // [N][C] rows, `stride` elements apart
+    const void* g;     // [C] gain (LayerNorm)
+    const void* b;     // [C] bias (LayerNorm forward)
+    const void* dy;    // gradient: d(loss)/d(LayerNorm output), rows like x
+    const void* dres;  // gradient: residual term added to dx (nullptr: none)
+    void* y;           // forward: output rows; colsum: the [C] sums
+    void* dx;          // gradient: rows like x
+    void* dg;          // gradient: [C]
+    void* db;          // gradient: [C]
+    void* workspace;   // fp32 column partials (layernorm_bwd_workgroups(N) x 2C, or
+                       // colsum_row_blocks(N) x C)
+    int N, C;
+    long long stride;
+    float eps;
+};
+
+int layernorm_bwd_workgroups(int N);
+int colsum_row_blocks(int N);
+hipError_t launch_layernorm_fwd(const NormArgs& a, hipStream_t st);
+hipError_t launch_layernorm_bwd(const NormArgs& a, hipStream_t st);
+hipError_t launch_colsum(const NormArgs& a, hipStream_t st);
+
 // launch_dq_* computes delta (from o and dO) as well as dq.
 hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dq_bf16(const AttnArgs& a, hipStream_t st);

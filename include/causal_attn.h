@@ -64,7 +64,7 @@ typedef enum {
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,          /* a required pointer is NULL              */
-    ATTN_ERR_SHAPE = 2,         /* B, H or T < 1                            */
+    ATTN_ERR_SHAPE = 2,         /* B, H or T < 1 (row passes: N, C, M)      */
     ATTN_ERR_UNSUPPORTED_D = 3, /* D not in {32, 64} (bf16: {32, 64, 128})  */
     ATTN_ERR_DTYPE = 4,         /* dtype not ATTN_F32 / ATTN_BF16           */
     ATTN_ERR_ALIGN = 5,         /* tensor not 16-byte (lse/delta 4-byte) aligned */
@@ -73,8 +73,8 @@ typedef enum {
     ATTN_ERR_ALIAS = 8,         /* an output overlaps an input or output    */
     ATTN_ERR_HIP = 9,           /* a kernel launch failed                   */
     ATTN_ERR_LAYOUT = 10,       /* strided views: unsupported dtype/D or strides */
-    ATTN_ERR_WORKSPACE = 11,    /* decode: workspace smaller than required  */
-    ATTN_ERR_PARAM = 12,        /* RoPE / QK norm parameters, or dropout_p    */
+    ATTN_ERR_WORKSPACE = 11,    /* a workspace smaller than required        */
+    ATTN_ERR_PARAM = 12,        /* RoPE / QK norm / LayerNorm parameters, or dropout_p */
     ATTN_ERR_SCRATCH = 13       /* attn_decode_noalloc: beyond its fixed scratch */
 } attn_status_t;
 
@@ -343,13 +343,55 @@ int attn_bwd_strided_rope(attn_view_t q, attn_view_t k, attn_view_t q_rot, attn_
                           int H, int T, int D, int window, float scale, int pos0, float rope_base,
                           float q_gain, float k_gain, float eps, int flags, int dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The row passes of the pre-norm sublayer around the attention (CS336
+ * tutorial, section 5.1: Block.forward adds attn(ln_1(x)) to x; section 3.4,
+ * class LayerNorm: mean and biased variance over the row, eps added under the
+ * square root, then gain and bias), and the gradient of its biases.
+ *
+ * attn_layernorm_fwd:  y[r][c] = (x[r][c] - mean_r) / sqrt(var_r + eps) * g[c] + b[c]
+ *   over N rows of C elements.  x, y: bf16 rows `stride` elements apart
+ *   (stride >= C, a multiple of 8; y uses the same stride); g, b: bf16 [C].
+ *   Requirements: N >= 1 and 8 <= C <= 4096 with C % 8 == 0 (else
+ *   ATTN_ERR_SHAPE); stride as stated (ATTN_ERR_LAYOUT); dtype ATTN_BF16
+ *   (ATTN_ERR_DTYPE); eps finite and >= 0 (ATTN_ERR_PARAM); x, y, g, b 16-byte
+ *   aligned (ATTN_ERR_ALIGN); y overlapping an input is ATTN_ERR_ALIAS.
+ *
+ * attn_layernorm_bwd:  the gradient of sum(dy * y) + sum(dres * x):
+ *   dx = rstd * (e - mean_c(e) - xh * mean_c(e * xh)) + dres,
+ *   with xh = (x - mean) * rstd, e = dy * g, rstd = 1 / sqrt(var + eps);
+ *   dg[c] = sum_r dy[r][c] * xh[r][c], db[c] = sum_r dy[r][c].
+ *   The row statistics are recomputed from x.  dres (the residual branch's
+ *   gradient) may be NULL.  x, dy, dres, dx: rows as in the forward; g, dg,
+ *   db: bf16 [C].  workspace: fp32 partial column sums, at least
+ *   attn_layernorm_workspace_bytes(N, C) bytes, 16-byte aligned (contents on
+ *   entry do not matter; undefined on return).  Checks as the forward, plus
+ *   ATTN_ERR_WORKSPACE; outputs and workspace may not overlap inputs or each
+ *   other (ATTN_ERR_ALIAS).
+ *
+ * attn_colsum:  out[j] = sum_r x[r][j] (the gradient of a bias added to every
+ *   row), for N rows of M bf16 elements `stride` apart; out bf16 [M].
+ *   8 <= M, M % 8 == 0, stride >= M and a multiple of 8; workspace of at least
+ *   attn_colsum_workspace_bytes(N, M) bytes.  Fixed summation order: blocks of
+ *   max(8, ceil(N / 64)) rows, then the blocks in a fixed order.
+ */
+size_t attn_layernorm_workspace_bytes(int N, int C);
+int attn_layernorm_fwd(const void* x, const void* g, const void* b, void* y, int N, int C,
+                       long long stride, float eps, int dtype, void* stream);
+int attn_layernorm_bwd(const void* x, const void* g, const void* dy, const void* dres, void* dx,
+                       void* dg, void* db, void* workspace, size_t workspace_bytes, int N, int C,
+                       long long stride, float eps, int dtype, void* stream);
+size_t attn_colsum_workspace_bytes(int N, int M);
+int attn_colsum(const void* x, void* out, void* workspace, size_t workspace_bytes, int N, int M,
+                long long stride, int dtype, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_str(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
 int attn_abi_version(void);
 
-#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 7)
+#define CAUSAL_ATTN_ABI_VERSION ((1 << 16) | 8)
 
 #ifdef __cplusplus
 }

@@ -546,3 +546,77 @@ def test_fused_prologue_validation(fwd):
     else:
         assert call(delta=P[1] + 64) == 8         # delta (an output) inside an input view
         assert call(delta=P[12]) == 8             # delta on lse
+
+
+# ---------------------------------------------------------------------------
+# row passes (attn_layernorm_fwd / _bwd, attn_colsum): invalid arguments only
+# ---------------------------------------------------------------------------
+
+N_, C_ = 64, 768
+
+
+def _ln_fwd(x=P[0], g=P[1], b=P[2], y=P[3], N=N_, C=C_, stride=C_, eps=1e-5, dtype=1):
+    return cat.load_library().attn_layernorm_fwd(x, g, b, y, N, C, stride, eps, dtype, None)
+
+
+def _ln_ws(N=N_, C=C_):
+    return cat.load_library().attn_layernorm_workspace_bytes(N, C)
+
+
+def _ln_bwd(x=P[0], g=P[1], dy=P[2], dres=P[3], dx=P[4], dg=P[5], db=P[6], ws=P[7],
+            ws_bytes=None, N=N_, C=C_, stride=C_, eps=1e-5, dtype=1):
+    ws_bytes = _ln_ws(N, C) if ws_bytes is None else ws_bytes
+    return cat.load_library().attn_layernorm_bwd(x, g, dy, dres, dx, dg, db, ws, ws_bytes, N, C,
+                                                 stride, eps, dtype, None)
+
+
+def _cs_ws(N=N_, M=C_):
+    return cat.load_library().attn_colsum_workspace_bytes(N, M)
+
+
+def _cs(x=P[0], out=P[1], ws=P[2], ws_bytes=None, N=N_, M=C_, stride=C_, dtype=1):
+    ws_bytes = _cs_ws(N, M) if ws_bytes is None else ws_bytes
+    return cat.load_library().attn_colsum(x, out, ws, ws_bytes, N, M, stride, dtype, None)
+
+
+def test_row_pass_workspace_bytes():
+    # LayerNorm gradient: [dg | db] partials per 16 rows; column sums: per block
+    # of max(8, ceil(N / 64)) rows
+    assert _ln_ws(8192, 768) == 512 * 2 * 768 * 4
+    assert _ln_ws(17, 8) == 2 * 2 * 8 * 4
+    assert _cs_ws(8192, 2304) == 64 * 2304 * 4
+    assert _cs_ws(8200, 8) == 64 * 8 * 4 and _cs_ws(33, 8) == 5 * 8 * 4
+    assert _ln_ws(0, 768) == 0 and _cs_ws(1, 0) == 0
+
+
+@pytest.mark.parametrize("name", ["x", "g", "b", "y"])
+def test_layernorm_fwd_null_pointer(name):
+    assert _ln_fwd(**{name: None}) == 1
+
+
+@pytest.mark.parametrize("name", ["x", "g", "dy", "dx", "dg", "db", "ws"])
+def test_layernorm_bwd_null_pointer(name):
+    assert _ln_bwd(**{name: None}) == 1
+
+
+@_last_check
+def test_row_pass_validation_order_and_codes():
+    # shape: N >= 1, 8 <= C <= 4096 (LayerNorm), C % 8 == 0
+    assert _ln_fwd(N=0) == 2 and _ln_fwd(C=4) == 2 and _ln_fwd(C=12, stride=16) == 2
+    assert _ln_fwd(C=4104, stride=4104) == 2 and _ln_bwd(C=0) == 2 and _cs(M=12, stride=16) == 2
+    assert _ln_fwd(dtype=0) == 4 and _ln_bwd(dtype=0) == 4 and _cs(dtype=2) == 4
+    assert _ln_fwd(stride=760) == 10 and _ln_fwd(stride=772) == 10 and _cs(stride=100) == 10
+    assert _ln_fwd(eps=-1.0) == 12 and _ln_fwd(eps=float("nan")) == 12
+    assert _ln_bwd(eps=float("inf")) == 12
+    assert _ln_fwd(x=P[0] + 8) == 5 and _ln_fwd(g=P[1] + 2) == 5 and _ln_fwd(y=P[3] + 4) == 5
+    assert _ln_bwd(dres=P[3] + 8) == 5 and _ln_bwd(ws=P[7] + 4) == 5 and _cs(out=P[1] + 2) == 5
+    assert _ln_bwd(ws_bytes=_ln_ws() - 1) == 11 and _cs(ws_bytes=_cs_ws() - 4) == 11
+    assert _ln_fwd(y=P[0]) == 8                    # y is x
+    assert _ln_fwd(y=P[1] - 64) == 8               # y runs into g
+    assert _ln_bwd(dx=P[2]) == 8                   # dx is dy
+    assert _ln_bwd(dx=P[3] + 16) == 8              # dx inside dres
+    assert _ln_bwd(dg=P[4] + 32) == 8              # dg inside dx
+    assert _ln_bwd(ws=P[6]) == 8                   # workspace over db
+    assert _cs(out=P[0] + 64) == 8 and _cs(ws=P[1]) == 8
+    # no residual term is allowed
+    assert _ln_bwd(dres=None, dx=P[0]) == 8

@@ -9,7 +9,8 @@ NaN) than the release library, whose LDS holds whatever an earlier workgroup
 left.  Every entry point whose kernels use LDS runs here on both libraries,
 and the outputs must agree bit for bit: ragged lengths, windows, dropout (drawn
 and stored bits), the fused prologue, head dims 32, 64 and 128, fp32, both
-backward forms, and both decode paths.
+backward forms, both decode paths, and the LayerNorm gradient (whose column
+partials meet in LDS).
 """
 import math
 import os
@@ -179,3 +180,23 @@ def test_decode_both_paths(libs, B, H, T_max, D):
         return [o, lse, o2, lse2]
 
     _same(f"decode B={B} H={H} T_max={T_max} D={D}", _both(libs, run))
+
+
+@pytest.mark.parametrize("N,C", [(333, 768), (70, 1000), (9, 4096)])
+def test_layernorm_gradient(libs, N, C):
+    import causal_head_self_amd as cat
+    _note(f"[lds poison] layernorm bwd N={N} C={C}")
+    dev = torch.device("cuda")
+    g0 = torch.Generator().manual_seed(15)
+    x, dy, dres = (torch.randn((N, C), generator=g0).to(torch.bfloat16).to(dev) for _ in range(3))
+    gain = torch.randn(C, generator=g0).to(torch.bfloat16).to(dev)
+
+    def run():
+        dx = torch.empty_like(x)
+        dg = torch.empty(C, dtype=torch.bfloat16, device=dev)
+        db = torch.empty_like(dg)
+        ws = torch.empty(cat.layernorm_workspace_bytes(N, C), dtype=torch.uint8, device=dev)
+        cat.layernorm_bwd(x, gain, dy, dx, dg, db, ws, dres=dres)
+        return [dx, dg, db]
+
+    _same(f"layernorm bwd N={N} C={C}", _both(libs, run))

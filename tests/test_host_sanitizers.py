@@ -113,11 +113,11 @@ def test_library_host_code_under_asan_and_ubsan(tmp_path):
     rt = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
     if not rt:
         pytest.skip("clang's ASan runtime is not installed")
-    objs = [os.path.join(PKG, "_build", n + ".o") for n in
-            ("attn_bf16", "attn_bf16_d64", "attn_bwd_plain", "attn_decode", "attn_f32", "attn_rope")]
+    from causal_head_self_amd import build as hip_build
+    objs = [os.path.join(PKG, "_build", os.path.splitext(n)[0] + ".o") for n in hip_build.SOURCES
+            if n != "attn_api.hip"]
     missing = [o for o in objs if not os.path.exists(o)]
     assert not missing, f"build the library first (python -m causal_head_self_amd.build): {missing}"
-    from causal_head_self_amd import build as hip_build
     api_o = str(tmp_path / "attn_api_san.o")
     lib = str(tmp_path / "libcausal_attn_san.so")
     # the sanitizers instrument the host pass only (each flag after -Xarch_host)
