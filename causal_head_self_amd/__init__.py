@@ -550,11 +550,19 @@ def layernorm_bwd(x, g, dy, dx, dg, db, workspace, dres=None, eps: float = 1e-5,
     check(rc)
 
 
-def colsum(x, out, workspace, stream=None) -> None:
-    """C ABI attn_colsum: out[j] = sum over the rows of x [N, M] (bf16) of x[:, j];
-    workspace a byte tensor of at least colsum_workspace_bytes(N, M)."""
-    N, M, st = _rows(x, "x")
-    rc = load_library().attn_colsum(x.data_ptr(), _vec(out, "out", M), _ptr(workspace, "workspace"),
-                                    workspace.numel() * workspace.element_size(), N, M, st,
-                                    ATTN_BF16, _stream(stream))
+def colsum(x, out, workspace=None, stream=None) -> None:
+    """C ABI attn_colsum: out[j] = sum over the rows of x [N, M] of x[:, j], out
+    bf16 [M].  x bf16 (workspace: a byte tensor of at least
+    colsum_workspace_bytes(N, M)) or float32 (a few rows; no workspace)."""
+    f32 = x.dtype == torch.float32
+    if f32:
+        if not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+            raise ValueError("x must be a 2-D GPU tensor with contiguous rows")
+        N, M, st = int(x.shape[0]), int(x.shape[1]), int(x.stride(0))
+    else:
+        N, M, st = _rows(x, "x")
+    ws, ws_bytes = (None, 0) if workspace is None else (
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size())
+    rc = load_library().attn_colsum(x.data_ptr(), _vec(out, "out", M), ws, ws_bytes, N, M, st,
+                                    ATTN_F32 if f32 else ATTN_BF16, _stream(stream))
     check(rc)

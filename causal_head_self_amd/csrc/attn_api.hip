@@ -818,10 +818,10 @@ namespace {
 // Bytes of N rows of C bf16 elements `stride` apart.
 size_t rows_bytes(int N, int C, long long stride) { return ((size_t)(N - 1) * stride + C) * 2; }
 
-int rows_check(int N, int C, long long stride, int dtype, int c_max)
+int rows_check(int N, int C, long long stride, int dtype, int c_max, bool f32_ok = false)
 {
     if (N < 1 || C < 8 || C % 8 || C > c_max) return ATTN_ERR_SHAPE;
-    if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (dtype != ATTN_BF16 && !(f32_ok && dtype == ATTN_F32)) return ATTN_ERR_DTYPE;
     if (stride < C || stride % 8) return ATTN_ERR_LAYOUT;
     if ((long long)(N - 1) * stride > (1LL << 40)) return ATTN_ERR_OVERFLOW;
     return ATTN_OK;
@@ -920,14 +920,15 @@ int attn_layernorm_bwd(const void* x, const void* g, const void* dy, const void*
 int attn_colsum(const void* x, void* out, void* workspace, size_t workspace_bytes, int N, int M,
                 long long stride, int dtype, void* stream)
 {
-    if (!x || !out || !workspace) return ATTN_ERR_NULL;
-    int st = rows_check(N, M, stride, dtype, 1 << 24);
+    const bool f32 = dtype == ATTN_F32;
+    if (!x || !out || (!workspace && !f32)) return ATTN_ERR_NULL;
+    int st = rows_check(N, M, stride, dtype, 1 << 30, true);
     if (st != ATTN_OK) return st;
-    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
-    const size_t need = attn_colsum_workspace_bytes(N, M);
+    if (!aligned16(x) || !aligned16(out) || (!f32 && !aligned16(workspace))) return ATTN_ERR_ALIGN;
+    const size_t need = f32 ? 0 : attn_colsum_workspace_bytes(N, M);
     if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    const Span sp[3] = {span_of(out, 2 * (size_t)M), span_of(workspace, need),
-                        span_of(x, rows_bytes(N, M, stride))};
+    const size_t in_bytes = ((size_t)(N - 1) * stride + M) * (f32 ? 4 : 2);
+    const Span sp[3] = {span_of(out, 2 * (size_t)M), span_of(workspace, need), span_of(x, in_bytes)};
     if (spans_alias(sp, 2, 3)) return ATTN_ERR_ALIAS;
     cattn::NormArgs a{};
     a.x = x;
@@ -936,6 +937,7 @@ int attn_colsum(const void* x, void* out, void* workspace, size_t workspace_byte
     a.N = N;
     a.C = M;
     a.stride = stride;
+    a.f32 = f32;
     return status(cattn::launch_colsum(a, (hipStream_t)stream));
 }
 

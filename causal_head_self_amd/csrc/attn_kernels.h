@@ -119,6 +119,7 @@ struct NormArgs {
     int N, C;
     long long stride;
     float eps;
+    bool f32;          // colsum: fp32 rows (x), no workspace
 };
 
 int layernorm_bwd_workgroups(int N);

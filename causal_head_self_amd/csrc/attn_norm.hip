@@ -26,7 +26,7 @@ namespace norm {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;  // rows in flight per workgroup
 constexpr int kMaxC = 4096;            // LDS of the column partials: 2 * kMaxC floats
-constexpr int kColThreads = 256;       // colsum: 8 columns per thread
+constexpr int kColThreads = 64;        // colsum: 8 columns per thread, one wave per block
 constexpr int kColBlock = kColThreads * 8;
 
 // Sum over the 64 lanes, the same value in every lane, in VALU cross-lane
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void layernorm_fwd_kernel(
 // its wave j every kWaves-th of them from row j.  Each lane keeps the dg and db
 // partial sums of its columns over the wave's rows; the four waves add theirs
 // in LDS in wave order, and the workgroup writes [dg | db] (2C floats) to
-// part[w].  A wave loads the next row's x, dy and dres before it works on the
+// part[w].  A wave loads the next row's x and dy before it works on the
 // current one, so that their latency overlaps that work.
 template <int NCH>
 __device__ __forceinline__ void load_row(const bf16* __restrict__ p, int lane, int nch,
@@ -170,23 +170,23 @@ __global__ __launch_bounds__(kThreads) void layernorm_bwd_kernel(
     if (kAhead && row < r1) {
         load_row<NCH>(x + (size_t)row * stride, lane, nch, xv);
         load_row<NCH>(dy + (size_t)row * stride, lane, nch, dv);
-        if (dres) load_row<NCH>(dres + (size_t)row * stride, lane, nch, rv);
     }
     for (; row < r1; row += kWaves) {
         const size_t off = (size_t)row * stride;
         if (!kAhead) {
             load_row<NCH>(x + off, lane, nch, xv);
             load_row<NCH>(dy + off, lane, nch, dv);
-            if (dres) load_row<NCH>(dres + off, lane, nch, rv);
         }
+        // dres of this row is used last: loaded before the next row's x and dy,
+        // it can be waited for while those are still in flight
+        if (dres) load_row<NCH>(dres + off, lane, nch, rv);
         // the next row's operands (past C every value is 0, and so is every term
         // below that multiplies dy)
-        float xn[NCH][8], dn[NCH][8], rn[NCH][8];
+        float xn[NCH][8], dn[NCH][8];
         const int nxt = row + kWaves;
         if (kAhead && nxt < r1) {
             load_row<NCH>(x + (size_t)nxt * stride, lane, nch, xn);
             load_row<NCH>(dy + (size_t)nxt * stride, lane, nch, dn);
-            if (dres) load_row<NCH>(dres + (size_t)nxt * stride, lane, nch, rn);
         }
         float s = 0.f;
 #pragma unroll
@@ -239,7 +239,6 @@ __global__ __launch_bounds__(kThreads) void layernorm_bwd_kernel(
                 for (int e = 0; e < 8; ++e) {
                     xv[i][e] = xn[i][e];
                     dv[i][e] = dn[i][e];
-                    rv[i][e] = rn[i][e];
                 }
         }
     }
@@ -337,6 +336,23 @@ __global__ __launch_bounds__(64 * kRedWaves) void colsum_reduce_kernel(
     }
 }
 
+// Column sums of a few fp32 rows (the split-K partial products of a weight
+// gradient), rounded once to bf16: thread t takes columns 4t .. 4t + 3 and
+// adds rows 0, 1, ... in order.
+__global__ __launch_bounds__(256) void sum_rows_f32_kernel(const float* __restrict__ x, int P,
+                                                           int M, long long stride,
+                                                           bf16* __restrict__ out)
+{
+    const long long col = 4LL * ((long long)blockIdx.x * 256 + threadIdx.x);
+    if (col >= M) return;
+    f32x4 acc = *(const f32x4*)(x + col);
+    for (int p = 1; p < P; ++p) acc += *(const f32x4*)(x + (size_t)p * stride + col);
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[e];
+    *(bf16x4*)(out + col) = o;
+}
+
 int nch_of(int C) { return (C + 511) / 512; }
 
 template <int NCH>
@@ -361,9 +377,9 @@ void bwd_launch(const NormArgs& a, int n_wg, int rows_per_wg, hipStream_t st)
 // Rows per workgroup of the LayerNorm gradient (16: four per wave) and of the
 // column sums (32); the partial buffers follow from them.
 int layernorm_bwd_workgroups(int N) { return (N + 15) / 16; }
-// Column sums: at most 64 row blocks (of at least 8 rows), so that the
+// Column sums: at most 128 row blocks (of at least 8 rows), so that the
 // reduction over them is one pass of independent loads.
-int colsum_rows_per_block(int N) { return max(8, (N + 63) / 64); }
+int colsum_rows_per_block(int N) { return max(8, (N + 127) / 128); }
 int colsum_row_blocks(int N) { return (N + colsum_rows_per_block(N) - 1) / colsum_rows_per_block(N); }
 
 hipError_t launch_layernorm_fwd(const NormArgs& a, hipStream_t st)
@@ -398,6 +414,12 @@ hipError_t launch_layernorm_bwd(const NormArgs& a, hipStream_t st)
 
 hipError_t launch_colsum(const NormArgs& a, hipStream_t st)
 {
+    if (a.f32) {  // few rows: one pass, no partials
+        const long long threads = (a.C + 3) / 4;
+        hipLaunchKernelGGL(norm::sum_rows_f32_kernel, dim3((unsigned)((threads + 255) / 256)),
+                           dim3(256), 0, st, (const float*)a.x, a.N, a.C, a.stride, (bf16*)a.y);
+        return hipGetLastError();
+    }
     const int P = colsum_row_blocks(a.N);
     hipLaunchKernelGGL(norm::colsum_part_kernel,
                        dim3(P, (a.C + norm::kColBlock - 1) / norm::kColBlock), dim3(norm::kColThreads),

@@ -20,9 +20,9 @@ hipBLASLt GEMMs:
     merge copies);
   * the two linear layers are GEMMs (torch.addmm / mm); their weight
     gradients u^T dqkv and a^T dy, reductions over all B*T rows, are taken
-    as a batch of GEMMs over row blocks with fp32 results (split K) that are
-    then added in fp32 and rounded once, because a single GEMM with a short
-    output and a long reduction fills few compute units;
+    as a batch of GEMMs over row blocks with fp32 results (split K) that the
+    library's column sum adds in fp32 and rounds once, because a single GEMM
+    with a short output and a long reduction fills few compute units;
   * the bias gradients are the library's column sums (attn_colsum).
 Other shapes use torch's LayerNorm and autograd around the attention op
 (contiguous [B, H, T, D] copies when the head dim has no strided kernel).
@@ -40,7 +40,8 @@ from . import (attn_bwd_strided, attn_fwd_strided, causal_attention, causal_atte
 
 def _weight_grad(a: torch.Tensor, g: torch.Tensor) -> torch.Tensor:
     """a^T g for a [N, K], g [N, M]: split K over row blocks (a batch of GEMMs
-    with fp32 results), the blocks added in fp32 and rounded once to a's dtype.
+    with fp32 results), the blocks added in order in fp32 (attn_colsum on the
+    fp32 partials) and rounded once to bf16.
     Block counts measured at the sublayer's shapes: 2 for the c_attn weight
     (K x M = 768 x 2304), 16 for c_proj (768 x 768)."""
     N, K = a.shape
@@ -52,7 +53,10 @@ def _weight_grad(a: torch.Tensor, g: torch.Tensor) -> torch.Tensor:
         return torch.mm(a.t(), g)
     ap = a.view(parts, N // parts, K).transpose(1, 2)
     gp = g.view(parts, N // parts, M)
-    return torch.bmm(ap, gp, out_dtype=torch.float32).sum(0).to(a.dtype)
+    part = torch.bmm(ap, gp, out_dtype=torch.float32)  # [parts, K, M]
+    out = torch.empty((K, M), dtype=a.dtype, device=a.device)
+    colsum(part.view(parts, K * M), out.view(K * M))  # the blocks in order, one rounding
+    return out
 
 
 def _bias_grad(g: torch.Tensor) -> torch.Tensor:

@@ -370,10 +370,13 @@ int attn_bwd_strided_rope(attn_view_t q, attn_view_t k, attn_view_t q_rot, attn_
  *   other (ATTN_ERR_ALIAS).
  *
  * attn_colsum:  out[j] = sum_r x[r][j] (the gradient of a bias added to every
- *   row), for N rows of M bf16 elements `stride` apart; out bf16 [M].
- *   8 <= M, M % 8 == 0, stride >= M and a multiple of 8; workspace of at least
- *   attn_colsum_workspace_bytes(N, M) bytes.  Fixed summation order: blocks of
- *   max(8, ceil(N / 64)) rows, then the blocks in a fixed order.
+ *   row), for N rows of M elements `stride` apart; out bf16 [M], each sum
+ *   rounded once.  8 <= M <= 2^30, M % 8 == 0, stride >= M and a multiple of 8.
+ *   dtype ATTN_BF16: workspace of at least attn_colsum_workspace_bytes(N, M)
+ *   bytes; fixed summation order: blocks of max(8, ceil(N / 128)) rows, then
+ *   the blocks in a fixed order.  dtype ATTN_F32 (a few rows, such as the
+ *   partial products of a weight gradient split over row blocks): the rows
+ *   are added in order, no workspace (it may be NULL).
  */
 size_t attn_layernorm_workspace_bytes(int N, int C);
 int attn_layernorm_fwd(const void* x, const void* g, const void* b, void* y, int N, int C,

@@ -581,11 +581,11 @@ def _cs(x=P[0], out=P[1], ws=P[2], ws_bytes=None, N=N_, M=C_, stride=C_, dtype=1
 
 def test_row_pass_workspace_bytes():
     # LayerNorm gradient: [dg | db] partials per 16 rows; column sums: per block
-    # of max(8, ceil(N / 64)) rows
+    # of max(8, ceil(N / 128)) rows
     assert _ln_ws(8192, 768) == 512 * 2 * 768 * 4
     assert _ln_ws(17, 8) == 2 * 2 * 8 * 4
-    assert _cs_ws(8192, 2304) == 64 * 2304 * 4
-    assert _cs_ws(8200, 8) == 64 * 8 * 4 and _cs_ws(33, 8) == 5 * 8 * 4
+    assert _cs_ws(8192, 2304) == 128 * 2304 * 4
+    assert _cs_ws(8200, 8) == 127 * 8 * 4 and _cs_ws(33, 8) == 5 * 8 * 4
     assert _ln_ws(0, 768) == 0 and _cs_ws(1, 0) == 0
 
 
@@ -620,3 +620,7 @@ def test_row_pass_validation_order_and_codes():
     assert _cs(out=P[0] + 64) == 8 and _cs(ws=P[1]) == 8
     # no residual term is allowed
     assert _ln_bwd(dres=None, dx=P[0]) == 8
+    # fp32 rows (split-K partials): no workspace needed, the other checks as for bf16
+    assert _cs(ws=None) == 1
+    assert _cs(dtype=0, ws=None, M=12, stride=16) == 2 and _cs(dtype=0, ws=None, stride=100) == 10
+    assert _cs(dtype=0, ws=None, x=P[0] + 8) == 5 and _cs(dtype=0, ws=None, out=P[0] + 64) == 8

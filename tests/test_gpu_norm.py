@@ -117,6 +117,20 @@ def test_colsum_matches_oracle(N, M, stride):
     _check("colsum", _np(out), oracle.colsum(_np(x)))
 
 
+@pytest.mark.parametrize("P,M", [(1, 8), (2, 768 * 2304), (16, 768 * 768), (5, 1032)])
+def test_colsum_of_fp32_rows_matches_oracle(P, M):
+    """The split-K epilogue of the weight gradients: a few fp32 rows added in
+    order and rounded once to bf16."""
+    import causal_head_self_amd as cat
+    _note(f"[colsum fp32] P={P} M={M}")
+    g = torch.Generator().manual_seed(51)
+    x = (torch.randn((P, M), generator=g) * 30.0).cuda()
+    out = torch.empty(M, dtype=torch.bfloat16, device="cuda")
+    cat.colsum(x, out)
+    torch.cuda.synchronize()
+    _check("colsum fp32", _np(out), oracle.colsum(x.double().cpu().numpy()))
+
+
 def test_row_passes_are_deterministic():
     import causal_head_self_amd as cat
     N, C = 1000, 768
