@@ -52,6 +52,9 @@ KERNEL_SOURCES = {
                "causal_head_self_amd/csrc/attn_device.h"],
     "rope": ["causal_head_self_amd/csrc/attn_rope.hip",
              "causal_head_self_amd/csrc/attn_device.h"],
+    "norm": ["causal_head_self_amd/csrc/attn_norm.hip",
+             "causal_head_self_amd/csrc/attn_device.h",
+             "causal_head_self_amd/sublayer.py"],
 }
 
 
