@@ -71,6 +71,25 @@ __device__ __forceinline__ void store8(bf16* p, const float (&v)[8])
     *(bf16x8*)p = t;
 }
 
+// Row chunks are loaded for every lane, from clamped addresses (a lane whose
+// chunk lies past C reloads the last one and counts it as zero), so the loads
+// are not under divergent branches and the wait for them comes only where the
+// values are used.
+template <int NCH>
+__device__ __forceinline__ void load_raw(const bf16* __restrict__ p, int lane, int nch,
+                                         bf16x8 (&r)[NCH])
+{
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) r[i] = *(const bf16x8*)(p + 8 * min(lane + 64 * i, nch - 1));
+}
+
+// Element e of chunk i as fp32, 0 past C.
+template <int NCH>
+__device__ __forceinline__ float val(const bf16x8 (&r)[NCH], int i, int e, bool ok)
+{
+    return ok ? (float)r[i][e] : 0.f;
+}
+
 // NCH: chunks of 8 per lane, ceil(C / 512).
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void layernorm_fwd_kernel(
@@ -81,18 +100,15 @@ __global__ __launch_bounds__(kThreads) void layernorm_fwd_kernel(
     const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (row >= N) return;
     const int nch = C >> 3;
-    const bf16* xr = x + (size_t)row * stride;
-    float v[NCH][8];
+    bf16x8 xr[NCH], gr[NCH], br[NCH];
+    load_raw<NCH>(x + (size_t)row * stride, lane, nch, xr);
+    load_raw<NCH>(g, lane, nch, gr);
+    load_raw<NCH>(b, lane, nch, br);
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nch) {
-            load8(xr + 8 * c, v[i]);
+    for (int i = 0; i < NCH; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s += v[i][e];
-        }
-    }
+        for (int e = 0; e < 8; ++e) s += val<NCH>(xr, i, e, lane + 64 * i < nch);
     const float inv_c = 1.0f / (float)C;
     const float mean = wave_sum(s) * inv_c;
     float q = 0.f;
@@ -101,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void layernorm_fwd_kernel(
         if (lane + 64 * i < nch)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float d = v[i][e] - mean;
+                const float d = (float)xr[i][e] - mean;
                 q = fmaf(d, d, q);
             }
     const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_c + eps);
@@ -110,11 +126,10 @@ __global__ __launch_bounds__(kThreads) void layernorm_fwd_kernel(
     for (int i = 0; i < NCH; ++i) {
         const int c = lane + 64 * i;
         if (c < nch) {
-            float gv[8], bv[8], o[8];
-            load8(g + 8 * c, gv);
-            load8(b + 8 * c, bv);
+            float o[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf((v[i][e] - mean) * rstd, gv[e], bv[e]);
+            for (int e = 0; e < 8; ++e)
+                o[e] = fmaf(((float)xr[i][e] - mean) * rstd, (float)gr[i][e], (float)br[i][e]);
             store8(yr + 8 * c, o);
         }
     }
@@ -124,24 +139,9 @@ __global__ __launch_bounds__(kThreads) void layernorm_fwd_kernel(
 // its wave j every kWaves-th of them from row j.  Each lane keeps the dg and db
 // partial sums of its columns over the wave's rows; the four waves add theirs
 // in LDS in wave order, and the workgroup writes [dg | db] (2C floats) to
-// part[w].  A wave loads the next row's x and dy before it works on the
-// current one, so that their latency overlaps that work.
-template <int NCH>
-__device__ __forceinline__ void load_row(const bf16* __restrict__ p, int lane, int nch,
-                                         float (&v)[NCH][8])
-{
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nch) {
-            load8(p + 8 * c, v[i]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-        }
-    }
-}
-
+// part[w].  A wave loads the next row's x and dy (the last row again when
+// there is none) before it works on the current one, so that their latency
+// overlaps that work.
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void layernorm_bwd_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ g, const bf16* __restrict__ dy,
@@ -154,45 +154,44 @@ __global__ __launch_bounds__(kThreads) void layernorm_bwd_kernel(
     const int wave = threadIdx.x >> 6;
     const int nch = C >> 3;
     const float inv_c = 1.0f / (float)C;
-    float gv[NCH][8], ag[NCH][8], ab[NCH][8];
-    load_row<NCH>(g, lane, nch, gv);
+    bf16x8 gr[NCH];
+    load_raw<NCH>(g, lane, nch, gr);
+    float ag[NCH][8], ab[NCH][8];
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
     const int r0 = blockIdx.x * rows_per_wg;
     const int r1 = min(N, r0 + rows_per_wg);
-    // with 8 chunks per lane the second set of row registers would spill: load
-    // each row as it comes instead
+    // with 8 chunks per lane a second set of row registers would spill: each
+    // row is then loaded as it comes
     constexpr bool kAhead = NCH <= 4;
-    float xv[NCH][8], dv[NCH][8], rv[NCH][8];
+    bf16x8 xr[NCH], dr[NCH], rr[NCH];
     int row = r0 + wave;
     if (kAhead && row < r1) {
-        load_row<NCH>(x + (size_t)row * stride, lane, nch, xv);
-        load_row<NCH>(dy + (size_t)row * stride, lane, nch, dv);
+        load_raw<NCH>(x + (size_t)row * stride, lane, nch, xr);
+        load_raw<NCH>(dy + (size_t)row * stride, lane, nch, dr);
     }
     for (; row < r1; row += kWaves) {
         const size_t off = (size_t)row * stride;
         if (!kAhead) {
-            load_row<NCH>(x + off, lane, nch, xv);
-            load_row<NCH>(dy + off, lane, nch, dv);
+            load_raw<NCH>(x + off, lane, nch, xr);
+            load_raw<NCH>(dy + off, lane, nch, dr);
         }
         // dres of this row is used last: loaded before the next row's x and dy,
         // it can be waited for while those are still in flight
-        if (dres) load_row<NCH>(dres + off, lane, nch, rv);
-        // the next row's operands (past C every value is 0, and so is every term
-        // below that multiplies dy)
-        float xn[NCH][8], dn[NCH][8];
-        const int nxt = row + kWaves;
-        if (kAhead && nxt < r1) {
-            load_row<NCH>(x + (size_t)nxt * stride, lane, nch, xn);
-            load_row<NCH>(dy + (size_t)nxt * stride, lane, nch, dn);
+        if (dres) load_raw<NCH>(dres + off, lane, nch, rr);
+        const size_t nxt = (size_t)min(row + kWaves, r1 - 1) * stride;
+        bf16x8 xn[NCH], dn[NCH];
+        if (kAhead) {
+            load_raw<NCH>(x + nxt, lane, nch, xn);
+            load_raw<NCH>(dy + nxt, lane, nch, dn);
         }
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < NCH; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s += xv[i][e];
+            for (int e = 0; e < 8; ++e) s += val<NCH>(xr, i, e, lane + 64 * i < nch);
         const float mean = wave_sum(s) * inv_c;
         float q = 0.f;
 #pragma unroll
@@ -200,23 +199,26 @@ __global__ __launch_bounds__(kThreads) void layernorm_bwd_kernel(
             if (lane + 64 * i < nch)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float d = xv[i][e] - mean;
+                    const float d = (float)xr[i][e] - mean;
                     q = fmaf(d, d, q);
                 }
         const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_c + eps);
         float s1 = 0.f, s2 = 0.f;
+        float xh[NCH][8];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i)
+        for (int i = 0; i < NCH; ++i) {
+            const bool ok = lane + 64 * i < nch;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float xh = (xv[i][e] - mean) * rstd;
-                const float ge = dv[i][e] * gv[i][e];
-                xv[i][e] = xh;
+                xh[i][e] = ((float)xr[i][e] - mean) * rstd;
+                const float d = val<NCH>(dr, i, e, ok);  // 0 past C: so is every term below
+                const float ge = d * (float)gr[i][e];
                 s1 += ge;
-                s2 = fmaf(ge, xh, s2);
-                ag[i][e] = fmaf(dv[i][e], xh, ag[i][e]);
-                ab[i][e] += dv[i][e];
+                s2 = fmaf(ge, xh[i][e], s2);
+                ag[i][e] = fmaf(d, xh[i][e], ag[i][e]);
+                ab[i][e] += d;
             }
+        }
         const float m1 = wave_sum(s1) * inv_c;
         const float m2 = wave_sum(s2) * inv_c;
 #pragma unroll
@@ -226,20 +228,18 @@ __global__ __launch_bounds__(kThreads) void layernorm_bwd_kernel(
                 float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    o[e] = rstd * (dv[i][e] * gv[i][e] - m1 - xv[i][e] * m2);
-                    if (dres) o[e] += rv[i][e];
+                    o[e] = rstd * ((float)dr[i][e] * (float)gr[i][e] - m1 - xh[i][e] * m2);
+                    if (dres) o[e] += (float)rr[i][e];
                 }
                 store8(dx + off + 8 * c, o);
             }
         }
-        if (kAhead && nxt < r1) {
+        if (kAhead) {
 #pragma unroll
-            for (int i = 0; i < NCH; ++i)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xv[i][e] = xn[i][e];
-                    dv[i][e] = dn[i][e];
-                }
+            for (int i = 0; i < NCH; ++i) {
+                xr[i] = xn[i];
+                dr[i] = dn[i];
+            }
         }
     }
     // the workgroup's column partials: waves 0..3 in turn
