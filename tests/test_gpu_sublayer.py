@@ -1,5 +1,9 @@
 """GPU parity of the pre-norm attention sublayer (LayerNorm -> c_attn -> causal
-MHA (HIP kernels) -> c_proj + residual) against the fp64 oracle sublayer.
+MHA -> c_proj + residual) against the fp64 oracle sublayer.  In bf16 at head
+dim 64 the step is one autograd function: the HIP LayerNorm forward and
+gradient (with the residual term), the attention kernels on strided views,
+hipBLASLt GEMMs with split-K weight gradients and HIP column sums for the bias
+gradients; every output and parameter gradient is compared.
 
 x, y and dx keep the plain bf16 tolerance 2e-2.  Tensors that are not unit
 variance (weight and bias gradients, summed over B*T rows, and the LN-weight
