@@ -73,6 +73,14 @@ def test_sublayer_small():
     _compare(got, ref)
 
 
+def test_sublayer_head_dim_32_takes_the_generic_path():
+    """Head dim 32 has no strided kernel: torch's LayerNorm and autograd around
+    the contiguous attention op (causal_attention on [B, H, T, D] copies)."""
+    cfg = workloads.SublayerConfig("d32", B=2, T=70, C=64, H=2, n_layer=12, dtype="bf16")
+    got, ref = _run(cfg, cfg.B)
+    _compare(got, ref)
+
+
 def test_sublayer_full_config():
     cfg = workloads.SUBLAYER_CONFIG
     got, ref = _run(cfg, cfg.B)
