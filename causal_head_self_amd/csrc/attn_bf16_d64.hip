@@ -763,15 +763,18 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
 
     bf16x8 qreg[4 * NP], greg[4 * NP];
     float dsum = 0.f;
-    const bf16* qr = head_of(a.Q, bh, a.H) + (size_t)qrow * a.Q.st + 8 * hi;
-    const bf16* gr = head_of(a.dO, bh, a.H) + (size_t)qrow * a.dO.st + 8 * hi;
-    const bf16* orr = head_of(a.O, bh, a.H) + (size_t)qrow * a.O.st + 8 * hi;
+    // rows past T read row T-1: their P is 0 (lse = -inf below) and nothing of
+    // theirs is stored, and unconditional loads are all in flight at once
+    const int qld = min(qrow, T - 1);
+    const bf16* qr = head_of(a.Q, bh, a.H) + (size_t)qld * a.Q.st + 8 * hi;
+    const bf16* gr = head_of(a.dO, bh, a.H) + (size_t)qld * a.dO.st + 8 * hi;
+    const bf16* orr = head_of(a.O, bh, a.H) + (size_t)qld * a.O.st + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < 4 * NP; ++ks) {
-        qreg[ks] = valid ? *(const bf16x8*)(qr + 16 * ks) : zero_bf16x8();
-        greg[ks] = valid ? *(const bf16x8*)(gr + 16 * ks) : zero_bf16x8();
+        qreg[ks] = *(const bf16x8*)(qr + 16 * ks);
+        greg[ks] = *(const bf16x8*)(gr + 16 * ks);
         if constexpr (!kDeltaIn) {
-            const bf16x8 orow = valid ? *(const bf16x8*)(orr + 16 * ks) : zero_bf16x8();
+            const bf16x8 orow = *(const bf16x8*)(orr + 16 * ks);
 #pragma unroll
             for (int e = 0; e < 8; ++e) dsum = fmaf((float)greg[ks][e], (float)orow[e], dsum);
         }
@@ -994,12 +997,15 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     rows_load_async(i_hi, sR0);
 
     bf16x8 kreg[4 * NP], vreg[4 * NP];
-    const bf16* kr = head_of(a.K, bh, a.H) + (size_t)key * a.K.st + 8 * hi;
-    const bf16* vr = head_of(a.V, bh, a.H) + (size_t)key * a.V.st + 8 * hi;
+    // keys past T read key T-1: they are masked on every query and their dK, dV
+    // rows are not stored
+    const int kld = min(key, T - 1);
+    const bf16* kr = head_of(a.K, bh, a.H) + (size_t)kld * a.K.st + 8 * hi;
+    const bf16* vr = head_of(a.V, bh, a.H) + (size_t)kld * a.V.st + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < 4 * NP; ++ks) {
-        kreg[ks] = valid ? *(const bf16x8*)(kr + 16 * ks) : zero_bf16x8();
-        vreg[ks] = valid ? *(const bf16x8*)(vr + 16 * ks) : zero_bf16x8();
+        kreg[ks] = *(const bf16x8*)(kr + 16 * ks);
+        vreg[ks] = *(const bf16x8*)(vr + 16 * ks);
     }
     wait_async_copies();
     rows_finish(i_hi, sG0, sO0, sR0);
