@@ -209,7 +209,10 @@ __device__ __forceinline__ void tiles_load_async(char* tile, const bf16* __restr
     if constexpr (NP == 2) tile_load_async(tile + kTileBytes, head + HD, st, row0, T, wave, tc);
 }
 
-__device__ __forceinline__ void wait_async_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima) as the builtin, which
+// the compiler's wait-count pass sees, so that it does not wait again later for
+// copies it cannot tell have landed
+__device__ __forceinline__ void wait_async_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ bf16x8 lds_row_read(const char* tile, int off)
 {
