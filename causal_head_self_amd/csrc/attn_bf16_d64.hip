@@ -173,12 +173,19 @@ struct TileCopy {
 // All addresses are a wave-uniform base plus a 32-bit per-lane offset (the
 // scalar-base form of global_load_lds), which keeps 64-bit address arithmetic
 // out of the vector registers.
+// kOpaque: take the lane index through an opaque copy, so that the per-lane
+// offsets are recomputed at every copy instead of being kept live across the
+// loops.  The kernels that run short of registers (dropout, head dim 128) use
+// it: there the compiler otherwise spills those offsets, and reloading them
+// makes each copy wait for the one issued before it.
+template <bool kOpaque>
 __device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restrict__ head, int st,
                                                 int row0, int T, int wave, const TileCopy& tc)
 {
     const char* base = (const char*)head;
     const uint32_t sb = (uint32_t)st * 2u;
-    const int lane = __lane_id();
+    int lane = __lane_id();
+    if constexpr (kOpaque) asm volatile("" : "+v"(lane));
     if (row0 + kTile <= T) {  // wave-uniform: every row exists
         const char* b = base + (size_t)row0 * sb;
 #pragma unroll
@@ -201,12 +208,12 @@ __device__ __forceinline__ void tile_load_async(char* tile, const bf16* __restri
 }
 
 // The NP panels of a tile: columns 64p.. of the head go to panel p.
-template <int NP>
+template <int NP, bool kOpaque = false>
 __device__ __forceinline__ void tiles_load_async(char* tile, const bf16* __restrict__ head, int st,
                                                  int row0, int T, int wave, const TileCopy& tc)
 {
-    tile_load_async(tile, head, st, row0, T, wave, tc);
-    if constexpr (NP == 2) tile_load_async(tile + kTileBytes, head + HD, st, row0, T, wave, tc);
+    tile_load_async<kOpaque>(tile, head, st, row0, T, wave, tc);
+    if constexpr (NP == 2) tile_load_async<kOpaque>(tile + kTileBytes, head + HD, st, row0, T, wave, tc);
 }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima) as the builtin, which
@@ -568,8 +575,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const int lo = max(0, qt * kRowsPerWG - W + 1) / kTile;  // the workgroup's first tile
     const int first_w = max(0, q0w - W + 1) / kTile;        // the wave's first tile
 
-    tiles_load_async<NP>(sK0, Kh, K.st, lo * kTile, T, wave, tc);
-    tiles_load_async<NP>(sV0, Vh, V.st, lo * kTile, T, wave, tc);
+    tiles_load_async<NP, kDrop || NP == 2>(sK0, Kh, K.st, lo * kTile, T, wave, tc);
+    tiles_load_async<NP, kDrop || NP == 2>(sV0, Vh, V.st, lo * kTile, T, wave, tc);
 
     bf16x8 qreg[4 * NP];
     const bf16* qh = head_of(Q, bh, H);
@@ -684,8 +691,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         wait_async_copies();
         __syncthreads();
         if (j + 1 < n_kv) {
-            tiles_load_async<NP>(kl, Kh, K.st, (j + 1) * kTile, T, wave, tc);
-            tiles_load_async<NP>(vl, Vh, V.st, (j + 1) * kTile, T, wave, tc);
+            tiles_load_async<NP, kDrop || NP == 2>(kl, Kh, K.st, (j + 1) * kTile, T, wave, tc);
+            tiles_load_async<NP, kDrop || NP == 2>(vl, Vh, V.st, (j + 1) * kTile, T, wave, tc);
         }
         // a tile needs the mask if it crosses the diagonal or the window's lower edge
         if (j >= first_w && j <= last_w)
@@ -761,8 +768,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     const int lo = max(0, qt * kRowsPerWG - W + 1) / kTile;  // the workgroup's first tile
     const int first_w = max(0, q0w - W + 1) / kTile;        // the wave's first tile
 
-    tiles_load_async<NP>(sK0, Kh, a.K.st, lo * kTile, T, wave, tc);
-    tiles_load_async<NP>(sV0, Vh, a.V.st, lo * kTile, T, wave, tc);
+    tiles_load_async<NP, kDrop || NP == 2>(sK0, Kh, a.K.st, lo * kTile, T, wave, tc);
+    tiles_load_async<NP, kDrop || NP == 2>(sV0, Vh, a.V.st, lo * kTile, T, wave, tc);
 
     bf16x8 qreg[4 * NP], greg[4 * NP];
     float dsum = 0.f;
@@ -866,8 +873,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
         wait_async_copies();
         __syncthreads();
         if (j + 1 < n_kv) {
-            tiles_load_async<NP>(kl, Kh, a.K.st, (j + 1) * kTile, T, wave, tc);
-            tiles_load_async<NP>(vl, Vh, a.V.st, (j + 1) * kTile, T, wave, tc);
+            tiles_load_async<NP, kDrop || NP == 2>(kl, Kh, a.K.st, (j + 1) * kTile, T, wave, tc);
+            tiles_load_async<NP, kDrop || NP == 2>(vl, Vh, a.V.st, (j + 1) * kTile, T, wave, tc);
         }
         if (j < first_w || j > last_w) return;
         const int k0 = j * kTile;
@@ -994,9 +1001,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
 
     // Tiles are visited from the last one down to the diagonal, so that every item
     // of a head streams the same tile at about the same time (they share it in L2).
-    tiles_load_async<NP>(sQ0, Qh, a.Q.st, i_hi * kTile, T, wave, tc);
-    tiles_load_async<NP>(sG0, Gh, a.dO.st, i_hi * kTile, T, wave, tc);
-    if (kDeltaFromO) tiles_load_async<NP>(sO0, Oh, a.O.st, i_hi * kTile, T, wave, tc);
+    tiles_load_async<NP, kDrop || NP == 2>(sQ0, Qh, a.Q.st, i_hi * kTile, T, wave, tc);
+    tiles_load_async<NP, kDrop || NP == 2>(sG0, Gh, a.dO.st, i_hi * kTile, T, wave, tc);
+    if (kDeltaFromO) tiles_load_async<NP, kDrop || NP == 2>(sO0, Oh, a.O.st, i_hi * kTile, T, wave, tc);
     rows_load_async(i_hi, sR0);
 
     bf16x8 kreg[4 * NP], vreg[4 * NP];
@@ -1126,9 +1133,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         __syncthreads();
         const bool more = i > i0;
         if (more) {
-            tiles_load_async<NP>(ql, Qh, a.Q.st, (i - 1) * kTile, T, wave, tc);
-            tiles_load_async<NP>(gl, Gh, a.dO.st, (i - 1) * kTile, T, wave, tc);
-            if (kDeltaFromO) tiles_load_async<NP>(ol, Oh, a.O.st, (i - 1) * kTile, T, wave, tc);
+            tiles_load_async<NP, kDrop || NP == 2>(ql, Qh, a.Q.st, (i - 1) * kTile, T, wave, tc);
+            tiles_load_async<NP, kDrop || NP == 2>(gl, Gh, a.dO.st, (i - 1) * kTile, T, wave, tc);
+            if (kDeltaFromO) tiles_load_async<NP, kDrop || NP == 2>(ol, Oh, a.O.st, (i - 1) * kTile, T, wave, tc);
             rows_load_async(i - 1, rl);
         }
         if (i >= first_w && i <= last_w) {
