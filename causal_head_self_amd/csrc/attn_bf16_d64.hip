@@ -744,7 +744,7 @@ struct BwdParams {
 // formed here from the item's O and dO rows and stored.
 template <int NP, bool kDrop, bool kKeep = false, bool kRope = false, bool kDeltaIn = false>
 __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char* sK0, char* sK1,
-                                        char* sV0, char* sV1,
+                                        char* sV0, char* sV1, float (*sW0)[kTile], float (*sW1)[kTile],
                                         const RopeArg<kRope>& rp = RopeArg<kRope>{})
 {
     const int BH = a.BH, T = a.T;
@@ -768,8 +768,22 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     const int lo = max(0, qt * kRowsPerWG - W + 1) / kTile;  // the workgroup's first tile
     const int first_w = max(0, q0w - W + 1) / kTile;        // the wave's first tile
 
+    // Stored keep bits travel with the tiles: for 64-key tile j each wave copies
+    // the words of its 32 queries for key columns 2j (lanes 0-31) and 2j + 1
+    // (lanes 32-63) into row `wave` of a keep buffer (sW0 / sW1), 4 bytes per
+    // lane; a word read from memory right before its use would wait for every
+    // copy in flight.  Rows past T and columns past the last read the last ones.
+    auto keep_load_async = [&](int j, float (*wb)[kTile]) {
+        if constexpr (kKeep) {
+            const int wcol = min(2 * j + hi, (T + 31) / 32 - 1);
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(a.dr.keep + keep_index(bh, wcol, min(q0w + li, T - 1), T)),
+                (__attribute__((address_space(3))) void*)wb[wave], 4, 0, 0);
+        }
+    };
     tiles_load_async<NP, kDrop || NP == 2>(sK0, Kh, a.K.st, lo * kTile, T, wave, tc);
     tiles_load_async<NP, kDrop || NP == 2>(sV0, Vh, a.V.st, lo * kTile, T, wave, tc);
+    keep_load_async(lo, sW0);
 
     bf16x8 qreg[4 * NP], greg[4 * NP];
     float dsum = 0.f;
@@ -808,7 +822,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
     for (int dt = 0; dt < 2 * NP; ++dt) dqacc[dt] = f32x16{};
 
     // keys 32h .. 32h+31 of tile j: S^T, dP^T - Delta, dS^T, dQ^T += K^T dS^T
-    auto half = [&](int h, bool diag, int k0, const char* kc, const char* vc) {
+    auto half = [&](int h, bool diag, int k0, const char* kc, const char* vc,
+                    const float (*wc)[kTile]) {
         // dP^T - Delta (without dropout), or dP^T alone, to be masked first
         f32x16 sv = f32x16{}, pv = kDrop ? f32x16{} : ndl;
 #pragma unroll
@@ -832,9 +847,8 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
             // dS = P (keep * keep_scale * dP - Delta).  Lane half hi draws keys
             // 16hi .. 16hi+15 of the half; w has bit b for key 32h + b.
             uint32_t w;
-            if constexpr (kKeep) {  // stored by the forward
-                const uint32_t* words = a.dr.keep + keep_index(bh, (k0 + 32 * h) / 32, 0, T);
-                w = valid ? words[(uint32_t)qrow] : 0u;
+            if constexpr (kKeep) {  // stored by the forward, staged with the tile
+                w = valid ? ((const uint32_t*)wc[wave])[32 * h + li] : 0u;
             } else {
                 const int blk0 = (k0 + 32 * h) / 8 + 2 * hi;
                 const uint32_t own = drop_bits8(a.dr, bh, qrow, blk0) |
@@ -867,27 +881,30 @@ __device__ __forceinline__ void dq_item(const BwdParams& a, int bh, int qt, char
         }
     };
 
-    // after the barrier K(j), V(j) sit in kc, vc; every wave is done with tile j-1
-    // (in kl, vl), whose buffers are refilled with tile j+1.
-    auto step = [&](int j, const char* kc, const char* vc, char* kl, char* vl) {
+    // after the barrier K(j), V(j) (and its keep words) sit in kc, vc (wc); every
+    // wave is done with tile j-1 (in kl, vl, wl), whose buffers are refilled with
+    // tile j+1.
+    auto step = [&](int j, const char* kc, const char* vc, const float (*wc)[kTile], char* kl,
+                    char* vl, float (*wl)[kTile]) {
         wait_async_copies();
         __syncthreads();
         if (j + 1 < n_kv) {
             tiles_load_async<NP, kDrop || NP == 2>(kl, Kh, a.K.st, (j + 1) * kTile, T, wave, tc);
             tiles_load_async<NP, kDrop || NP == 2>(vl, Vh, a.V.st, (j + 1) * kTile, T, wave, tc);
+            keep_load_async(j + 1, wl);
         }
         if (j < first_w || j > last_w) return;
         const int k0 = j * kTile;
         // masked: the diagonal tile and tiles crossing the window's lower edge
         const bool diag = j == last_w || k0 <= q0w + 31 - W;
-        half(0, diag, k0, kc, vc);
+        half(0, diag, k0, kc, vc, wc);
         // keys 32..63 of the diagonal tile matter only if a query of the wave reaches them
-        if (j < last_w || k0 + 32 <= q0w + 31) half(1, diag, k0, kc, vc);
+        if (j < last_w || k0 + 32 <= q0w + 31) half(1, diag, k0, kc, vc, wc);
     };
 
     for (int j = lo; j < n_kv; j += 2) {
-        step(j, sK0, sV0, sK1, sV1);
-        if (j + 1 < n_kv) step(j + 1, sK1, sV1, sK0, sV0);
+        step(j, sK0, sV0, sW0, sK1, sV1, sW1);
+        if (j + 1 < n_kv) step(j + 1, sK1, sV1, sW1, sK0, sV0, sW0);
     }
 
     if constexpr (kRope) {  // through the prologue's transposed Jacobian (every lane takes part)
@@ -962,6 +979,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     // past T) and -Delta (0 past T); with kDeltaFromO every wave forms -Delta of
     // the 16 rows it copied from dO and O (4 lanes per row).  The next barrier
     // publishes them.
+    // With stored keep bits, each wave also copies the words of its 32 keys for
+    // the tile's 64 queries into row 2 + wave (a word read from memory right
+    // before its use would wait for every copy in flight).
     auto rows_load_async = [&](int i, float (*rt)[kTile]) {
         const uint32_t o = (uint32_t)min(i * kTile + lane, T - 1) * 4u;
         if (wave == 0)
@@ -970,6 +990,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         if (!kDeltaFromO && wave == 1)
             __builtin_amdgcn_global_load_lds((const void*)((const char*)Dh + o),
                                              (__attribute__((address_space(3))) void*)rt[1], 4, 0, 0);
+        if constexpr (kKeep) {
+            // keys past T (a wave of the last block) read the last word column
+            const int wcol = min(k0w / 32, (T + 31) / 32 - 1);
+            __builtin_amdgcn_global_load_lds(
+                (const void*)((const char*)(a.dr.keep + keep_index(bh, wcol, 0, T)) + o),
+                (__attribute__((address_space(3))) void*)rt[2 + wave], 4, 0, 0);
+        }
     };
     auto rows_finish = [&](int i, const char* gt, const char* ot, float (*rt)[kTile]) {
         // The lane-dependent addresses are recomputed here from an opaque copy of the
@@ -1021,8 +1048,8 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     rows_finish(i_hi, sG0, sO0, sR0);
     f32x16 dkacc[2 * NP] = {}, dvacc[2 * NP] = {};
 
-    // Dropout: the keep bits of a half are drawn at the end of the half before
-    // it (and those of the first half before the loop), when its S and dP
+    // Drawn dropout bits: the keep bits of a half are drawn at the end of the half
+    // before it (and those of the first half before the loop), when its S and dP
     // accumulators are dead: drawn later, with them live, the draws spilled.
     // Halves run in this order: tiles from min(i_hi, last_w) down to first_w,
     // in each tile half 0 (if some query of it reaches a key of the wave) and
@@ -1031,14 +1058,18 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     auto runs_half0 = [&](int i) { return i > first_w || i * kTile + 31 >= k0w; };
     auto draw_half = [&](int i, int h) -> uint32_t {
         const int blk0 = k0w / 8 + 2 * hi, qd = i * kTile + 32 * h + li;
-        if constexpr (kKeep)  // stored by the forward: this lane half's 16 keys of the word
-            return qd < T ? (a.dr.keep[keep_index(bh, k0w / 32, 0, T) + (uint32_t)qd] >> (16 * hi)) & 0xFFFFu
-                          : 0u;
-        else
-            return drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
+        return drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
+    };
+    // Stored bits: this lane half's 16 keys of the word of query 32h + li of the
+    // tile whose row buffer is rt (staged there by rows_load_async)
+    auto staged_half = [&](int i, int h, const float (*rt)[kTile]) -> uint32_t {
+        const uint32_t w = ((const uint32_t*)rt[2 + wave])[32 * h + li];
+        return i * kTile + 32 * h + li < T ? (w >> (16 * hi)) & 0xFFFFu : 0u;
     };
     uint32_t dbits = 0;  // keep bits of the half about to run
-    if constexpr (kDrop) {
+    if constexpr (kKeep) {  // the first tile's words are staged only by the step before it
+        if (i_hi >= first_w && i_hi <= last_w) dbits = staged_half(i_hi, runs_half0(i_hi) ? 0 : 1, sR0);
+    } else if constexpr (kDrop) {
         const int i_first = min(i_hi, last_w);
         if (i_first >= first_w) dbits = draw_half(i_first, runs_half0(i_first) ? 0 : 1);
     }
@@ -1116,7 +1147,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
                     dkacc[2 * p + dt] = mfma32x32x16(lds_tr_read(qc, o0, o1), sb, dkacc[2 * p + dt]);
                 }
         }
-        if constexpr (kDrop) {  // the bits of the next half to run (if any)
+        if constexpr (kKeep) {  // the second half's words are in this tile's buffer
+            if (h == 0) dbits = staged_half(q0 / kTile, 1, rc);
+        } else if constexpr (kDrop) {  // the bits of the next half to run (if any)
             const int i = q0 / kTile;
             if (h == 0)
                 dbits = draw_half(i, 1);
@@ -1149,6 +1182,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
         if (more) {
             wait_async_copies();
             rows_finish(i - 1, gl, ol, rl);
+            if constexpr (kKeep)  // tile i-1's words have landed: its first half's bits
+                if (i - 1 >= first_w && i - 1 <= last_w)
+                    dbits = staged_half(i - 1, runs_half0(i - 1) ? 0 : 1, rl);
         }
     };
 
@@ -1202,10 +1238,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char sK1[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV0[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sV1[NP * kTileBytes];
-    lds_poison(sK0, sK1, sV0, sV1);
+    __shared__ __attribute__((aligned(16))) float sW0[kKeep ? 4 : 1][kTile];  // keep words per wave
+    __shared__ __attribute__((aligned(16))) float sW1[kKeep ? 4 : 1][kTile];
+    lds_poison(sK0, sK1, sV0, sV1, sW0, sW1);
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     dq_item<NP, kDrop, kKeep, kRope>(a, item % a.BH, n_qtiles - 1 - item / a.BH, sK0, sK1, sV0, sV1,
-                                     rp);
+                                     sW0, sW1, rp);
 }
 
 // dK, dV alone, from a Delta in memory.
@@ -1217,8 +1255,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char sQ1[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sG0[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sG1[NP * kTileBytes];
-    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];  // [-lse*log2e, -Delta] per row
-    __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    // [-lse*log2e, -Delta] per row, then (stored keep bits) each wave's keep words
+    __shared__ __attribute__((aligned(16))) float sR0[kKeep ? 6 : 2][kTile];
+    __shared__ __attribute__((aligned(16))) float sR1[kKeep ? 6 : 2][kTile];
     lds_poison(sQ0, sQ1, sG0, sG1, sR0, sR1);
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     dkdv_item<NP, false, kDrop, kKeep, kRope>(a, item % a.BH, item / a.BH, sQ0, sQ1, sG0, sG1,
@@ -1244,8 +1283,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     __shared__ __attribute__((aligned(1024))) char s3[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char s4[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char s5[kTileBytes];
-    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];
-    __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    // row values, then (stored keep bits) each wave's keep words: rows 2..5 serve
+    // the dK/dV items and, as the keep buffers, the dQ items
+    __shared__ __attribute__((aligned(16))) float sR0[kKeep ? 6 : 2][kTile];
+    __shared__ __attribute__((aligned(16))) float sR1[kKeep ? 6 : 2][kTile];
     lds_poison(s0, s1, s2, s3, s4, s5, sR0, sR1);
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     const int BH = a.BH;
@@ -1253,7 +1294,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     if (r < BH)
         dkdv_item<1, true, kDrop, kKeep, kRope>(a, r, level, s0, s1, s2, s3, s4, s5, sR0, sR1, rp);
     else
-        dq_item<1, kDrop, kKeep, kRope>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3, rp);
+        dq_item<1, kDrop, kKeep, kRope>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3, sR0 + 2,
+                                        sR1 + 2, rp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1307,8 +1349,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(1024))) char s1[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char s2[NP * kTileBytes];
     __shared__ __attribute__((aligned(1024))) char s3[NP * kTileBytes];
-    __shared__ __attribute__((aligned(16))) float sR0[2][kTile];
-    __shared__ __attribute__((aligned(16))) float sR1[2][kTile];
+    __shared__ __attribute__((aligned(16))) float sR0[kKeep ? 6 : 2][kTile];
+    __shared__ __attribute__((aligned(16))) float sR1[kKeep ? 6 : 2][kTile];
     lds_poison(s0, s1, s2, s3, sR0, sR1);
     const int item = item_of(blockIdx.x, gridDim.x, n_cu);
     const int BH = a.BH;
@@ -1317,7 +1359,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         dkdv_item<NP, false, kDrop, kKeep, kRope>(a, r, level, s0, s1, s2, s3, nullptr, nullptr, sR0,
                                                   sR1, rp);
     else
-        dq_item<NP, kDrop, kKeep, kRope, true>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3, rp);
+        dq_item<NP, kDrop, kKeep, kRope, true>(a, r - BH, n_blocks - 1 - level, s0, s1, s2, s3,
+                                               sR0 + 2, sR1 + 2, rp);
 }
 
 #ifndef CATTN_D64_KERNELS_ONLY
