@@ -128,6 +128,16 @@ __device__ __forceinline__ uint32_t drop_bits8(const Dropout& dr, int bh, int i,
     return b;
 }
 
+// x through an empty asm statement: the compiler cannot treat values computed
+// from the result as loop-invariant, so it recomputes them where they are used
+// instead of hoisting them out of a loop (where they may be kept live across the
+// tiles and spilled)
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // The value of x held by lane l ^ 32 (v_permlane32_swap; which of the two
 // results is the other lane's is told apart by comparing with x itself).
 __device__ __forceinline__ uint32_t other_half_u32(uint32_t x)
@@ -635,8 +645,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         uint32_t kw_lo = 0, kw_hi = 0;
         if constexpr (kDrop) {
             uint32_t own = 0;
+            if constexpr (kKeep && NP == 1) {
+                // counters through opaque copies in the head-dim-64 kernel with
+                // stored bits only: there the per-lane Philox terms the compiler
+                // hoists out of the tile loop were spilled; elsewhere recomputing
+                // them costs more than keeping them
+                const int qo = opaque(qrow), bo = opaque(8 * j + 4 * hi);
 #pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) own |= drop_bits8(dr, bh, qrow, 8 * j + 4 * hi + m4) << (8 * m4);
+                for (int m4 = 0; m4 < 4; ++m4) own |= drop_bits8(dr, bh, qo, bo + m4) << (8 * m4);
+            } else {
+#pragma unroll
+                for (int m4 = 0; m4 < 4; ++m4) own |= drop_bits8(dr, bh, qrow, 8 * j + 4 * hi + m4) << (8 * m4);
+            }
             const uint32_t oth = other_half_u32(own);
             kw_lo = hi ? oth : own;
             kw_hi = hi ? own : oth;
@@ -1062,9 +1082,14 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     };
     // Stored bits: this lane half's 16 keys of the word of query 32h + li of the
     // tile whose row buffer is rt (staged there by rows_load_async)
+    // (lane-dependent addresses from an opaque copy of the lane index, recomputed
+    // here rather than kept live across the loop, as in rows_finish)
     auto staged_half = [&](int i, int h, const float (*rt)[kTile]) -> uint32_t {
-        const uint32_t w = ((const uint32_t*)rt[2 + wave])[32 * h + li];
-        return i * kTile + 32 * h + li < T ? (w >> (16 * hi)) & 0xFFFFu : 0u;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int l32 = ln & 31;
+        const uint32_t w = ((const uint32_t*)rt[2 + wave])[32 * h + l32];
+        return i * kTile + 32 * h + l32 < T ? (w >> (16 * (ln >> 5))) & 0xFFFFu : 0u;
     };
     uint32_t dbits = 0;  // keep bits of the half about to run
     if constexpr (kKeep) {  // the first tile's words are staged only by the step before it
