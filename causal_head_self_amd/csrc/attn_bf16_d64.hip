@@ -1078,7 +1078,16 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
     auto runs_half0 = [&](int i) { return i > first_w || i * kTile + 31 >= k0w; };
     auto draw_half = [&](int i, int h) -> uint32_t {
         const int blk0 = k0w / 8 + 2 * hi, qd = i * kTile + 32 * h + li;
-        return drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
+        if constexpr (NP == 2) {
+            // head dim 128: the key block through an opaque copy.  Hoisted out of
+            // the tile loop, the Philox terms of this lane's fixed block make the
+            // compiler spill resident rows, reloaded (waiting for the copies in
+            // flight) every half; at head dim 64 recomputing them costs more.
+            const int bo = opaque(blk0);
+            return drop_bits8<false>(a.dr, bh, qd, bo) | (drop_bits8<false>(a.dr, bh, qd, bo + 1) << 8);
+        } else {
+            return drop_bits8<false>(a.dr, bh, qd, blk0) | (drop_bits8<false>(a.dr, bh, qd, blk0 + 1) << 8);
+        }
     };
     // Stored bits: this lane half's 16 keys of the word of query 32h + li of the
     // tile whose row buffer is rt (staged there by rows_load_async)
