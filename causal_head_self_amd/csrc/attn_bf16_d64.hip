@@ -1245,14 +1245,22 @@ __device__ __forceinline__ void dkdv_item(const BwdParams& a, int bh, int kb, ch
                             rp.pos0 + key, hi);
         return;
     }
-    if (valid) {
-        bf16* krow = head_of(a.dK, bh, a.H) + (size_t)key * a.dK.st;
-        bf16* vrow = head_of(a.dV, bh, a.H) + (size_t)key * a.dV.st;
+    // with dropout the lane's key and half are recomputed here from an opaque copy
+    // of the lane index (kept live across the loop, they were spilled)
+    int key_e = key, hi_e = hi;
+    if constexpr (kDrop) {
+        const int le = opaque(lane);
+        key_e = k0w + (le & 31);
+        hi_e = le >> 5;
+    }
+    if (kDrop ? key_e < T : valid) {
+        bf16* krow = head_of(a.dK, bh, a.H) + (size_t)key_e * a.dK.st;
+        bf16* vrow = head_of(a.dV, bh, a.H) + (size_t)key_e * a.dV.st;
 #pragma unroll
         for (int dt = 0; dt < 2 * NP; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int d = 32 * dt + 8 * g + 4 * hi;
+                const int d = 32 * dt + 8 * g + 4 * hi_e;
                 store_bf16x4(krow + d, dkacc[dt][4 * g] * scale, dkacc[dt][4 * g + 1] * scale,
                              dkacc[dt][4 * g + 2] * scale, dkacc[dt][4 * g + 3] * scale);
                 const float vs = kDrop ? a.dr.keep_scale : 1.0f;
