@@ -195,10 +195,11 @@ int attn_bwd_strided(attn_view_t q, attn_view_t k, attn_view_t v, attn_view_t o,
  *   keep:       uint32 words, [B*H][ceil(T/32)][T]: bit t of word (b*H + h, w, i)
  *               is the keep decision of query i and key 32 w + t (1 = kept).  The
  *               forward writes the words of the (query, 32-key block) pairs it
- *               visits and never writes the rest.  With a window the backward
- *               may read words the forward did not write, but only for pairs
- *               outside the window, whose weight is zero whatever the bit says,
- *               so the results do not depend on them.  The caller owns the
+ *               visits and never writes the rest.  The backward may read words
+ *               the forward did not write (in a tile that crosses the diagonal,
+ *               or with a window), but only for pairs the mask removes, whose
+ *               weight is zero whatever the bit says, so the results do not
+ *               depend on them.  The caller owns the
  *               buffer; 4-byte aligned; it must not overlap any other buffer of
  *               the call (ATTN_ERR_ALIAS).
  *   keep_bytes: its size, at least attn_dropout_keep_bytes(B, H, T)
