@@ -588,12 +588,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     tiles_load_async<NP, kDrop || NP == 2>(sK0, Kh, K.st, lo * kTile, T, wave, tc);
     tiles_load_async<NP, kDrop || NP == 2>(sV0, Vh, V.st, lo * kTile, T, wave, tc);
 
+    // rows past T read row T-1 (nothing of theirs is stored): unconditional loads
+    // are all in flight at once, where loads under a divergent branch went out one
+    // branch at a time
     bf16x8 qreg[4 * NP];
-    const bf16* qh = head_of(Q, bh, H);
+    const bf16* qr = head_of(Q, bh, H) + (size_t)min(qrow, T - 1) * Q.st + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 4 * NP; ++ks)
-        qreg[ks] = (qrow < T) ? *(const bf16x8*)(qh + (size_t)qrow * Q.st + 16 * ks + 8 * hi)
-                              : zero_bf16x8();
+    for (int ks = 0; ks < 4 * NP; ++ks) qreg[ks] = *(const bf16x8*)(qr + 16 * ks);
     if constexpr (kRope) {  // the query rows after the prologue, also kept for the backward
         rope_rows<NP>(qreg, rp, rp.pos0 + qrow, hi);
         if (qrow < T) {
